@@ -1,0 +1,132 @@
+// device.h -- gfx950 device helpers shared by the CSA/HCA kernels: storage-format
+// codecs (bf16, OCP fp8 e4m3fn, e2m1 + e8m0 block scales), MFMA wrappers, wave
+// reductions.  Internal header of the HIP library; not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csl {
+
+enum Fmt { F32 = 0, BF16 = 1, KV_PACKED = 2, MXFP4 = 3 };
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define CSL_LOG2E 1.4426950408889634f
+#define CSL_LN2 0.6931471805599453f
+
+// ---------------------------------------------------------------------------
+// Storage codecs.  Stored KV rows: the RoPE dims as bf16, then the remaining
+// dims as fp8 e4m3fn (mixed-precision KV cache).  Indexer operands may be MXFP4:
+// e2m1 nibbles (even element in the low nibble) with one e8m0 scale per 32.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// fp32 -> OCP e4m3fn, round to nearest even, saturating to +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a != a) return 0x7fu;
+    if (a < 0x1p-6f) {                       // subnormal range: quantum 2^-9
+        return sign | (uint32_t)rintf(a * 512.0f);  // 8 -> 0x08, the smallest normal
+    }
+    if (a >= 448.0f) return sign | 0x7eu;
+    const uint32_t au = __float_as_uint(a);
+    const int e = (int)(au >> 23) - 127;     // -6 .. 8
+    const uint32_t m = au & 0x7fffffu;
+    const uint32_t mr = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // 0..8, carry ok
+    uint32_t code = ((uint32_t)(e + 7) << 3) + mr;
+    if (code > 0x7eu) code = 0x7eu;
+    return sign | code;
+}
+
+// Value already divided by its block scale -> e2m1 code, nearest-even, saturating.
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne_sat(float x) {
+    const float a = fabsf(x);
+    uint32_t c;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 5;
+    else if (a <= 5.0f) c = 6;
+    else c = 7;
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// Shared exponent of an MXFP4 block: the smallest e with 6 * 2^e >= amax.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    int E;
+    const float f = frexpf(amax, &E);        // amax = f * 2^E, f in [0.5, 1)
+    int e = (f <= 0.75f) ? E - 3 : E - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 4 fp8 e4m3fn (one dword) -> 4 bf16 (two dwords).  The gfx950 conversion is the
+// OCP e4m3fn decode; every e4m3 value is exact in bf16, so truncation is exact.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).  -0 is
+// folded onto +0 first so that equal scores compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (layouts checked on gfx950):
+//  16x16x32 bf16 : A lane l = row l%16, k 8*(l/16)..+8; B lane l = col l%16, same k
+//  16x16x4  f32  : A lane l = row l%16, k = l/16;       B lane l = col l%16, k = l/16
+//  16x16x128 fp4 (scaled): A lane l = row l%16, k 32*(l/16)..+32 (16 bytes in dwords
+//                0..3, low nibble first), e8m0 scale (byte 0) for that 32-block.
+//  C (all three): lane l holds C[4*(l/16)+i][l%16], i = 0..3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f mfma_bf16(const u32x4& a, const u32x4& b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
+                                                   0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_fp4(const u32x4& a, const u32x4& b, int sa, int sb, v4f c) {
+    v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, sa, 0, sb);
+}
+
+// LDS transpose read (gfx950): within each 16-lane group, lane i receives element
+// (i % 4) of the 64-bit chunks read by source lanes 4*j + i/4, j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, 64); }
+
+}  // namespace csl

@@ -1,0 +1,149 @@
+"""GPU parity of csa_attend / hca_attend against the oracle (x-techcon article,
+section 2: CSA step 3 and the HCA subsection; mixed-precision KV rows).
+Tolerance: max-abs 2e-2 for bf16/fp8 inputs with fp32 accumulation; 1e-4 for the
+fp32 path (fp32 MFMA, fp32 probabilities)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_sparse_long_02_amd import gen, ops
+from tests.gpu_util import dev, host, max_abs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {O.F32: 1e-4, O.BF16: 2e-2, O.KV_PACKED: 2e-2}
+
+
+def _kv(fmt, B, N, d, r, seed):
+    x = gen.normal((B, N, d), seed)
+    return gen.store(x, fmt, r)
+
+
+def _q(fmt, B, Tq, H, d, seed):
+    q = gen.normal((B, Tq, H, d), seed)
+    return q if fmt == O.F32 else q.to(torch.bfloat16)
+
+
+def _oracle_q(q):
+    return host(q) if q.dtype == torch.float32 else host(q.view(torch.int16))
+
+
+CSA_CASES = [
+    # (name, fmt, B, Tq, H, d, r, N, k, W, nwin_rows, positions)
+    ("packed_decode", O.KV_PACKED, 2, 1, 64, 512, 64, 5000, 512, 128, 300, "end"),
+    ("packed_h128_tq3", O.KV_PACKED, 2, 3, 128, 512, 64, 3000, 256, 128, 300, "end"),
+    ("bf16_small", O.BF16, 2, 5, 8, 128, 0, 600, 64, 16, 100, "ragged"),
+    ("f32_cfg1", O.F32, 1, 64, 8, 128, 32, 512, 64, 128, 2048, "cfg1"),
+    ("packed_many_q", O.KV_PACKED, 4, 200, 16, 256, 64, 400, 40, 8, 64, "ragged"),  # nsplit = 1 path
+]
+
+
+def _positions(kind, B, Tq, last):
+    if kind == "end":
+        return gen.positions(B, Tq, last)
+    if kind == "cfg1":
+        return gen.positions(B, Tq, 2047)
+    rng = np.random.default_rng(9)
+    p = rng.integers(-1, last + 1, size=(B, Tq)).astype(np.int32)
+    p[0, 0] = 0
+    return torch.from_numpy(p)
+
+
+@pytest.mark.parametrize("case", CSA_CASES, ids=[c[0] for c in CSA_CASES])
+def test_csa_attend_parity(gpu, case):
+    name, fmt, B, Tq, H, d, r, N, k, W, nwin, pk = case
+    kvc = _kv(fmt, B, N, d, r, 500 + d)
+    kvw = _kv(fmt, B, nwin, d, r, 501 + d)          # ring buffer of nwin rows (pos0 = 0)
+    q = _q(fmt, B, Tq, H, d, 502 + d)
+    qpos = _positions(pk, B, Tq, 4 * N - 1).to(torch.int32)
+    rng = np.random.default_rng(503)
+    idx = np.sort(rng.integers(-1, N + 2, size=(B, Tq, k)), axis=-1).astype(np.int32)
+    idx[..., -3:] = -1                               # padding slots
+    scale = 1 / math.sqrt(d)
+    kw = dict(W=W, H=H, d=d, r=r, scale=scale)
+    go, gl = ops.csa_attend(dev(q), dev(kvc), dev(idx), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, kvw_pos0=0,
+                            kvw_rows=nwin, **kw)
+    torch.cuda.synchronize()
+    oo, ol = O.csa_attend(_oracle_q(q), O.F32 if fmt == O.F32 else O.BF16, host(kvc), fmt, N, idx, host(kvw), 0, nwin, host(qpos), **kw)
+    err = max_abs(host(go), oo)
+    assert err <= TOL[fmt], "%s: max-abs %.3g" % (name, err)
+    fin = np.isfinite(ol)
+    assert np.array_equal(fin, np.isfinite(host(gl)))
+    assert max_abs(host(gl)[fin], ol[fin]) <= 10 * TOL[fmt]
+    print("%s: max-abs %.3g" % (name, err))
+
+
+HCA_CASES = [
+    # (name, fmt, B, Tq, H, d, r, N, m, W, positions)
+    ("packed_decode", O.KV_PACKED, 3, 1, 64, 512, 64, 1200, 128, 128, "end"),
+    ("packed_ragged", O.KV_PACKED, 2, 4, 64, 512, 64, 700, 128, 128, "ragged"),
+    ("bf16_h8", O.BF16, 2, 6, 8, 128, 0, 300, 4, 32, "ragged"),
+    ("f32_h8", O.F32, 1, 5, 8, 128, 0, 200, 4, 64, "ragged"),
+]
+
+
+@pytest.mark.parametrize("case", HCA_CASES, ids=[c[0] for c in HCA_CASES])
+def test_hca_attend_parity(gpu, case):
+    name, fmt, B, Tq, H, d, r, N, m, W, pk = case
+    kvc = _kv(fmt, B, N, d, r, 600 + d)
+    L = N * m
+    kvw = _kv(fmt, B, L, d, r, 601 + d)            # linear window buffer over all positions
+    q = _q(fmt, B, Tq, H, d, 602 + d)
+    qpos = _positions(pk, B, Tq, L - 1).to(torch.int32)
+    scale = 1 / math.sqrt(d)
+    kw = dict(W=W, H=H, d=d, r=r, scale=scale)
+    go, gl = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, m=m, kvw_pos0=0,
+                            kvw_rows=L, **kw)
+    torch.cuda.synchronize()
+    oo, ol = O.hca_attend(_oracle_q(q), O.F32 if fmt == O.F32 else O.BF16, host(kvc), fmt, N, m, host(kvw), 0, L, host(qpos), **kw)
+    err = max_abs(host(go), oo)
+    assert err <= TOL[fmt], "%s: max-abs %.3g" % (name, err)
+    fin = np.isfinite(ol)
+    assert np.array_equal(fin, np.isfinite(host(gl)))
+    assert max_abs(host(gl)[fin], ol[fin]) <= 10 * TOL[fmt]
+    print("%s: max-abs %.3g" % (name, err))
+
+
+def test_csa_with_every_entry_equals_hca_on_gpu(gpu):
+    fmt, B, H, d, r, N, m, W = O.KV_PACKED, 2, 64, 512, 64, 300, 4, 128
+    kvc = _kv(fmt, B, N, d, r, 71)
+    kvw = _kv(fmt, B, 256, d, r, 72)
+    q = _q(fmt, B, 1, H, d, 73)
+    qpos = gen.positions(B, 1, N * m - 1).to(torch.int32)
+    idx = torch.arange(N, dtype=torch.int32).expand(B, 1, N).contiguous()
+    kw = dict(kvw_pos0=0, kvw_rows=256, W=W, H=H, d=d, r=r, scale=0.05)
+    a, la = ops.csa_attend(dev(q), dev(kvc), dev(idx), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, **kw)
+    b, lb = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, m=m, **kw)
+    torch.cuda.synchronize()
+    assert max_abs(host(a), host(b)) <= 1e-5
+    assert max_abs(host(la), host(lb)) <= 1e-5
+
+
+def test_empty_attended_set(gpu):
+    fmt, B, H, d = O.KV_PACKED, 1, 64, 512
+    kvc = _kv(fmt, B, 10, d, 64, 81)
+    q = _q(fmt, B, 2, H, d, 82)
+    idx = torch.full((B, 2, 16), -1, dtype=torch.int32)
+    qpos = torch.tensor([[5, 9]], dtype=torch.int32)
+    o, l = ops.csa_attend(dev(q), dev(kvc), dev(idx), dev(kvc), dev(qpos), kv_fmt=fmt, n_cap=10, kvw_pos0=0,
+                          kvw_rows=10, W=0, H=H, d=d, r=64, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+def test_attend_bf16_output_and_determinism(gpu):
+    fmt, B, H, d, r, N, m, W = O.KV_PACKED, 2, 64, 512, 64, 900, 128, 128
+    kvc = _kv(fmt, B, N, d, r, 91)
+    kvw = _kv(fmt, B, 200, d, r, 92)
+    q = _q(fmt, B, 1, H, d, 93)
+    qpos = gen.positions(B, 1, N * m - 1).to(torch.int32)
+    kw = dict(kv_fmt=fmt, n_cap=N, m=m, kvw_pos0=0, kvw_rows=200, W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    f1, l1 = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), **kw)
+    f2, l2 = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), **kw)
+    b1, _ = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), out_fmt=O.BF16, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2) and torch.equal(l1, l2)
+    assert torch.equal(b1, f1.to(torch.bfloat16))
