@@ -61,7 +61,7 @@ bool plan_index(int B, int Tq, int64_t n_cap, int k, int& S, int& nslices, int& 
     const int64_t target_blocks = 1024;
     const int64_t work = (n_cap > 0 ? n_cap : 1) * (int64_t)(B > 0 ? B : 1) * (Tq > 0 ? Tq : 1);
     const int64_t need = (work + target_blocks - 1) / target_blocks;
-    S = 256;
+    S = 512;   // at least one key per thread of the 512-thread scoring block
     while (S < need && S < 16384) S <<= 1;
     for (;;) {
         nslices = n_cap <= 0 ? 1 : (int)((n_cap + S - 1) / S);
@@ -72,17 +72,22 @@ bool plan_index(int B, int Tq, int64_t n_cap, int k, int& S, int& nslices, int& 
     }
 }
 
+int index_cst(int nslices, int kk) { return ((nslices * kk + 4095) / 4096) * 4096; }
+
 size_t index_ws(int B, int Tq, int S, int nslices, int kk) {
     (void)S;
     if (nslices <= 1) return 0;
-    return (size_t)B * Tq * nslices * kk * 8 + 256;
+    const size_t q = (size_t)B * Tq;
+    return q * index_cst(nslices, kk) * 8 + q * nslices * 4 + 512;
 }
 
 constexpr int ATT_TILE = 32;
 constexpr int ATT_MIN_RPS = 128;
 constexpr int ATT_MAX_SPLIT = 128;
 
-void plan_attend(int B, int Tq, int H, int64_t rows_max, int& nhb, int& nsplit, int& rps) {
+constexpr int ATT_MAX_CSA_RPS = 1536;   // rows of a CSA split whose indices are staged in LDS
+
+void plan_attend(int B, int Tq, int H, int64_t rows_max, bool csa, int& nhb, int& nsplit, int& rps) {
     nhb = (H + 63) / 64;
     const int64_t L = rows_max > 0 ? rows_max : 1;
     const int64_t total_q = (int64_t)B * Tq * nhb;
@@ -92,6 +97,7 @@ void plan_attend(int B, int Tq, int H, int64_t rows_max, int& nhb, int& nsplit, 
     int64_t r = (L + ns - 1) / ns;
     r = (r + ATT_TILE - 1) / ATT_TILE * ATT_TILE;
     if (r < ATT_MIN_RPS) r = ATT_MIN_RPS;
+    if (csa && r > ATT_MAX_CSA_RPS) r = ATT_MAX_CSA_RPS;
     rps = (int)r;
     nsplit = (int)((L + r - 1) / r);
 }
@@ -177,7 +183,8 @@ int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int
     if (d < 32 || d > 1024 || d % 32) return fail(CSL_EUNSUPPORTED, "%s: d = %d must be a multiple of 32 in [32, 1024]", fn, d);
     if (x_fmt != CSL_F32 && x_fmt != CSL_BF16) return fail(CSL_EINVAL, "%s: x_fmt must be F32 or BF16", fn);
     if (out_fmt < CSL_F32 || out_fmt > CSL_MXFP4) return fail(CSL_EINVAL, "%s: unknown out_fmt %d", fn, out_fmt);
-    if (out_fmt == CSL_KV_PACKED && (r < 0 || r > d || r % 8)) return fail(CSL_EINVAL, "%s: packed output needs r %% 8 == 0, 0 <= r <= d", fn);
+    if (out_fmt == CSL_KV_PACKED && (r < 0 || r > d || r % 8 || (d + r) % 16))
+        return fail(CSL_EINVAL, "%s: packed output needs r %% 8 == 0, (d + r) %% 16 == 0, 0 <= r <= d", fn);
     if (z_ch != 1 && z_ch != d) return fail(CSL_EINVAL, "%s: z_ch must be 1 or d", fn);
     if ((int64_t)n_e * m > ((int64_t)1 << 40)) return fail(CSL_EINVAL, "%s: entry range too large", fn);
     if (B == 0 || n_e == 0) { g_err.clear(); return CSL_OK; }
@@ -243,10 +250,12 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
     a.q_pos = q_pos; a.B = B; a.Tq = Tq; a.H_I = H_I; a.d_I = d_I; a.m = m; a.n_cap = n_cap; a.k = k;
     a.out_idx = out_idx; a.out_score = out_score;
     a.S = S; a.nslices = nslices; a.kk = kk;
+    a.cst = index_cst(nslices, kk);
     if (nslices > 1) {
-        const size_t nc = (size_t)B * Tq * nslices * kk;
+        const size_t nc = (size_t)B * Tq * a.cst;
         a.cand_key = (uint32_t*)ws;
-        a.cand_idx = (int32_t*)((uint8_t*)ws + ((nc * 4 + 255) & ~(size_t)255));
+        a.cand_idx = (int32_t*)((uint8_t*)ws + nc * 4);
+        a.tbound = (uint32_t*)((uint8_t*)ws + nc * 8);
     }
     return launched(csl::launch_index_topk(a, (hipStream_t)stream));
 }
@@ -254,7 +263,7 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max) {
     if (B < 0 || Tq < 0 || H < 1) return 0;
     int nhb, nsplit, rps;
-    plan_attend(B, Tq, H, rows_max, nhb, nsplit, rps);
+    plan_attend(B, Tq, H, rows_max, true, nhb, nsplit, rps);   // the CSA cap only adds splits
     return attend_ws(B, Tq, d, nhb, nsplit);
 }
 
@@ -268,7 +277,7 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
     if (rc) return rc;
     const int64_t rows_max = (idx ? (int64_t)k : n_cap) + W;
     int nhb, nsplit, rps;
-    plan_attend(B, Tq, H, rows_max, nhb, nsplit, rps);
+    plan_attend(B, Tq, H, rows_max, true, nhb, nsplit, rps);
     const size_t need = attend_ws(B, Tq, d, nhb, nsplit);
     if (B * (int64_t)Tq == 0) { g_err.clear(); return CSL_OK; }
     if (out_lse && !al4(out_lse)) return fail(CSL_EINVAL, "%s: out_lse misaligned", fn);

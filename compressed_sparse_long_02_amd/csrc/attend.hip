@@ -11,14 +11,18 @@
 //
 // Design (gfx950): a block owns one query token x 64 heads x one split of the
 // attended row list (CSA: the selected indices then the window; HCA: entries
-// 0..n(t)-1 then the window).  Rows are gathered 32 at a time into LDS as bf16
-// (fp8 -> bf16 with the hardware OCP conversion).  Each of the 4 waves owns 16
-// heads: S = Q.K^T with 16x16x32 bf16 MFMA (Q in registers, K fragments from LDS),
-// an online softmax on the accumulators, P staged through LDS, then O += P.V with
-// V fragments read from the same row-major tile by the gfx950 LDS transpose read,
-// so no transposed copy of V is ever written.  fp32 rows take the same path with
-// 16x16x4 f32 MFMA.  Splits write (o, lse) partials that k_attend_combine merges
-// in a fixed order (deterministic, no atomics).
+// 0..n(t)-1 then the window).  Rows are gathered 32 at a time with the direct
+// global->LDS loads of gfx950 (no staging registers), one tile ahead of the
+// compute, then converted once into a padded bf16 tile (fp8 -> bf16 with the
+// hardware OCP conversion).  Each of the 4 waves owns 16 heads: S = Q.K^T with
+// 16x16x32 bf16 MFMA (Q in registers, K fragments from LDS), an online softmax
+// on the accumulators with a lazy rescale, P staged through LDS, then O += P.V
+// with V fragments read from the same row-major tile by the gfx950 LDS transpose
+// read, so no transposed copy of V is ever written.  fp32 rows take the same path
+// with 16x16x4 f32 MFMA.  Splits write (o, lse) partials that k_attend_combine
+// merges in a fixed order (deterministic, no atomics).
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -36,24 +40,38 @@ __device__ __forceinline__ int64_t att_n_visible(int64_t t, int m, int64_t n_cap
 template <int D, int FMT>
 struct AttLds {
     static constexpr bool F32P = FMT == F32;
-    static constexpr int KSTR = F32P ? D + 4 : D + 8;          // elements per LDS row
+    static constexpr int KSTR = F32P ? D + 4 : D + 8;          // elements per K-tile row (bank padding)
     static constexpr int PSTR = F32P ? ATT_TILE + 4 : ATT_TILE + 8;
     static constexpr int ESZ = F32P ? 4 : 2;
-    static constexpr size_t KL_BYTES = (size_t)ATT_TILE * KSTR * ESZ;
-    static constexpr size_t PL_BYTES = (size_t)4 * 16 * PSTR * ESZ;
-    static constexpr size_t BYTES = KL_BYTES + PL_BYTES + ATT_TILE * (8 + 4);
+    static constexpr int KL_ELEMS = ATT_TILE * KSTR;
+    static constexpr int RAW_BYTES = ATT_TILE * D * (F32P ? 4 : 2);   // largest stored row: bf16 / fp32
+    static constexpr int PL_ELEMS = 4 * 16 * PSTR;
 };
+constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (host plan)
+
+// Position of key e (0..7) of an 8-key group inside P's LDS row: even keys first,
+// then odd ones, matching the row order of the transposed V reads below.
+__device__ __forceinline__ int p_perm(int key) { return (key & ~7) + ((key & 1) ? 4 + ((key & 7) >> 1) : ((key & 7) >> 1)); }
+
+constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
 
 template <int D, int FMT>
 __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     using L = AttLds<D, FMT>;
     constexpr bool F32P = L::F32P;
     constexpr int KSTR = L::KSTR, PSTR = L::PSTR;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* kl = smem;
-    uint8_t* pl = smem + L::KL_BYTES;
-    const uint8_t** rowptr = (const uint8_t**)(smem + L::KL_BYTES + L::PL_BYTES);
-    int* rowok = (int*)(smem + L::KL_BYTES + L::PL_BYTES + ATT_TILE * 8);
+    using KT = typename std::conditional<F32P, float, uint16_t>::type;
+    // separate LDS objects: the asynchronous global->LDS loads only ever write `raw`,
+    // which lets the compiler see that reads of the K tile and P do not alias them
+    __shared__ __attribute__((aligned(16))) KT kl_s[L::KL_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint8_t raw[L::RAW_BYTES];
+    __shared__ __attribute__((aligned(16))) KT pl_s[L::PL_ELEMS];
+    __shared__ const uint8_t* rowptr[2 * ATT_TILE];
+    __shared__ int rowok[2 * ATT_TILE];
+    __shared__ int sidx[ATT_MAX_SIDX];
+    uint8_t* kl = (uint8_t*)kl_s;
+    uint8_t* pl = (uint8_t*)pl_s;
+    const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
 
     const int sp = blockIdx.x, hb = blockIdx.y;
     const int64_t bq = blockIdx.z;
@@ -68,7 +86,15 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     const int64_t v_begin = (int64_t)sp * a.rps;
     int64_t v_end = v_begin + a.rps;
     if (v_end > L_all) v_end = L_all;
-    const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
+    const int ntiles = v_end > v_begin ? (int)((v_end - v_begin + ATT_TILE - 1) / ATT_TILE) : 0;
+    const int cpr = (int)(rb / 16);                     // 16-byte chunks per stored row
+    const int nch = ATT_TILE * cpr;
+
+    // ---- the split's slice of the index list, staged once (CSA)
+    if (a.idx) {
+        const int64_t e_end = v_end < n_ent ? v_end : n_ent;
+        for (int64_t v = v_begin + tid; v < e_end; v += ATT_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
+    }
 
     // ---- Q fragments (A operand): head h = hb*64 + wv*16 + col
     const int h_a = hb * 64 + wv * 16 + col;
@@ -85,6 +111,43 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         for (int ks = 0; ks < QKS; ++ks)
             qb[ks] = h_a < a.H ? *(const u32x4*)(qrow + (32 * ks + 8 * g) * 2) : u32x4{0, 0, 0, 0};
     }
+    __syncthreads();
+
+    // rows of tile `it` -> rowptr/rowok slot it&1 (threads 0..TILE-1)
+    auto resolve = [&](int it) {
+        if (tid < ATT_TILE) {
+            const int64_t v = v_begin + (int64_t)it * ATT_TILE + tid;
+            const uint8_t* p = nullptr;
+            if (v < v_end) {
+                if (v < n_ent) {
+                    const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
+                    if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+                } else {
+                    const int64_t pos = w0 + (v - n_ent);
+                    int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
+                    if (slot < 0) slot += a.kvw_rows;
+                    p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
+                }
+            }
+            rowptr[(it & 1) * ATT_TILE + tid] = p;
+            rowok[(it & 1) * ATT_TILE + tid] = p != nullptr;
+        }
+    };
+    // asynchronous gather of tile `it` into the raw LDS tile: lane l of a wave writes
+    // chunk 64*wc + l at raw + 1024*wc + 16*l (direct global -> LDS loads)
+    auto gather = [&](int it) {
+        const uint8_t** rp = rowptr + (it & 1) * ATT_TILE;
+        for (int wc = wv; wc * 64 < nch; wc += ATT_NT / 64) {
+            const int c = wc * 64 + lane;
+            if (c < nch) {
+                const int rr = c / cpr, pc = c - rr * cpr;
+                const uint8_t* p = rp[rr];
+                if (p)
+                    __builtin_amdgcn_global_load_lds((const void*)(p + 16 * pc),
+                                                     (__attribute__((address_space(3))) void*)(raw + 1024 * wc), 16, 0, 0);
+            }
+        }
+    };
 
     constexpr int NDB = D / 16;
     v4f o[NDB];
@@ -93,81 +156,73 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float l_run[4] = {0.f, 0.f, 0.f, 0.f};
     const float sl2 = a.scale * CSL_LOG2E;
+    const int nch_bf = FMT == KV_PACKED ? a.r / 8 : cpr;    // chunks stored as bf16
 
-    const int nch_bf = FMT == KV_PACKED ? a.r / 8 : (FMT == BF16 ? D / 8 : 0);
-    const int nch = FMT == F32 ? D / 4 : (FMT == BF16 ? D / 8 : a.r / 8 + (D - a.r) / 16);
-
-    for (int64_t v0 = v_begin; v0 < v_end; v0 += ATT_TILE) {
-        // ---- resolve the tile's rows
-        if (tid < ATT_TILE) {
-            const int64_t v = v0 + tid;
-            const uint8_t* p = nullptr;
-            int ok = 0;
-            if (v < v_end) {
-                if (v < n_ent) {
-                    int64_t s = v;
-                    if (a.idx) s = a.idx[bq * a.k + v];
-                    if (s >= 0 && s < a.n_cap) { p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb; ok = 1; }
-                } else {
-                    const int64_t pos = w0 + (v - n_ent);
-                    int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
-                    if (slot < 0) slot += a.kvw_rows;
-                    p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
-                    ok = 1;
-                }
-            }
-            rowptr[tid] = p;
-            rowok[tid] = ok;
-        }
+    if (ntiles > 0) {
+        resolve(0);
         __syncthreads();
-        // ---- gather + convert the tile into LDS (row-major, compute dtype)
-        for (int job = tid; job < ATT_TILE * nch; job += ATT_NT) {
-            const int rr = job / nch, c = job - rr * nch;
-            const uint8_t* p = rowptr[rr];
+        gather(0);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+        const int* ok = rowok + (it & 1) * ATT_TILE;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // ---- convert the raw tile into the padded compute-dtype K tile
+        for (int c = tid; c < nch; c += ATT_NT) {
+            const int rr = c / cpr, pc = c - rr * cpr;
+            u32x4 v = *(const u32x4*)(raw + 16 * c);
+            if (!ok[rr]) v = u32x4{0, 0, 0, 0};
             if constexpr (F32P) {
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (p) v = *(const float4*)(p + 16 * c);
-                *(float4*)(kl + ((size_t)rr * KSTR + 4 * c) * 4) = v;
-            } else if (FMT == BF16 || c < nch_bf) {
-                u32x4 v = {0, 0, 0, 0};
-                if (p) v = *(const u32x4*)(p + 16 * c);
-                *(u32x4*)(kl + ((size_t)rr * KSTR + 8 * c) * 2) = v;
+                *(u32x4*)(kl + ((size_t)rr * KSTR + 4 * pc) * 4) = v;
+            } else if (FMT == BF16 || pc < nch_bf) {
+                *(u32x4*)(kl + ((size_t)rr * KSTR + 8 * pc) * 2) = v;
             } else {
-                const int c8 = c - nch_bf;
-                u32x4 v = {0, 0, 0, 0};
-                if (p) v = *(const u32x4*)(p + 2 * a.r + 16 * c8);
+                const int c8 = pc - nch_bf;
                 uint32_t c0, c1, c2, c3, c4, c5, c6, c7;
                 e4m3x4_to_bf16x4(v[0], c0, c1);
                 e4m3x4_to_bf16x4(v[1], c2, c3);
                 e4m3x4_to_bf16x4(v[2], c4, c5);
                 e4m3x4_to_bf16x4(v[3], c6, c7);
-                const u32x4 lo = {c0, c1, c2, c3}, hi = {c4, c5, c6, c7};
                 uint8_t* dst = kl + ((size_t)rr * KSTR + a.r + 16 * c8) * 2;
-                *(u32x4*)dst = lo;
-                *(u32x4*)(dst + 16) = hi;
+                *(u32x4*)dst = u32x4{c0, c1, c2, c3};
+                *(u32x4*)(dst + 16) = u32x4{c4, c5, c6, c7};
             }
         }
-        __syncthreads();
-        // ---- S = Q K^T for this wave's 16 heads x 32 rows
-        v4f s[2];
+        if (it + 1 < ntiles) resolve(it + 1);
+        lds_barrier();
+        if (it + 1 < ntiles) gather(it + 1);          // overlaps the MFMA work below
+        // ---- S = Q K^T for this wave's 16 heads x 32 rows: two independent MFMA
+        //      chains (rows 0-15, 16-31), operands read one k-step ahead
+        v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (F32P) {
+            const float* k0 = (const float*)kl + (size_t)col * KSTR + g;
+            const float* k1 = k0 + 16 * KSTR;
+            float b0 = k0[0], b1 = k1[0];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            v4f c = {0.f, 0.f, 0.f, 0.f};
-            const int row = nb * 16 + col;
-            if constexpr (F32P) {
-                const float* kr = (const float*)kl + (size_t)row * KSTR;
-#pragma unroll
-                for (int ks = 0; ks < QKS; ++ks) c = mfma_f32(qf[ks], kr[4 * ks + g], c);
-            } else {
-                const uint8_t* kr = kl + (size_t)row * KSTR * 2;
-#pragma unroll
-                for (int ks = 0; ks < QKS; ++ks) c = mfma_bf16(qb[ks], *(const u32x4*)(kr + (32 * ks + 8 * g) * 2), c);
+            for (int ks = 0; ks < QKS; ++ks) {
+                float n0 = 0.f, n1 = 0.f;
+                if (ks + 1 < QKS) { n0 = k0[4 * (ks + 1)]; n1 = k1[4 * (ks + 1)]; }
+                s[0] = mfma_f32(qf[ks], b0, s[0]);
+                s[1] = mfma_f32(qf[ks], b1, s[1]);
+                b0 = n0; b1 = n1;
             }
-            s[nb] = c;
+        } else {
+            const uint8_t* k0 = kl + ((size_t)col * KSTR + 8 * g) * 2;
+            const uint8_t* k1 = k0 + (size_t)16 * KSTR * 2;
+            u32x4 b0 = *(const u32x4*)k0, b1 = *(const u32x4*)k1;
+#pragma unroll
+            for (int ks = 0; ks < QKS; ++ks) {
+                u32x4 n0 = b0, n1 = b1;
+                if (ks + 1 < QKS) { n0 = *(const u32x4*)(k0 + 64 * (ks + 1)); n1 = *(const u32x4*)(k1 + 64 * (ks + 1)); }
+                s[0] = mfma_bf16(qb[ks], b0, s[0]);
+                s[1] = mfma_bf16(qb[ks], b1, s[1]);
+                b0 = n0; b1 = n1;
+            }
         }
-        // ---- online softmax (base 2); lane holds heads 4g+i of rows nb*16+col
-        const bool ok0 = rowok[col] != 0, ok1 = rowok[16 + col] != 0;
-        float p0[4], p1[4];
+        // ---- online softmax (base 2), lazy rescale; lane holds heads 4g+i of rows nb*16+col
+        const bool ok0 = ok[col] != 0, ok1 = ok[16 + col] != 0;
+        float p0[4], p1[4], corr[4];
+        bool need = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float x0 = ok0 ? s[0][i] * sl2 : -INFINITY;
@@ -177,28 +232,30 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
             mx = fmaxf(mx, shfl_xor(mx, 2));
             mx = fmaxf(mx, shfl_xor(mx, 4));
             mx = fmaxf(mx, shfl_xor(mx, 8));
-            const float mnew = fmaxf(m_run[i], mx);
-            float corr, e0, e1;
-            if (mnew == -INFINITY) {
-                corr = 1.f; e0 = 0.f; e1 = 0.f;
-            } else {
-                corr = exp2f(m_run[i] - mnew);
-                e0 = exp2f(x0 - mnew);
-                e1 = exp2f(x1 - mnew);
+            corr[i] = 1.f;
+            if (mx > m_run[i] + ATT_TAU) {           // the reference max moves up
+                corr[i] = exp2f(m_run[i] - mx);      // 0 on the first valid tile
+                m_run[i] = mx;
+                need = true;
             }
+            const float e0 = m_run[i] == -INFINITY ? 0.f : exp2f(x0 - m_run[i]);
+            const float e1 = m_run[i] == -INFINITY ? 0.f : exp2f(x1 - m_run[i]);
             float rs = e0 + e1;
             rs += shfl_xor(rs, 1);
             rs += shfl_xor(rs, 2);
             rs += shfl_xor(rs, 4);
             rs += shfl_xor(rs, 8);
-            l_run[i] = l_run[i] * corr + rs;
-            m_run[i] = mnew;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db][i] *= corr;
+            l_run[i] = l_run[i] * corr[i] + rs;
             p0[i] = e0;
             p1[i] = e1;
         }
-        // ---- P -> LDS: pl[wave][head 4g+i][row]
+        if (__builtin_amdgcn_read_exec() & __ballot(need)) {   // wave-uniform: some head rescaled
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[db][i] *= corr[i];
+        }
+        // ---- P -> LDS: pl[wave][head 4g+i][row position]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = 4 * g + i;
@@ -208,11 +265,11 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
                 pr[16 + col] = p1[i];
             } else {
                 uint16_t* pr = (uint16_t*)pl + ((size_t)wv * 16 + hh) * PSTR;
-                pr[col] = (uint16_t)f32_to_bf16_rne(p0[i]);
-                pr[16 + col] = (uint16_t)f32_to_bf16_rne(p1[i]);
+                pr[p_perm(col)] = (uint16_t)f32_to_bf16_rne(p0[i]);
+                pr[p_perm(16 + col)] = (uint16_t)f32_to_bf16_rne(p1[i]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- O += P V
         if constexpr (F32P) {
             const float* pr = (const float*)pl + ((size_t)wv * 16 + col) * PSTR;
@@ -225,19 +282,24 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
                 for (int db = 0; db < NDB; ++db) o[db] = mfma_f32(pa, vr[16 * db], o[db]);
             }
         } else {
+            // k slot j of lane group g holds key 8g + 2j (j < 4) or 8g + 2(j-4) + 1: the
+            // source rows of one transposed read are 2 apart, which spreads them over
+            // all 32 banks (row stride = 4 banks mod 32)
             const u32x4 pa = *(const u32x4*)((const uint16_t*)pl + ((size_t)wv * 16 + col) * PSTR + 8 * g);
             const uint16_t* kb = (const uint16_t*)kl;
-            const uint16_t* v0p = kb + (size_t)(8 * g + (col >> 2)) * KSTR + 4 * (col & 3);
-            const uint16_t* v1p = v0p + 4 * KSTR;
+            const uint16_t* v0p = kb + (size_t)(8 * g + 2 * (col >> 2)) * KSTR + 4 * (col & 3);
+            const uint16_t* v1p = v0p + KSTR;
+            u32x2 r0 = lds_read_tr16(v0p), r1 = lds_read_tr16(v1p);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x2 r0 = lds_read_tr16(v0p + 16 * db);
-                const u32x2 r1 = lds_read_tr16(v1p + 16 * db);
+                u32x2 n0 = r0, n1 = r1;
+                if (db + 1 < NDB) { n0 = lds_read_tr16(v0p + 16 * (db + 1)); n1 = lds_read_tr16(v1p + 16 * (db + 1)); }
                 const u32x4 vb = {r0[0], r0[1], r1[0], r1[1]};
                 o[db] = mfma_bf16(pa, vb, o[db]);
+                r0 = n0; r1 = n1;
             }
         }
-        __syncthreads();
+        // the next iteration starts with a full barrier before the K tile is rewritten
     }
 
     // ---- finish: normalise, write output or the split's partial
@@ -271,22 +333,28 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 }
 
 // Merge of split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
+// One block per (query, 4 heads): the 64 heads of a head block spread over 16
+// blocks so that the merge reads its partials with the whole GPU.
+constexpr int CMB_HEADS = 4;
+
 template <int D>
 __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
-    extern __shared__ float wts[];   // [nsplit][64] weights, then [64] 1/den, [64] lse
-    const int hb = blockIdx.x;
+    extern __shared__ float wts[];   // [nsplit][CMB_HEADS] weights, then 1/den, lse
+    const int hb = blockIdx.x / (64 / CMB_HEADS);
+    const int h0 = (blockIdx.x % (64 / CMB_HEADS)) * CMB_HEADS;   // first head within the head block
     const int64_t bq = blockIdx.y;
     const int tid = threadIdx.x;
     const int64_t base = (bq * a.nhb + hb) * (int64_t)a.nsplit;
-    float* inv = wts + a.nsplit * 64;
-    float* lse_o = inv + 64;
-    if (tid < 64) {
+    float* inv = wts + a.nsplit * CMB_HEADS;
+    float* lse_o = inv + CMB_HEADS;
+    if (tid < CMB_HEADS) {
+        const int hh = h0 + tid;
         float M = -INFINITY;
-        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[(base + s) * 64 + tid]);
+        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[(base + s) * 64 + hh]);
         float den = 0.f;
         for (int s = 0; s < a.nsplit; ++s) {
-            const float w = M == -INFINITY ? 0.f : expf(a.ws_lse[(base + s) * 64 + tid] - M);
-            wts[s * 64 + tid] = w;
+            const float w = M == -INFINITY ? 0.f : expf(a.ws_lse[(base + s) * 64 + hh] - M);
+            wts[s * CMB_HEADS + tid] = w;
             den += w;
         }
         inv[tid] = den > 0.f ? 1.f / den : 0.f;
@@ -294,18 +362,19 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
     }
     __syncthreads();
     constexpr int C4 = D / 4;
-    for (int item = tid; item < 64 * C4; item += 256) {
-        const int hh = item / C4, c = (item - hh * C4) * 4;
+    for (int item = tid; item < CMB_HEADS * C4; item += 256) {
+        const int j = item / C4, c = (item - j * C4) * 4;
+        const int hh = h0 + j;
         const int h = hb * 64 + hh;
         if (h >= a.H) continue;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < a.nsplit; ++s) {
-            const float w = wts[s * 64 + hh];
+            const float w = wts[s * CMB_HEADS + j];
             const float4 v = *(const float4*)(a.ws_o + ((base + s) * 64 + hh) * D + c);
             acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
             acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
         }
-        const float iv = inv[hh];
+        const float iv = inv[j];
         acc.x *= iv; acc.y *= iv; acc.z *= iv; acc.w *= iv;
         if (a.out_fmt == F32) {
             *(float4*)((float*)a.out + (bq * a.H + h) * D + c) = acc;
@@ -316,19 +385,20 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
             *(uint2*)((uint16_t*)a.out + (bq * a.H + h) * D + c) = pk;
         }
     }
-    if (a.lse && tid < 64 && hb * 64 + tid < a.H) a.lse[bq * a.H + hb * 64 + tid] = lse_o[tid];
+    if (a.lse && tid < CMB_HEADS && hb * 64 + h0 + tid < a.H) a.lse[bq * a.H + hb * 64 + h0 + tid] = lse_o[tid];
 }
 
 template <int D, int FMT>
 static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq));
-    const size_t lds = AttLds<D, FMT>::BYTES;
-    hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), lds, s, a);
+    const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
+    if (a.idx && a.rps > ATT_MAX_SIDX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * 64 + 128);
-    hipLaunchKernelGGL((k_attend_combine<D>), dim3((unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq)), dim3(256),
-                       lds2, s, a);
+    const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + 2 * CMB_HEADS);
+    hipLaunchKernelGGL((k_attend_combine<D>), dim3((unsigned)(a.nhb * (64 / CMB_HEADS)), (unsigned)((int64_t)a.B * a.Tq)),
+                       dim3(256), lds2, s, a);
     return hipGetLastError();
 }
 

@@ -7,125 +7,239 @@
 // entry i pools raw positions (i+1)m-win .. (i+1)m-1, win = 2m with overlap, m
 // without; positions < 0 are left out of the softmax.
 //
-// Streaming, HBM-bound kernel: one thread owns 4 consecutive channels of one entry,
-// walks the window once with an online softmax (no second pass over the rows), and
-// stores the entry in its storage format (fp32, bf16, packed bf16+e4m3fn, or MXFP4
-// with one e8m0 scale per 32 channels).  d/4 consecutive threads form one entry, so
-// each raw row is read as contiguous 8- or 16-byte pieces by adjacent lanes.
+// Streaming, HBM-bound kernel.  A thread owns 8 consecutive channels (one 16-byte
+// bf16 load per row); d/8 adjacent threads cover a row, and RG such groups split
+// the window's rows between them, each running an online softmax over its rows.
+// The RG partial (max, sum, weighted sum) triples are merged through LDS, then the
+// entry is stored in its format: fp32, bf16, packed bf16 + e4m3fn, or MXFP4 (one
+// e8m0 scale per 32 channels, taken over 4 adjacent threads).  Splitting the rows
+// keeps a 128-row HCA window from becoming a 128-deep dependent loop per thread.
 #include "device.h"
 #include "launch.h"
 
 namespace csl {
 
-template <int XF, int OF, bool ZC1>
-__global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
-    const int TPE = a.d >> 2;                 // threads per entry
-    const int EPB = 256 / TPE;                // entries per block
-    const int eg = threadIdx.x / TPE;
-    const int c0 = (threadIdx.x - eg * TPE) * 4;
-    const int b = blockIdx.y;
-    const int64_t q = (int64_t)blockIdx.x * EPB + eg;
-    const bool active = eg < EPB && q < a.n_e;
-    const int64_t i = a.e_begin + (active ? q : 0);
+struct CmpGeom {
+    int TPR;  // threads per row (d / 8)
+    int RG;   // row groups per entry
+    int EPB;  // entries per block
+};
+
+__host__ __device__ inline int pow2_at_least(int v) {
+    int w = 1;
+    while (w < v) w <<= 1;
+    return w;
+}
+
+// Long windows (HCA's 128 rows) get 1024-thread blocks so that each row group
+// walks only a few rows; short windows keep 256-thread blocks.
+__host__ __device__ inline int cmp_threads(int d, int win) { return (d / 8) * pow2_at_least(win) >= 1024 ? 1024 : 256; }
+
+__host__ __device__ inline CmpGeom cmp_geom(int d, int win, int nt) {
+    CmpGeom g;
+    g.TPR = d / 8;
+    int rg = nt / g.TPR;
+    const int w2 = pow2_at_least(win);
+    if (rg > w2) rg = w2;
+    if (rg < 1) rg = 1;
+    g.RG = rg;
+    g.EPB = nt / (g.TPR * g.RG);
+    if (g.EPB < 1) g.EPB = 1;
+    return g;
+}
+
+template <int XF>
+__device__ __forceinline__ void load8(const uint8_t* row, int c0, float* v) {
+    if (XF == F32) {
+        const float4 a = *(const float4*)(row + (int64_t)c0 * 4);
+        const float4 b = *(const float4*)(row + (int64_t)c0 * 4 + 16);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const u32x4 u = *(const u32x4*)(row + (int64_t)c0 * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_f32(u[i] & 0xffffu);
+            v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+        }
+    }
+}
+
+template <int XF, int OF, bool ZC1, int CMP_NT>
+__global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     const int win = a.overlap ? 2 * a.m : a.m;
+    const CmpGeom G = cmp_geom(a.d, win, CMP_NT);
+    const int per_entry = G.TPR * G.RG;
+    const int ep = threadIdx.x / per_entry;
+    const int rg = (threadIdx.x / G.TPR) % G.RG;
+    const int tr = threadIdx.x % G.TPR;
+    const int c0 = tr * 8;
+    const int b = blockIdx.y;
+    const int64_t q = (int64_t)blockIdx.x * G.EPB + ep;
+    const bool active = ep < G.EPB && q < a.n_e;
+    const int64_t i = a.e_begin + (active ? q : 0);
     const int64_t p0 = (i + 1) * a.m - win;
     const int64_t xrb = XF == F32 ? 4 * (int64_t)a.d : 2 * (int64_t)a.d;
+    constexpr int NC = ZC1 ? 1 : 8;   // softmax channels carried per thread
 
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float den[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[8], mx[NC], den[NC];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) { mx[c] = -INFINITY; den[c] = 0.f; }
+
     if (active) {
         const uint8_t* xb = a.x + (int64_t)b * a.x_bstride;
         const float* zb = (const float*)((const uint8_t*)a.z + (int64_t)b * a.z_bstride);
-        for (int jw = p0 < 0 ? (int)(-p0) : 0; jw < win; ++jw) {
+        const int j0 = p0 < 0 ? (int)(-p0) : 0;
+#pragma unroll 4
+        for (int jw = j0 + ((rg - j0) % G.RG + G.RG) % G.RG; jw < win; jw += G.RG) {
             const int64_t row = p0 + jw - a.x_pos0;
-            float lg[4];
-            if (ZC1) {
-                const float v = zb[row] + a.bias[jw];
-                lg[0] = lg[1] = lg[2] = lg[3] = v;
+            float xv[8];
+            load8<XF>(xb + row * xrb, c0, xv);
+            float lg[NC];
+            if constexpr (ZC1) {
+                lg[0] = zb[row] + a.bias[jw];
             } else {
-                const float4 zz = *(const float4*)(zb + row * a.z_ch + c0);
-                const float4 bb = *(const float4*)(a.bias + (int64_t)jw * a.z_ch + c0);
-                lg[0] = zz.x + bb.x; lg[1] = zz.y + bb.y; lg[2] = zz.z + bb.z; lg[3] = zz.w + bb.w;
-            }
-            float xv[4];
-            if (XF == F32) {
-                const float4 v = *(const float4*)(xb + row * xrb + (int64_t)c0 * 4);
-                xv[0] = v.x; xv[1] = v.y; xv[2] = v.z; xv[3] = v.w;
-            } else {
-                const uint2 v = *(const uint2*)(xb + row * xrb + (int64_t)c0 * 2);
-                xv[0] = bf16_to_f32(v.x & 0xffffu); xv[1] = bf16_to_f32(v.x >> 16);
-                xv[2] = bf16_to_f32(v.y & 0xffffu); xv[3] = bf16_to_f32(v.y >> 16);
+                const float* zr = zb + row * a.z_ch + c0;
+                const float* br = a.bias + (int64_t)jw * a.z_ch + c0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) lg[c] = zr[c] + br[c];
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 if (lg[c] > mx[c]) {
                     const float s = expf(mx[c] - lg[c]);
                     den[c] *= s;
-                    acc[c] *= s;
+                    if constexpr (ZC1) {
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc) acc[cc] *= s;
+                    } else {
+                        acc[c] *= s;
+                    }
                     mx[c] = lg[c];
                 }
                 const float e = expf(lg[c] - mx[c]);
                 den[c] += e;
-                acc[c] = fmaf(e, xv[c], acc[c]);
+                if constexpr (ZC1) {
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) acc[cc] = fmaf(e, xv[cc], acc[cc]);
+                } else {
+                    acc[c] = fmaf(e, xv[c], acc[c]);
+                }
             }
         }
     }
-    float v[4];
+
+    // ---- merge the RG row-group partials (fixed order: deterministic)
+    __shared__ float s_acc[CMP_NT * 8];
+    __shared__ float s_mx[CMP_NT * NC];
+    __shared__ float s_den[CMP_NT * NC];
+    float v[8];
+    if (G.RG > 1) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = active ? acc[c] / den[c] : 0.0f;
+        for (int c = 0; c < 8; ++c) s_acc[threadIdx.x * 8 + c] = acc[c];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) { s_mx[threadIdx.x * NC + c] = mx[c]; s_den[threadIdx.x * NC + c] = den[c]; }
+        __syncthreads();
+        const int base = ep * per_entry + tr;   // thread of row group 0 for these channels
+        const int ng = ep < G.EPB ? G.RG : 0;    // threads past the last entry merge nothing
+        float M[NC], S[NC], A[8];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            M[c] = -INFINITY;
+            for (int g = 0; g < ng; ++g) M[c] = fmaxf(M[c], s_mx[(base + g * G.TPR) * NC + c]);
+            S[c] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) A[c] = 0.f;
+        for (int g = 0; g < ng; ++g) {
+            const int tg = base + g * G.TPR;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float m_g = s_mx[tg * NC + c];
+                const float f = m_g == -INFINITY ? 0.f : expf(m_g - M[c]);
+                S[c] = fmaf(s_den[tg * NC + c], f, S[c]);
+                if constexpr (ZC1) {
+#pragma unroll
+                    for (int cc = 0; cc < 8; ++cc) A[cc] = fmaf(s_acc[tg * 8 + cc], f, A[cc]);
+                } else {
+                    A[c] = fmaf(s_acc[tg * 8 + c], f, A[c]);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = active ? A[c] / S[ZC1 ? 0 : c] : 0.f;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = active ? acc[c] / den[ZC1 ? 0 : c] : 0.f;
+    }
+    const bool writer = active && rg == 0;
 
     uint8_t* ob = a.out + (int64_t)b * a.out_bstride;
     if (OF == F32) {
-        if (active) *(float4*)(ob + q * 4 * (int64_t)a.d + (int64_t)c0 * 4) = make_float4(v[0], v[1], v[2], v[3]);
+        if (writer) {
+            float* o = (float*)(ob + q * 4 * (int64_t)a.d) + c0;
+            *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+            *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
     } else if (OF == BF16) {
-        if (active) {
-            uint2 o;
-            o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-            o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-            *(uint2*)(ob + q * 2 * (int64_t)a.d + (int64_t)c0 * 2) = o;
+        if (writer) {
+            u32x4 o;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) o[k2] = f32_to_bf16_rne(v[2 * k2]) | (f32_to_bf16_rne(v[2 * k2 + 1]) << 16);
+            *(u32x4*)(ob + q * 2 * (int64_t)a.d + (int64_t)c0 * 2) = o;
         }
     } else if (OF == KV_PACKED) {
-        if (active) {
+        if (writer) {
             const int64_t rb = 2 * (int64_t)a.r + (a.d - a.r);
             uint8_t* row = ob + q * rb;
             if (c0 < a.r) {
-                uint2 o;
-                o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-                o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-                *(uint2*)(row + 2 * c0) = o;
+                u32x4 o;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2)
+                    o[k2] = f32_to_bf16_rne(v[2 * k2]) | (f32_to_bf16_rne(v[2 * k2 + 1]) << 16);
+                *(u32x4*)(row + 2 * c0) = o;
             } else {
-                const uint32_t o = f32_to_e4m3_rne_sat(v[0]) | (f32_to_e4m3_rne_sat(v[1]) << 8) |
-                                   (f32_to_e4m3_rne_sat(v[2]) << 16) | (f32_to_e4m3_rne_sat(v[3]) << 24);
-                *(uint32_t*)(row + 2 * a.r + (c0 - a.r)) = o;
+                u32x2 o;
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+                    o[k2] = f32_to_e4m3_rne_sat(v[4 * k2]) | (f32_to_e4m3_rne_sat(v[4 * k2 + 1]) << 8) |
+                            (f32_to_e4m3_rne_sat(v[4 * k2 + 2]) << 16) | (f32_to_e4m3_rne_sat(v[4 * k2 + 3]) << 24);
+                *(u32x2*)(row + 2 * a.r + (c0 - a.r)) = o;
             }
         }
-    } else {  // MXFP4: 8 adjacent threads hold one 32-channel block
-        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    } else {  // MXFP4: 4 adjacent threads hold one 32-channel block
+        float am = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(v[c]));
         am = fmaxf(am, shfl_xor(am, 1));
         am = fmaxf(am, shfl_xor(am, 2));
-        am = fmaxf(am, shfl_xor(am, 4));
         const int e = mx_block_exponent(am);
-        uint32_t cd[4];
+        uint32_t w = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) cd[c] = f32_to_e2m1_rne_sat(ldexpf(v[c], -e));
-        if (active) {
-            uint8_t* row = ob + q * (int64_t)(a.d / 2);
-            *(uint16_t*)(row + c0 / 2) = (uint16_t)(cd[0] | (cd[1] << 4) | (cd[2] << 8) | (cd[3] << 12));
+        for (int c = 0; c < 8; ++c) w |= f32_to_e2m1_rne_sat(ldexpf(v[c], -e)) << (4 * c);
+        if (writer) {
+            *(uint32_t*)(ob + q * (int64_t)(a.d / 2) + c0 / 2) = w;
             if ((c0 & 31) == 0) a.out_scales[(int64_t)b * a.sc_bstride + q * (a.d / 32) + c0 / 32] = (uint8_t)(e + 127);
         }
     }
 }
 
+template <int XF, int OF, int NT>
+static hipError_t launch_c3(const CompressArgs& a, hipStream_t s) {
+    const CmpGeom G = cmp_geom(a.d, a.overlap ? 2 * a.m : a.m, NT);
+    dim3 grid((unsigned)((a.n_e + G.EPB - 1) / G.EPB), (unsigned)a.B);
+    if (a.z_ch == 1)
+        hipLaunchKernelGGL((k_compress<XF, OF, true, NT>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_compress<XF, OF, false, NT>), grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int XF, int OF>
 static hipError_t launch_c2(const CompressArgs& a, hipStream_t s) {
-    const int TPE = a.d / 4, EPB = 256 / TPE;
-    dim3 grid((unsigned)((a.n_e + EPB - 1) / EPB), (unsigned)a.B);
-    if (a.z_ch == 1)
-        hipLaunchKernelGGL((k_compress<XF, OF, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_compress<XF, OF, false>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return cmp_threads(a.d, a.overlap ? 2 * a.m : a.m) == 1024 ? launch_c3<XF, OF, 1024>(a, s)
+                                                               : launch_c3<XF, OF, 256>(a, s);
 }
 
 template <int XF>

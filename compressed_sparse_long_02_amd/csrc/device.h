@@ -114,8 +114,11 @@ __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v4f mfma_fp4(const u32x4& a, const u32x4& b, int sa, int sb, v4f c) {
-    v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
-    v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    // FP4 operands use only the low four registers of the eight-register operand
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i a4 = __builtin_bit_cast(v4i, a), b4 = __builtin_bit_cast(v4i, b);
+    const v8i A = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+    const v8i B = __builtin_shufflevector(b4, b4, 0, 1, 2, 3, -1, -1, -1, -1);
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, sa, 0, sb);
 }
 
@@ -128,5 +131,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, 64); }
+
+// max(x, 0) as an integer max on the bit pattern: negative floats are negative
+// integers, non-negative floats keep their bits (one instruction, no NaN quieting).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Workgroup barrier for LDS-only communication: waits for this wave's LDS
+// operations, not for its outstanding global loads (so asynchronous global->LDS
+// loads of a later tile stay in flight across it).  The memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace csl

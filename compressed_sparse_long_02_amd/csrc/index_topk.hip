@@ -18,12 +18,13 @@
 //    16x16x128 FP4 MFMA, which applies the e8m0 block scales in hardware (the
 //    exact equivalent of the pages' lossless FP4->FP8 upcast).  The ReLU + weighted
 //    head sum runs on the accumulator registers; scores never leave LDS.
-//  * The block then selects its slice's top min(k,S) with a 4-pass 8-bit radix
-//    select on order-preserving uint32 keys in LDS, and compacts the winners in
-//    index order with a block scan (ties: the first ones in index order).
+//  * The block then selects its slice's top min(k,S) with a radix select on
+//    order-preserving uint32 keys in LDS (11-bit digits from the highest bit where
+//    the keys differ), and compacts the winners in index order with a block scan
+//    (ties: the first ones in index order).
 //  * k_idx_merge (only when a query spans several slices): one block per query
-//    reloads the slices' candidates (index order is slice order) and repeats the
-//    same select; the winners come out ascending by index without a sort.
+//    streams the slices' candidates -- one contiguous array in entry order -- and
+//    repeats the same select; the winners come out ascending by index, no sort.
 #include "device.h"
 #include "launch.h"
 
@@ -33,16 +34,24 @@ namespace csl {
 // Block-wide helpers
 // ---------------------------------------------------------------------------
 
-// Exclusive scan of one int per thread over the block; `wsum` holds NT/64 ints.
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (no LDS round trips).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, true);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, true);   // row_bcast:31
+    return v;
+}
+
+// Exclusive prefix sum of one int per thread over the block (one barrier);
+// `wsum` holds NT/64 ints and must not be reused before the next barrier.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
     int base = 0, tot = 0;
@@ -52,92 +61,167 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
         base += (x < wv) ? s : 0;
         tot += s;
     }
-    __syncthreads();
     total = tot;
     return base + incl - v;
 }
 
 // Select the `want` largest of n keys (ties: smaller element index first) and call
 // emit(pos, i, key) for each winner, pos = 0.. in increasing element index.
-// Element i lives at keys[i + (i >> le)]; thread t owns elements [t*E, t*E + E).
-// `sh` is scratch of at least 256 + 8 + NT/64 uint32.
-template <int NT, typename Emit>
-__device__ __forceinline__ void block_topk(const uint32_t* keys, int n, int want, int E, int le,
-                                           uint32_t* sh, Emit emit) {
-    const int tid = threadIdx.x;
-    uint32_t* hist = sh;
-    int* misc = (int*)(sh + 256);
-    int* wsum = (int*)(sh + 264);
-    const bool all = n <= want;
-    uint32_t T = 0;
+// Thread t holds elements [t*E, t*E + E) in registers kv[0..E) (E <= EMAX).
+// `sh` is LDS scratch of at least TOPK_SCRATCH(NT) uint32.
+//
+// Radix select on the order-preserving keys.  The block first finds the min and
+// max key; the digits start at the highest bit where they differ (the bits above
+// it are common to every key), 11 bits (2048 bins) at a time, so the first pass
+// already spreads the keys over many bins instead of piling them onto the few
+// sign/exponent patterns that the top bits of real scores take.  A pass stops the
+// search early when the threshold bin holds exactly the remaining count.  Passes
+// run on registers: per pass, LDS atomics into one of two histograms (the other
+// is cleared meanwhile), then wave 0 alone locates the threshold digit -- two
+// barriers per pass.  The final compaction is one packed (greater, equal) scan.
+constexpr int TOPK_BINS = 2048;
+constexpr int TOPK_BITS = 11;
+constexpr int TOPK_EMAX = 32;
+#define TOPK_SCRATCH(NT) (2 * TOPK_BINS + 16 + 2 * ((NT) / 64) + 8)
+
+// If rank_r > 0, thread 0 also stores to *tb_out a value t such that at least rank_r
+// of the n keys are >= t (the lower edge of the first-pass bin holding the
+// rank_r-th largest key; 0 when the block learns nothing, which is always valid).
+template <int NT, int EMAX, typename Emit>
+__device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, int n, int want, uint32_t* sh,
+                                           Emit emit, int rank_r = 0, uint32_t* tb_out = nullptr) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int base = tid * E;
+    uint32_t* hist0 = sh;
+    uint32_t* hist1 = sh + TOPK_BINS;
+    uint32_t* misc = sh + 2 * TOPK_BINS;                    // [0] digit [1] above [2] in-bin, [4..] lo/hi
+    int* wsum = (int*)(sh + 2 * TOPK_BINS + 16);           // NT/64 for lo, NT/64 for hi / scans
+    uint32_t T = 0;        // select u > T, plus the first eq_take keys equal to T
     int eq_take = 0;
+    const bool all = n <= want;
+    if (all && tb_out && tid == 0) *tb_out = 0u;
     if (!all) {
-        uint32_t prefix = 0, pmask = 0;
-        int w = want;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int x = tid; x < 256; x += NT) hist[x] = 0;
-            __syncthreads();
-            for (int e = 0; e < E; ++e) {
-                const int i = tid * E + e;
-                if (i < n) {
-                    const uint32_t u = keys[i + (i >> le)];
-                    if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-                }
-            }
-            __syncthreads();
-            if (tid < 64) {
-                // lane L owns bins 4L..4L+3; counts of digits >= bin, from the top
-                const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
-                               h3 = hist[4 * tid + 3];
-                const uint32_t s = h0 + h1 + h2 + h3;
-                uint32_t suf = s;
+        // ---- min / max over the valid keys; clear the first histogram
+        uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t t = __shfl_down(suf, o, 64);
-                    if (tid + o < 64) suf += t;
-                }
-                const uint32_t above = suf - s;
-                const uint32_t c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1, c0 = c1 + h0;
-                const uint32_t uw = (uint32_t)w;
-                if (c3 >= uw && above < uw) { misc[0] = 4 * tid + 3; misc[1] = (int)above; }
-                else if (c2 >= uw && c3 < uw) { misc[0] = 4 * tid + 2; misc[1] = (int)c3; }
-                else if (c1 >= uw && c2 < uw) { misc[0] = 4 * tid + 1; misc[1] = (int)c2; }
-                else if (c0 >= uw && c1 < uw) { misc[0] = 4 * tid; misc[1] = (int)c1; }
+        for (int x = 0; x < EMAX; ++x) {
+            if (x < E && base + x < n) {
+                lo = kv[x] < lo ? kv[x] : lo;
+                hi = kv[x] > hi ? kv[x] : hi;
             }
-            __syncthreads();
-            const uint32_t dgt = (uint32_t)misc[0];
-            w -= misc[1];
-            prefix |= dgt << shift;
-            pmask |= 0xffu << shift;
-            __syncthreads();
         }
-        T = prefix;
-        eq_take = w;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t a = __shfl_xor(lo, o, 64), b = __shfl_xor(hi, o, 64);
+            lo = a < lo ? a : lo;
+            hi = b > hi ? b : hi;
+        }
+        if (lane == 0) { wsum[wv] = (int)lo; wsum[NT / 64 + wv] = (int)hi; }
+        for (int x = tid; x < TOPK_BINS; x += NT) hist0[x] = 0;
+        __syncthreads();
+        lo = (uint32_t)wsum[0]; hi = (uint32_t)wsum[NT / 64];
+        for (int x = 1; x < NT / 64; ++x) {
+            const uint32_t a = (uint32_t)wsum[x], b = (uint32_t)wsum[NT / 64 + x];
+            lo = a < lo ? a : lo;
+            hi = b > hi ? b : hi;
+        }
+        if (lo == hi) {
+            T = lo;                                  // every key ties
+            eq_take = want;
+            if (tb_out && tid == 0) *tb_out = lo;
+        } else {
+            int top = 31 - __builtin_clz(lo ^ hi);   // highest differing bit
+            uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
+            uint32_t prefix = hi & pmask;
+            int w = want;
+            bool exact = false;
+            for (int pass = 0;; ++pass) {
+                uint32_t* hcur = (pass & 1) ? hist1 : hist0;
+                uint32_t* hnxt = (pass & 1) ? hist0 : hist1;
+                const int width = top + 1 < TOPK_BITS ? top + 1 : TOPK_BITS;
+                const int shift = top + 1 - width;
+                const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+                for (int x = 0; x < EMAX; ++x) {
+                    if (x < E && base + x < n && (kv[x] & pmask) == prefix) atomicAdd(&hcur[(kv[x] >> shift) & dmask], 1u);
+                }
+                for (int x = tid; x < TOPK_BINS; x += NT) hnxt[x] = 0;
+                __syncthreads();
+                if (wv == 0) {
+                    // lane L owns bins [32L, 32L+32); counts of keys in bins above.
+                    // The bins are read twice (sum, then the walk) rather than held in
+                    // 32 registers next to the caller's keys.
+                    const u32x4* hp = (const u32x4*)(hcur + 32 * lane);
+                    uint32_t loc = 0;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const u32x4 v4 = hp[q];
+                        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
+                    }
+                    const int incl = wave_incl_scan((int)loc);
+                    const int tot = __shfl(incl, 63, 64);
+                    uint32_t c = (uint32_t)(tot - incl);   // keys in the bins of higher lanes
+                    const uint32_t rr = pass == 0 ? (uint32_t)rank_r : 0u;
+#pragma unroll
+                    for (int q = 7; q >= 0; --q) {
+                        const u32x4 v4 = hp[q];
+#pragma unroll
+                        for (int e = 3; e >= 0; --e) {
+                            const uint32_t hq = v4[e];
+                            const uint32_t cge = c + hq;
+                            if (cge >= (uint32_t)w && c < (uint32_t)w) {
+                                misc[0] = 32 * lane + 4 * q + e;
+                                misc[1] = c;
+                                misc[2] = hq;
+                            }
+                            if (rr > 0 && cge >= rr && c < rr) misc[3] = 32 * lane + 4 * q + e;
+                            c = cge;
+                        }
+                    }
+                }
+                __syncthreads();
+                if (pass == 0 && rank_r > 0 && tb_out && tid == 0) *tb_out = prefix | (misc[3] << shift);
+                const uint32_t dgt = misc[0];
+                w -= (int)misc[1];
+                const int inbin = (int)misc[2];
+                prefix |= dgt << shift;
+                pmask |= dmask << shift;
+                if (inbin == w) {                    // the whole bin is taken: select u >= prefix
+                    T = prefix - 1u;
+                    eq_take = 0;
+                    break;
+                }
+                if (shift == 0) { exact = true; break; }
+                top = shift - 1;
+            }
+            if (exact) {
+                T = prefix;
+                eq_take = w;
+            }
+        }
     }
-    // counts per thread, in element order
+    // ---- compaction in element order: one scan of packed (greater, equal) counts
     int my_gt = 0, my_eq = 0;
-    for (int e = 0; e < E; ++e) {
-        const int i = tid * E + e;
-        if (i < n) {
-            const uint32_t u = keys[i + (i >> le)];
-            if (all || u > T) ++my_gt;
-            else if (u == T) ++my_eq;
+#pragma unroll
+    for (int x = 0; x < EMAX; ++x) {
+        if (x < E && base + x < n) {
+            if (all || kv[x] > T) ++my_gt;
+            else if (kv[x] == T) ++my_eq;
         }
     }
     int tot;
-    const int eq_before = block_excl_scan<NT>(my_eq, wsum, tot);
-    int sel_eq = eq_take - eq_before;
-    sel_eq = sel_eq < 0 ? 0 : (sel_eq > my_eq ? my_eq : sel_eq);
-    int pos = block_excl_scan<NT>(my_gt + sel_eq, wsum, tot);
-    int r_eq = 0;
-    for (int e = 0; e < E; ++e) {
-        const int i = tid * E + e;
-        if (i < n) {
-            const uint32_t u = keys[i + (i >> le)];
+    const uint32_t pre = (uint32_t)block_excl_scan<NT>(my_gt | (my_eq << 16), wsum, tot);
+    const int gt_before = (int)(pre & 0xffffu), eq_before = (int)(pre >> 16);
+    int pos = gt_before + (eq_before < eq_take ? eq_before : eq_take);
+    int r_eq = eq_before;                             // equal keys before this thread's next one
+#pragma unroll
+    for (int x = 0; x < EMAX; ++x) {
+        if (x < E && base + x < n) {
+            const uint32_t u = kv[x];
             if (all || u > T) {
-                emit(pos++, i, u);
+                emit(pos++, base + x, u);
             } else if (u == T) {
-                if (r_eq < sel_eq) emit(pos++, i, u);
+                if (r_eq < eq_take) emit(pos++, base + x, u);
                 ++r_eq;
             }
         }
@@ -153,7 +237,7 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t n_cap) {
 // ---------------------------------------------------------------------------
 // Scoring + per-slice selection
 // ---------------------------------------------------------------------------
-constexpr int IDX_NT = 256;
+constexpr int IDX_NT = 512;   // 8 waves: enough loads in flight per CU to stream HBM
 constexpr int IDX_UNR = 4;   // 16-key tiles in flight per wave
 
 template <int FMT, int DI>
@@ -232,7 +316,8 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
 }
 
 template <int FMT, int DI, int HB>
-__global__ void __launch_bounds__(IDX_NT) k_idx_score(IndexArgs a) {
+__global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
+k_idx_score(IndexArgs a) {
     extern __shared__ uint32_t smem[];
     const int sl = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int64_t bq = (int64_t)b * a.Tq + j;
@@ -270,45 +355,70 @@ __global__ void __launch_bounds__(IDX_NT) k_idx_score(IndexArgs a) {
         const uint8_t* kbase = a.ki + (int64_t)b * a.ki_bstride;
         const uint8_t* sbase = a.ki_scales ? a.ki_scales + (int64_t)b * a.ks_bstride : nullptr;
         const int ntile = (ns + 15) >> 4;
-        for (int t0 = wv; t0 < ntile; t0 += 4 * IDX_UNR) {
-            KeyFrag<FMT, DI> kf[IDX_UNR];
+        // tiles of this wave: T = wv + 8u + 32k (group k, slot u); a lane's row is
+        // clamped to the slice end, so only the last tile re-reads a valid row and
+        // every load stays in bounds without a per-lane branch
+        // Loads are unconditional (a tile past the end re-reads the last tile, a lane
+        // past the slice end re-reads the last row) so the load stream is straight-line
+        // code and the compiler can wait for exactly the group in use (vmcnt(N)).
+        auto load_tile = [&](int T, KeyFrag<FMT, DI>& f) {
+            T = T < ntile ? T : ntile - 1;
+            int li = T * 16 + col;
+            li = li < ns ? li : ns - 1;
+            const int64_t row = s0 + li;
+            f.load(kbase + row * rb, sbase ? sbase + row * (DI / 32) : nullptr, g);
+        };
+        auto score_tile = [&](int T, const KeyFrag<FMT, DI>& f) {
+            float part = 0.f;
 #pragma unroll
-            for (int u = 0; u < IDX_UNR; ++u) {
-                const int li = (t0 + 4 * u) * 16 + col;
-                if (li < ns) {
-                    const int64_t s = s0 + li;
-                    kf[u].load(kbase + s * rb, sbase ? sbase + s * (DI / 32) : nullptr, g);
-                } else {
-                    kf[u].zero();
-                }
+            for (int hb = 0; hb < HB; ++hb) {
+                v4f c = {0.f, 0.f, 0.f, 0.f};
+                c = frag_dot<FMT, DI>(qf[hb], f, c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(c[i]), part);
             }
+            part += shfl_xor(part, 16);
+            part += shfl_xor(part, 32);
+            const int li = T * 16 + col;
+            if (g == 0 && T < ntile && li < ns) keys[li + (li >> le)] = score_key(part);
+        };
+        constexpr int NWV = IDX_NT / 64;
+        const int wvu = __builtin_amdgcn_readfirstlane(wv);           // wave-uniform
+        const int ngroups = wvu < ntile ? (ntile - wvu + NWV * IDX_UNR - 1) / (NWV * IDX_UNR) : 0;
+        KeyFrag<FMT, DI> fa[IDX_UNR], fb[IDX_UNR];
+        auto load_grp = [&](int k, KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
 #pragma unroll
-            for (int u = 0; u < IDX_UNR; ++u) {
-                const int tile = t0 + 4 * u;
-                if (tile < ntile) {
-                    float part = 0.f;
+            for (int u = 0; u < IDX_UNR; ++u) load_tile(wvu + NWV * (u + IDX_UNR * k), f[u]);
+        };
+        auto score_grp = [&](int k, const KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        v4f c = {0.f, 0.f, 0.f, 0.f};
-                        c = frag_dot<FMT, DI>(qf[hb], kf[u], c);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], fmaxf(c[i], 0.f), part);
-                    }
-                    part += shfl_xor(part, 16);
-                    part += shfl_xor(part, 32);
-                    const int li = tile * 16 + col;
-                    if (g == 0 && li < ns) keys[li + (li >> le)] = score_key(part);
-                }
-            }
+            for (int u = 0; u < IDX_UNR; ++u) score_tile(wvu + NWV * (u + IDX_UNR * k), f[u]);
+        };
+        // ping-pong: the next group's fragments load while the current one is scored.
+        // The prefetch is unconditional (past the end it re-reads the last tile, an L2
+        // hit) so every path into the loop body has the same loads in flight.
+        if (ngroups > 0) load_grp(0, fa);
+        for (int k = 0; k < ngroups; k += 2) {
+            load_grp(k + 1, fb);
+            score_grp(k, fa);
+            if (k + 1 >= ngroups) break;
+            load_grp(k + 2, fa);
+            score_grp(k + 1, fb);
         }
     }
     __syncthreads();
 
+    uint32_t kv[TOPK_EMAX];
+#pragma unroll
+    for (int x = 0; x < TOPK_EMAX; ++x) {
+        const int i = tid * E + x;
+        kv[x] = (x < E && i < ns) ? keys[i + (i >> le)] : 0u;
+    }
     const int want = ns < a.kk ? ns : a.kk;
     if (a.nslices == 1) {
         int32_t* oi = a.out_idx + bq * a.k;
         float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-        block_topk<IDX_NT>(keys, ns, want, E, le, sh, [&](int pos, int i, uint32_t u) {
+        block_topk<IDX_NT>(kv, E, ns, want, sh, [&](int pos, int i, uint32_t u) {
             oi[pos] = (int32_t)(s0 + i);
             if (os) os[pos] = key_score(u);
         });
@@ -318,12 +428,15 @@ __global__ void __launch_bounds__(IDX_NT) k_idx_score(IndexArgs a) {
             if (os) os[p] = -INFINITY;
         }
     } else {
-        uint32_t* ck = a.cand_key + (bq * a.nslices + sl) * a.kk;
-        int32_t* ci = a.cand_idx + (bq * a.nslices + sl) * a.kk;
-        block_topk<IDX_NT>(keys, ns, want, E, le, sh, [&](int pos, int i, uint32_t u) {
+        uint32_t* ck = a.cand_key + bq * (int64_t)a.cst + (int64_t)sl * a.kk;
+        int32_t* ci = a.cand_idx + bq * (int64_t)a.cst + (int64_t)sl * a.kk;
+        // rank r = ceil(k / non-empty slices): every slice's top-r together hold >= k keys
+        const int nse = (int)((n + a.S - 1) / a.S);
+        const int rr = nse > 0 ? (a.k + nse - 1) / nse : 0;
+        block_topk<IDX_NT>(kv, E, ns, want, sh, [&](int pos, int i, uint32_t u) {
             ck[pos] = u;
             ci[pos] = (int32_t)(s0 + i);
-        });
+        }, ns > 0 ? (rr < ns ? rr : ns) : 0, a.tbound + bq * a.nslices + sl);
     }
 }
 
@@ -333,6 +446,8 @@ __global__ void __launch_bounds__(IDX_NT) k_idx_score(IndexArgs a) {
 constexpr int MRG_NT = 1024;
 constexpr int MRG_MAXC = 32768;
 
+constexpr int MRG_SURV = 8192;   // survivors of the bound filter handled in LDS
+
 __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
     extern __shared__ uint32_t smem[];
     const int j = blockIdx.x, b = blockIdx.y;
@@ -340,50 +455,86 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
     const int tid = threadIdx.x;
     const int64_t t = a.q_pos[bq];
     const int64_t n = n_visible(t, a.m, a.n_cap);
-    // padded element count: E_M = pow2 >= ceil(nslices*kk / NT)
-    const int cmax = a.nslices * a.kk;
-    int E = 1;
-    while (E * MRG_NT < cmax) E <<= 1;
-    const int le = 31 - __builtin_clz(E);
-    uint32_t* keys = smem;
-    int* offs = (int*)(smem + MRG_MAXC + (MRG_MAXC >> 5) + 64);   // nslices + 1 ints
-    uint32_t* sh = smem + MRG_MAXC + (MRG_MAXC >> 5) + 64 + 72;
-    if (tid == 0) {
-        int acc = 0;
-        for (int s = 0; s < a.nslices; ++s) {
-            offs[s] = acc;
-            int64_t ns = n - (int64_t)s * a.S;
-            ns = ns < 0 ? 0 : (ns > a.S ? a.S : ns);
-            acc += (int)(ns < a.kk ? ns : a.kk);
-        }
-        offs[a.nslices] = acc;
-    }
-    __syncthreads();
-    const int total = offs[a.nslices];
-    for (int s = 0; s < a.nslices; ++s) {
-        const int o = offs[s], c = offs[s + 1] - o;
-        const uint32_t* src = a.cand_key + (bq * a.nslices + s) * a.kk;
-        for (int r = tid; r < c; r += MRG_NT) {
-            const int i = o + r;
-            keys[i + (i >> le)] = src[r];
+    // Every slice before the last non-empty one is full (n >= its end), so it kept
+    // exactly kk candidates: the candidates of a query form one contiguous array,
+    // element i belonging to slice i / kk, already in ascending entry order.
+    const int64_t nfull = n / a.S;
+    const int64_t rem = n - nfull * a.S;
+    const int total = (int)(nfull * a.kk + (rem < a.kk ? rem : a.kk));
+    const int nse = (int)(nfull + (rem > 0));
+    // Lower bound L of the k-th largest key: slice s reported t_s with at least r_s
+    // of its keys >= t_s (r_s = min(its size, ceil(k / nse))).  If the r_s add up to
+    // k, at least k keys are >= min_s t_s, so no key below it can be selected.
+    uint32_t L = 0u;
+    if (nse > 0) {
+        const int r = (a.k + nse - 1) / nse;
+        const int64_t sum_r = nfull * (r < a.S ? r : a.S) + (rem > 0 ? (rem < r ? rem : r) : 0);
+        if (sum_r >= a.k) {
+            L = 0xffffffffu;
+            for (int s = 0; s < nse; ++s) {
+                const uint32_t ts = a.tbound[bq * a.nslices + s];
+                L = ts < L ? ts : L;
+            }
         }
     }
+    uint32_t* sh = smem;                                   // TOPK_SCRATCH(MRG_NT)
+    int* win = (int*)(smem + TOPK_SCRATCH(MRG_NT));        // winners' element numbers, k <= 2048
+    uint32_t* wkey = (uint32_t*)(win + 2048);
+    uint32_t* sk = wkey + 2048;                            // survivors: keys
+    int* si = (int*)(sk + MRG_SURV);                       //            element numbers
+    const uint32_t* src = a.cand_key + bq * (int64_t)a.cst;
+    const int32_t* isrc = a.cand_idx + bq * (int64_t)a.cst;
+    // thread t owns elements [t*E, t*E + E): 16-byte loads, all issued unconditionally
+    const int E = a.cst / MRG_NT;                          // multiple of 4, <= TOPK_EMAX
+    uint32_t kv[TOPK_EMAX];
+    const u32x4* src4 = (const u32x4*)(src + (int64_t)tid * E);
+#pragma unroll
+    for (int q = 0; q < TOPK_EMAX / 4; ++q) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (4 * q < E) v = src4[q];
+        kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
+    }
+    // keep the keys >= L, compacted in element order
+    int mine = 0;
+#pragma unroll
+    for (int x = 0; x < TOPK_EMAX; ++x) mine += (x < E && tid * E + x < total && kv[x] >= L) ? 1 : 0;
+    int nsurv;
+    int off = block_excl_scan<MRG_NT>(mine, (int*)(sh + 2 * TOPK_BINS + 16), nsurv);
+    const int want = total < a.k ? total : a.k;
+    if (nsurv <= MRG_SURV) {
+#pragma unroll
+        for (int x = 0; x < TOPK_EMAX; ++x) {
+            if (x < E && tid * E + x < total && kv[x] >= L) { sk[off] = kv[x]; si[off] = tid * E + x; ++off; }
+        }
+        __syncthreads();
+        constexpr int E2MAX = MRG_SURV / MRG_NT;
+        const int E2 = (nsurv + MRG_NT - 1) / MRG_NT;
+        uint32_t kv2[E2MAX];
+#pragma unroll
+        for (int x = 0; x < E2MAX; ++x) kv2[x] = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] : 0u;
+        block_topk<MRG_NT>(kv2, E2, nsurv, want, sh, [&](int pos, int i, uint32_t u) {
+            win[pos] = si[i];
+            wkey[pos] = u;
+        });
+    } else {
+        __syncthreads();                                   // the scan's sums are read before reuse
+        block_topk<MRG_NT>(kv, E, total, want, sh, [&](int pos, int i, uint32_t u) {
+            win[pos] = i;
+            wkey[pos] = u;
+        });
+    }
     __syncthreads();
+    // the winners' entry indices and scores, gathered by all threads at once
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-    const int want = total < a.k ? total : a.k;
-    block_topk<MRG_NT>(keys, total, want, E, le, sh, [&](int pos, int i, uint32_t u) {
-        int lo = 0, hi = a.nslices - 1;          // slice s with offs[s] <= i < offs[s+1]
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (offs[mid] <= i) lo = mid; else hi = mid - 1;
+    for (int p = tid; p < a.k; p += MRG_NT) {
+        if (p < want) {
+            oi[p] = isrc[win[p]];
+            if (os) os[p] = key_score(wkey[p]);
+        } else {
+            oi[p] = -1;
+            if (os) os[p] = -INFINITY;
         }
-        oi[pos] = a.cand_idx[(bq * a.nslices + lo) * a.kk + (i - offs[lo])];
-        if (os) os[pos] = key_score(u);
-    });
-    for (int p = want + tid; p < a.k; p += MRG_NT) {
-        oi[p] = -1;
-        if (os) os[p] = -INFINITY;
     }
 }
 
@@ -393,7 +544,7 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
 template <int FMT, int DI, int HB>
 static hipError_t launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
-    const size_t lds = sizeof(uint32_t) * ((size_t)a.S + a.S / E + 256 + 8 + IDX_NT / 64 + 8);
+    const size_t lds = sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT));   // keys + scratch
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((k_idx_score<FMT, DI, HB>), grid, dim3(IDX_NT), lds, s, a);
     return hipGetLastError();
@@ -420,7 +571,7 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
         else e = launch_hb<F32, 128>(a, s);
     }
     if (e != hipSuccess || a.nslices == 1) return e;
-    const size_t lds = sizeof(uint32_t) * ((size_t)MRG_MAXC + (MRG_MAXC >> 5) + 64 + 72 + 256 + 8 + MRG_NT / 64 + 8);
+    const size_t lds = sizeof(uint32_t) * ((size_t)TOPK_SCRATCH(MRG_NT) + 2 * 2048 + 2 * MRG_SURV);
     hipLaunchKernelGGL(k_idx_merge, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(MRG_NT), lds, s, a);
     return hipGetLastError();
 }

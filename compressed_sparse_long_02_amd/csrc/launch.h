@@ -24,8 +24,10 @@ struct IndexArgs {
     int S;          // keys per slice (power of two, 256..16384)
     int nslices;    // slices per query
     int kk;         // candidates kept per slice = min(k, S)
-    uint32_t* cand_key;  // [B*Tq][nslices][kk]
-    int32_t* cand_idx;   // [B*Tq][nslices][kk]
+    int cst;        // per-query stride of the candidate arrays (multiple of 4096, >= nslices*kk)
+    uint32_t* cand_key;  // [B*Tq][cst]: slice s's candidates at [s*kk, s*kk + count)
+    int32_t* cand_idx;   // [B*Tq][cst]
+    uint32_t* tbound;    // [B*Tq][nslices]: per-slice lower bound of the top-r keys (see k_idx_merge)
 };
 
 struct AttendArgs {

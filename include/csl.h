@@ -93,7 +93,8 @@ int64_t csl_row_bytes(int fmt, int d, int r);
  *             codes are rounded to nearest even.  bf16/e4m3 stores round to
  *             nearest even; e4m3 saturates at +-448.
  *  Limits: d a multiple of 32 with 32 <= d <= 1024; for packed output r a
- *  multiple of 8 with 0 <= r <= d; m >= 1; e_begin >= 0.
+ *  multiple of 8 with 0 <= r <= d and d + r a multiple of 16 (16-byte rows);
+ *  m >= 1; e_begin >= 0.
  */
 int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
                 const float* z, int z_ch, int64_t z_bstride, const float* bias,

@@ -81,9 +81,11 @@ def test_index_topk_parity(gpu, case):
     print("case %s: queries with tie swaps %d, largest gap %.3g" % (case[0], n_sw, gap))
 
 
-def test_index_topk_ties_take_the_smallest_indices(gpu):
-    # every key identical -> every score ties -> the first k indices win
-    B, Tq, H_I, d_I, N, k = 1, 2, 16, 128, 3000, 100
+@pytest.mark.parametrize("N,k", [(3000, 100), (30000, 1024)])
+def test_index_topk_ties_take_the_smallest_indices(gpu, N, k):
+    # every key identical -> every score ties -> the first k indices win (the larger
+    # case leaves more tied candidates than the merge's bounded survivor buffer)
+    B, Tq, H_I, d_I = 1, 2, 16, 128
     q = gen.normal((B, Tq, H_I, d_I), 1)
     key = gen.normal((1, 1, d_I), 2).expand(B, N, d_I).contiguous()
     w = torch.ones((B, Tq, H_I))
