@@ -131,6 +131,8 @@ int validate_attend(const char* fn, const void* q, int q_fmt, const void* kv_c, 
         return fail(CSL_EUNSUPPORTED, "%s: q_fmt must be F32 with F32 KV and BF16 with BF16/packed KV", fn);
     if (kv_fmt == CSL_KV_PACKED && (r < 0 || r > d || r % 8 != 0 || (d - r) % 16 != 0 || (d + r) % 16 != 0))
         return fail(CSL_EINVAL, "%s: packed rows need r %% 8 == 0, (d-r) %% 16 == 0, (d+r) %% 16 == 0", fn);
+    if (kv_fmt == CSL_KV_PACKED && 4 * r > d)
+        return fail(CSL_EUNSUPPORTED, "%s: packed rows with r = %d > d/4 are not built", fn, r);
     if (out_fmt != CSL_F32 && out_fmt != CSL_BF16) return fail(CSL_EINVAL, "%s: out_fmt must be F32 or BF16", fn);
     if (B * (int64_t)Tq == 0) return CSL_OK;
     if (!q || !q_pos || !out) return fail(CSL_EINVAL, "%s: null q, q_pos or out", fn);

@@ -11,10 +11,9 @@
 //
 // Design (gfx950): a block owns one query token x 64 heads x one split of the
 // attended row list (CSA: the selected indices then the window; HCA: entries
-// 0..n(t)-1 then the window).  Rows are gathered 32 at a time with the direct
-// global->LDS loads of gfx950 (no staging registers), one tile ahead of the
-// compute, then converted once into a padded bf16 tile (fp8 -> bf16 with the
-// hardware OCP conversion).  Each of the 4 waves owns 16 heads: S = Q.K^T with
+// 0..n(t)-1 then the window).  Rows are gathered 32 at a time into registers,
+// one tile ahead of the compute, then converted once into a padded bf16 LDS tile
+// (fp8 -> bf16 with the hardware OCP conversion).  Each of the 4 waves owns 16 heads: S = Q.K^T with
 // 16x16x32 bf16 MFMA (Q in registers, K fragments from LDS), an online softmax
 // on the accumulators with a lazy rescale, P staged through LDS, then O += P.V
 // with V fragments read from the same row-major tile by the gfx950 LDS transpose
@@ -41,43 +40,52 @@ template <int D, int FMT>
 struct AttLds {
     static constexpr bool F32P = FMT == F32;
     static constexpr int KSTR = F32P ? D + 4 : D + 8;          // elements per K-tile row (bank padding)
-    static constexpr int PSTR = F32P ? ATT_TILE + 4 : ATT_TILE + 8;
-    static constexpr int ESZ = F32P ? 4 : 2;
     static constexpr int KL_ELEMS = ATT_TILE * KSTR;
-    static constexpr int RAW_BYTES = ATT_TILE * D * (F32P ? 4 : 2);   // largest stored row: bf16 / fp32
-    static constexpr int PL_ELEMS = 4 * 16 * PSTR;
+    // 16-byte chunks of the longest stored row (packed rows: r <= D/4 RoPE dims)
+    static constexpr int CPR_MAX = F32P ? D / 4 : (FMT == BF16 ? D / 8 : (D + D / 4) / 16);
+    static constexpr int NJ = (ATT_TILE * CPR_MAX + ATT_NT - 1) / ATT_NT;   // chunks per thread per tile
 };
 constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (host plan)
 
-// Position of key e (0..7) of an 8-key group inside P's LDS row: even keys first,
-// then odd ones, matching the row order of the transposed V reads below.
-__device__ __forceinline__ int p_perm(int key) { return (key & ~7) + ((key & 1) ? 4 + ((key & 7) >> 1) : ((key & 7) >> 1)); }
-
 constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap moves; every lane ends with identical bits.
+__device__ __forceinline__ float cross4_max(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float cross4_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// 16x16x16 bf16 MFMA: A lane l = row l%16, k 4*(l/16)..+4; B lane l = col l%16, same k.
+__device__ __forceinline__ v4f mfma_bf16_k16(const u32x2& a, const u32x2& b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);
+}
 
 template <int D, int FMT>
 __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     using L = AttLds<D, FMT>;
     constexpr bool F32P = L::F32P;
-    constexpr int KSTR = L::KSTR, PSTR = L::PSTR;
+    constexpr int KSTR = L::KSTR;
     using KT = typename std::conditional<F32P, float, uint16_t>::type;
-    // separate LDS objects: the asynchronous global->LDS loads only ever write `raw`,
-    // which lets the compiler see that reads of the K tile and P do not alias them
     __shared__ __attribute__((aligned(16))) KT kl_s[L::KL_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint8_t raw[L::RAW_BYTES];
-    __shared__ __attribute__((aligned(16))) KT pl_s[L::PL_ELEMS];
     __shared__ const uint8_t* rowptr[2 * ATT_TILE];
-    __shared__ int rowok[2 * ATT_TILE];
+    __shared__ uint32_t rowmask[2];
     __shared__ int sidx[ATT_MAX_SIDX];
     uint8_t* kl = (uint8_t*)kl_s;
-    uint8_t* pl = (uint8_t*)pl_s;
     const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
 
     const int sp = blockIdx.x, hb = blockIdx.y;
     const int64_t bq = blockIdx.z;
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-
     const int64_t t = a.q_pos[bq];
     const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
     const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
@@ -96,10 +104,16 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         for (int64_t v = v_begin + tid; v < e_end; v += ATT_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
     }
 
-    // ---- Q fragments (A operand): head h = hb*64 + wv*16 + col
+    // ---- Q fragments (B operand of S^T = K Q^T): head h = hb*64 + wv*16 + col.  The
+    //      first QR k-steps live in registers; for d = 512 the last QL k-steps are
+    //      read from LDS, which keeps the kernel inside 256 registers (two blocks/CU).
     const int h_a = hb * 64 + wv * 16 + col;
     constexpr int QKS = F32P ? D / 4 : D / 32;
-    u32x4 qb[F32P ? 1 : QKS];
+    constexpr int QL = (!F32P && D == 512) ? (FMT == BF16 ? 12 : 8) : 0;
+    constexpr int QR = QKS - QL;
+    constexpr int QSTR = QL * 32 + 8;                   // bf16 per head row in LDS (16-byte pad)
+    __shared__ __attribute__((aligned(16))) uint16_t ql_s[QL > 0 ? 64 * QSTR : 8];
+    u32x4 qb[F32P ? 1 : QR];
     float qf[F32P ? QKS : 1];
     if constexpr (F32P) {
         const float* qrow = (const float*)a.q + (bq * a.H + h_a) * D;
@@ -108,70 +122,88 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     } else {
         const uint8_t* qrow = a.q + (bq * a.H + h_a) * (int64_t)D * 2;
 #pragma unroll
-        for (int ks = 0; ks < QKS; ++ks)
+        for (int ks = 0; ks < QR; ++ks)
             qb[ks] = h_a < a.H ? *(const u32x4*)(qrow + (32 * ks + 8 * g) * 2) : u32x4{0, 0, 0, 0};
+        if constexpr (QL > 0) {
+            for (int c = tid; c < 64 * QL * 4; c += ATT_NT) {
+                const int hq = c / (QL * 4), pc = c - hq * (QL * 4);
+                const int hg = hb * 64 + hq;
+                const u32x4 v = hg < a.H ? *(const u32x4*)(a.q + ((bq * a.H + hg) * (int64_t)D + 32 * QR + 8 * pc) * 2)
+                                         : u32x4{0, 0, 0, 0};
+                *(u32x4*)(ql_s + hq * QSTR + 8 * pc) = v;
+            }
+        }
     }
     __syncthreads();
 
-    // rows of tile `it` -> rowptr/rowok slot it&1 (threads 0..TILE-1)
+    // rows of tile `it` -> rowptr slot it&1 and the validity mask (wave 0, lanes 0..31)
     auto resolve = [&](int it) {
-        if (tid < ATT_TILE) {
-            const int64_t v = v_begin + (int64_t)it * ATT_TILE + tid;
+        if (tid < 64) {
             const uint8_t* p = nullptr;
-            if (v < v_end) {
-                if (v < n_ent) {
-                    const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
-                    if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
-                } else {
-                    const int64_t pos = w0 + (v - n_ent);
-                    int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
-                    if (slot < 0) slot += a.kvw_rows;
-                    p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
+            if (tid < ATT_TILE) {
+                const int64_t v = v_begin + (int64_t)it * ATT_TILE + tid;
+                if (v < v_end) {
+                    if (v < n_ent) {
+                        const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
+                        if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+                    } else {
+                        const int64_t pos = w0 + (v - n_ent);
+                        int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
+                        if (slot < 0) slot += a.kvw_rows;
+                        p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
+                    }
                 }
+                rowptr[(it & 1) * ATT_TILE + tid] = p;
             }
-            rowptr[(it & 1) * ATT_TILE + tid] = p;
-            rowok[(it & 1) * ATT_TILE + tid] = p != nullptr;
+            const uint64_t m = __ballot(p != nullptr);
+            if (tid == 0) rowmask[it & 1] = (uint32_t)m;
         }
     };
-    // asynchronous gather of tile `it` into the raw LDS tile: lane l of a wave writes
-    // chunk 64*wc + l at raw + 1024*wc + 16*l (direct global -> LDS loads)
-    auto gather = [&](int it) {
+    // Register prefetch of a tile: thread `tid` owns chunks c = tid + ATT_NT*j of the
+    // tile (row c / cpr, 16-byte piece c % cpr), the same for every tile.  The loads
+    // of tile it+1 are issued right after tile it reaches LDS and are consumed at the
+    // top of the next iteration, so a whole tile of MFMA work hides their latency.
+    // Every load is issued (an empty row re-reads the query row and is zeroed), which
+    // keeps the load stream branch-free.
+    constexpr int NJ = L::NJ;
+    u32x4 R[NJ];
+    uint32_t okm = 0;
+    auto load_regs = [&](int it) {
         const uint8_t** rp = rowptr + (it & 1) * ATT_TILE;
-        for (int wc = wv; wc * 64 < nch; wc += ATT_NT / 64) {
-            const int c = wc * 64 + lane;
-            if (c < nch) {
-                const int rr = c / cpr, pc = c - rr * cpr;
-                const uint8_t* p = rp[rr];
-                if (p)
-                    __builtin_amdgcn_global_load_lds((const void*)(p + 16 * pc),
-                                                     (__attribute__((address_space(3))) void*)(raw + 1024 * wc), 16, 0, 0);
-            }
+        okm = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = tid + ATT_NT * j;
+            const int rr = c / cpr;
+            const uint8_t* p = c < nch ? rp[rr] : nullptr;
+            const bool okc = p != nullptr;
+            R[j] = ld_global<u32x4>(okc ? p + 16 * (c - rr * cpr) : a.q);
+            okm |= okc ? 1u << j : 0u;
         }
     };
 
     constexpr int NDB = D / 16;
-    v4f o[NDB];
+    v4f o[NDB];          // O^T: lane holds dims 16*db + 4g + i of head col
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float l_run[4] = {0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = a.scale * CSL_LOG2E;
     const int nch_bf = FMT == KV_PACKED ? a.r / 8 : cpr;    // chunks stored as bf16
 
     if (ntiles > 0) {
         resolve(0);
         __syncthreads();
-        gather(0);
+        load_regs(0);
     }
     for (int it = 0; it < ntiles; ++it) {
-        const int* ok = rowok + (it & 1) * ATT_TILE;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // ---- convert the raw tile into the padded compute-dtype K tile
-        for (int c = tid; c < nch; c += ATT_NT) {
+        lds_barrier();                                  // the previous tile's K/V reads are done
+        // ---- the prefetched chunks -> the padded compute-dtype K tile
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = tid + ATT_NT * j;
+            if (c >= nch) continue;
             const int rr = c / cpr, pc = c - rr * cpr;
-            u32x4 v = *(const u32x4*)(raw + 16 * c);
-            if (!ok[rr]) v = u32x4{0, 0, 0, 0};
+            const u32x4 v = ((okm >> j) & 1u) ? R[j] : u32x4{0, 0, 0, 0};
             if constexpr (F32P) {
                 *(u32x4*)(kl + ((size_t)rr * KSTR + 4 * pc) * 4) = v;
             } else if (FMT == BF16 || pc < nch_bf) {
@@ -189,146 +221,127 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
             }
         }
         if (it + 1 < ntiles) resolve(it + 1);
-        lds_barrier();
-        if (it + 1 < ntiles) gather(it + 1);          // overlaps the MFMA work below
-        // ---- S = Q K^T for this wave's 16 heads x 32 rows: two independent MFMA
-        //      chains (rows 0-15, 16-31), operands read one k-step ahead
+        lds_barrier();                                  // K tile and the next rows' pointers visible
+        if (it + 1 < ntiles) load_regs(it + 1);         // in flight during the MFMA work below
+        const uint32_t rmask = rowmask[it & 1];
+        // ---- S^T = K Q^T: rows 16*r2 + 4g + i of head col, two independent MFMA chains
         v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
         if constexpr (F32P) {
             const float* k0 = (const float*)kl + (size_t)col * KSTR + g;
             const float* k1 = k0 + 16 * KSTR;
-            float b0 = k0[0], b1 = k1[0];
 #pragma unroll
             for (int ks = 0; ks < QKS; ++ks) {
-                float n0 = 0.f, n1 = 0.f;
-                if (ks + 1 < QKS) { n0 = k0[4 * (ks + 1)]; n1 = k1[4 * (ks + 1)]; }
-                s[0] = mfma_f32(qf[ks], b0, s[0]);
-                s[1] = mfma_f32(qf[ks], b1, s[1]);
-                b0 = n0; b1 = n1;
+                s[0] = mfma_f32(k0[4 * ks], qf[ks], s[0]);
+                s[1] = mfma_f32(k1[4 * ks], qf[ks], s[1]);
             }
         } else {
             const uint8_t* k0 = kl + ((size_t)col * KSTR + 8 * g) * 2;
             const uint8_t* k1 = k0 + (size_t)16 * KSTR * 2;
-            u32x4 b0 = *(const u32x4*)k0, b1 = *(const u32x4*)k1;
 #pragma unroll
-            for (int ks = 0; ks < QKS; ++ks) {
-                u32x4 n0 = b0, n1 = b1;
-                if (ks + 1 < QKS) { n0 = *(const u32x4*)(k0 + 64 * (ks + 1)); n1 = *(const u32x4*)(k1 + 64 * (ks + 1)); }
-                s[0] = mfma_bf16(qb[ks], b0, s[0]);
-                s[1] = mfma_bf16(qb[ks], b1, s[1]);
-                b0 = n0; b1 = n1;
+            for (int ks = 0; ks < QR; ++ks) {
+                s[0] = mfma_bf16(*(const u32x4*)(k0 + 64 * ks), qb[ks], s[0]);
+                s[1] = mfma_bf16(*(const u32x4*)(k1 + 64 * ks), qb[ks], s[1]);
+            }
+            const uint16_t* qlp = ql_s + (wv * 16 + col) * QSTR + 8 * g;
+#pragma unroll
+            for (int ks = QR; ks < QKS; ++ks) {
+                const u32x4 qv = *(const u32x4*)(qlp + 32 * (ks - QR));
+                s[0] = mfma_bf16(*(const u32x4*)(k0 + 64 * ks), qv, s[0]);
+                s[1] = mfma_bf16(*(const u32x4*)(k1 + 64 * ks), qv, s[1]);
             }
         }
-        // ---- online softmax (base 2), lazy rescale; lane holds heads 4g+i of rows nb*16+col
-        const bool ok0 = ok[col] != 0, ok1 = ok[16 + col] != 0;
-        float p0[4], p1[4], corr[4];
-        bool need = false;
+        // ---- online softmax (base 2) for head col over this tile's 32 rows, lazy rescale
+        float x[2][4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = ok0 ? s[0][i] * sl2 : -INFINITY;
-            const float x1 = ok1 ? s[1][i] * sl2 : -INFINITY;
-            float mx = fmaxf(x0, x1);
-            mx = fmaxf(mx, shfl_xor(mx, 1));
-            mx = fmaxf(mx, shfl_xor(mx, 2));
-            mx = fmaxf(mx, shfl_xor(mx, 4));
-            mx = fmaxf(mx, shfl_xor(mx, 8));
-            corr[i] = 1.f;
-            if (mx > m_run[i] + ATT_TAU) {           // the reference max moves up
-                corr[i] = exp2f(m_run[i] - mx);      // 0 on the first valid tile
-                m_run[i] = mx;
-                need = true;
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool okr = (rmask >> (16 * r2 + 4 * g + i)) & 1u;
+                x[r2][i] = okr ? s[r2][i] * sl2 : -INFINITY;
+                mx = fmaxf(mx, x[r2][i]);
             }
-            const float e0 = m_run[i] == -INFINITY ? 0.f : exp2f(x0 - m_run[i]);
-            const float e1 = m_run[i] == -INFINITY ? 0.f : exp2f(x1 - m_run[i]);
-            float rs = e0 + e1;
-            rs += shfl_xor(rs, 1);
-            rs += shfl_xor(rs, 2);
-            rs += shfl_xor(rs, 4);
-            rs += shfl_xor(rs, 8);
-            l_run[i] = l_run[i] * corr[i] + rs;
-            p0[i] = e0;
-            p1[i] = e1;
+        mx = cross4_max(mx);
+        float corr = 1.f;
+        const bool need = mx > m_run + ATT_TAU;             // the reference max moves up
+        if (need) {
+            corr = exp2f(m_run - mx);                        // 0 on the first valid tile
+            m_run = mx;
         }
+        float rs = 0.f;
+        u32x2 pb[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[r2][i] = m_run == -INFINITY ? 0.f : exp2f(x[r2][i] - m_run);
+                rs += x[r2][i];
+            }
+            pb[r2] = u32x2{f32_to_bf16_rne(x[r2][0]) | (f32_to_bf16_rne(x[r2][1]) << 16),
+                           f32_to_bf16_rne(x[r2][2]) | (f32_to_bf16_rne(x[r2][3]) << 16)};
+        }
+        l_run = l_run * corr + cross4_sum(rs);
         if (__builtin_amdgcn_read_exec() & __ballot(need)) {   // wave-uniform: some head rescaled
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[db][i] *= corr[i];
+                for (int i = 0; i < 4; ++i) o[db][i] *= corr;
         }
-        // ---- P -> LDS: pl[wave][head 4g+i][row position]
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 4 * g + i;
-            if constexpr (F32P) {
-                float* pr = (float*)pl + ((size_t)wv * 16 + hh) * PSTR;
-                pr[col] = p0[i];
-                pr[16 + col] = p1[i];
-            } else {
-                uint16_t* pr = (uint16_t*)pl + ((size_t)wv * 16 + hh) * PSTR;
-                pr[p_perm(col)] = (uint16_t)f32_to_bf16_rne(p0[i]);
-                pr[p_perm(16 + col)] = (uint16_t)f32_to_bf16_rne(p1[i]);
-            }
-        }
-        lds_barrier();
-        // ---- O += P V
+        // ---- O^T += V^T P^T: P^T (rows x heads) is the S^T accumulator layout, so the
+        //      probabilities never leave registers
         if constexpr (F32P) {
-            const float* pr = (const float*)pl + ((size_t)wv * 16 + col) * PSTR;
             const float* kf = (const float*)kl;
 #pragma unroll
-            for (int ks = 0; ks < ATT_TILE / 4; ++ks) {
-                const float pa = pr[4 * ks + g];
-                const float* vr = kf + (size_t)(4 * ks + g) * KSTR + col;
+            for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] = mfma_f32(pa, vr[16 * db], o[db]);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const float* vr = kf + (size_t)(16 * r2 + 4 * g + i) * KSTR + col;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) o[db] = mfma_f32(vr[16 * db], x[r2][i], o[db]);
+                }
         } else {
-            // k slot j of lane group g holds key 8g + 2j (j < 4) or 8g + 2(j-4) + 1: the
-            // source rows of one transposed read are 2 apart, which spreads them over
-            // all 32 banks (row stride = 4 banks mod 32)
-            const u32x4 pa = *(const u32x4*)((const uint16_t*)pl + ((size_t)wv * 16 + col) * PSTR + 8 * g);
+            // V^T fragments by the LDS transpose read: source lane 16g + s reads the four
+            // dims 16*db + 4*(s%4).. of row 16*r2 + 4g + s/4, so lane (g, col) receives
+            // dim 16*db + col of rows 16*r2 + 4g + 0..3
             const uint16_t* kb = (const uint16_t*)kl;
-            const uint16_t* v0p = kb + (size_t)(8 * g + 2 * (col >> 2)) * KSTR + 4 * (col & 3);
-            const uint16_t* v1p = v0p + KSTR;
-            u32x2 r0 = lds_read_tr16(v0p), r1 = lds_read_tr16(v1p);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                u32x2 n0 = r0, n1 = r1;
-                if (db + 1 < NDB) { n0 = lds_read_tr16(v0p + 16 * (db + 1)); n1 = lds_read_tr16(v1p + 16 * (db + 1)); }
-                const u32x4 vb = {r0[0], r0[1], r1[0], r1[1]};
-                o[db] = mfma_bf16(pa, vb, o[db]);
-                r0 = n0; r1 = n1;
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const uint16_t* vp = kb + (size_t)(16 * r2 + 4 * g + (col >> 2)) * KSTR + 4 * (col & 3);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[db] = mfma_bf16_k16(lds_read_tr16(vp + 16 * db), pb[r2], o[db]);
             }
         }
-        // the next iteration starts with a full barrier before the K tile is rewritten
+        // the next iteration starts with a barrier before the K tile is rewritten
     }
 
     // ---- finish: normalise, write output or the split's partial
+    const int hh = wv * 16 + col;                  // head within the block
+    const int h = hb * 64 + hh;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
+    if (a.nsplit == 1) {
+        if (h < a.H) {
+            if (a.out_fmt == F32) {
+                float* orow = (float*)a.out + (bq * a.H + h) * D + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int hh = wv * 16 + 4 * g + i;       // head within the block
-        const int h = hb * 64 + hh;
-        const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
-        const float lse = l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * CSL_LN2 : -INFINITY;
-        if (a.nsplit == 1) {
-            if (h < a.H) {
-                if (a.out_fmt == F32) {
-                    float* orow = (float*)a.out + (bq * a.H + h) * D;
+                for (int db = 0; db < NDB; ++db)
+                    *(float4*)(orow + 16 * db) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+            } else {
+                uint16_t* orow = (uint16_t*)a.out + (bq * a.H + h) * D + 4 * g;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) orow[16 * db + col] = o[db][i] * inv;
-                } else {
-                    uint16_t* orow = (uint16_t*)a.out + (bq * a.H + h) * D;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) orow[16 * db + col] = (uint16_t)f32_to_bf16_rne(o[db][i] * inv);
-                }
-                if (a.lse && col == 0) a.lse[bq * a.H + h] = lse;
+                for (int db = 0; db < NDB; ++db)
+                    *(u32x2*)(orow + 16 * db) = u32x2{f32_to_bf16_rne(o[db][0] * inv) | (f32_to_bf16_rne(o[db][1] * inv) << 16),
+                                                      f32_to_bf16_rne(o[db][2] * inv) | (f32_to_bf16_rne(o[db][3] * inv) << 16)};
             }
-        } else {
-            const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
-            float* orow = a.ws_o + prow * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) orow[16 * db + col] = o[db][i] * inv;
-            if (col == 0) a.ws_lse[prow] = lse;
+            if (a.lse && g == 0) a.lse[bq * a.H + h] = lse;
         }
+    } else {
+        const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
+        float* orow = a.ws_o + prow * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            *(float4*)(orow + 16 * db) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+        if (g == 0) a.ws_lse[prow] = lse;
     }
 }
 

@@ -132,6 +132,38 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, 64); }
 
+// Load through a pointer known to address global memory.  A pointer that went
+// through LDS (or any generic pointer the compiler cannot trace to a kernel
+// argument) would otherwise become a flat load, which also counts against the LDS
+// wait counter: every later LDS wait would then wait for the global load too.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+
+// Reductions over each row of 16 lanes with DPP moves (VALU, no LDS round trip):
+// swap neighbours, swap pairs, mirror the halves of 8, mirror the halves of 16.
+// After each step the partners hold identical values, so every lane of the row ends
+// with the same bits (the sum is order-independent only up to commutativity).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));     // quad_perm(1,0,3,2)
+    x = fmaxf(x, dpp_mov<0x4E>(x));     // quad_perm(2,3,0,1)
+    x = fmaxf(x, dpp_mov<0x141>(x));    // row_half_mirror
+    x = fmaxf(x, dpp_mov<0x140>(x));    // row_mirror
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x141>(x);
+    x += dpp_mov<0x140>(x);
+    return x;
+}
+
 // max(x, 0) as an integer max on the bit pattern: negative floats are negative
 // integers, non-negative floats keep their bits (one instruction, no NaN quieting).
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }

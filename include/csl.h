@@ -146,7 +146,8 @@ size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
  *             buffer (kvw_pos0 = its first position) or a ring (kvw_pos0 = 0).  The
  *             caller keeps positions t-W+1 .. t resident.
  *  out        [B][Tq][H][d], out_fmt CSL_F32 or CSL_BF16;  out_lse fp32 [B][Tq][H] or NULL.
- *  Limits: d in {64, 128, 256, 512}; packed: r multiple of 8, d-r multiple of 16.
+ *  Limits: d in {64, 128, 256, 512}; packed: r multiple of 8, d-r multiple of 16,
+ *  r <= d/4 (CSL_EUNSUPPORTED beyond).
  *  ws         device workspace of at least csl_attend_workspace(...) bytes
  *             (split partials; may be NULL when that size is 0).
  */
