@@ -81,7 +81,8 @@ size_t index_ws(int B, int Tq, int S, int nslices, int kk) {
     return q * index_cst(nslices, kk) * 8 + q * nslices * 4 + 512;
 }
 
-constexpr int ATT_TILE = 32;
+constexpr int ATT_STEP = 32;            // rows a block stages per iteration; split lengths are multiples
+constexpr int ATT_TARGET_BLOCKS = 256;  // one block (4 waves, one per SIMD) per compute unit
 constexpr int ATT_MIN_RPS = 128;
 constexpr int ATT_MAX_SPLIT = 128;
 
@@ -91,11 +92,11 @@ void plan_attend(int B, int Tq, int H, int64_t rows_max, bool csa, int& nhb, int
     nhb = (H + 63) / 64;
     const int64_t L = rows_max > 0 ? rows_max : 1;
     const int64_t total_q = (int64_t)B * Tq * nhb;
-    int64_t ns = total_q > 0 ? (512 + total_q - 1) / total_q : 1;
+    int64_t ns = total_q > 0 ? (ATT_TARGET_BLOCKS + total_q - 1) / total_q : 1;
     if (ns < 1) ns = 1;
     if (ns > ATT_MAX_SPLIT) ns = ATT_MAX_SPLIT;
     int64_t r = (L + ns - 1) / ns;
-    r = (r + ATT_TILE - 1) / ATT_TILE * ATT_TILE;
+    r = (r + ATT_STEP - 1) / ATT_STEP * ATT_STEP;
     if (r < ATT_MIN_RPS) r = ATT_MIN_RPS;
     if (csa && r > ATT_MAX_CSA_RPS) r = ATT_MAX_CSA_RPS;
     rps = (int)r;

@@ -48,6 +48,8 @@ struct AttLds {
 constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (host plan)
 
 constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
+constexpr float ATT_HEADROOM = 64.0f;   // largest x - m_ref (base 2) accepted without a rescale
+constexpr float ATT_REF_LIFT = 32.0f;   // m_ref starts this far above the first tile's largest logit
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
 // the gfx950 row-swap moves; every lane ends with identical bits.
@@ -345,6 +347,326 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 / packed rows: register-blocked kernel.  A block (4 waves) owns one query
+// x 64 heads x one split.  Wave w covers heads 32*(w&1) .. +31 as two 16-head MFMA
+// blocks, and the half w>>1 of the head dim: every K or V fragment it reads from
+// LDS feeds two MFMAs (one per head block).  Q (32 heads x d/2, bf16) and O^T (32
+// heads x d/2, fp32) stay in registers (one wave per SIMD holds up to 512).
+//   S^T = K Q^T : 16x16x32 bf16 over the wave's d/2 dims (A = K rows from LDS,
+//   B = Q from registers); the two halves are added through LDS, in the same
+//   order by both waves, so they hold bit-identical scores and softmax state.
+//   O^T += V^T P^T : 16x16x32 bf16 over the 32 rows of the tile; lane slot j < 4
+//   is row 4g + j and slot 4 + j is row 16 + 4g + j, which is how the S^T
+//   accumulators sit in the lane, so P never leaves registers; V^T comes from two
+//   LDS transpose reads (rows 4g.. and 16 + 4g..).
+// ---------------------------------------------------------------------------
+template <int D, int FMT>
+struct MqLds {
+    static constexpr int KSTR = D + 8;                           // bf16 per K-tile row
+    static constexpr int TILE_ELEMS = ATT_TILE * KSTR;
+    // 16-byte chunks per thread and tile: bf16 chunks (RoPE dims, or every dim of a
+    // bf16 row) and fp8 chunks (the other dims of a packed row, r <= D/4)
+    static constexpr int JB = FMT == BF16 ? (ATT_TILE * D / 8 + ATT_NT - 1) / ATT_NT : (ATT_TILE * D / 4 / 8 + ATT_NT - 1) / ATT_NT;
+    static constexpr int J8 = FMT == BF16 ? 0 : (ATT_TILE * D / 16 + ATT_NT - 1) / ATT_NT;
+};
+
+template <int D, int FMT>
+__global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
+    using L = MqLds<D, FMT>;
+    constexpr int KSTR = L::KSTR;
+    constexpr int QH = D / 64;                          // k-steps of 32 dims per half
+    constexpr int NDH = D / 32;                         // 16-dim output blocks per half
+    constexpr int JB = L::JB, J8 = L::J8, NJ = JB + J8;
+    constexpr int PF = 3;                               // tiles whose rows are in flight
+    constexpr int NSLOT = PF + 1;                       // row-pointer slots
+    __shared__ __attribute__((aligned(16))) uint16_t kl_s[L::TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) v4f sx[4 * 2 * 2 * 64];   // [wave][r2][hk][lane]
+    __shared__ const uint8_t* rowptr[NSLOT * ATT_TILE];
+    __shared__ uint32_t rowmask[NSLOT];
+    __shared__ int sidx[ATT_MAX_SIDX];
+    uint8_t* kl = (uint8_t*)kl_s;
+    const int rbf = FMT == BF16 ? D : a.r;              // dims stored as bf16
+    const int64_t rb = FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r);
+
+    const int sp = blockIdx.x, hb = blockIdx.y;
+    const int64_t bq = blockIdx.z;
+    const int b = (int)(bq / a.Tq);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int hg = wv & 1, dh = wv >> 1;
+    const int64_t t = a.q_pos[bq];
+    const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
+    const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
+    const int64_t w0 = t - n_win + 1;
+    const int64_t L_all = n_ent + n_win;
+    const int64_t v_begin = (int64_t)sp * a.rps;
+    int64_t v_end = v_begin + a.rps;
+    if (v_end > L_all) v_end = L_all;
+    const int ntiles = v_end > v_begin ? (int)((v_end - v_begin + ATT_TILE - 1) / ATT_TILE) : 0;
+
+    if (a.idx) {
+        const int64_t e_end = v_end < n_ent ? v_end : n_ent;
+        for (int64_t v = v_begin + tid; v < e_end; v += ATT_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
+    }
+    // Q fragments (B operands of S^T = K Q^T) of the wave's two head blocks, its dims
+    u32x4 qb[2][QH];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+        const int h = hb * 64 + 32 * hg + 16 * hk + col;
+        const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
+#pragma unroll
+        for (int ks = 0; ks < QH; ++ks) {
+            const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
+            qb[hk][ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
+        }
+    }
+    // this thread's chunks of a tile, the same for every tile: j < JB are bf16 chunks
+    // (row, 16-byte piece of the first 2*rbf bytes), the others fp8 chunks (row,
+    // 16-byte piece of the fp8 part); -1 when beyond the tile
+    int crow[NJ], cpc[NJ];
+    {
+        const int nbc = rbf / 8, n8c = (D - rbf) / 16;   // chunks per row of each kind
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const bool bf = j < JB;
+            const int c = tid + ATT_NT * (bf ? j : j - JB);
+            const int per = bf ? nbc : n8c;
+            crow[j] = (per > 0 && c < ATT_TILE * per) ? c / per : -1;
+            cpc[j] = per > 0 ? c - (c / per) * per : 0;
+        }
+    }
+    __syncthreads();
+
+    // rows of tile `it` -> rowptr slot it % NSLOT and the validity mask (wave 0)
+    auto resolve = [&](int it) {
+        if (tid < 64) {
+            const uint8_t* p = nullptr;
+            if (tid < ATT_TILE) {
+                const int64_t v = v_begin + (int64_t)it * ATT_TILE + tid;
+                if (v < v_end) {
+                    if (v < n_ent) {
+                        const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
+                        if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+                    } else {
+                        const int64_t pos = w0 + (v - n_ent);
+                        int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
+                        if (slot < 0) slot += a.kvw_rows;
+                        p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
+                    }
+                }
+                rowptr[(it % NSLOT) * ATT_TILE + tid] = p;
+            }
+            const uint64_t m = __ballot(p != nullptr);
+            if (tid == 0) rowmask[it % NSLOT] = (uint32_t)m;
+        }
+    };
+    // Register prefetch, PF tiles deep.  Every load is issued (an empty row re-reads
+    // the query row; its chunks are zeroed when the tile is written to LDS), which
+    // keeps the load stream branch-free.
+    auto load_regs = [&](int it, u32x4 (&Rb)[NJ]) {
+        const uint8_t** rp = rowptr + (it % NSLOT) * ATT_TILE;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const uint8_t* p = crow[j] >= 0 ? rp[crow[j]] : nullptr;
+            const int off = j < JB ? 16 * cpc[j] : 2 * rbf + 16 * cpc[j];
+            Rb[j] = ld_global<u32x4>(p ? p + off : a.q);
+        }
+    };
+
+    // Softmax with a fixed reference per head: m_ref = ATT_REF_LIFT above the largest
+    // logit (base 2) of the first tile that has a valid row; every probability is
+    // exp2(x - m_ref) and is never rescaled, so the O^T accumulators stay in place.
+    // fp32 / bf16 hold x - m_ref <= ATT_HEADROOM with room to spare; if a later logit
+    // goes beyond, the block recomputes its split once with m_ref = the largest logit.
+    v4f o[2][NDH];
+    float m_ref[2], l_lane[2], m_seen[2] = {-INFINITY, -INFINITY};
+    const float sl2 = a.scale * CSL_LOG2E;
+    v4f* sx_mine = sx + wv * 256 + lane;
+    const v4f* sx_part = sx + (wv ^ 2) * 256 + lane;
+    u32x4 R0[NJ], R1[NJ], R2[NJ];
+    bool ovf = false;
+
+    // one tile: its prefetched rows (Rb) -> LDS, refill Rb with tile it+PF, then
+    // S^T, probabilities and O^T for the tile
+    auto tile = [&](int it, u32x4 (&Rb)[NJ]) {
+        lds_barrier();                                  // the previous tile's K/V and S reads are done
+        const uint32_t rmask = rowmask[it % NSLOT];
+        const bool full = rmask == 0xffffffffu;         // wave-uniform
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (crow[j] < 0) continue;
+            u32x4 v = Rb[j];
+            if (!full && !((rmask >> crow[j]) & 1u)) v = u32x4{0, 0, 0, 0};
+            uint8_t* rowp = kl + (size_t)crow[j] * KSTR * 2;
+            if (j < JB) {
+                *(u32x4*)(rowp + 16 * cpc[j]) = v;
+            } else {
+                typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+                u32x4 lo, hi;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    lo[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.0f, false));
+                    lo[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e], 1.0f, true));
+                    hi[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e + 2], 1.0f, false));
+                    hi[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[e + 2], 1.0f, true));
+                }
+                uint8_t* dst = rowp + (rbf + 16 * cpc[j]) * 2;
+                *(u32x4*)dst = lo;
+                *(u32x4*)(dst + 16) = hi;
+            }
+        }
+        if (it + PF < ntiles) resolve(it + PF);
+        lds_barrier();                                  // K tile and the row pointers of tile it+PF visible
+        if (it + PF < ntiles) load_regs(it + PF, Rb);
+        // ---- partial S^T over this wave's half of the dims: s[r2][hk]
+        v4f s[2][2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) s[r2][hk] = v4f{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* k0 = kl_s + (size_t)col * KSTR + 32 * QH * dh + 8 * g;
+        const uint16_t* k1 = k0 + 16 * KSTR;
+#pragma unroll
+        for (int ks = 0; ks < QH; ++ks) {
+            const u32x4 a0 = *(const u32x4*)(k0 + 32 * ks);
+            const u32x4 a1 = *(const u32x4*)(k1 + 32 * ks);
+            s[0][0] = mfma_bf16(a0, qb[0][ks], s[0][0]);
+            s[1][0] = mfma_bf16(a1, qb[0][ks], s[1][0]);
+            s[0][1] = mfma_bf16(a0, qb[1][ks], s[0][1]);
+            s[1][1] = mfma_bf16(a1, qb[1][ks], s[1][1]);
+            if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) sx_mine[(r2 * 2 + hk) * 64] = s[r2][hk];
+        lds_barrier();                                  // both halves of S^T visible
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) {
+                const v4f p = sx_part[(r2 * 2 + hk) * 64];
+                s[r2][hk] = dh == 0 ? s[r2][hk] + p : p + s[r2][hk];   // low half + high half
+            }
+        // ---- probabilities (lane: head col, rows 16*r2 + 4g + i)
+        u32x4 pb[2];
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+            float x[2][4];
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[r2][i] = s[r2][hk][i] * sl2;
+            if (!full) {
+#pragma unroll
+                for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((rmask >> (16 * r2 + 4 * g + i)) & 1u)) x[r2][i] = -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                             fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            m_seen[hk] = fmaxf(m_seen[hk], mx);
+            if (__builtin_amdgcn_read_exec() & __ballot(m_ref[hk] == -INFINITY)) {   // no reference yet
+                const float tmax = cross4_max(mx);
+                if (m_ref[hk] == -INFINITY && tmax != -INFINITY) m_ref[hk] = tmax + ATT_REF_LIFT;
+            }
+            ovf |= mx > m_ref[hk] + ATT_HEADROOM;
+            const float mr = m_ref[hk] == -INFINITY ? 0.f : m_ref[hk];   // no reference: every x is -inf
+            float ls = 0.f;
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[r2][i] = __builtin_amdgcn_exp2f(x[r2][i] - mr);   // 0 for invalid rows
+                    ls += x[r2][i];
+                }
+            l_lane[hk] += ls;
+            pb[hk] = u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
+                           pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+        }
+        // ---- O^T += V^T P^T over this wave's dims (one V^T fragment feeds both head blocks)
+        const uint16_t* vp0 = kl_s + (size_t)(4 * g + (col >> 2)) * KSTR + 16 * NDH * dh + 4 * (col & 3);
+        const uint16_t* vp1 = vp0 + 16 * KSTR;
+#pragma unroll
+        for (int db = 0; db < NDH; ++db) {
+            const u32x2 t0 = lds_read_tr16(vp0 + 16 * db);
+            const u32x2 t1 = lds_read_tr16(vp1 + 16 * db);
+            const u32x4 va = {t0[0], t0[1], t1[0], t1[1]};
+            o[0][db] = mfma_bf16(va, pb[0], o[0][db]);
+            o[1][db] = mfma_bf16(va, pb[1], o[1][db]);
+            if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+        }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+#pragma unroll
+            for (int db = 0; db < NDH; ++db) o[hk][db] = v4f{0.f, 0.f, 0.f, 0.f};
+            m_ref[hk] = pass == 0 ? -INFINITY : cross4_max(m_seen[hk]);
+            l_lane[hk] = 0.f;
+        }
+        ovf = false;
+        __syncthreads();                                // slots and tiles of a previous pass are free
+        for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
+        __syncthreads();
+        if (0 < ntiles) load_regs(0, R0);
+        if (1 < ntiles) load_regs(1, R1);
+        if (2 < ntiles) load_regs(2, R2);
+        for (int it = 0; it < ntiles; it += PF) {
+            tile(it, R0);
+            if (it + 1 < ntiles) tile(it + 1, R1);
+            if (it + 2 < ntiles) tile(it + 2, R2);
+        }
+        // the whole block redoes the split only if some wave overflowed
+        if (!__syncthreads_or(ovf ? 1 : 0)) break;
+    }
+    float l_run[2], m_run[2];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+        l_run[hk] = cross4_sum(l_lane[hk]);
+        m_run[hk] = m_ref[hk];
+    }
+
+    // ---- finish: normalise, write the output or the split's partial (this wave's dims)
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+        const int hh = 32 * hg + 16 * hk + col;          // head within the block
+        const int h = hb * 64 + hh;
+        const float inv = l_run[hk] > 0.f ? 1.f / l_run[hk] : 0.f;
+        const float lse = l_run[hk] > 0.f ? (m_run[hk] + log2f(l_run[hk])) * CSL_LN2 : -INFINITY;
+        const int d0 = 16 * NDH * dh + 4 * g;
+        if (a.nsplit == 1) {
+            if (h < a.H) {
+                if (a.out_fmt == F32) {
+                    float* orow = (float*)a.out + (bq * a.H + h) * D + d0;
+#pragma unroll
+                    for (int db = 0; db < NDH; ++db)
+                        *(float4*)(orow + 16 * db) = make_float4(o[hk][db][0] * inv, o[hk][db][1] * inv,
+                                                                 o[hk][db][2] * inv, o[hk][db][3] * inv);
+                } else {
+                    uint16_t* orow = (uint16_t*)a.out + (bq * a.H + h) * D + d0;
+#pragma unroll
+                    for (int db = 0; db < NDH; ++db)
+                        *(u32x2*)(orow + 16 * db) =
+                            u32x2{f32_to_bf16_rne(o[hk][db][0] * inv) | (f32_to_bf16_rne(o[hk][db][1] * inv) << 16),
+                                  f32_to_bf16_rne(o[hk][db][2] * inv) | (f32_to_bf16_rne(o[hk][db][3] * inv) << 16)};
+                }
+                if (a.lse && g == 0 && dh == 0) a.lse[bq * a.H + h] = lse;
+            }
+        } else {
+            const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
+            float* orow = a.ws_o + prow * D + d0;
+#pragma unroll
+            for (int db = 0; db < NDH; ++db)
+                *(float4*)(orow + 16 * db) = make_float4(o[hk][db][0] * inv, o[hk][db][1] * inv,
+                                                         o[hk][db][2] * inv, o[hk][db][3] * inv);
+            if (g == 0 && dh == 0) a.ws_lse[prow] = lse;
+        }
+    }
+}
+
 // Merge of split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One block per (query, 4 heads): the 64 heads of a head block spread over 16
 // blocks so that the merge reads its partials with the whole GPU.
@@ -406,7 +728,11 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq));
     const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
     if (a.idx && a.rps > ATT_MAX_SIDX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
+    if constexpr (FMT == F32) {
+        hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_attend_mq<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + 2 * CMB_HEADS);

@@ -79,6 +79,13 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Two fp32 -> two bf16 in one dword (element 0 in the low half), round to nearest
+// even, by the gfx950 packed conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
+
 // 4 fp8 e4m3fn (one dword) -> 4 bf16 (two dwords).  The gfx950 conversion is the
 // OCP e4m3fn decode; every e4m3 value is exact in bf16, so truncation is exact.
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
