@@ -147,3 +147,28 @@ def test_attend_bf16_output_and_determinism(gpu):
     torch.cuda.synchronize()
     assert torch.equal(f1, f2) and torch.equal(l1, l2)
     assert torch.equal(b1, f1.to(torch.bfloat16))
+
+
+def test_logits_far_above_the_first_tile_are_recomputed(gpu):
+    # The first 32 entries are tiny, later ones full size, and the softmax scale is large:
+    # later logits exceed the first tile's maximum by far more than the kernel's fixed
+    # softmax reference allows, so the split must be recomputed with the true maximum.
+    # Without that, exp2 overflows to inf and the output is NaN.
+    fmt, B, H, d, r, N, m, W = O.KV_PACKED, 2, 64, 512, 64, 700, 1, 0
+    x = gen.normal((B, N, d), 611)
+    x[:, :32] *= 0.01
+    kvc = gen.store(x, fmt, r)
+    q = _q(fmt, B, 1, H, d, 612)
+    qpos = gen.positions(B, 1, N - 1).to(torch.int32)
+    kw = dict(W=W, H=H, d=d, r=r, scale=2.0)
+    go, gl = ops.hca_attend(dev(q), dev(kvc), dev(kvc), dev(qpos), kv_fmt=fmt, n_cap=N, m=m, kvw_pos0=0,
+                            kvw_rows=N, **kw)
+    torch.cuda.synchronize()
+    oo, ol = O.hca_attend(_oracle_q(q), O.BF16, host(kvc), fmt, N, m, host(kvc), 0, N, host(qpos), **kw)
+    # the logits span hundreds of binades, so this does reach the recompute path
+    kd = O.decode_rows(host(kvc), fmt, d, r).reshape(B, N, d)
+    s = np.einsum("bhd,bnd->bhn", host(q.float()).astype(np.float64)[:, 0], kd) * 2.0
+    assert (s[..., 32:].max(-1) - s[..., :32].max(-1)).min() * 1.4427 > 96 + 32
+    err = max_abs(host(go), oo)
+    assert np.all(np.isfinite(host(go))) and err <= TOL[fmt], "max-abs %.3g" % err
+    assert max_abs(host(gl), ol) <= 10 * TOL[fmt]
