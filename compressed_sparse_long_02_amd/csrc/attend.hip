@@ -548,8 +548,10 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
                 const v4f p = sx_part[(r2 * 2 + hk) * 64];
                 s[r2][hk] = dh == 0 ? s[r2][hk] + p : p + s[r2][hk];   // low half + high half
             }
-        // ---- probabilities (lane: head col, rows 16*r2 + 4g + i)
-        u32x4 pb[2];
+        // ---- probabilities (lane: head col, rows 16*r2 + 4g + i), as a bf16 pair
+        //      hi + lo: P = hi + lo to ~2^-17 relative, so P.V keeps fp32-level accuracy
+        //      even where V has large channels
+        u32x4 pb[2], pl[2];
 #pragma unroll
         for (int hk = 0; hk < 2; ++hk) {
             float x[2][4];
@@ -582,8 +584,13 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
                     ls += x[r2][i];
                 }
             l_lane[hk] += ls;
-            pb[hk] = u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
-                           pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a0 = x[e >> 1][2 * (e & 1)], a1 = x[e >> 1][2 * (e & 1) + 1];
+                const uint32_t h = pack_bf16x2(a0, a1);
+                pb[hk][e] = h;
+                pl[hk][e] = pack_bf16x2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
+            }
         }
         // ---- O^T += V^T P^T over this wave's dims (one V^T fragment feeds both head blocks)
         const uint16_t* vp0 = kl_s + (size_t)(4 * g + (col >> 2)) * KSTR + 16 * NDH * dh + 4 * (col & 3);
@@ -595,6 +602,8 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
             const u32x4 va = {t0[0], t0[1], t1[0], t1[1]};
             o[0][db] = mfma_bf16(va, pb[0], o[0][db]);
             o[1][db] = mfma_bf16(va, pb[1], o[1][db]);
+            o[0][db] = mfma_bf16(va, pl[0], o[0][db]);
+            o[1][db] = mfma_bf16(va, pl[1], o[1][db]);
             if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
         }
     };

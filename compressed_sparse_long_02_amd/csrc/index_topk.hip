@@ -465,17 +465,11 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
     // Lower bound L of the k-th largest key: slice s reported t_s with at least r_s
     // of its keys >= t_s (r_s = min(its size, ceil(k / nse))).  If the r_s add up to
     // k, at least k keys are >= min_s t_s, so no key below it can be selected.
-    uint32_t L = 0u;
+    bool use_bound = false;
     if (nse > 0) {
         const int r = (a.k + nse - 1) / nse;
         const int64_t sum_r = nfull * (r < a.S ? r : a.S) + (rem > 0 ? (rem < r ? rem : r) : 0);
-        if (sum_r >= a.k) {
-            L = 0xffffffffu;
-            for (int s = 0; s < nse; ++s) {
-                const uint32_t ts = a.tbound[bq * a.nslices + s];
-                L = ts < L ? ts : L;
-            }
-        }
+        use_bound = sum_r >= a.k;
     }
     uint32_t* sh = smem;                                   // TOPK_SCRATCH(MRG_NT)
     int* win = (int*)(smem + TOPK_SCRATCH(MRG_NT));        // winners' element numbers, k <= 2048
@@ -494,6 +488,20 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
         if (4 * q < E) v = src4[q];
         kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
     }
+    // L = min_s t_s: wave 0 reads the (at most 64) slice bounds in parallel while the
+    // candidate loads are in flight
+    uint32_t* lsh = sh + 2 * TOPK_BINS + 12;
+    if (tid < 64) {
+        uint32_t ts = (use_bound && tid < nse) ? a.tbound[bq * a.nslices + tid] : 0xffffffffu;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t u = __shfl_xor(ts, o, 64);
+            ts = u < ts ? u : ts;
+        }
+        if (tid == 0) *lsh = use_bound ? ts : 0u;
+    }
+    __syncthreads();
+    const uint32_t L = *lsh;
     // keep the keys >= L, compacted in element order
     int mine = 0;
 #pragma unroll

@@ -67,5 +67,6 @@ def score_error_bound(qd, wd, Kd):
     2 * n * 2^-24 * max_s sum_h |w_h| sum_i |q_hi k_si|, n = d_I + H_I terms on the
     longest accumulation path.  qd [Tq, H, d], wd [Tq, H], Kd [N, d] (decoded)."""
     Tq, H, d = qd.shape
-    mag = np.einsum("th,thi,si->ts", np.abs(wd), np.abs(qd), np.abs(Kd))
+    wq = (np.abs(wd)[:, :, None] * np.abs(qd)).sum(axis=1)          # [Tq, d]
+    mag = wq @ np.abs(Kd).T                                          # [Tq, N]
     return 2.0 * (d + H) * 2.0 ** -24 * mag.max(axis=1)
