@@ -28,6 +28,7 @@
 namespace csl {
 
 constexpr int ATT_NT = 256;
+constexpr int MQ_NT = 512;   // threads of the bf16 / packed-row attention kernel (8 waves)
 constexpr int ATT_TILE = 32;
 
 __device__ __forceinline__ int64_t att_n_visible(int64_t t, int m, int64_t n_cap) {
@@ -367,12 +368,12 @@ struct MqLds {
     static constexpr int TILE_ELEMS = ATT_TILE * KSTR;
     // 16-byte chunks per thread and tile: bf16 chunks (RoPE dims, or every dim of a
     // bf16 row) and fp8 chunks (the other dims of a packed row, r <= D/4)
-    static constexpr int JB = FMT == BF16 ? (ATT_TILE * D / 8 + ATT_NT - 1) / ATT_NT : (ATT_TILE * D / 4 / 8 + ATT_NT - 1) / ATT_NT;
-    static constexpr int J8 = FMT == BF16 ? 0 : (ATT_TILE * D / 16 + ATT_NT - 1) / ATT_NT;
+    static constexpr int JB = FMT == BF16 ? (ATT_TILE * D / 8 + MQ_NT - 1) / MQ_NT : (ATT_TILE * D / 4 / 8 + MQ_NT - 1) / MQ_NT;
+    static constexpr int J8 = FMT == BF16 ? 0 : (ATT_TILE * D / 16 + MQ_NT - 1) / MQ_NT;
 };
 
 template <int D, int FMT>
-__global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
+__global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     using L = MqLds<D, FMT>;
     constexpr int KSTR = L::KSTR;
     constexpr int QH = D / 64;                          // k-steps of 32 dims per half
@@ -381,7 +382,7 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
     constexpr int PF = 3;                               // tiles whose rows are in flight
     constexpr int NSLOT = PF + 1;                       // row-pointer slots
     __shared__ __attribute__((aligned(16))) uint16_t kl_s[L::TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) v4f sx[4 * 2 * 2 * 64];   // [wave][r2][hk][lane]
+    __shared__ __attribute__((aligned(16))) v4f sx[MQ_NT / 64 * 2 * 64];   // [wave][r2][lane]
     __shared__ const uint8_t* rowptr[NSLOT * ATT_TILE];
     __shared__ uint32_t rowmask[NSLOT];
     __shared__ int sidx[ATT_MAX_SIDX];
@@ -393,7 +394,7 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
     const int64_t bq = blockIdx.z;
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-    const int hg = wv & 1, dh = wv >> 1;
+    const int hg = wv & 3, dh = wv >> 2;
     const int64_t t = a.q_pos[bq];
     const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
     const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
@@ -406,18 +407,17 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
 
     if (a.idx) {
         const int64_t e_end = v_end < n_ent ? v_end : n_ent;
-        for (int64_t v = v_begin + tid; v < e_end; v += ATT_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
+        for (int64_t v = v_begin + tid; v < e_end; v += MQ_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
     }
-    // Q fragments (B operands of S^T = K Q^T) of the wave's two head blocks, its dims
-    u32x4 qb[2][QH];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-        const int h = hb * 64 + 32 * hg + 16 * hk + col;
+    // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the dims
+    u32x4 qb[QH];
+    {
+        const int h = hb * 64 + 16 * hg + col;
         const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
 #pragma unroll
         for (int ks = 0; ks < QH; ++ks) {
             const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
-            qb[hk][ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
+            qb[ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
         }
     }
     // this thread's chunks of a tile, the same for every tile: j < JB are bf16 chunks
@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const bool bf = j < JB;
-            const int c = tid + ATT_NT * (bf ? j : j - JB);
+            const int c = tid + MQ_NT * (bf ? j : j - JB);
             const int per = bf ? nbc : n8c;
             crow[j] = (per > 0 && c < ATT_TILE * per) ? c / per : -1;
             cpc[j] = per > 0 ? c - (c / per) * per : 0;
@@ -478,11 +478,11 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
     // exp2(x - m_ref) and is never rescaled, so the O^T accumulators stay in place.
     // fp32 / bf16 hold x - m_ref <= ATT_HEADROOM with room to spare; if a later logit
     // goes beyond, the block recomputes its split once with m_ref = the largest logit.
-    v4f o[2][NDH];
-    float m_ref[2], l_lane[2], m_seen[2] = {-INFINITY, -INFINITY};
+    v4f o[NDH];
+    float m_ref, l_lane, m_seen = -INFINITY;
     const float sl2 = a.scale * CSL_LOG2E;
-    v4f* sx_mine = sx + wv * 256 + lane;
-    const v4f* sx_part = sx + (wv ^ 2) * 256 + lane;
+    v4f* sx_mine = sx + wv * 128 + lane;
+    const v4f* sx_part = sx + (wv ^ 4) * 128 + lane;
     u32x4 R0[NJ], R1[NJ], R2[NJ];
     bool ovf = false;
 
@@ -518,47 +518,33 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
         if (it + PF < ntiles) resolve(it + PF);
         lds_barrier();                                  // K tile and the row pointers of tile it+PF visible
         if (it + PF < ntiles) load_regs(it + PF, Rb);
-        // ---- partial S^T over this wave's half of the dims: s[r2][hk]
-        v4f s[2][2];
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk) s[r2][hk] = v4f{0.f, 0.f, 0.f, 0.f};
+        // ---- partial S^T over this wave's half of the dims: s[r2] (rows 16*r2 + 4g + i)
+        v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
         const uint16_t* k0 = kl_s + (size_t)col * KSTR + 32 * QH * dh + 8 * g;
         const uint16_t* k1 = k0 + 16 * KSTR;
 #pragma unroll
         for (int ks = 0; ks < QH; ++ks) {
-            const u32x4 a0 = *(const u32x4*)(k0 + 32 * ks);
-            const u32x4 a1 = *(const u32x4*)(k1 + 32 * ks);
-            s[0][0] = mfma_bf16(a0, qb[0][ks], s[0][0]);
-            s[1][0] = mfma_bf16(a1, qb[0][ks], s[1][0]);
-            s[0][1] = mfma_bf16(a0, qb[1][ks], s[0][1]);
-            s[1][1] = mfma_bf16(a1, qb[1][ks], s[1][1]);
-            if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            s[0] = mfma_bf16(*(const u32x4*)(k0 + 32 * ks), qb[ks], s[0]);
+            s[1] = mfma_bf16(*(const u32x4*)(k1 + 32 * ks), qb[ks], s[1]);
         }
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk) sx_mine[(r2 * 2 + hk) * 64] = s[r2][hk];
+        sx_mine[0] = s[0];
+        sx_mine[64] = s[1];
         lds_barrier();                                  // both halves of S^T visible
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-            for (int hk = 0; hk < 2; ++hk) {
-                const v4f p = sx_part[(r2 * 2 + hk) * 64];
-                s[r2][hk] = dh == 0 ? s[r2][hk] + p : p + s[r2][hk];   // low half + high half
-            }
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const v4f p = sx_part[64 * r2];
+            s[r2] = dh == 0 ? s[r2] + p : p + s[r2];    // low half + high half
+        }
         // ---- probabilities (lane: head col, rows 16*r2 + 4g + i), as a bf16 pair
         //      hi + lo: P = hi + lo to ~2^-17 relative, so P.V keeps fp32-level accuracy
         //      even where V has large channels
-        u32x4 pb[2], pl[2];
-#pragma unroll
-        for (int hk = 0; hk < 2; ++hk) {
+        u32x4 pb, pl;
+        {
             float x[2][4];
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[r2][i] = s[r2][hk][i] * sl2;
+                for (int i = 0; i < 4; ++i) x[r2][i] = s[r2][i] * sl2;
             if (!full) {
 #pragma unroll
                 for (int r2 = 0; r2 < 2; ++r2)
@@ -568,13 +554,13 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
             }
             float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                              fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-            m_seen[hk] = fmaxf(m_seen[hk], mx);
-            if (__builtin_amdgcn_read_exec() & __ballot(m_ref[hk] == -INFINITY)) {   // no reference yet
+            m_seen = fmaxf(m_seen, mx);
+            if (__builtin_amdgcn_read_exec() & __ballot(m_ref == -INFINITY)) {   // no reference yet
                 const float tmax = cross4_max(mx);
-                if (m_ref[hk] == -INFINITY && tmax != -INFINITY) m_ref[hk] = tmax + ATT_REF_LIFT;
+                if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + ATT_REF_LIFT;
             }
-            ovf |= mx > m_ref[hk] + ATT_HEADROOM;
-            const float mr = m_ref[hk] == -INFINITY ? 0.f : m_ref[hk];   // no reference: every x is -inf
+            ovf |= mx > m_ref + ATT_HEADROOM;
+            const float mr = m_ref == -INFINITY ? 0.f : m_ref;   // no reference: every x is -inf
             float ls = 0.f;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2)
@@ -583,13 +569,13 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
                     x[r2][i] = __builtin_amdgcn_exp2f(x[r2][i] - mr);   // 0 for invalid rows
                     ls += x[r2][i];
                 }
-            l_lane[hk] += ls;
+            l_lane += ls;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a0 = x[e >> 1][2 * (e & 1)], a1 = x[e >> 1][2 * (e & 1) + 1];
                 const uint32_t h = pack_bf16x2(a0, a1);
-                pb[hk][e] = h;
-                pl[hk][e] = pack_bf16x2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
+                pb[e] = h;
+                pl[e] = pack_bf16x2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
             }
         }
         // ---- O^T += V^T P^T over this wave's dims (one V^T fragment feeds both head blocks)
@@ -600,22 +586,16 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
             const u32x2 t0 = lds_read_tr16(vp0 + 16 * db);
             const u32x2 t1 = lds_read_tr16(vp1 + 16 * db);
             const u32x4 va = {t0[0], t0[1], t1[0], t1[1]};
-            o[0][db] = mfma_bf16(va, pb[0], o[0][db]);
-            o[1][db] = mfma_bf16(va, pb[1], o[1][db]);
-            o[0][db] = mfma_bf16(va, pl[0], o[0][db]);
-            o[1][db] = mfma_bf16(va, pl[1], o[1][db]);
-            if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+            o[db] = mfma_bf16(va, pb, o[db]);
+            o[db] = mfma_bf16(va, pl, o[db]);
         }
     };
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk) {
-#pragma unroll
-            for (int db = 0; db < NDH; ++db) o[hk][db] = v4f{0.f, 0.f, 0.f, 0.f};
-            m_ref[hk] = pass == 0 ? -INFINITY : cross4_max(m_seen[hk]);
-            l_lane[hk] = 0.f;
-        }
+        for (int db = 0; db < NDH; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+        m_ref = pass == 0 ? -INFINITY : cross4_max(m_seen);
+        l_lane = 0.f;
         ovf = false;
         __syncthreads();                                // slots and tiles of a previous pass are free
         for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
@@ -631,20 +611,14 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
         // the whole block redoes the split only if some wave overflowed
         if (!__syncthreads_or(ovf ? 1 : 0)) break;
     }
-    float l_run[2], m_run[2];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-        l_run[hk] = cross4_sum(l_lane[hk]);
-        m_run[hk] = m_ref[hk];
-    }
+    const float l_run = cross4_sum(l_lane), m_run = m_ref;
 
     // ---- finish: normalise, write the output or the split's partial (this wave's dims)
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-        const int hh = 32 * hg + 16 * hk + col;          // head within the block
+    {
+        const int hh = 16 * hg + col;                   // head within the block
         const int h = hb * 64 + hh;
-        const float inv = l_run[hk] > 0.f ? 1.f / l_run[hk] : 0.f;
-        const float lse = l_run[hk] > 0.f ? (m_run[hk] + log2f(l_run[hk])) * CSL_LN2 : -INFINITY;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
         const int d0 = 16 * NDH * dh + 4 * g;
         if (a.nsplit == 1) {
             if (h < a.H) {
@@ -652,15 +626,14 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
                     float* orow = (float*)a.out + (bq * a.H + h) * D + d0;
 #pragma unroll
                     for (int db = 0; db < NDH; ++db)
-                        *(float4*)(orow + 16 * db) = make_float4(o[hk][db][0] * inv, o[hk][db][1] * inv,
-                                                                 o[hk][db][2] * inv, o[hk][db][3] * inv);
+                        *(float4*)(orow + 16 * db) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                                                                 o[db][3] * inv);
                 } else {
                     uint16_t* orow = (uint16_t*)a.out + (bq * a.H + h) * D + d0;
 #pragma unroll
                     for (int db = 0; db < NDH; ++db)
-                        *(u32x2*)(orow + 16 * db) =
-                            u32x2{f32_to_bf16_rne(o[hk][db][0] * inv) | (f32_to_bf16_rne(o[hk][db][1] * inv) << 16),
-                                  f32_to_bf16_rne(o[hk][db][2] * inv) | (f32_to_bf16_rne(o[hk][db][3] * inv) << 16)};
+                        *(u32x2*)(orow + 16 * db) = u32x2{pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
+                                                          pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
                 }
                 if (a.lse && g == 0 && dh == 0) a.lse[bq * a.H + h] = lse;
             }
@@ -669,8 +642,7 @@ __global__ void __launch_bounds__(ATT_NT, 1) k_attend_mq(AttendArgs a) {
             float* orow = a.ws_o + prow * D + d0;
 #pragma unroll
             for (int db = 0; db < NDH; ++db)
-                *(float4*)(orow + 16 * db) = make_float4(o[hk][db][0] * inv, o[hk][db][1] * inv,
-                                                         o[hk][db][2] * inv, o[hk][db][3] * inv);
+                *(float4*)(orow + 16 * db) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
             if (g == 0 && dh == 0) a.ws_lse[prow] = lse;
         }
     }
@@ -740,7 +712,7 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     if constexpr (FMT == F32) {
         hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_attend_mq<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
+        hipLaunchKernelGGL((k_attend_mq<D, FMT>), grid, dim3(MQ_NT), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
