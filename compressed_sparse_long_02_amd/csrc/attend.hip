@@ -650,54 +650,77 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
 
 // Merge of split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One block per (query, 4 heads): the 64 heads of a head block spread over 16
-// blocks so that the merge reads its partials with the whole GPU.
+// blocks so that the merge reads its partials with the whole GPU.  Wave w owns head
+// h0 + w for the weights (lane s holds split s, in passes of 64); the data loop
+// issues the loads of 8 splits before accumulating them, in split order.
 constexpr int CMB_HEADS = 4;
+constexpr int CMB_UNR = 8;
+constexpr int CMB_NT = 512;
 
 template <int D>
-__global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
-    extern __shared__ float wts[];   // [nsplit][CMB_HEADS] weights, then 1/den, lse
+__global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
+    extern __shared__ float wts[];   // [CMB_HEADS][nsplit] normalised weights, then lse
     const int hb = blockIdx.x / (64 / CMB_HEADS);
     const int h0 = (blockIdx.x % (64 / CMB_HEADS)) * CMB_HEADS;   // first head within the head block
     const int64_t bq = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int64_t base = (bq * a.nhb + hb) * (int64_t)a.nsplit;
-    float* inv = wts + a.nsplit * CMB_HEADS;
-    float* lse_o = inv + CMB_HEADS;
-    if (tid < CMB_HEADS) {
-        const int hh = h0 + tid;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ns = a.nsplit;
+    const int64_t base = (bq * a.nhb + hb) * (int64_t)ns;
+    float* lse_o = wts + CMB_HEADS * ns;
+    if (wv < CMB_HEADS) {
+        const int hh = h0 + wv;
         float M = -INFINITY;
-        for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[(base + s) * 64 + hh]);
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
+            M = fmaxf(M, l);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
         float den = 0.f;
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float w = M == -INFINITY ? 0.f : expf(a.ws_lse[(base + s) * 64 + hh] - M);
-            wts[s * CMB_HEADS + tid] = w;
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
+            const float w = M == -INFINITY ? 0.f : expf(l - M);
+            if (s0 + lane < ns) wts[wv * ns + s0 + lane] = w;
             den += w;
         }
-        inv[tid] = den > 0.f ? 1.f / den : 0.f;
-        lse_o[tid] = den > 0.f ? M + logf(den) : -INFINITY;
+        // fixed-order sum over the wave (butterfly: every lane gets the same bits)
+#pragma unroll
+        for (int o = 1; o <= 32; o <<= 1) den += __shfl_xor(den, o, 64);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        for (int s0 = 0; s0 < ns; s0 += 64)
+            if (s0 + lane < ns) wts[wv * ns + s0 + lane] *= inv;
+        if (lane == 0) lse_o[wv] = den > 0.f ? M + logf(den) : -INFINITY;
     }
     __syncthreads();
     constexpr int C4 = D / 4;
-    for (int item = tid; item < CMB_HEADS * C4; item += 256) {
+    for (int item = tid; item < CMB_HEADS * C4; item += CMB_NT) {
         const int j = item / C4, c = (item - j * C4) * 4;
         const int hh = h0 + j;
         const int h = hb * 64 + hh;
         if (h >= a.H) continue;
+        const float* src = a.ws_o + (base * 64 + hh) * D + c;
+        const float* wj = wts + j * ns;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float w = wts[s * CMB_HEADS + j];
-            const float4 v = *(const float4*)(a.ws_o + ((base + s) * 64 + hh) * D + c);
-            acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-            acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+        for (int s0 = 0; s0 < ns; s0 += CMB_UNR) {
+            float4 v[CMB_UNR];
+#pragma unroll
+            for (int u = 0; u < CMB_UNR; ++u) {
+                const int sc = s0 + u < ns ? s0 + u : ns - 1;     // clamped: every load in bounds
+                v[u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+            }
+#pragma unroll
+            for (int u = 0; u < CMB_UNR; ++u) {
+                const float w = s0 + u < ns ? wj[s0 + u] : 0.f;
+                acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
+                acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
+            }
         }
-        const float iv = inv[j];
-        acc.x *= iv; acc.y *= iv; acc.z *= iv; acc.w *= iv;
         if (a.out_fmt == F32) {
             *(float4*)((float*)a.out + (bq * a.H + h) * D + c) = acc;
         } else {
             uint2 pk;
-            pk.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
-            pk.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+            pk.x = pack_bf16x2(acc.x, acc.y);
+            pk.y = pack_bf16x2(acc.z, acc.w);
             *(uint2*)((uint16_t*)a.out + (bq * a.H + h) * D + c) = pk;
         }
     }
@@ -716,9 +739,9 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + 2 * CMB_HEADS);
+    const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + CMB_HEADS);
     hipLaunchKernelGGL((k_attend_combine<D>), dim3((unsigned)(a.nhb * (64 / CMB_HEADS)), (unsigned)((int64_t)a.B * a.Tq)),
-                       dim3(256), lds2, s, a);
+                       dim3(CMB_NT), lds2, s, a);
     return hipGetLastError();
 }
 
