@@ -52,21 +52,6 @@ constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until 
 constexpr float ATT_HEADROOM = 64.0f;   // largest x - m_ref (base 2) accepted without a rescale
 constexpr float ATT_REF_LIFT = 32.0f;   // m_ref starts this far above the first tile's largest logit
 
-// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
-// the gfx950 row-swap moves; every lane ends with identical bits.
-__device__ __forceinline__ float cross4_max(float x) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-__device__ __forceinline__ float cross4_sum(float x) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // 16x16x16 bf16 MFMA: A lane l = row l%16, k 4*(l/16)..+4; B lane l = col l%16, same k.
 __device__ __forceinline__ v4f mfma_bf16_k16(const u32x2& a, const u32x2& b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);

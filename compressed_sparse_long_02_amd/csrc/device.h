@@ -139,6 +139,21 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, 64); }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap moves; every lane ends with identical bits.
+__device__ __forceinline__ float cross4_max(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float cross4_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Load through a pointer known to address global memory.  A pointer that went
 // through LDS (or any generic pointer the compiler cannot trace to a kernel
 // argument) would otherwise become a flat load, which also counts against the LDS

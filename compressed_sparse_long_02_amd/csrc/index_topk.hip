@@ -46,6 +46,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
+// Minimum / maximum over the 64 lanes: DPP within each row of 16, then the gfx950
+// row swaps across rows (VALU only).
+template <bool MAXOP>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+    auto f = [](uint32_t a, uint32_t b) { return MAXOP ? (a > b ? a : b) : (a < b ? a : b); };
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));    // quad_perm(1,0,3,2)
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));    // quad_perm(2,3,0,1)
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));   // row_half_mirror
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));   // row_mirror
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = f(p[0], p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return f(q[0], q[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_minmax_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_minmax_u32<true>(v); }
+
 // Exclusive prefix sum of one int per thread over the block (one barrier);
 // `wsum` holds NT/64 ints and must not be reused before the next barrier.
 template <int NT>
@@ -80,9 +97,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 // is cleared meanwhile), then wave 0 alone locates the threshold digit -- two
 // barriers per pass.  The final compaction is one packed (greater, equal) scan.
 constexpr int TOPK_BINS = 2048;
+// Histograms are stored with 4 pad words after every 32 bins (bin b at b + 4*(b/32)),
+// so that lane L of the scanning wave, which reads bins 32L..32L+31 as 16-byte
+// vectors, starts at word 36L: 16 consecutive lanes then touch 16 different
+// 16-byte bank groups instead of the same two.
+constexpr int TOPK_HSZ = TOPK_BINS + TOPK_BINS / 8;
+__device__ __forceinline__ int hpad(uint32_t b) { return (int)(b + 4 * (b >> 5)); }
 constexpr int TOPK_BITS = 11;
 constexpr int TOPK_EMAX = 32;
-#define TOPK_SCRATCH(NT) (2 * TOPK_BINS + 16 + 2 * ((NT) / 64) + 8)
+#define TOPK_SCRATCH(NT) (2 * TOPK_HSZ + 16 + 2 * ((NT) / 64) + 8)
 
 // If rank_r > 0, thread 0 also stores to *tb_out a value t such that at least rank_r
 // of the n keys are >= t (the lower edge of the first-pass bin holding the
@@ -93,9 +116,9 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int base = tid * E;
     uint32_t* hist0 = sh;
-    uint32_t* hist1 = sh + TOPK_BINS;
-    uint32_t* misc = sh + 2 * TOPK_BINS;                    // [0] digit [1] above [2] in-bin, [4..] lo/hi
-    int* wsum = (int*)(sh + 2 * TOPK_BINS + 16);           // NT/64 for lo, NT/64 for hi / scans
+    uint32_t* hist1 = sh + TOPK_HSZ;
+    uint32_t* misc = sh + 2 * TOPK_HSZ;                     // [0] digit [1] above [2] in-bin [3] rank bin
+    int* wsum = (int*)(sh + 2 * TOPK_HSZ + 16);            // NT/64 for lo, NT/64 for hi / scans
     uint32_t T = 0;        // select u > T, plus the first eq_take keys equal to T
     int eq_take = 0;
     const bool all = n <= want;
@@ -110,14 +133,10 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
                 hi = kv[x] > hi ? kv[x] : hi;
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const uint32_t a = __shfl_xor(lo, o, 64), b = __shfl_xor(hi, o, 64);
-            lo = a < lo ? a : lo;
-            hi = b > hi ? b : hi;
-        }
+        lo = wave_min_u32(lo);
+        hi = wave_max_u32(hi);
         if (lane == 0) { wsum[wv] = (int)lo; wsum[NT / 64 + wv] = (int)hi; }
-        for (int x = tid; x < TOPK_BINS; x += NT) hist0[x] = 0;
+        for (int x = tid; x < TOPK_HSZ; x += NT) hist0[x] = 0;
         __syncthreads();
         lo = (uint32_t)wsum[0]; hi = (uint32_t)wsum[NT / 64];
         for (int x = 1; x < NT / 64; ++x) {
@@ -143,15 +162,15 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
                 const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
                 for (int x = 0; x < EMAX; ++x) {
-                    if (x < E && base + x < n && (kv[x] & pmask) == prefix) atomicAdd(&hcur[(kv[x] >> shift) & dmask], 1u);
+                    if (x < E && base + x < n && (kv[x] & pmask) == prefix) atomicAdd(&hcur[hpad((kv[x] >> shift) & dmask)], 1u);
                 }
-                for (int x = tid; x < TOPK_BINS; x += NT) hnxt[x] = 0;
+                for (int x = tid; x < TOPK_HSZ; x += NT) hnxt[x] = 0;
                 __syncthreads();
                 if (wv == 0) {
                     // lane L owns bins [32L, 32L+32); counts of keys in bins above.
                     // The bins are read twice (sum, then the walk) rather than held in
                     // 32 registers next to the caller's keys.
-                    const u32x4* hp = (const u32x4*)(hcur + 32 * lane);
+                    const u32x4* hp = (const u32x4*)(hcur + 36 * lane);
                     uint32_t loc = 0;
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
@@ -377,8 +396,7 @@ k_idx_score(IndexArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(c[i]), part);
             }
-            part += shfl_xor(part, 16);
-            part += shfl_xor(part, 32);
+            part = cross4_sum(part);                    // the 64 heads of the 4 lane rows
             const int li = T * 16 + col;
             if (g == 0 && T < ntile && li < ns) keys[li + (li >> le)] = score_key(part);
         };
@@ -490,14 +508,9 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
     }
     // L = min_s t_s: wave 0 reads the (at most 64) slice bounds in parallel while the
     // candidate loads are in flight
-    uint32_t* lsh = sh + 2 * TOPK_BINS + 12;
+    uint32_t* lsh = sh + 2 * TOPK_HSZ + 12;
     if (tid < 64) {
-        uint32_t ts = (use_bound && tid < nse) ? a.tbound[bq * a.nslices + tid] : 0xffffffffu;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const uint32_t u = __shfl_xor(ts, o, 64);
-            ts = u < ts ? u : ts;
-        }
+        const uint32_t ts = wave_min_u32((use_bound && tid < nse) ? a.tbound[bq * a.nslices + tid] : 0xffffffffu);
         if (tid == 0) *lsh = use_bound ? ts : 0u;
     }
     __syncthreads();
@@ -507,7 +520,7 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
 #pragma unroll
     for (int x = 0; x < TOPK_EMAX; ++x) mine += (x < E && tid * E + x < total && kv[x] >= L) ? 1 : 0;
     int nsurv;
-    int off = block_excl_scan<MRG_NT>(mine, (int*)(sh + 2 * TOPK_BINS + 16), nsurv);
+    int off = block_excl_scan<MRG_NT>(mine, (int*)(sh + 2 * TOPK_HSZ + 16), nsurv);
     const int want = total < a.k ? total : a.k;
     if (nsurv <= MRG_SURV) {
 #pragma unroll
