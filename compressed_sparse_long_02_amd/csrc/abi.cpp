@@ -212,10 +212,36 @@ int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int
     return launched(csl::launch_compress(a, (hipStream_t)stream));
 }
 
+// Many queries per call (prefill): the dense path scores every (query, key) pair into
+// the workspace, a pass of at most DENSE_WS_MAX bytes at a time.
+constexpr int DENSE_MIN_TQ = 64;
+constexpr size_t DENSE_WS_MAX = (size_t)2 << 30;
+
+bool dense_path(int fmt, int d_I, int H_I, int Tq) {
+    return fmt == CSL_BF16 && d_I == 128 && (H_I == 16 || H_I == 32 || H_I == 64 || H_I == 128) && Tq >= DENSE_MIN_TQ;
+}
+int64_t dense_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64_t)3; }
+int dense_tc(int B, int Tq, int64_t n_cap) {
+    const size_t per_q = (size_t)(B > 0 ? B : 1) * ((size_t)dense_stride(n_cap) + 2048) * 4;
+    size_t tc = DENSE_WS_MAX / per_q;
+    const size_t tq4 = ((size_t)Tq + 3) & ~(size_t)3;
+    if (tc > tq4) tc = tq4;
+    tc &= ~(size_t)3;
+    return tc < 4 ? 4 : (int)tc;
+}
+size_t dense_ws(int B, int Tq, int64_t n_cap) {
+    return (size_t)B * dense_tc(B, Tq, n_cap) * ((size_t)dense_stride(n_cap) + 2048) * 4 + 256;
+}
+
 size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
+    if (B < 0 || Tq < 0 || k < 1) return 0;
     int S, ns, kk;
-    if (B < 0 || Tq < 0 || k < 1 || !plan_index(B, Tq, n_cap, k, S, ns, kk)) return 0;
-    return index_ws(B, Tq, S, ns, kk);
+    size_t ws = plan_index(B, Tq, n_cap, k, S, ns, kk) ? index_ws(B, Tq, S, ns, kk) : 0;
+    if (Tq >= DENSE_MIN_TQ) {                            // the dense path may be taken (fmt, d_I, H_I unknown here)
+        const size_t d = dense_ws(B, Tq, n_cap);
+        ws = d > ws ? d : ws;
+    }
+    return ws;
 }
 
 int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
@@ -233,10 +259,11 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
                      (ki_fmt == CSL_BF16 && (d_I == 32 || d_I == 64 || d_I == 128)) ||
                      (ki_fmt == CSL_MXFP4 && d_I == 128);
     if (!dok) return fail(CSL_EUNSUPPORTED, "%s: (fmt %d, d_I %d) not built", fn, ki_fmt, d_I);
-    int S, nslices, kk;
-    if (!plan_index(B, Tq, n_cap, k, S, nslices, kk))
+    const bool dense = dense_path(ki_fmt, d_I, H_I, Tq);
+    int S = 0, nslices = 1, kk = k;
+    if (!dense && !plan_index(B, Tq, n_cap, k, S, nslices, kk))
         return fail(CSL_EUNSUPPORTED, "%s: n_cap = %lld with k = %d exceeds the candidate merge", fn, (long long)n_cap, k);
-    const size_t need = index_ws(B, Tq, S, nslices, kk);
+    const size_t need = dense ? dense_ws(B, Tq, n_cap) : index_ws(B, Tq, S, nslices, kk);
     if (B * (int64_t)Tq == 0) { g_err.clear(); return CSL_OK; }
     if (!qi || !w || !q_pos || !out_idx || (n_cap > 0 && !ki)) return fail(CSL_EINVAL, "%s: null pointer argument", fn);
     if ((ki_fmt == CSL_MXFP4) != (qi_scales != nullptr) || (ki_fmt == CSL_MXFP4) != (ki_scales != nullptr || n_cap == 0))
@@ -254,7 +281,13 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
     a.out_idx = out_idx; a.out_score = out_score;
     a.S = S; a.nslices = nslices; a.kk = kk;
     a.cst = index_cst(nslices, kk);
-    if (nslices > 1) {
+    if (dense) {
+        a.dense = 1;
+        a.Tc = dense_tc(B, Tq, n_cap);
+        a.sstride = dense_stride(n_cap);
+        a.scores = (uint32_t*)ws;
+        a.hist = (uint32_t*)((uint8_t*)ws + (size_t)B * a.Tc * a.sstride * 4);
+    } else if (nslices > 1) {
         const size_t nc = (size_t)B * Tq * a.cst;
         a.cand_key = (uint32_t*)ws;
         a.cand_idx = (int32_t*)((uint8_t*)ws + nc * 4);

@@ -560,6 +560,290 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Many queries (prefill chunks): a dense score pass, then a select per query
+// ---------------------------------------------------------------------------
+// With thousands of queries per call the per-query slices above would re-read every
+// key once per query.  Instead a block scores 4 queries against a range of keys: the
+// keys stream through LDS in tiles of 128 and each key fragment read from LDS feeds
+// one MFMA per 16 heads, the query fragments stay in registers.  Every score is
+// written to HBM as its order-preserving key (4 bytes per pair, a few percent of
+// the MFMA time) together with a per-query histogram of the keys' top 11 bits.  The
+// select then needs a single pass over each query's keys in most cases.
+constexpr int DNS_NT = 512;       // 8 waves: wave w scores query w & 3, keys 64*(w >> 2) .. +64 of a tile
+constexpr int DNS_QB = 4;         // queries per block
+constexpr int DNS_KT = 128;       // keys per tile
+constexpr int DNS_TPB = 32;       // tiles per block
+constexpr int DNS_KSTR = 272;     // bytes per key row in LDS (256 + 16 pad: conflict-free fragment reads)
+constexpr int DSEL_NT = 1024;
+constexpr int DSEL_CAP = 8192;    // survivors the select holds in LDS
+
+__global__ void k_fill_u32(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+template <int HB>
+__global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][DNS_KT * DNS_KSTR];
+    __shared__ uint32_t hist[DNS_QB * TOPK_BINS];
+    __shared__ int64_t nq[DNS_QB];
+    const int kx = blockIdx.x, qg = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int qw = wv & 3, kh = wv >> 2;
+    if (tid < DNS_QB) {
+        const int jl = qg * DNS_QB + tid, jq = a.qc0 + jl;
+        nq[tid] = (jl < a.Tc && jq < a.Tq) ? n_visible(a.q_pos[(int64_t)b * a.Tq + jq], a.m, a.n_cap) : 0;
+    }
+    for (int x = tid; x < DNS_QB * TOPK_BINS; x += DNS_NT) hist[x] = 0u;
+    __syncthreads();
+    int64_t nmax = 0;
+#pragma unroll
+    for (int u = 0; u < DNS_QB; ++u) nmax = nq[u] > nmax ? nq[u] : nmax;
+    const int64_t k0 = (int64_t)kx * DNS_KT * DNS_TPB;
+    if (k0 >= nmax) return;                              // block-uniform
+    const int64_t k1 = k0 + DNS_KT * DNS_TPB < nmax ? k0 + DNS_KT * DNS_TPB : nmax;
+    const int nt = (int)((k1 - k0 + DNS_KT - 1) / DNS_KT);
+    const int jl = qg * DNS_QB + qw;
+    const int64_t n = nq[qw];
+    const int jq_c = a.qc0 + jl < a.Tq ? a.qc0 + jl : a.Tq - 1;   // addresses stay inside the batch
+    const int64_t bq = (int64_t)b * a.Tq + jq_c;
+
+    // query fragments (A operand, rows = heads) and head weights of this wave's query
+    u32x4 qa[HB][4];
+    float wh[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 16 + col;
+        const uint8_t* qrow = a.qi + (bq * a.H_I + (h < a.H_I ? h : 0)) * 256;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 v = *(const u32x4*)(qrow + 64 * ks + 16 * g);
+            qa[hb][ks] = (h < a.H_I && n > 0) ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = hb * 16 + 4 * g + i;
+            wh[hb][i] = hh < a.H_I ? a.w[bq * a.H_I + hh] : 0.f;
+        }
+    }
+    // key tiles: thread tid moves chunks c = tid + 512 j (key c / 16, 16-byte piece c % 16);
+    // keys past the range re-read the range's last key (scored, then ignored)
+    const uint8_t* kbase = a.ki + (int64_t)b * a.ki_bstride;
+    u32x4 R[4];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = tid + DNS_NT * j;
+            int64_t key = k0 + (int64_t)t * DNS_KT + (c >> 4);
+            key = key < k1 ? key : k1 - 1;
+            R[j] = ld_global<u32x4>(kbase + key * 256 + 16 * (c & 15));
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = tid + DNS_NT * j;
+            *(u32x4*)(&kt[buf][(c >> 4) * DNS_KSTR + 16 * (c & 15)]) = R[j];
+        }
+    };
+    uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
+    load_tile(0);
+    store_tile(0);
+    lds_barrier();
+    for (int t = 0; t < nt; ++t) {
+        if (t + 1 < nt) load_tile(t + 1);               // in flight during the MFMA work
+        if (n > 0) {
+            v4f acc[4][HB];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) acc[kb][hb] = v4f{0.f, 0.f, 0.f, 0.f};
+            const uint8_t* tb = &kt[t & 1][(64 * kh + col) * DNS_KSTR + 16 * g];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DNS_KSTR + 64 * ks);
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) acc[kb][hb] = mfma_bf16(qa[hb][ks], bf, acc[kb][hb]);
+                }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float part = 0.f;
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(acc[kb][hb][i]), part);
+                part = cross4_sum(part);
+                const int64_t sidx = k0 + (int64_t)t * DNS_KT + 64 * kh + 16 * kb + col;
+                if (g == 0 && sidx < n) {
+                    const uint32_t key = score_key(part);
+                    srow[sidx] = key;
+                    atomicAdd(&hist[qw * TOPK_BINS + (key >> 21)], 1u);
+                }
+            }
+        }
+        if (t + 1 < nt) store_tile((t + 1) & 1);
+        lds_barrier();
+    }
+    // add this block's histograms into the per-query ones (integer adds: order-free)
+    for (int x = tid; x < DNS_QB * TOPK_BINS; x += DNS_NT) {
+        const int u = x / TOPK_BINS;
+        const uint32_t v = hist[x];
+        if (v && qg * DNS_QB + u < a.Tc)
+            atomicAdd(&a.hist[((int64_t)b * a.Tc + qg * DNS_QB + u) * TOPK_BINS + (x - u * TOPK_BINS)], v);
+    }
+}
+
+// Wave 0 locates, in a padded 2048-bin histogram, the bin b where the count of keys in
+// higher bins is < need <= that count + hist[b]: misc[0] = b, misc[1] = count above,
+// misc[2] = hist[b].  Caller: wave 0 only, need >= 1 and <= total.
+__device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint32_t* misc) {
+    const int lane = threadIdx.x & 63;
+    const u32x4* h4 = (const u32x4*)(hp + 36 * lane);
+    uint32_t loc = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const u32x4 v4 = h4[q];
+        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
+    }
+    const int incl = wave_incl_scan((int)loc);
+    const int tot = __shfl(incl, 63, 64);
+    uint32_t c = (uint32_t)(tot - incl);
+#pragma unroll
+    for (int q = 7; q >= 0; --q) {
+        const u32x4 v4 = h4[q];
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+            const uint32_t cge = c + v4[e];
+            if (cge >= need && c < need) { misc[0] = 32 * lane + 4 * q + e; misc[1] = c; misc[2] = v4[e]; }
+            c = cge;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int jl = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, wv = tid >> 6;
+    const int jq = a.qc0 + jl;
+    const int64_t bq = (int64_t)b * a.Tq + jq;
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    int32_t* oi = a.out_idx + bq * a.k;
+    float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
+    const uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
+    if (n <= a.k) {                                      // every visible entry, then padding
+        for (int p = tid; p < a.k; p += DSEL_NT) {
+            oi[p] = p < n ? p : -1;
+            if (os) os[p] = p < n ? key_score(srow[p]) : -INFINITY;
+        }
+        return;
+    }
+    uint32_t* sh = smem;                                 // TOPK_SCRATCH(DSEL_NT): histograms, misc, scans
+    uint32_t* misc = sh + 2 * TOPK_HSZ;
+    int* wsum = (int*)(sh + 2 * TOPK_HSZ + 16);
+    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);           // survivors: keys, then entry indices
+    int* si = (int*)(sk + DSEL_CAP);
+    int* win = si + DSEL_CAP;                            // winners (k <= 2048)
+    uint32_t* wkey = (uint32_t*)(win + 2048);
+    // ---- threshold: refine 11 + 11 + 10 key bits until the keys at or above it fit
+    const uint32_t* gh = a.hist + ((int64_t)b * a.Tc + jl) * TOPK_BINS;
+    for (int x = tid; x < TOPK_BINS; x += DSEL_NT) sh[hpad(x)] = gh[x];
+    __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+    int need = a.k;
+    int shift = 21;
+    bool exact = false;
+    uint32_t above_total = 0;                            // keys strictly above the current bin
+    for (int level = 0;; ++level) {
+        if (wv == 0) find_bin(sh, (uint32_t)need, misc);
+        __syncthreads();
+        const uint32_t bin = misc[0], above = misc[1], inbin = misc[2];
+        __syncthreads();
+        prefix |= bin << shift;
+        pmask |= (level < 2 ? 0x7ffu : 0x3ffu) << shift;
+        above_total += above;
+        need -= (int)above;
+        if (above_total + inbin <= (uint32_t)DSEL_CAP || shift == 0) { exact = shift == 0 && above_total + inbin > (uint32_t)DSEL_CAP; break; }
+        // histogram of the next digit among the keys of this bin (one pass over the keys)
+        const int nshift = shift == 21 ? 10 : 0;
+        const uint32_t dmask = nshift == 10 ? 0x7ffu : 0x3ffu;
+        for (int x = tid; x < TOPK_HSZ; x += DSEL_NT) sh[x] = 0u;
+        __syncthreads();
+        for (int64_t s = tid; s < n; s += DSEL_NT) {
+            const uint32_t u = srow[s];
+            if ((u & pmask) == prefix) atomicAdd(&sh[hpad((u >> nshift) & dmask)], 1u);
+        }
+        __syncthreads();
+        shift = nshift;
+    }
+    // keys kept: (u & pmask) > prefix, or == prefix (the bin) -- in the exact case only
+    // the first `need` keys equal to the threshold (smaller indices win ties)
+    const uint32_t lo = prefix;                          // bin lower edge (bits below the digit are 0)
+    int nsurv = 0, eq_seen = 0;
+    constexpr int CH = 16;
+    for (int64_t base = 0; base < n; base += (int64_t)DSEL_NT * CH) {
+        uint32_t kv[CH];
+        const int64_t s0 = base + (int64_t)tid * CH;
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) {
+            int64_t sq = s0 + 4 * q;
+            sq = sq < n ? sq : ((n - 1) & ~(int64_t)3);  // clamped inside the (4-padded) row
+            const u32x4 v = *(const u32x4*)(srow + sq);
+            kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
+        }
+        int my_gt = 0, my_eq = 0;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            if (s0 + x < n) {
+                if (exact) { my_gt += kv[x] > lo ? 1 : 0; my_eq += kv[x] == lo ? 1 : 0; }
+                else my_gt += kv[x] >= lo ? 1 : 0;
+            }
+        }
+        int tot;
+        const uint32_t pre = (uint32_t)block_excl_scan<DSEL_NT>(my_gt | (my_eq << 16), wsum, tot);
+        int gt_b = (int)(pre & 0xffffu), eq_b = (int)(pre >> 16);
+        const int eq_take = need - eq_seen;              // exact case: equal keys still to take
+        int pos = nsurv + gt_b + (exact ? (eq_b < eq_take ? (eq_b > 0 ? eq_b : 0) : (eq_take > 0 ? eq_take : 0)) : 0);
+        int r_eq = eq_b;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            if (s0 + x < n) {
+                const uint32_t u = kv[x];
+                bool keep;
+                if (exact) {
+                    keep = u > lo;
+                    if (u == lo) { keep = r_eq < eq_take; ++r_eq; }
+                } else {
+                    keep = u >= lo;
+                }
+                if (keep && pos < DSEL_CAP) { sk[pos] = u; si[pos] = (int)(s0 + x); ++pos; }
+            }
+        }
+        const int tgt = tot & 0xffff, teq = tot >> 16;
+        nsurv += tgt + (exact ? (teq < eq_take ? teq : (eq_take > 0 ? eq_take : 0)) : 0);
+        if (exact) eq_seen += teq;
+        __syncthreads();                                 // wsum reuse
+    }
+    nsurv = nsurv < DSEL_CAP ? nsurv : DSEL_CAP;
+    // ---- exact top-k among the survivors (in entry order), then the output
+    constexpr int E2MAX = DSEL_CAP / DSEL_NT;
+    const int E2 = (nsurv + DSEL_NT - 1) / DSEL_NT;
+    uint32_t kv2[E2MAX];
+#pragma unroll
+    for (int x = 0; x < E2MAX; ++x) kv2[x] = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] : 0u;
+    __syncthreads();
+    block_topk<DSEL_NT>(kv2, E2, nsurv, a.k, sh, [&](int pos, int i, uint32_t u) {
+        win[pos] = si[i];
+        wkey[pos] = u;
+    });
+    __syncthreads();
+    for (int p = tid; p < a.k; p += DSEL_NT) {
+        oi[p] = win[p];
+        if (os) os[p] = key_score(wkey[p]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
 template <int FMT, int DI, int HB>
@@ -579,8 +863,31 @@ static hipError_t launch_hb(const IndexArgs& a, hipStream_t s) {
     return launch_score<FMT, DI, 8>(a, s);
 }
 
+static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
+    const int hb = (a.H_I + 15) / 16;
+    const size_t sel_lds = sizeof(uint32_t) * ((size_t)TOPK_SCRATCH(DSEL_NT) + 2 * DSEL_CAP + 2 * 2048);
+    for (int q0 = 0; q0 < a.Tq; q0 += a.Tc) {
+        a.qc0 = q0;
+        const int tc = a.Tq - q0 < a.Tc ? a.Tq - q0 : a.Tc;
+        const int64_t nh = (int64_t)a.B * a.Tc * TOPK_BINS;
+        hipLaunchKernelGGL(k_fill_u32, dim3(512), dim3(256), 0, s, a.hist, nh);
+        dim3 grid((unsigned)((a.n_cap + DNS_KT * DNS_TPB - 1) / (DNS_KT * DNS_TPB)), (unsigned)((tc + DNS_QB - 1) / DNS_QB),
+                  (unsigned)a.B);
+        if (grid.x == 0) grid.x = 1;
+        if (hb <= 1) hipLaunchKernelGGL(k_idx_dense_score<1>, grid, dim3(DNS_NT), 0, s, a);
+        else if (hb <= 2) hipLaunchKernelGGL(k_idx_dense_score<2>, grid, dim3(DNS_NT), 0, s, a);
+        else if (hb <= 4) hipLaunchKernelGGL(k_idx_dense_score<4>, grid, dim3(DNS_NT), 0, s, a);
+        else hipLaunchKernelGGL(k_idx_dense_score<8>, grid, dim3(DNS_NT), 0, s, a);
+        hipLaunchKernelGGL(k_idx_dense_select, dim3((unsigned)tc, (unsigned)a.B), dim3(DSEL_NT), sel_lds, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     if (a.B <= 0 || a.Tq <= 0) return hipSuccess;
+    if (a.dense) return launch_dense(a, s);
     hipError_t e;
     if (a.ki_fmt == MXFP4) e = launch_hb<MXFP4, 128>(a, s);
     else if (a.ki_fmt == BF16) {

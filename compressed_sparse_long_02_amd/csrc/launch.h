@@ -28,6 +28,13 @@ struct IndexArgs {
     uint32_t* cand_key;  // [B*Tq][cst]: slice s's candidates at [s*kk, s*kk + count)
     int32_t* cand_idx;   // [B*Tq][cst]
     uint32_t* tbound;    // [B*Tq][nslices]: per-slice lower bound of the top-r keys (see k_idx_merge)
+    // dense path (many queries): queries qc0 .. qc0+Tc-1 per pass
+    int dense;           // 1: score every (query, key) pair to HBM, then select per query
+    int Tc;              // queries per pass
+    int qc0;             // first query of the pass (set by the launcher)
+    int64_t sstride;     // score row stride (n_cap rounded up to a multiple of 4)
+    uint32_t* scores;    // [B][Tc][sstride] order-preserving score keys
+    uint32_t* hist;      // [B][Tc][2048] histogram of the keys' top 11 bits
 };
 
 struct AttendArgs {

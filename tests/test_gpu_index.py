@@ -110,3 +110,50 @@ def test_index_topk_is_deterministic(gpu):
     b = ops.index_topk(*args, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+DENSE_CASES = [
+    # (name, B, Tq, H_I, N, m, k, positions): Tq >= 64 with a bf16 d_I = 128 indexer takes the
+    # many-query path (every score to HBM, then one select per query)
+    ("dense_h64", 1, 96, 64, 20000, 4, 512, "ragged"),
+    ("dense_h16_b2", 2, 64, 16, 9000, 4, 256, "ragged"),
+    ("dense_h32_small_n", 1, 70, 32, 700, 1, 1024, "ragged"),     # many queries with n(t) < k
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_index_topk_many_queries(gpu, case):
+    _, B, Tq, H_I, N, m, k, pk = case
+    d_I, fmt = 128, O.BF16
+    qi, _, ki, _, qd, kd = _inputs(fmt, B, Tq, H_I, d_I, N, 900 + N)
+    w = gen.normal((B, Tq, H_I), 901 + N, 1 / math.sqrt(H_I))
+    qpos = _positions(pk, B, Tq, N, m).to(torch.int32)
+    kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
+    gi, gs = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=fmt, k=k, **kw)
+    torch.cuda.synchronize()
+    oi, _ = O.index_topk(host(qi), fmt, host(w), host(ki), fmt, host(qpos), k=k, **kw)
+    allsc = oracle_all_scores(host(qi), fmt, host(w), host(ki), fmt, host(qpos), **kw)
+    bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
+    n_sw, gap = check_topk(host(gi), oi, allsc, k, abs_bound=bound)
+    gi_h, gs_h = host(gi), host(gs)
+    for b in range(B):
+        for j in range(Tq):
+            v = gi_h[b, j] >= 0
+            ref = allsc[b, j, gi_h[b, j, v]]
+            assert np.all(np.abs(gs_h[b, j, v] - ref) <= bound[b, j] + 1e-6 * np.abs(ref)), (b, j)
+            assert np.all(np.isneginf(gs_h[b, j, ~v]))
+    print("case %s: queries with tie swaps %d, largest gap %.3g" % (case[0], n_sw, gap))
+
+
+def test_index_topk_many_queries_all_tied(gpu):
+    # every score equal: the select refines all three digit levels and keeps the
+    # k smallest indices among more tied keys than it can hold
+    B, Tq, H_I, d_I, N, k = 1, 64, 16, 128, 12000, 1000
+    q = gen.normal((B, Tq, H_I, d_I), 31)
+    key = gen.normal((1, 1, d_I), 32).expand(B, N, d_I).contiguous()
+    w = torch.ones((B, Tq, H_I))
+    qpos = gen.positions(B, Tq, 4 * N - 1)
+    gi, _ = ops.index_topk(dev(gen.store(q, O.BF16)), dev(w), dev(gen.store(key, O.BF16)), dev(qpos), fmt=O.BF16,
+                           H_I=H_I, d_I=d_I, m=4, n_cap=N, k=k)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gi)[0], np.tile(np.arange(k), (Tq, 1)))
