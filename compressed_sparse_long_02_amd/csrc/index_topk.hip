@@ -569,8 +569,8 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
 // written to HBM as its order-preserving key (4 bytes per pair, a few percent of
 // the MFMA time) together with a per-query histogram of the keys' top 11 bits.  The
 // select then needs a single pass over each query's keys in most cases.
-constexpr int DNS_NT = 512;       // 8 waves: wave w scores query w & 3, keys 64*(w >> 2) .. +64 of a tile
-constexpr int DNS_QB = 4;         // queries per block
+constexpr int DNS_NT = 512;       // 8 waves: wave w scores query w against every key of a tile
+constexpr int DNS_QB = 8;         // queries per block
 constexpr int DNS_KT = 128;       // keys per tile
 constexpr int DNS_TPB = 32;       // tiles per block
 constexpr int DNS_KSTR = 272;     // bytes per key row in LDS (256 + 16 pad: conflict-free fragment reads)
@@ -588,7 +588,7 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
     __shared__ int64_t nq[DNS_QB];
     const int kx = blockIdx.x, qg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
-    const int qw = wv & 3, kh = wv >> 2;
+    const int qw = wv;
     if (tid < DNS_QB) {
         const int jl = qg * DNS_QB + tid, jq = a.qc0 + jl;
         nq[tid] = (jl < a.Tc && jq < a.Tq) ? n_visible(a.q_pos[(int64_t)b * a.Tq + jq], a.m, a.n_cap) : 0;
@@ -651,7 +651,7 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
     lds_barrier();
     for (int t = 0; t < nt; ++t) {
         if (t + 1 < nt) load_tile(t + 1);               // in flight during the MFMA work
-        if (n > 0) {
+        if (n > 0) for (int kh = 0; kh < 2; ++kh) {     // the tile's two halves of 64 keys
             v4f acc[4][HB];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
