@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle CPU sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=20)
+    p.add_argument("--workload", choices=["stack", "prefill"], default="stack",
+                   help="stack: the 4-layer decode stack (default); prefill: one CSA prefill chunk")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="also run a plain device copy of this many MiB (the reference kernel for HBM counters)")
     return p.parse_args()
@@ -206,6 +208,135 @@ def recorded_traffic(B, ctx):
     return int(fields["traffic_bytes_per_launch"])
 
 
+class Prefill:
+    """One CSA layer appending a chunk of 8,192 tokens to 1,048,576 cached ones: compress the
+    chunk's 2,048 entries (KV and bf16 indexer keys, with the 4 look-back rows), index the
+    8,192 queries against the 264,192 entries (64 heads x 128, bf16, top-1024, causal) and
+    attend with 128 heads of 512 over the selected entries plus a 128-token window."""
+
+    def __init__(self, device):
+        import torch
+        from compressed_sparse_long_02_amd import gen
+        self.H, self.d, self.r, self.m, self.HI, self.dI, self.k, self.W, self.C = 128, 512, 64, 4, 64, 128, 1024, 128, 8192
+        self.T0 = 1 << 20
+        self.N0 = self.T0 // self.m
+        self.N = (self.T0 + self.C) // self.m
+        d, r, dI, m, C, W = self.d, self.r, self.dI, self.m, self.C, self.W
+        self.cache = torch.empty((1, self.N, d + r), dtype=torch.uint8, device=device)
+        self.keys = torch.empty((1, self.N, dI * 2), dtype=torch.uint8, device=device)
+        for s0 in range(0, self.N0, 32768):
+            c = min(32768, self.N0 - s0)
+            self.cache[:, s0:s0 + c] = gen.pack_kv(gen.normal((1, c, d), 5000 + s0, device=device), r)
+            self.keys[:, s0:s0 + c] = gen.bf16_bytes(gen.normal((1, c, dI), 6000 + s0, device=device))
+        self.x = gen.bf16_bytes(gen.normal((1, C + m, d), 7001, device=device))
+        self.xi = gen.bf16_bytes(gen.normal((1, C + m, dI), 7002, device=device))
+        self.z = gen.random_logits((1, C + m, 1), 7003, device=device)
+        self.zi = gen.random_logits((1, C + m, 1), 7004, device=device)
+        self.bias = gen.random_logits((2 * m, 1), 7005, device=device)
+        self.bias_i = gen.random_logits((2 * m, 1), 7006, device=device)
+        self.kvw = gen.pack_kv(gen.normal((1, W + C, d), 7007, device=device), r)
+        self.q_pos = torch.arange(self.T0, self.T0 + C, dtype=torch.int32, device=device).view(1, C)
+        self.qi = gen.bf16_bytes(gen.normal((1, C, self.HI, dI), 7008, device=device))
+        self.w = gen.normal((1, C, self.HI), 7009, 1 / math.sqrt(self.HI), device=device)
+        self.q = gen.normal((1, C, self.H, d), 7010, device=device).to(torch.bfloat16)
+        self.idx = torch.empty((1, C, self.k), dtype=torch.int32, device=device)
+        self.out = torch.empty((1, C, self.H, d), dtype=torch.bfloat16, device=device)
+        torch.cuda.synchronize()
+
+    def compress(self):
+        from compressed_sparse_long_02_amd import ops as F
+        ne = self.C // self.m
+        kw = dict(m=self.m, overlap=True, e_begin=self.N0, n_e=ne, x_pos0=self.T0 - self.m)
+        F.kv_compress(self.x, F.BF16, self.z, self.bias, d=self.d, r=self.r, out_fmt=F.KV_PACKED,
+                      out=self.cache[:, self.N0:self.N], **kw)
+        F.kv_compress(self.xi, F.BF16, self.zi, self.bias_i, d=self.dI, out_fmt=F.BF16,
+                      out=self.keys[:, self.N0:self.N], **kw)
+
+    def index(self):
+        from compressed_sparse_long_02_amd import ops as F
+        F.index_topk(self.qi, self.w, self.keys, self.q_pos, fmt=F.BF16, H_I=self.HI, d_I=self.dI, m=self.m,
+                     n_cap=self.N, k=self.k, out_idx=self.idx, with_scores=False)
+
+    def attend(self):
+        from compressed_sparse_long_02_amd import ops as F
+        F.csa_attend(self.q, self.cache, self.idx, self.kvw, self.q_pos, kv_fmt=F.KV_PACKED, n_cap=self.N,
+                     kvw_pos0=self.T0 - self.W, kvw_rows=self.W + self.C, W=self.W, H=self.H, d=self.d, r=self.r,
+                     scale=1 / math.sqrt(self.d), out_fmt=F.BF16, out=self.out, with_lse=False)
+
+    def step(self):
+        self.compress()
+        self.index()
+        self.attend()
+
+    def index_flops(self):
+        """2 * H_I * d_I per visible (query, entry) pair."""
+        pairs = sum(min((self.T0 + j + 1) // self.m, self.N) for j in range(self.C))
+        return 2 * self.HI * self.dI * pairs
+
+    def attend_flops(self):
+        return 4 * self.C * self.H * (self.k + self.W) * self.d
+
+
+def prefill_cpu_baseline(pf, nq):
+    """The oracle on `nq` of the chunk's queries (index + attend over the same inputs), timed on the
+    host cores and scaled to the 8,192 queries of the chunk (compression excluded: < 0.1% of it)."""
+    import numpy as np
+    import torch
+    import oracle as O
+    sel = np.linspace(0, pf.C - 1, nq).astype(np.int64)
+    h = lambda x: x.detach().cpu().numpy()
+    qi, w, qpos = h(pf.qi[:, sel]), h(pf.w[:, sel]), h(pf.q_pos[:, sel])
+    keys, cache, kvw, q = h(pf.keys), h(pf.cache), h(pf.kvw), h(pf.q[:, sel].view(torch.int16))
+    t0 = time.perf_counter()
+    idx, _ = O.index_topk(qi, O.BF16, w, keys, O.BF16, qpos, H_I=pf.HI, d_I=pf.dI, m=pf.m, n_cap=pf.N, k=pf.k)
+    O.csa_attend(q, O.BF16, cache, O.KV_PACKED, pf.N, idx, kvw, pf.T0 - pf.W, pf.W + pf.C, qpos, W=pf.W, H=pf.H,
+                 d=pf.d, r=pf.r, scale=1 / math.sqrt(pf.d))
+    dt = time.perf_counter() - t0
+    return {"value": round(nq / dt, 4), "unit": "tokens/s", "cores": min(nq, O.num_threads()), "kind": "oracle",
+            "sample": "%d of the chunk's 8192 queries (index_topk + csa_attend), %.1f s on the host" % (nq, dt)}
+
+
+def main_prefill(args):
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] building the prefill-chunk inputs", file=sys.stderr, flush=True)
+    pf = Prefill(dev)
+    pf.step()
+    torch.cuda.synchronize()
+    steps, warm = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
+    for _ in range(warm):
+        pf.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pf.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    t_idx = time_calls(pf.index, 3)
+    t_att = time_calls(pf.attend, 3)
+    t_cmp = time_calls(pf.compress, 3)
+    fi = pf.index_flops()
+    ach = fi / (t_idx * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "index_topk (bf16 64x128 indexer, 8192 queries x 264,192 entries, top-1024)",
+            "achieved": round(ach, 1), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4),
+            "traffic": None, "flops_per_launch": fi, "ms_per_launch": round(t_idx, 3)}
+    kernels = {"index_topk": {"ms": round(t_idx, 3), "TFLOP/s": round(ach, 1)},
+               "csa_attend": {"ms": round(t_att, 3), "TFLOP/s": round(pf.attend_flops() / (t_att * 1e-3) / 1e12, 1)},
+               "kv_compress_x2": {"ms": round(t_cmp, 3)}}
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(pf, 48)
+    line = {
+        "metric": "CSA prefill-chunk tokens/sec at 1M ctx; indexer MFMA %", "value": round(pf.C / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "CSA prefill chunk: 8192 tokens on 1,048,576 cached (compress + index + attend)",
+                   "global_batch": 1, "seq_len": pf.T0 + pf.C, "heads": pf.H, "head_dim": pf.d,
+                   "indexer": "bf16 64x128, top-k 1024", "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def time_calls(fn, iters):
     """Average duration of fn() on torch's current stream, by HIP events."""
     import torch
@@ -266,6 +397,8 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prefill":
+        return main_prefill(args)
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
