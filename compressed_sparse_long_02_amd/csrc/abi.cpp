@@ -222,14 +222,14 @@ bool dense_path(int fmt, int d_I, int H_I, int Tq) {
 }
 int64_t dense_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64_t)3; }
 int dense_tc(int B, int Tq, int64_t n_cap) {
-    // queries per pass: a multiple of 8 (the score kernel's query group), the passes
+    // queries per pass: a multiple of 12 (the score kernel's query group), the passes
     // as even as possible, each within DENSE_WS_MAX
     const size_t per_q = (size_t)(B > 0 ? B : 1) * ((size_t)dense_stride(n_cap) + 2048) * 4;
-    size_t cap = (DENSE_WS_MAX / per_q) & ~(size_t)7;
-    if (cap < 8) cap = 8;
+    size_t cap = (DENSE_WS_MAX / per_q) / 12 * 12;
+    if (cap < 12) cap = 12;
     const size_t tq = Tq > 0 ? (size_t)Tq : 1;
     const size_t passes = (tq + cap - 1) / cap;
-    const size_t tc = ((tq + passes - 1) / passes + 7) & ~(size_t)7;
+    const size_t tc = ((tq + passes - 1) / passes + 11) / 12 * 12;
     return (int)(tc < cap ? tc : cap);
 }
 size_t dense_ws(int B, int Tq, int64_t n_cap) {

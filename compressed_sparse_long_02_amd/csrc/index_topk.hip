@@ -569,8 +569,8 @@ __global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
 // written to HBM as its order-preserving key (4 bytes per pair, a few percent of
 // the MFMA time) together with a per-query histogram of the keys' top 11 bits.  The
 // select then needs a single pass over each query's keys in most cases.
-constexpr int DNS_NT = 512;       // 8 waves: wave w scores query w against every key of a tile
-constexpr int DNS_QB = 8;         // queries per block
+constexpr int DNS_NT = 768;       // 12 waves (3 per SIMD): wave w scores query w against every key of a tile
+constexpr int DNS_QB = 12;        // queries per block
 constexpr int DNS_KT = 128;       // keys per tile
 constexpr int DNS_TPB = 32;       // tiles per block
 constexpr int DNS_KSTR = 272;     // bytes per key row in LDS (256 + 16 pad: conflict-free fragment reads)
@@ -582,9 +582,10 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n) {
 }
 
 template <int HB>
-__global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
+__global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t kt[2][DNS_KT * DNS_KSTR];
-    __shared__ uint32_t hist[DNS_QB * TOPK_BINS];
+    // per-query histograms, two 16-bit counts per word (a block sees at most 4096 keys)
+    __shared__ uint32_t hist[DNS_QB * TOPK_BINS / 2];
     __shared__ int64_t nq[DNS_QB];
     const int kx = blockIdx.x, qg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
@@ -593,7 +594,7 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
         const int jl = qg * DNS_QB + tid, jq = a.qc0 + jl;
         nq[tid] = (jl < a.Tc && jq < a.Tq) ? n_visible(a.q_pos[(int64_t)b * a.Tq + jq], a.m, a.n_cap) : 0;
     }
-    for (int x = tid; x < DNS_QB * TOPK_BINS; x += DNS_NT) hist[x] = 0u;
+    for (int x = tid; x < DNS_QB * TOPK_BINS / 2; x += DNS_NT) hist[x] = 0u;
     __syncthreads();
     int64_t nmax = 0;
 #pragma unroll
@@ -628,11 +629,12 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
     // key tiles: thread tid moves chunks c = tid + 512 j (key c / 16, 16-byte piece c % 16);
     // keys past the range re-read the range's last key (scored, then ignored)
     const uint8_t* kbase = a.ki + (int64_t)b * a.ki_bstride;
-    u32x4 R[4];
+    constexpr int NR = (DNS_KT * 16 + DNS_NT - 1) / DNS_NT;   // 16-byte chunks per thread and tile
+    u32x4 R[NR];
     auto load_tile = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + DNS_NT * j;
+        for (int j = 0; j < NR; ++j) {
+            const int c = tid + DNS_NT * j < DNS_KT * 16 ? tid + DNS_NT * j : DNS_KT * 16 - 1;
             int64_t key = k0 + (int64_t)t * DNS_KT + (c >> 4);
             key = key < k1 ? key : k1 - 1;
             R[j] = ld_global<u32x4>(kbase + key * 256 + 16 * (c & 15));
@@ -640,9 +642,9 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NR; ++j) {
             const int c = tid + DNS_NT * j;
-            *(u32x4*)(&kt[buf][(c >> 4) * DNS_KSTR + 16 * (c & 15)]) = R[j];
+            if (c < DNS_KT * 16) *(u32x4*)(&kt[buf][(c >> 4) * DNS_KSTR + 16 * (c & 15)]) = R[j];
         }
     };
     uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
@@ -651,34 +653,33 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
     lds_barrier();
     for (int t = 0; t < nt; ++t) {
         if (t + 1 < nt) load_tile(t + 1);               // in flight during the MFMA work
-        if (n > 0) for (int kh = 0; kh < 2; ++kh) {     // the tile's two halves of 64 keys
-            v4f acc[4][HB];
+        // eight blocks of 16 keys, one after the other: the epilogue of a block (ReLU,
+        // head weights, the sum over the 4 lane rows) overlaps the next block's MFMAs
+        if (n > 0) {
+            const uint8_t* tb = &kt[t & 1][col * DNS_KSTR + 16 * g];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < DNS_KT / 16; ++kb) {
+                v4f acc[HB];
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) acc[kb][hb] = v4f{0.f, 0.f, 0.f, 0.f};
-            const uint8_t* tb = &kt[t & 1][(64 * kh + col) * DNS_KSTR + 16 * g];
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                for (int ks = 0; ks < 4; ++ks) {
                     const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DNS_KSTR + 64 * ks);
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) acc[kb][hb] = mfma_bf16(qa[hb][ks], bf, acc[kb][hb]);
+                    for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16(qa[hb][ks], bf, acc[hb]);
                 }
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
                 float part = 0.f;
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(acc[kb][hb][i]), part);
+                    for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(acc[hb][i]), part);
                 part = cross4_sum(part);
-                const int64_t sidx = k0 + (int64_t)t * DNS_KT + 64 * kh + 16 * kb + col;
+                const int64_t sidx = k0 + (int64_t)t * DNS_KT + 16 * kb + col;
                 if (g == 0 && sidx < n) {
                     const uint32_t key = score_key(part);
                     srow[sidx] = key;
-                    atomicAdd(&hist[qw * TOPK_BINS + (key >> 21)], 1u);
+                    const uint32_t bin = key >> 21;
+                    atomicAdd(&hist[qw * (TOPK_BINS / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
                 }
             }
         }
@@ -686,11 +687,14 @@ __global__ void __launch_bounds__(DNS_NT, 2) k_idx_dense_score(IndexArgs a) {
         lds_barrier();
     }
     // add this block's histograms into the per-query ones (integer adds: order-free)
-    for (int x = tid; x < DNS_QB * TOPK_BINS; x += DNS_NT) {
-        const int u = x / TOPK_BINS;
+    for (int x = tid; x < DNS_QB * TOPK_BINS / 2; x += DNS_NT) {
+        const int u = x / (TOPK_BINS / 2);
         const uint32_t v = hist[x];
-        if (v && qg * DNS_QB + u < a.Tc)
-            atomicAdd(&a.hist[((int64_t)b * a.Tc + qg * DNS_QB + u) * TOPK_BINS + (x - u * TOPK_BINS)], v);
+        if (v && qg * DNS_QB + u < a.Tc) {
+            uint32_t* gh = a.hist + ((int64_t)b * a.Tc + qg * DNS_QB + u) * TOPK_BINS + 2 * (x - u * (TOPK_BINS / 2));
+            if (v & 0xffffu) atomicAdd(gh, v & 0xffffu);
+            if (v >> 16) atomicAdd(gh + 1, v >> 16);
+        }
     }
 }
 
