@@ -394,17 +394,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         const int64_t e_end = v_end < n_ent ? v_end : n_ent;
         for (int64_t v = v_begin + tid; v < e_end; v += MQ_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
     }
-    // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the dims
-    u32x4 qb[QH];
-    {
-        const int h = hb * 64 + 16 * hg + col;
-        const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
-#pragma unroll
-        for (int ks = 0; ks < QH; ++ks) {
-            const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
-            qb[ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
-        }
-    }
     // this thread's chunks of a tile, the same for every tile: j < JB are bf16 chunks
     // (row, 16-byte piece of the first 2*rbf bytes), the others fp8 chunks (row,
     // 16-byte piece of the fp8 part); -1 when beyond the tile
@@ -469,6 +458,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     v4f* sx_mine = sx + wv * 128 + lane;
     const v4f* sx_part = sx + (wv ^ 4) * 128 + lane;
     u32x4 R0[NJ], R1[NJ], R2[NJ];
+    u32x4 qb[QH];
     bool ovf = false;
 
     // one tile: its prefetched rows (Rb) -> LDS, refill Rb with tile it+PF, then
@@ -576,18 +566,36 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         }
     };
 
+    // first rows in flight before the query loads, so that the two latencies overlap
+    auto start_rows = [&]() {
+        for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
+        lds_barrier();
+        if (0 < ntiles) load_regs(0, R0);
+        if (1 < ntiles) load_regs(1, R1);
+        if (2 < ntiles) load_regs(2, R2);
+    };
+    start_rows();
+    // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the dims
+    {
+        const int h = hb * 64 + 16 * hg + col;
+        const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
+#pragma unroll
+        for (int ks = 0; ks < QH; ++ks) {
+            const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
+            qb[ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
+        }
+    }
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int db = 0; db < NDH; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
         m_ref = pass == 0 ? -INFINITY : cross4_max(m_seen);
         l_lane = 0.f;
         ovf = false;
-        __syncthreads();                                // slots and tiles of a previous pass are free
-        for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
-        __syncthreads();
-        if (0 < ntiles) load_regs(0, R0);
-        if (1 < ntiles) load_regs(1, R1);
-        if (2 < ntiles) load_regs(2, R2);
+        if (pass > 0) {
+            __syncthreads();                            // slots and tiles of the first pass are free
+            start_rows();
+        }
         for (int it = 0; it < ntiles; it += PF) {
             tile(it, R0);
             if (it + 1 < ntiles) tile(it + 1, R1);
