@@ -54,31 +54,36 @@ int launched(hipError_t e) {
 }
 
 // ---- planning (also used by the workspace queries) -------------------------
-constexpr int MAX_CAND = 32768;
-constexpr int MAX_SLICES = 64;
+constexpr int MAX_SLICES = 1024;        // slices of one query (the row select scans their counts in one pass)
+constexpr int MAX_S = 16384;            // keys one scoring block holds in LDS
+constexpr int64_t MAX_NCAP = (int64_t)MAX_S * MAX_SLICES;
 
-bool plan_index(int B, int Tq, int64_t n_cap, int k, int& S, int& nslices, int& kk) {
-    const int64_t target_blocks = 1024;
+// Slices of S keys (a power of two in [512, 16384]), about 512 scoring blocks in all
+// (two per compute unit).  One slice per query: the block selects; several: the
+// split path over score rows.
+void plan_index(int B, int Tq, int64_t n_cap, int& S, int& nslices) {
+    const int64_t target_blocks = 512;
     const int64_t work = (n_cap > 0 ? n_cap : 1) * (int64_t)(B > 0 ? B : 1) * (Tq > 0 ? Tq : 1);
     const int64_t need = (work + target_blocks - 1) / target_blocks;
     S = 512;   // at least one key per thread of the 512-thread scoring block
-    while (S < need && S < 16384) S <<= 1;
-    for (;;) {
-        nslices = n_cap <= 0 ? 1 : (int)((n_cap + S - 1) / S);
-        kk = k < S ? k : S;
-        if (nslices == 1 || ((int64_t)nslices * kk <= MAX_CAND && nslices <= MAX_SLICES)) return true;
-        if (S >= 16384) return false;
-        S <<= 1;
-    }
+    while (S < need && S < MAX_S) S <<= 1;
+    while (n_cap > (int64_t)S * MAX_SLICES && S < MAX_S) S <<= 1;
+    nslices = n_cap <= 0 ? 1 : (int)((n_cap + S - 1) / S);
 }
 
-int index_cst(int nslices, int kk) { return ((nslices * kk + 4095) / 4096) * 4096; }
+int64_t row_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64_t)3; }
 
-size_t index_ws(int B, int Tq, int S, int nslices, int kk) {
-    (void)S;
+size_t index_ws(int B, int Tq, int64_t n_cap, int nslices) {
     if (nslices <= 1) return 0;
     const size_t q = (size_t)B * Tq;
-    return q * index_cst(nslices, kk) * 8 + q * nslices * 4 + 512;
+    return q * ((size_t)3 * row_stride(n_cap) + (size_t)nslices * (csl::IDX_SLOT_W + 1) + 2048) * 4 + 256;
+}
+
+// Split path: slices per filter block, about 256 filter blocks (one per compute unit) in all.
+int index_spb(int B, int Tq, int nslices) {
+    const int64_t q = (int64_t)(B > 0 ? B : 1) * (Tq > 0 ? Tq : 1);
+    int64_t spb = ((int64_t)nslices * q + 255) / 256;
+    return (int)(spb < 1 ? 1 : (spb > nslices ? nslices : spb));
 }
 
 constexpr int ATT_STEP = 32;            // rows a block stages per iteration; split lengths are multiples
@@ -220,11 +225,10 @@ constexpr size_t DENSE_WS_MAX = (size_t)2 << 30;
 bool dense_path(int fmt, int d_I, int H_I, int Tq) {
     return fmt == CSL_BF16 && d_I == 128 && (H_I == 16 || H_I == 32 || H_I == 64 || H_I == 128) && Tq >= DENSE_MIN_TQ;
 }
-int64_t dense_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64_t)3; }
 int dense_tc(int B, int Tq, int64_t n_cap) {
     // queries per pass: a multiple of 12 (the score kernel's query group), the passes
     // as even as possible, each within DENSE_WS_MAX
-    const size_t per_q = (size_t)(B > 0 ? B : 1) * ((size_t)dense_stride(n_cap) + 2048) * 4;
+    const size_t per_q = (size_t)(B > 0 ? B : 1) * ((size_t)row_stride(n_cap) + 2048) * 4;
     size_t cap = (DENSE_WS_MAX / per_q) / 12 * 12;
     if (cap < 12) cap = 12;
     const size_t tq = Tq > 0 ? (size_t)Tq : 1;
@@ -233,13 +237,14 @@ int dense_tc(int B, int Tq, int64_t n_cap) {
     return (int)(tc < cap ? tc : cap);
 }
 size_t dense_ws(int B, int Tq, int64_t n_cap) {
-    return (size_t)B * dense_tc(B, Tq, n_cap) * ((size_t)dense_stride(n_cap) + 2048) * 4 + 256;
+    return (size_t)B * dense_tc(B, Tq, n_cap) * ((size_t)row_stride(n_cap) + 2048) * 4 + 256;
 }
 
 size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
     if (B < 0 || Tq < 0 || k < 1) return 0;
-    int S, ns, kk;
-    size_t ws = plan_index(B, Tq, n_cap, k, S, ns, kk) ? index_ws(B, Tq, S, ns, kk) : 0;
+    int S, ns;
+    plan_index(B, Tq, n_cap, S, ns);
+    size_t ws = index_ws(B, Tq, n_cap, ns);
     if (Tq >= DENSE_MIN_TQ) {                            // the dense path may be taken (fmt, d_I, H_I unknown here)
         const size_t d = dense_ws(B, Tq, n_cap);
         ws = d > ws ? d : ws;
@@ -263,10 +268,10 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
                      (ki_fmt == CSL_MXFP4 && d_I == 128);
     if (!dok) return fail(CSL_EUNSUPPORTED, "%s: (fmt %d, d_I %d) not built", fn, ki_fmt, d_I);
     const bool dense = dense_path(ki_fmt, d_I, H_I, Tq);
-    int S = 0, nslices = 1, kk = k;
-    if (!dense && !plan_index(B, Tq, n_cap, k, S, nslices, kk))
-        return fail(CSL_EUNSUPPORTED, "%s: n_cap = %lld with k = %d exceeds the candidate merge", fn, (long long)n_cap, k);
-    const size_t need = dense ? dense_ws(B, Tq, n_cap) : index_ws(B, Tq, S, nslices, kk);
+    if (n_cap > MAX_NCAP) return fail(CSL_EUNSUPPORTED, "%s: n_cap must be <= 2^24", fn);
+    int S = 0, nslices = 1;
+    if (!dense) plan_index(B, Tq, n_cap, S, nslices);
+    const size_t need = dense ? dense_ws(B, Tq, n_cap) : index_ws(B, Tq, n_cap, nslices);
     if (B * (int64_t)Tq == 0) { g_err.clear(); return CSL_OK; }
     if (!qi || !w || !q_pos || !out_idx || (n_cap > 0 && !ki)) return fail(CSL_EINVAL, "%s: null pointer argument", fn);
     if ((ki_fmt == CSL_MXFP4) != (qi_scales != nullptr) || (ki_fmt == CSL_MXFP4) != (ki_scales != nullptr || n_cap == 0))
@@ -282,19 +287,24 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
     a.ki = (const uint8_t*)ki; a.ki_fmt = ki_fmt; a.ki_scales = ki_scales; a.ki_bstride = ki_bstride; a.ks_bstride = ks_bstride;
     a.q_pos = q_pos; a.B = B; a.Tq = Tq; a.H_I = H_I; a.d_I = d_I; a.m = m; a.n_cap = n_cap; a.k = k;
     a.out_idx = out_idx; a.out_score = out_score;
-    a.S = S; a.nslices = nslices; a.kk = kk;
-    a.cst = index_cst(nslices, kk);
+    a.S = S; a.nslices = nslices;
     if (dense) {
         a.dense = 1;
         a.Tc = dense_tc(B, Tq, n_cap);
-        a.sstride = dense_stride(n_cap);
+        a.sstride = row_stride(n_cap);
         a.scores = (uint32_t*)ws;
         a.hist = (uint32_t*)((uint8_t*)ws + (size_t)B * a.Tc * a.sstride * 4);
     } else if (nslices > 1) {
-        const size_t nc = (size_t)B * Tq * a.cst;
-        a.cand_key = (uint32_t*)ws;
-        a.cand_idx = (int32_t*)((uint8_t*)ws + nc * 4);
-        a.tbound = (uint32_t*)((uint8_t*)ws + nc * 8);
+        a.spb = index_spb(B, Tq, nslices);
+        a.sstride = row_stride(n_cap);
+        const size_t q = (size_t)B * Tq;
+        const size_t nr = q * a.sstride * 4;           // bytes of one [B*Tq][sstride] array
+        a.scores = (uint32_t*)ws;
+        a.cand_key = (uint32_t*)((uint8_t*)ws + nr);
+        a.cand_idx = (int32_t*)((uint8_t*)ws + 2 * nr);
+        a.hist = (uint32_t*)((uint8_t*)ws + 3 * nr);
+        a.seg_cnt = (int32_t*)(a.hist + q * nslices * csl::IDX_SLOT_W);
+        a.row_hist = (uint32_t*)(a.seg_cnt + q * nslices);
     }
     return launched(csl::launch_index_topk(a, (hipStream_t)stream));
 }

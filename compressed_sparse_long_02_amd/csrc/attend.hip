@@ -476,7 +476,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             if (j < JB) {
                 *(u32x4*)(rowp + 16 * cpc[j]) = v;
             } else {
-                typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
                 u32x4 lo, hi;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -723,7 +722,6 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
 template <int D, int FMT>
 static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq));
-    const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
     if (a.idx && a.rps > ATT_MAX_SIDX) return hipErrorInvalidValue;
     if constexpr (FMT == F32) {
         hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);

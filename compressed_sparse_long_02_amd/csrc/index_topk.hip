@@ -107,22 +107,18 @@ constexpr int TOPK_BITS = 11;
 constexpr int TOPK_EMAX = 32;
 #define TOPK_SCRATCH(NT) (2 * TOPK_HSZ + 16 + 2 * ((NT) / 64) + 8)
 
-// If rank_r > 0, thread 0 also stores to *tb_out a value t such that at least rank_r
-// of the n keys are >= t (the lower edge of the first-pass bin holding the
-// rank_r-th largest key; 0 when the block learns nothing, which is always valid).
 template <int NT, int EMAX, typename Emit>
 __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, int n, int want, uint32_t* sh,
-                                           Emit emit, int rank_r = 0, uint32_t* tb_out = nullptr) {
+                                           Emit emit) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int base = tid * E;
     uint32_t* hist0 = sh;
     uint32_t* hist1 = sh + TOPK_HSZ;
-    uint32_t* misc = sh + 2 * TOPK_HSZ;                     // [0] digit [1] above [2] in-bin [3] rank bin
+    uint32_t* misc = sh + 2 * TOPK_HSZ;                     // [0] digit [1] above [2] in-bin
     int* wsum = (int*)(sh + 2 * TOPK_HSZ + 16);            // NT/64 for lo, NT/64 for hi / scans
     uint32_t T = 0;        // select u > T, plus the first eq_take keys equal to T
     int eq_take = 0;
     const bool all = n <= want;
-    if (all && tb_out && tid == 0) *tb_out = 0u;
     if (!all) {
         // ---- min / max over the valid keys; clear the first histogram
         uint32_t lo = 0xffffffffu, hi = 0u;
@@ -147,7 +143,6 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
         if (lo == hi) {
             T = lo;                                  // every key ties
             eq_take = want;
-            if (tb_out && tid == 0) *tb_out = lo;
         } else {
             int top = 31 - __builtin_clz(lo ^ hi);   // highest differing bit
             uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
@@ -180,7 +175,10 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
                     const int incl = wave_incl_scan((int)loc);
                     const int tot = __shfl(incl, 63, 64);
                     uint32_t c = (uint32_t)(tot - incl);   // keys in the bins of higher lanes
-                    const uint32_t rr = pass == 0 ? (uint32_t)rank_r : 0u;
+                    // the lane's first bin, opaque to the compiler so that the 32 bin
+                    // numbers below are formed where used, not hoisted out of the pass loop
+                    int lb = 32 * lane;
+                    asm volatile("" : "+v"(lb));
 #pragma unroll
                     for (int q = 7; q >= 0; --q) {
                         const u32x4 v4 = hp[q];
@@ -189,17 +187,15 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
                             const uint32_t hq = v4[e];
                             const uint32_t cge = c + hq;
                             if (cge >= (uint32_t)w && c < (uint32_t)w) {
-                                misc[0] = 32 * lane + 4 * q + e;
+                                misc[0] = lb + 4 * q + e;
                                 misc[1] = c;
                                 misc[2] = hq;
                             }
-                            if (rr > 0 && cge >= rr && c < rr) misc[3] = 32 * lane + 4 * q + e;
                             c = cge;
                         }
                     }
                 }
                 __syncthreads();
-                if (pass == 0 && rank_r > 0 && tb_out && tid == 0) *tb_out = prefix | (misc[3] << shift);
                 const uint32_t dgt = misc[0];
                 w -= (int)misc[1];
                 const int inbin = (int)misc[2];
@@ -334,10 +330,17 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
     return FMT == F32 ? 4 * (int64_t)DI : (FMT == BF16 ? 2 * (int64_t)DI : (int64_t)DI / 2);
 }
 
-template <int FMT, int DI, int HB>
+// SPLIT = false: one slice per query, selected in the block.  SPLIT = true: the
+// block writes its slice's keys to the query's score row and the nonzero bins of
+// their top-11-bit histogram, as (bin << 21 | count) words, to the slice's list;
+// k_idx_split_filter and k_idx_split_select finish the query.
+constexpr int SLOT_W = IDX_SLOT_W;
+constexpr int MAX_SLICES_PER_ROW = 1024;
+static_assert(SLOT_W >= TOPK_BINS + 1 && 4 * IDX_NT == TOPK_BINS, "slice lists: 4 bins per scoring thread");
+template <int FMT, int DI, int HB, bool SPLIT>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
 k_idx_score(IndexArgs a) {
-    extern __shared__ uint32_t smem[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     const int sl = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int64_t bq = (int64_t)b * a.Tq + j;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
@@ -345,11 +348,17 @@ k_idx_score(IndexArgs a) {
     const int le = 31 - __builtin_clz(E);
     uint32_t* keys = smem;
     uint32_t* sh = smem + a.S + (a.S >> le);
+    uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the histogram
 
     const int64_t t = a.q_pos[bq];
     const int64_t n = n_visible(t, a.m, a.n_cap);
     const int64_t s0 = (int64_t)sl * a.S;
     const int ns = (int)(n - s0 < 0 ? 0 : (n - s0 > a.S ? a.S : n - s0));
+    if constexpr (SPLIT) {
+        if (ns <= 0) return;
+        for (int x = tid; x < TOPK_BINS; x += IDX_NT) hs[x] = 0u;
+        __syncthreads();
+    }
 
     if (ns > 0) {
         // q fragments (A operand: rows = heads) and head weights, kept in registers
@@ -398,7 +407,15 @@ k_idx_score(IndexArgs a) {
             }
             part = cross4_sum(part);                    // the 64 heads of the 4 lane rows
             const int li = T * 16 + col;
-            if (g == 0 && T < ntile && li < ns) keys[li + (li >> le)] = score_key(part);
+            if (g == 0 && T < ntile && li < ns) {
+                const uint32_t u = score_key(part);
+                if constexpr (SPLIT) {
+                    keys[li] = u;
+                    atomicAdd(&hs[u >> (32 - TOPK_BITS)], 1u);
+                } else {
+                    keys[li + (li >> le)] = u;
+                }
+            }
         };
         constexpr int NWV = IDX_NT / 64;
         const int wvu = __builtin_amdgcn_readfirstlane(wv);           // wave-uniform
@@ -425,6 +442,29 @@ k_idx_score(IndexArgs a) {
         }
     }
     __syncthreads();
+    if constexpr (SPLIT) {
+        // the slice's keys to its part of the score row in 16-byte stores (s0 and the
+        // row stride are multiples of 4), the histogram into the query's
+        uint32_t* srow = a.scores + bq * a.sstride + s0;
+        for (int i = 4 * tid; i < ns; i += 4 * IDX_NT) {
+            if (i + 4 <= ns) {
+                *(u32x4*)(srow + i) = *(const u32x4*)(keys + i);
+            } else {
+                for (int x = i; x < ns; ++x) srow[x] = keys[x];
+            }
+        }
+        // bins 4t .. 4t+3 per thread; the nonzero ones compacted into the list
+        const u32x4 hv = *(const u32x4*)(hs + 4 * tid);
+        const int nz = (hv[0] != 0) + (hv[1] != 0) + (hv[2] != 0) + (hv[3] != 0);
+        int tot;
+        int o = 1 + block_excl_scan<IDX_NT>(nz, (int*)(hs + TOPK_BINS), tot);
+        uint32_t* slot = a.hist + (bq * a.nslices + sl) * (int64_t)SLOT_W;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (hv[x]) slot[o++] = ((uint32_t)(4 * tid + x) << 21) | hv[x];
+        if (tid == 0) slot[0] = (uint32_t)tot;
+        return;
+    }
 
     uint32_t kv[TOPK_EMAX];
 #pragma unroll
@@ -432,130 +472,16 @@ k_idx_score(IndexArgs a) {
         const int i = tid * E + x;
         kv[x] = (x < E && i < ns) ? keys[i + (i >> le)] : 0u;
     }
-    const int want = ns < a.kk ? ns : a.kk;
-    if (a.nslices == 1) {
-        int32_t* oi = a.out_idx + bq * a.k;
-        float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-        block_topk<IDX_NT>(kv, E, ns, want, sh, [&](int pos, int i, uint32_t u) {
-            oi[pos] = (int32_t)(s0 + i);
-            if (os) os[pos] = key_score(u);
-        });
-        const int cnt = ns < a.k ? ns : a.k;
-        for (int p = cnt + tid; p < a.k; p += IDX_NT) {
-            oi[p] = -1;
-            if (os) os[p] = -INFINITY;
-        }
-    } else {
-        uint32_t* ck = a.cand_key + bq * (int64_t)a.cst + (int64_t)sl * a.kk;
-        int32_t* ci = a.cand_idx + bq * (int64_t)a.cst + (int64_t)sl * a.kk;
-        // rank r = ceil(k / non-empty slices): every slice's top-r together hold >= k keys
-        const int nse = (int)((n + a.S - 1) / a.S);
-        const int rr = nse > 0 ? (a.k + nse - 1) / nse : 0;
-        block_topk<IDX_NT>(kv, E, ns, want, sh, [&](int pos, int i, uint32_t u) {
-            ck[pos] = u;
-            ci[pos] = (int32_t)(s0 + i);
-        }, ns > 0 ? (rr < ns ? rr : ns) : 0, a.tbound + bq * a.nslices + sl);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Merge of per-slice candidates (one block per query)
-// ---------------------------------------------------------------------------
-constexpr int MRG_NT = 1024;
-constexpr int MRG_MAXC = 32768;
-
-constexpr int MRG_SURV = 8192;   // survivors of the bound filter handled in LDS
-
-__global__ void __launch_bounds__(MRG_NT) k_idx_merge(IndexArgs a) {
-    extern __shared__ uint32_t smem[];
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int64_t bq = (int64_t)b * a.Tq + j;
-    const int tid = threadIdx.x;
-    const int64_t t = a.q_pos[bq];
-    const int64_t n = n_visible(t, a.m, a.n_cap);
-    // Every slice before the last non-empty one is full (n >= its end), so it kept
-    // exactly kk candidates: the candidates of a query form one contiguous array,
-    // element i belonging to slice i / kk, already in ascending entry order.
-    const int64_t nfull = n / a.S;
-    const int64_t rem = n - nfull * a.S;
-    const int total = (int)(nfull * a.kk + (rem < a.kk ? rem : a.kk));
-    const int nse = (int)(nfull + (rem > 0));
-    // Lower bound L of the k-th largest key: slice s reported t_s with at least r_s
-    // of its keys >= t_s (r_s = min(its size, ceil(k / nse))).  If the r_s add up to
-    // k, at least k keys are >= min_s t_s, so no key below it can be selected.
-    bool use_bound = false;
-    if (nse > 0) {
-        const int r = (a.k + nse - 1) / nse;
-        const int64_t sum_r = nfull * (r < a.S ? r : a.S) + (rem > 0 ? (rem < r ? rem : r) : 0);
-        use_bound = sum_r >= a.k;
-    }
-    uint32_t* sh = smem;                                   // TOPK_SCRATCH(MRG_NT)
-    int* win = (int*)(smem + TOPK_SCRATCH(MRG_NT));        // winners' element numbers, k <= 2048
-    uint32_t* wkey = (uint32_t*)(win + 2048);
-    uint32_t* sk = wkey + 2048;                            // survivors: keys
-    int* si = (int*)(sk + MRG_SURV);                       //            element numbers
-    const uint32_t* src = a.cand_key + bq * (int64_t)a.cst;
-    const int32_t* isrc = a.cand_idx + bq * (int64_t)a.cst;
-    // thread t owns elements [t*E, t*E + E): 16-byte loads, all issued unconditionally
-    const int E = a.cst / MRG_NT;                          // multiple of 4, <= TOPK_EMAX
-    uint32_t kv[TOPK_EMAX];
-    const u32x4* src4 = (const u32x4*)(src + (int64_t)tid * E);
-#pragma unroll
-    for (int q = 0; q < TOPK_EMAX / 4; ++q) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (4 * q < E) v = src4[q];
-        kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
-    }
-    // L = min_s t_s: wave 0 reads the (at most 64) slice bounds in parallel while the
-    // candidate loads are in flight
-    uint32_t* lsh = sh + 2 * TOPK_HSZ + 12;
-    if (tid < 64) {
-        const uint32_t ts = wave_min_u32((use_bound && tid < nse) ? a.tbound[bq * a.nslices + tid] : 0xffffffffu);
-        if (tid == 0) *lsh = use_bound ? ts : 0u;
-    }
-    __syncthreads();
-    const uint32_t L = *lsh;
-    // keep the keys >= L, compacted in element order
-    int mine = 0;
-#pragma unroll
-    for (int x = 0; x < TOPK_EMAX; ++x) mine += (x < E && tid * E + x < total && kv[x] >= L) ? 1 : 0;
-    int nsurv;
-    int off = block_excl_scan<MRG_NT>(mine, (int*)(sh + 2 * TOPK_HSZ + 16), nsurv);
-    const int want = total < a.k ? total : a.k;
-    if (nsurv <= MRG_SURV) {
-#pragma unroll
-        for (int x = 0; x < TOPK_EMAX; ++x) {
-            if (x < E && tid * E + x < total && kv[x] >= L) { sk[off] = kv[x]; si[off] = tid * E + x; ++off; }
-        }
-        __syncthreads();
-        constexpr int E2MAX = MRG_SURV / MRG_NT;
-        const int E2 = (nsurv + MRG_NT - 1) / MRG_NT;
-        uint32_t kv2[E2MAX];
-#pragma unroll
-        for (int x = 0; x < E2MAX; ++x) kv2[x] = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] : 0u;
-        block_topk<MRG_NT>(kv2, E2, nsurv, want, sh, [&](int pos, int i, uint32_t u) {
-            win[pos] = si[i];
-            wkey[pos] = u;
-        });
-    } else {
-        __syncthreads();                                   // the scan's sums are read before reuse
-        block_topk<MRG_NT>(kv, E, total, want, sh, [&](int pos, int i, uint32_t u) {
-            win[pos] = i;
-            wkey[pos] = u;
-        });
-    }
-    __syncthreads();
-    // the winners' entry indices and scores, gathered by all threads at once
+    const int want = ns < a.k ? ns : a.k;
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-    for (int p = tid; p < a.k; p += MRG_NT) {
-        if (p < want) {
-            oi[p] = isrc[win[p]];
-            if (os) os[p] = key_score(wkey[p]);
-        } else {
-            oi[p] = -1;
-            if (os) os[p] = -INFINITY;
-        }
+    block_topk<IDX_NT>(kv, E, ns, want, sh, [&](int pos, int i, uint32_t u) {
+        oi[pos] = (int32_t)(s0 + i);
+        if (os) os[pos] = key_score(u);
+    });
+    for (int p = want + tid; p < a.k; p += IDX_NT) {
+        oi[p] = -1;
+        if (os) os[p] = -INFINITY;
     }
 }
 
@@ -713,46 +639,44 @@ __device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint
     const int incl = wave_incl_scan((int)loc);
     const int tot = __shfl(incl, 63, 64);
     uint32_t c = (uint32_t)(tot - incl);
+    int fb = -1;                                         // bin within the lane's 32 (a select, not 32 live constants)
+    uint32_t fa = 0, fc = 0;
 #pragma unroll
     for (int q = 7; q >= 0; --q) {
         const u32x4 v4 = h4[q];
 #pragma unroll
         for (int e = 3; e >= 0; --e) {
             const uint32_t cge = c + v4[e];
-            if (cge >= need && c < need) { misc[0] = 32 * lane + 4 * q + e; misc[1] = c; misc[2] = v4[e]; }
+            if (cge >= need && c < need) { fb = 4 * q + e; fa = c; fc = v4[e]; }
             c = cge;
         }
     }
+    if (fb >= 0) { misc[0] = 32 * lane + fb; misc[1] = fa; misc[2] = fc; }
 }
 
-__global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
-    extern __shared__ uint32_t smem[];
-    const int jl = blockIdx.x, b = blockIdx.y;
+// Select over one query's score row (1024 threads).  On entry sh[0 .. TOPK_HSZ)
+// holds the row's padded histogram of the keys' top 11 bits, visible to every
+// thread.  LDS layout from smem: TOPK_SCRATCH(DSEL_NT) (histograms, misc, scans) |
+// survivor keys [DSEL_CAP] | their entry indices [DSEL_CAP] | winners [2048] |
+// winner keys [2048].
+// The threshold is refined 11 + 11 + 10 key bits at a time (one pass over the row per
+// extra level) until the keys at or above it fit in DSEL_CAP.  If the first level
+// fits and gather(sk, si) returns the survivor count (>= 0), the survivors come from
+// there (the split path filtered them already); otherwise one pass over the row
+// collects them.  Then an exact radix select among the survivors, in entry order.
+template <typename Gather>
+__device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64_t n, const uint32_t* srow,
+                                           uint32_t* smem, Gather gather) {
     const int tid = threadIdx.x, wv = tid >> 6;
-    const int jq = a.qc0 + jl;
-    const int64_t bq = (int64_t)b * a.Tq + jq;
-    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-    const uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
-    if (n <= a.k) {                                      // every visible entry, then padding
-        for (int p = tid; p < a.k; p += DSEL_NT) {
-            oi[p] = p < n ? p : -1;
-            if (os) os[p] = p < n ? key_score(srow[p]) : -INFINITY;
-        }
-        return;
-    }
-    uint32_t* sh = smem;                                 // TOPK_SCRATCH(DSEL_NT): histograms, misc, scans
+    uint32_t* sh = smem;
     uint32_t* misc = sh + 2 * TOPK_HSZ;
     int* wsum = (int*)(sh + 2 * TOPK_HSZ + 16);
-    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);           // survivors: keys, then entry indices
+    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);
     int* si = (int*)(sk + DSEL_CAP);
-    int* win = si + DSEL_CAP;                            // winners (k <= 2048)
+    int* win = si + DSEL_CAP;
     uint32_t* wkey = (uint32_t*)(win + 2048);
-    // ---- threshold: refine 11 + 11 + 10 key bits until the keys at or above it fit
-    const uint32_t* gh = a.hist + ((int64_t)b * a.Tc + jl) * TOPK_BINS;
-    for (int x = tid; x < TOPK_BINS; x += DSEL_NT) sh[hpad(x)] = gh[x];
-    __syncthreads();
     uint32_t prefix = 0, pmask = 0;
     int need = a.k;
     int shift = 21;
@@ -783,9 +707,12 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
     // keys kept: (u & pmask) > prefix, or == prefix (the bin) -- in the exact case only
     // the first `need` keys equal to the threshold (smaller indices win ties)
     const uint32_t lo = prefix;                          // bin lower edge (bits below the digit are 0)
-    int nsurv = 0, eq_seen = 0;
+    int nsurv = shift == 21 ? gather(sk, si) : -1;
+    const bool gathered = nsurv >= 0;
+    if (!gathered) nsurv = 0;
+    int eq_seen = 0;
     constexpr int CH = 16;
-    for (int64_t base = 0; base < n; base += (int64_t)DSEL_NT * CH) {
+    for (int64_t base = 0; base < n && !gathered; base += (int64_t)DSEL_NT * CH) {
         uint32_t kv[CH];
         const int64_t s0 = base + (int64_t)tid * CH;
 #pragma unroll
@@ -829,16 +756,24 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
         __syncthreads();                                 // wsum reuse
     }
     nsurv = nsurv < DSEL_CAP ? nsurv : DSEL_CAP;
-    // ---- exact top-k among the survivors (in entry order), then the output
+    // ---- exact top-k among the survivors (in entry order), then the output.  The
+    // fewer than k survivors above the threshold bin [lo, lo + 2^shift) are all kept:
+    // clamped to the bin's upper edge they tie above every in-bin key, so the radix
+    // select only resolves the bits below the bin's digits.
     constexpr int E2MAX = DSEL_CAP / DSEL_NT;
     const int E2 = (nsurv + DSEL_NT - 1) / DSEL_NT;
+    const uint64_t cap64 = (uint64_t)lo + ((uint64_t)1 << shift);
+    const uint32_t cap = cap64 > 0xffffffffull ? 0xffffffffu : (uint32_t)cap64;
     uint32_t kv2[E2MAX];
 #pragma unroll
-    for (int x = 0; x < E2MAX; ++x) kv2[x] = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] : 0u;
+    for (int x = 0; x < E2MAX; ++x) {
+        const uint32_t u = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] : 0u;
+        kv2[x] = u < cap ? u : cap;
+    }
     __syncthreads();
-    block_topk<DSEL_NT>(kv2, E2, nsurv, a.k, sh, [&](int pos, int i, uint32_t u) {
+    block_topk<DSEL_NT>(kv2, E2, nsurv, a.k, sh, [&](int pos, int i, uint32_t) {
         win[pos] = si[i];
-        wkey[pos] = u;
+        wkey[pos] = sk[i];
     });
     __syncthreads();
     for (int p = tid; p < a.k; p += DSEL_NT) {
@@ -847,29 +782,202 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
     }
 }
 
+// Every visible entry (n <= k), then padding.
+__device__ __forceinline__ void take_all(const IndexArgs& a, int64_t bq, int64_t n, const uint32_t* srow, int tid, int nt) {
+    int32_t* oi = a.out_idx + bq * a.k;
+    float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
+    for (int p = tid; p < a.k; p += nt) {
+        oi[p] = p < n ? p : -1;
+        if (os) os[p] = p < n ? key_score(srow[p]) : -INFINITY;
+    }
+}
+
+// Dense path: one block per query of the pass; the histogram comes from the score kernel.
+__global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    const int jl = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t bq = (int64_t)b * a.Tq + a.qc0 + jl;
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    const uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
+    if (n <= a.k) {
+        take_all(a, bq, n, srow, tid, DSEL_NT);
+        return;
+    }
+    const uint32_t* gh = a.hist + ((int64_t)b * a.Tc + jl) * TOPK_BINS;
+    for (int x = tid; x < TOPK_BINS; x += DSEL_NT) smem[hpad(x)] = gh[x];
+    __syncthreads();
+    select_row(a, bq, n, srow, smem, [](uint32_t*, int*) { return -1; });
+}
+
+// Split path, step 2: blocks of `spb` consecutive slices (FS = spb * S keys) per
+// query.  Each block sums the query's slice histograms (the score kernel's
+// (bin << 21 | count) lists) into LDS and finds the threshold bin, the one holding
+// the k-th largest key; block 0 stores the summed histogram for the select.  If the
+// keys in that bin or above fit in DSEL_CAP, the block copies its range's such keys,
+// with their entry indices and in entry order, to its segment [f*FS, ..) of the
+// candidate rows, and their count to seg_cnt; otherwise the select refines the
+// threshold over the score row.
+constexpr int FLT_NT = 1024;
+constexpr int FLT_CH = 16;        // keys per thread per chunk
+
+__global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t sh[TOPK_HSZ];
+    __shared__ uint32_t misc[4];
+    __shared__ int wsum[FLT_NT / 64 + 8];
+    __shared__ int soff[MAX_SLICES_PER_ROW];
+    const int fb = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wv = tid >> 6;
+    const int64_t bq = (int64_t)b * a.Tq + j;
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    if (n <= a.k) return;                                // the select takes every entry
+    const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
+    const int nfb = (nseg + a.spb - 1) / a.spb;          // filter blocks with keys
+    if (fb >= nfb) return;
+    const uint32_t* srow = a.scores + bq * a.sstride;
+    const int64_t FS = (int64_t)a.spb * a.S;
+    const int64_t f0 = (int64_t)fb * FS;
+    const int nf = (int)(n - f0 < FS ? n - f0 : FS);     // keys of this block
+    auto load_chunk = [&](int c0, uint32_t (&kv)[FLT_CH]) {
+#pragma unroll
+        for (int q = 0; q < FLT_CH / 4; ++q) {
+            int64_t sq = f0 + c0 + tid * FLT_CH + 4 * q;
+            sq = sq < n ? sq : ((n - 1) & ~(int64_t)3);  // clamped inside the (4-padded) row
+            const u32x4 v = *(const u32x4*)(srow + sq);
+            kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
+        }
+    };
+    uint32_t kv[FLT_CH];
+    load_chunk(0, kv);                                   // in flight while the histogram is summed
+    // ---- the slices' lists, flattened over the block
+    const uint32_t* slots = a.hist + bq * (int64_t)a.nslices * SLOT_W;
+    const int c = tid < nseg ? (int)slots[(int64_t)tid * SLOT_W] : 0;
+    for (int x = tid; x < TOPK_HSZ; x += FLT_NT) sh[x] = 0u;
+    int npairs;
+    const int off = block_excl_scan<FLT_NT>(c, wsum, npairs);
+    if (tid < nseg) soff[tid] = off;
+    __syncthreads();
+    for (int p = tid; p < npairs; p += FLT_NT) {
+        int l = 0, h = nseg - 1;                         // last slice whose list starts at or before p
+        while (l < h) {
+            const int mid = (l + h + 1) >> 1;
+            if (soff[mid] <= p) l = mid; else h = mid - 1;
+        }
+        const uint32_t pr = slots[(int64_t)l * SLOT_W + 1 + (p - soff[l])];
+        atomicAdd(&sh[hpad(pr >> 21)], pr & 0x1fffffu);
+    }
+    __syncthreads();
+    if (fb == 0) {
+        uint32_t* gh = a.row_hist + bq * TOPK_BINS;
+        for (int x = tid; x < TOPK_BINS; x += FLT_NT) gh[x] = sh[hpad(x)];
+    }
+    if (wv == 0) find_bin(sh, (uint32_t)a.k, misc);
+    __syncthreads();
+    if (misc[1] + misc[2] > (uint32_t)DSEL_CAP) return;
+    // ---- keys in the threshold bin or above, in entry order
+    const uint32_t lo = misc[0] << (32 - TOPK_BITS);
+    uint32_t* ck = a.cand_key + bq * a.sstride + f0;
+    int32_t* ci = a.cand_idx + bq * a.sstride + f0;
+    int cnt = 0;
+    for (int c0 = 0; c0 < nf; c0 += FLT_NT * FLT_CH) {
+        if (c0 > 0) load_chunk(c0, kv);
+        const int e0 = c0 + tid * FLT_CH;                // block offset of kv[0]
+        int my = 0;
+#pragma unroll
+        for (int x = 0; x < FLT_CH; ++x) my += (e0 + x < nf && kv[x] >= lo) ? 1 : 0;
+        int tot;
+        int pos = cnt + block_excl_scan<FLT_NT>(my, wsum, tot);
+#pragma unroll
+        for (int x = 0; x < FLT_CH; ++x) {
+            if (e0 + x < nf && kv[x] >= lo) { ck[pos] = kv[x]; ci[pos] = (int32_t)(f0 + e0 + x); ++pos; }
+        }
+        cnt += tot;
+        __syncthreads();                                 // wsum reuse
+    }
+    if (tid == 0) a.seg_cnt[bq * a.nslices + fb] = cnt;
+}
+
+// Split path, step 3: one block per query.
+__global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t bq = (int64_t)b * a.Tq + j;
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    const uint32_t* srow = a.scores + bq * a.sstride;
+    if (n <= a.k) {
+        take_all(a, bq, n, srow, tid, DSEL_NT);
+        return;
+    }
+    const uint32_t* gh = a.row_hist + bq * TOPK_BINS;
+    for (int x = tid; x < TOPK_BINS; x += DSEL_NT) smem[hpad(x)] = gh[x];
+    __syncthreads();
+    const int nfb = (int)(((n + a.S - 1) / a.S + a.spb - 1) / a.spb);
+    const int64_t FS = (int64_t)a.spb * a.S;
+    int* wsum = (int*)(smem + 2 * TOPK_HSZ + 16);
+    select_row(a, bq, n, srow, smem, [&](uint32_t* sk, int* si) {
+        // the filter blocks' segments in block order = entry order
+        int* foff = (int*)(sk + 2 * DSEL_CAP);           // the winner area, free until the final select
+        const int cc = tid < nfb ? a.seg_cnt[bq * a.nslices + tid] : 0;
+        int tot;
+        const int o = block_excl_scan<DSEL_NT>(cc, wsum, tot);
+        tot = tot < DSEL_CAP ? tot : DSEL_CAP;           // equal to the keys in and above the bin
+        if (tid < nfb) foff[tid] = o;
+        __syncthreads();
+        const uint32_t* ck = a.cand_key + bq * a.sstride;
+        const int32_t* ci = a.cand_idx + bq * a.sstride;
+        for (int p = tid; p < tot; p += DSEL_NT) {
+            int l = 0, h = nfb - 1;                      // last block whose segment starts at or before p
+            while (l < h) {
+                const int mid = (l + h + 1) >> 1;
+                if (foff[mid] <= p) l = mid; else h = mid - 1;
+            }
+            const int64_t src = (int64_t)l * FS + (p - foff[l]);
+            sk[p] = ck[src];
+            si[p] = ci[src];
+        }
+        __syncthreads();
+        return tot;
+    });
+}
+
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
-template <int FMT, int DI, int HB>
-static hipError_t launch_score(const IndexArgs& a, hipStream_t s) {
+template <int FMT, int DI, int HB, bool SPLIT>
+static void launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
-    const size_t lds = sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT));   // keys + scratch
+    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_BINS + 16)              // keys, histogram, scan
+                             : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT));   // keys + scratch
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
-    hipLaunchKernelGGL((k_idx_score<FMT, DI, HB>), grid, dim3(IDX_NT), lds, s, a);
-    return hipGetLastError();
+    hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
 }
 
-template <int FMT, int DI>
-static hipError_t launch_hb(const IndexArgs& a, hipStream_t s) {
+template <int FMT, int DI, bool SPLIT>
+static void launch_hb(const IndexArgs& a, hipStream_t s) {
     const int hb = (a.H_I + 15) / 16;
-    if (hb <= 1) return launch_score<FMT, DI, 1>(a, s);
-    if (hb <= 4) return launch_score<FMT, DI, 4>(a, s);
-    return launch_score<FMT, DI, 8>(a, s);
+    if (hb <= 1) launch_score<FMT, DI, 1, SPLIT>(a, s);
+    else if (hb <= 4) launch_score<FMT, DI, 4, SPLIT>(a, s);
+    else launch_score<FMT, DI, 8, SPLIT>(a, s);
 }
+
+template <bool SPLIT>
+static void launch_fmt(const IndexArgs& a, hipStream_t s) {
+    if (a.ki_fmt == MXFP4) launch_hb<MXFP4, 128, SPLIT>(a, s);
+    else if (a.ki_fmt == BF16) {
+        if (a.d_I == 32) launch_hb<BF16, 32, SPLIT>(a, s);
+        else if (a.d_I == 64) launch_hb<BF16, 64, SPLIT>(a, s);
+        else launch_hb<BF16, 128, SPLIT>(a, s);
+    } else {
+        if (a.d_I == 32) launch_hb<F32, 32, SPLIT>(a, s);
+        else launch_hb<F32, 128, SPLIT>(a, s);
+    }
+}
+
+static constexpr size_t sel_lds() { return sizeof(uint32_t) * ((size_t)TOPK_SCRATCH(DSEL_NT) + 2 * DSEL_CAP + 2 * 2048); }
 
 static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
     const int hb = (a.H_I + 15) / 16;
-    const size_t sel_lds = sizeof(uint32_t) * ((size_t)TOPK_SCRATCH(DSEL_NT) + 2 * DSEL_CAP + 2 * 2048);
     for (int q0 = 0; q0 < a.Tq; q0 += a.Tc) {
         a.qc0 = q0;
         const int tc = a.Tq - q0 < a.Tc ? a.Tq - q0 : a.Tc;
@@ -882,7 +990,7 @@ static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
         else if (hb <= 2) hipLaunchKernelGGL(k_idx_dense_score<2>, grid, dim3(DNS_NT), 0, s, a);
         else if (hb <= 4) hipLaunchKernelGGL(k_idx_dense_score<4>, grid, dim3(DNS_NT), 0, s, a);
         else hipLaunchKernelGGL(k_idx_dense_score<8>, grid, dim3(DNS_NT), 0, s, a);
-        hipLaunchKernelGGL(k_idx_dense_select, dim3((unsigned)tc, (unsigned)a.B), dim3(DSEL_NT), sel_lds, s, a);
+        hipLaunchKernelGGL(k_idx_dense_select, dim3((unsigned)tc, (unsigned)a.B), dim3(DSEL_NT), sel_lds(), s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -892,19 +1000,15 @@ static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
     if (a.B <= 0 || a.Tq <= 0) return hipSuccess;
     if (a.dense) return launch_dense(a, s);
-    hipError_t e;
-    if (a.ki_fmt == MXFP4) e = launch_hb<MXFP4, 128>(a, s);
-    else if (a.ki_fmt == BF16) {
-        if (a.d_I == 32) e = launch_hb<BF16, 32>(a, s);
-        else if (a.d_I == 64) e = launch_hb<BF16, 64>(a, s);
-        else e = launch_hb<BF16, 128>(a, s);
-    } else {
-        if (a.d_I == 32) e = launch_hb<F32, 32>(a, s);
-        else e = launch_hb<F32, 128>(a, s);
+    if (a.nslices == 1) {
+        launch_fmt<false>(a, s);
+        return hipGetLastError();
     }
-    if (e != hipSuccess || a.nslices == 1) return e;
-    const size_t lds = sizeof(uint32_t) * ((size_t)TOPK_SCRATCH(MRG_NT) + 2 * 2048 + 2 * MRG_SURV);
-    hipLaunchKernelGGL(k_idx_merge, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(MRG_NT), lds, s, a);
+    // split: score rows + slice histograms, filter, select
+    launch_fmt<true>(a, s);
+    const int nfb = (a.nslices + a.spb - 1) / a.spb;
+    hipLaunchKernelGGL(k_idx_split_filter, dim3((unsigned)nfb, (unsigned)a.Tq, (unsigned)a.B), dim3(FLT_NT), 0, s, a);
+    hipLaunchKernelGGL(k_idx_split_select, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(DSEL_NT), sel_lds(), s, a);
     return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 
 namespace csl {
 
+constexpr int IDX_SLOT_W = 2048 + 8;   // words per slice histogram list: count, then <= 2048 entries
+
 struct CompressArgs {
     const uint8_t* x; int x_fmt; int64_t x_bstride; int64_t x_pos0; int64_t n_tok;
     const float* z; int z_ch; int64_t z_bstride;
@@ -21,20 +23,22 @@ struct IndexArgs {
     int B, Tq, H_I, d_I, m; int64_t n_cap; int k;
     int32_t* out_idx; float* out_score;
     // plan
-    int S;          // keys per slice (power of two, 256..16384)
-    int nslices;    // slices per query
-    int kk;         // candidates kept per slice = min(k, S)
-    int cst;        // per-query stride of the candidate arrays (multiple of 4096, >= nslices*kk)
-    uint32_t* cand_key;  // [B*Tq][cst]: slice s's candidates at [s*kk, s*kk + count)
-    int32_t* cand_idx;   // [B*Tq][cst]
-    uint32_t* tbound;    // [B*Tq][nslices]: per-slice lower bound of the top-r keys (see k_idx_merge)
+    int S;          // keys per slice (power of two in [512, 16384])
+    int nslices;    // slices per query (<= 1024)
+    int spb;        // split path: slices per filter block
+    // rows of the split (nslices > 1) and dense paths, in the workspace
+    int64_t sstride;     // row stride (n_cap rounded up to a multiple of 4)
+    uint32_t* scores;    // order-preserving score keys: split [B*Tq][sstride], dense [B][Tc][sstride]
+    uint32_t* hist;      // dense: [B][Tc][2048] histograms of the keys' top 11 bits;
+                         // split: [B*Tq][nslices][IDX_SLOT_W] per-slice lists of nonzero bins
+    uint32_t* cand_key;  // split: [B*Tq][sstride], filter block f's kept keys at [f*spb*S, ..)
+    int32_t* cand_idx;   // split: [B*Tq][sstride], their entry indices
+    int32_t* seg_cnt;    // split: [B*Tq][nslices] keys kept per filter block
+    uint32_t* row_hist;  // split: [B*Tq][2048] the summed histogram of each row
     // dense path (many queries): queries qc0 .. qc0+Tc-1 per pass
     int dense;           // 1: score every (query, key) pair to HBM, then select per query
-    int Tc;              // queries per pass
+    int Tc;              // rows per pass
     int qc0;             // first query of the pass (set by the launcher)
-    int64_t sstride;     // score row stride (n_cap rounded up to a multiple of 4)
-    uint32_t* scores;    // [B][Tc][sstride] order-preserving score keys
-    uint32_t* hist;      // [B][Tc][2048] histogram of the keys' top 11 bits
 };
 
 struct AttendArgs {

@@ -118,9 +118,11 @@ int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int
  *             ki_scales + b*ks_bstride + s*(d_I/32) for CSL_MXFP4.
  *  Formats: qi_fmt == ki_fmt, one of CSL_F32 (d_I 32 or 128), CSL_BF16 (d_I 32, 64
  *  or 128), CSL_MXFP4 (d_I 128; scales applied by the scaled FP4 MFMA).
- *  Limits: H_I <= 128, 1 <= k <= 2048, n_cap*k small enough that the candidate
- *  merge holds <= 32768 candidates per query (n_cap <= 262144 at k = 1024).
- *  ws         device workspace of at least csl_index_topk_workspace(...) bytes.
+ *  Limits: H_I <= 128, 1 <= k <= 2048, n_cap <= 2^24 (CSL_EUNSUPPORTED beyond).
+ *  ws         device workspace of at least csl_index_topk_workspace(...) bytes
+ *             (0 for small calls; a little over 12 * B * Tq * n_cap bytes when a query's
+ *             entries span several scoring blocks: score rows and filtered
+ *             candidates are staged there).
  */
 int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
                const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,

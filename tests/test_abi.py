@@ -97,7 +97,7 @@ def test_index_rejects_bad_arguments_on_the_host():
     assert call(qi_fmt=1) == _lib.CSL_EUNSUPPORTED                  # formats must match
     assert call(H_I=200) == _lib.CSL_EUNSUPPORTED
     assert call(qi_scales=None) == _lib.CSL_EINVAL
-    assert call(n_cap=10 ** 7) == _lib.CSL_EUNSUPPORTED             # beyond the candidate merge
+    assert call(n_cap=(1 << 24) + 1) == _lib.CSL_EUNSUPPORTED       # beyond 1024 slices of 16384
     assert call(Tq=0) == _lib.CSL_OK
 
 

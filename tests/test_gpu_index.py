@@ -37,7 +37,7 @@ def _inputs(fmt, B, Tq, H_I, d_I, N, seed):
 CASES = [
     # (fmt, B, Tq, H_I, d_I, N, m, k, positions)
     ("cfg1", O.F32, 1, 64, 4, 32, 512, 4, 64, "last"),        # config 1 indexer: single slice
-    ("bf16_multi", O.BF16, 2, 3, 16, 128, 4096, 4, 512, "last"),  # config-2-like, merge path
+    ("bf16_multi", O.BF16, 2, 3, 16, 128, 4096, 4, 512, "last"),  # config-2-like, split path
     ("bf16_ragged", O.BF16, 3, 4, 16, 64, 3000, 4, 256, "ragged"),
     ("fp4_multi", O.MXFP4, 2, 2, 64, 128, 20000, 4, 1024, "last"),
     ("fp4_short", O.MXFP4, 2, 3, 64, 128, 5000, 4, 1024, "ragged"),  # n(t) < k: padding
@@ -84,7 +84,8 @@ def test_index_topk_parity(gpu, case):
 @pytest.mark.parametrize("N,k", [(3000, 100), (30000, 1024)])
 def test_index_topk_ties_take_the_smallest_indices(gpu, N, k):
     # every key identical -> every score ties -> the first k indices win (the larger
-    # case leaves more tied candidates than the merge's bounded survivor buffer)
+    # case leaves more tied candidates than the split path's filter keeps in LDS, so
+    # the row select refines the threshold down to the last key bit)
     B, Tq, H_I, d_I = 1, 2, 16, 128
     q = gen.normal((B, Tq, H_I, d_I), 1)
     key = gen.normal((1, 1, d_I), 2).expand(B, N, d_I).contiguous()
@@ -95,6 +96,30 @@ def test_index_topk_ties_take_the_smallest_indices(gpu, N, k):
     torch.cuda.synchronize()
     assert np.array_equal(host(gi)[0, 0], np.arange(k))
     assert np.array_equal(host(gi)[0, 1], np.arange(k))
+
+
+def test_index_topk_clustered_scores_refine_the_threshold(gpu):
+    # keys = one shared key + 1% noise: nearly every score lands in the same top-11-bit
+    # bin, more candidates than the split path's filter keeps in LDS, so the row select
+    # refines the threshold with the next digits
+    B, Tq, H_I, d_I, N, k = 1, 2, 16, 128, 40000, 1024
+    base = gen.normal((1, 1, d_I), 21)
+    keys = base.expand(B, N, d_I) + 0.01 * gen.normal((B, N, d_I), 22)
+    q = gen.normal((B, Tq, H_I, d_I), 23)
+    w = torch.ones((B, Tq, H_I))
+    qpos = gen.positions(B, Tq, 4 * N - 1)
+    qs_, ks_ = gen.store(q, O.BF16), gen.store(keys, O.BF16)
+    kw = dict(H_I=H_I, d_I=d_I, m=4, n_cap=N)
+    gi, _ = ops.index_topk(dev(qs_), dev(w), dev(ks_), dev(qpos), fmt=O.BF16, k=k, **kw)
+    torch.cuda.synchronize()
+    oi, _ = O.index_topk(host(qs_), O.BF16, host(w), host(ks_), O.BF16, host(qpos), k=k, **kw)
+    allsc = oracle_all_scores(host(qs_), O.BF16, host(w), host(ks_), O.BF16, host(qpos), **kw)
+    qd = BF.decode(host(qs_), O.BF16, d_I).reshape(B, Tq, H_I, d_I)
+    kd = BF.decode(host(ks_), O.BF16, d_I).reshape(B, N, d_I)
+    bound = np.stack([score_error_bound(qd[0], host(w)[0].astype(np.float64), kd[0])])
+    s = np.sort(allsc[0, 0][np.isfinite(allsc[0, 0])])[::-1]
+    assert s[-1] > 0.95 * s[0]                                # one narrow band of scores
+    check_topk(host(gi), oi, allsc, k, abs_bound=bound)
 
 
 def test_index_topk_is_deterministic(gpu):
