@@ -243,6 +243,36 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
     }
 }
 
+// Wave 0 locates, in a padded 2048-bin histogram, the bin b where the count of keys in
+// higher bins is < need <= that count + hist[b]: misc[0] = b, misc[1] = count above,
+// misc[2] = hist[b].  Caller: wave 0 only, need >= 1 and <= total.
+__device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint32_t* misc) {
+    const int lane = threadIdx.x & 63;
+    const u32x4* h4 = (const u32x4*)(hp + 36 * lane);
+    uint32_t loc = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const u32x4 v4 = h4[q];
+        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
+    }
+    const int incl = wave_incl_scan((int)loc);
+    const int tot = __shfl(incl, 63, 64);
+    uint32_t c = (uint32_t)(tot - incl);
+    int fb = -1;                                         // bin within the lane's 32 (a select, not 32 live constants)
+    uint32_t fa = 0, fc = 0;
+#pragma unroll
+    for (int q = 7; q >= 0; --q) {
+        const u32x4 v4 = h4[q];
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+            const uint32_t cge = c + v4[e];
+            if (cge >= need && c < need) { fb = 4 * q + e; fa = c; fc = v4[e]; }
+            c = cge;
+        }
+    }
+    if (fb >= 0) { misc[0] = 32 * lane + fb; misc[1] = fa; misc[2] = fc; }
+}
+
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t n_cap) {
     if (t < 0) return 0;
     const int64_t n = (t + 1) / m;
@@ -253,7 +283,7 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t n_cap) {
 // Scoring + per-slice selection
 // ---------------------------------------------------------------------------
 constexpr int IDX_NT = 512;   // 8 waves: enough loads in flight per CU to stream HBM
-constexpr int IDX_UNR = 4;   // 16-key tiles in flight per wave
+constexpr int IDX_UNR = 4;   // 16-key tiles in flight per wave (one per lane group in the epilogue)
 
 template <int FMT, int DI>
 struct KeyFrag;
@@ -336,6 +366,7 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
 // k_idx_split_filter and k_idx_split_select finish the query.
 constexpr int SLOT_W = IDX_SLOT_W;
 constexpr int MAX_SLICES_PER_ROW = 1024;
+constexpr int ROWH_W = IDX_ROWH_W;
 static_assert(SLOT_W >= TOPK_BINS + 1 && 4 * IDX_NT == TOPK_BINS, "slice lists: 4 bins per scoring thread");
 template <int FMT, int DI, int HB, bool SPLIT>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
@@ -348,7 +379,7 @@ k_idx_score(IndexArgs a) {
     const int le = 31 - __builtin_clz(E);
     uint32_t* keys = smem;
     uint32_t* sh = smem + a.S + (a.S >> le);
-    uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the histogram
+    uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the padded histogram
 
     const int64_t t = a.q_pos[bq];
     const int64_t n = n_visible(t, a.m, a.n_cap);
@@ -356,7 +387,7 @@ k_idx_score(IndexArgs a) {
     const int ns = (int)(n - s0 < 0 ? 0 : (n - s0 > a.S ? a.S : n - s0));
     if constexpr (SPLIT) {
         if (ns <= 0) return;
-        for (int x = tid; x < TOPK_BINS; x += IDX_NT) hs[x] = 0u;
+        for (int x = tid; x < TOPK_HSZ; x += IDX_NT) hs[x] = 0u;
         __syncthreads();
     }
 
@@ -396,7 +427,8 @@ k_idx_score(IndexArgs a) {
             const int64_t row = s0 + li;
             f.load(kbase + row * rb, sbase ? sbase + row * (DI / 32) : nullptr, g);
         };
-        auto score_tile = [&](int T, const KeyFrag<FMT, DI>& f) {
+        // per lane: the 16 heads of its row group for its key, ReLU-gated and weighted
+        auto head_sum = [&](const KeyFrag<FMT, DI>& f) {
             float part = 0.f;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
@@ -405,17 +437,7 @@ k_idx_score(IndexArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(c[i]), part);
             }
-            part = cross4_sum(part);                    // the 64 heads of the 4 lane rows
-            const int li = T * 16 + col;
-            if (g == 0 && T < ntile && li < ns) {
-                const uint32_t u = score_key(part);
-                if constexpr (SPLIT) {
-                    keys[li] = u;
-                    atomicAdd(&hs[u >> (32 - TOPK_BITS)], 1u);
-                } else {
-                    keys[li + (li >> le)] = u;
-                }
-            }
+            return part;
         };
         constexpr int NWV = IDX_NT / 64;
         const int wvu = __builtin_amdgcn_readfirstlane(wv);           // wave-uniform
@@ -425,9 +447,33 @@ k_idx_score(IndexArgs a) {
 #pragma unroll
             for (int u = 0; u < IDX_UNR; ++u) load_tile(wvu + NWV * (u + IDX_UNR * k), f[u]);
         };
+        // The four tiles' partial sums are reduced across the 4 lane groups together:
+        // two 32-lane swaps and one 16-lane swap leave tile u's totals in lane group
+        // g(u) = 0, 2, 1, 3, so every lane then finishes one key.
         auto score_grp = [&](int k, const KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
+            float p[IDX_UNR];
 #pragma unroll
-            for (int u = 0; u < IDX_UNR; ++u) score_tile(wvu + NWV * (u + IDX_UNR * k), f[u]);
+            for (int u = 0; u < IDX_UNR; ++u) {
+                p[u] = head_sum(f[u]);
+                __builtin_amdgcn_sched_barrier(0);       // one tile's accumulators live at a time
+            }
+            const auto a01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+            const auto a23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+            const float s01 = __uint_as_float(a01[0]) + __uint_as_float(a01[1]);
+            const float s23 = __uint_as_float(a23[0]) + __uint_as_float(a23[1]);
+            const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+            const float tot = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+            const int T = wvu + NWV * (((g & 1) << 1 | g >> 1) + IDX_UNR * k);
+            const int li = T * 16 + col;
+            if (T < ntile && li < ns) {
+                const uint32_t u = score_key(tot);
+                if constexpr (SPLIT) {
+                    keys[li] = u;
+                    atomicAdd(&hs[hpad(u >> (32 - TOPK_BITS))], 1u);
+                } else {
+                    keys[li + (li >> le)] = u;
+                }
+            }
         };
         // ping-pong: the next group's fragments load while the current one is scored.
         // The prefetch is unconditional (past the end it re-reads the last tile, an L2
@@ -453,15 +499,28 @@ k_idx_score(IndexArgs a) {
                 for (int x = i; x < ns; ++x) srow[x] = keys[x];
             }
         }
-        // bins 4t .. 4t+3 per thread; the nonzero ones compacted into the list
-        const u32x4 hv = *(const u32x4*)(hs + 4 * tid);
-        const int nz = (hv[0] != 0) + (hv[1] != 0) + (hv[2] != 0) + (hv[3] != 0);
+        // The list keeps the nonzero bins from the top down to the one holding the
+        // slice's min(k, ns)-th largest key: that key is at most the query's k-th
+        // largest, so the bins left out lie below the query's threshold bin, and the
+        // counts at and above it are exact.
+        uint32_t* misc = hs + TOPK_HSZ + 16;
+        if (wv == 0) find_bin(hs, (uint32_t)(ns < a.k ? ns : a.k), misc);
+        const u32x4 hv = *(const u32x4*)(hs + hpad(4 * tid));    // bins 4t .. 4t+3
+        __syncthreads();
+        const uint32_t bmin = misc[0];
+        uint32_t keep[4];
+        int nz = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            keep[x] = (uint32_t)(4 * tid + x) >= bmin ? hv[x] : 0u;
+            nz += keep[x] != 0;
+        }
         int tot;
-        int o = 1 + block_excl_scan<IDX_NT>(nz, (int*)(hs + TOPK_BINS), tot);
+        int o = 1 + block_excl_scan<IDX_NT>(nz, (int*)(hs + TOPK_HSZ), tot);
         uint32_t* slot = a.hist + (bq * a.nslices + sl) * (int64_t)SLOT_W;
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-            if (hv[x]) slot[o++] = ((uint32_t)(4 * tid + x) << 21) | hv[x];
+            if (keep[x]) slot[o++] = ((uint32_t)(4 * tid + x) << 21) | keep[x];
         if (tid == 0) slot[0] = (uint32_t)tot;
         return;
     }
@@ -624,36 +683,6 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
     }
 }
 
-// Wave 0 locates, in a padded 2048-bin histogram, the bin b where the count of keys in
-// higher bins is < need <= that count + hist[b]: misc[0] = b, misc[1] = count above,
-// misc[2] = hist[b].  Caller: wave 0 only, need >= 1 and <= total.
-__device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint32_t* misc) {
-    const int lane = threadIdx.x & 63;
-    const u32x4* h4 = (const u32x4*)(hp + 36 * lane);
-    uint32_t loc = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const u32x4 v4 = h4[q];
-        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
-    }
-    const int incl = wave_incl_scan((int)loc);
-    const int tot = __shfl(incl, 63, 64);
-    uint32_t c = (uint32_t)(tot - incl);
-    int fb = -1;                                         // bin within the lane's 32 (a select, not 32 live constants)
-    uint32_t fa = 0, fc = 0;
-#pragma unroll
-    for (int q = 7; q >= 0; --q) {
-        const u32x4 v4 = h4[q];
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-            const uint32_t cge = c + v4[e];
-            if (cge >= need && c < need) { fb = 4 * q + e; fa = c; fc = v4[e]; }
-            c = cge;
-        }
-    }
-    if (fb >= 0) { misc[0] = 32 * lane + fb; misc[1] = fa; misc[2] = fc; }
-}
-
 // Select over one query's score row (1024 threads).  On entry sh[0 .. TOPK_HSZ)
 // holds the row's padded histogram of the keys' top 11 bits, visible to every
 // thread.  LDS layout from smem: TOPK_SCRATCH(DSEL_NT) (histograms, misc, scans) |
@@ -664,9 +693,14 @@ __device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint
 // fits and gather(sk, si) returns the survivor count (>= 0), the survivors come from
 // there (the split path filtered them already); otherwise one pass over the row
 // collects them.  Then an exact radix select among the survivors, in entry order.
+struct BinInfo {          // the first level's threshold bin, when already known
+    bool have;
+    uint32_t bin, above, inbin;
+};
+
 template <typename Gather>
 __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64_t n, const uint32_t* srow,
-                                           uint32_t* smem, Gather gather) {
+                                           uint32_t* smem, Gather gather, BinInfo b0 = BinInfo{false, 0, 0, 0}) {
     const int tid = threadIdx.x, wv = tid >> 6;
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
@@ -683,10 +717,13 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
     bool exact = false;
     uint32_t above_total = 0;                            // keys strictly above the current bin
     for (int level = 0;; ++level) {
-        if (wv == 0) find_bin(sh, (uint32_t)need, misc);
-        __syncthreads();
-        const uint32_t bin = misc[0], above = misc[1], inbin = misc[2];
-        __syncthreads();
+        uint32_t bin = b0.bin, above = b0.above, inbin = b0.inbin;
+        if (level > 0 || !b0.have) {
+            if (wv == 0) find_bin(sh, (uint32_t)need, misc);
+            __syncthreads();
+            bin = misc[0]; above = misc[1]; inbin = misc[2];
+            __syncthreads();
+        }
         prefix |= bin << shift;
         pmask |= (level < 2 ? 0x7ffu : 0x3ffu) << shift;
         above_total += above;
@@ -867,12 +904,13 @@ __global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
         atomicAdd(&sh[hpad(pr >> 21)], pr & 0x1fffffu);
     }
     __syncthreads();
-    if (fb == 0) {
-        uint32_t* gh = a.row_hist + bq * TOPK_BINS;
-        for (int x = tid; x < TOPK_BINS; x += FLT_NT) gh[x] = sh[hpad(x)];
-    }
     if (wv == 0) find_bin(sh, (uint32_t)a.k, misc);
     __syncthreads();
+    if (fb == 0) {                                       // for the select: the histogram and its threshold bin
+        uint32_t* gh = a.row_hist + bq * ROWH_W;
+        for (int x = tid; x < TOPK_BINS; x += FLT_NT) gh[x] = sh[hpad(x)];
+        if (tid < 3) gh[TOPK_BINS + tid] = misc[tid];
+    }
     if (misc[1] + misc[2] > (uint32_t)DSEL_CAP) return;
     // ---- keys in the threshold bin or above, in entry order
     const uint32_t lo = misc[0] << (32 - TOPK_BITS);
@@ -909,7 +947,8 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
         take_all(a, bq, n, srow, tid, DSEL_NT);
         return;
     }
-    const uint32_t* gh = a.row_hist + bq * TOPK_BINS;
+    const uint32_t* gh = a.row_hist + bq * ROWH_W;
+    const BinInfo b0{true, gh[TOPK_BINS], gh[TOPK_BINS + 1], gh[TOPK_BINS + 2]};
     for (int x = tid; x < TOPK_BINS; x += DSEL_NT) smem[hpad(x)] = gh[x];
     __syncthreads();
     const int nfb = (int)(((n + a.S - 1) / a.S + a.spb - 1) / a.spb);
@@ -938,7 +977,7 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
         }
         __syncthreads();
         return tot;
-    });
+    }, b0);
 }
 
 // ---------------------------------------------------------------------------
@@ -947,7 +986,7 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
 template <int FMT, int DI, int HB, bool SPLIT>
 static void launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
-    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_BINS + 16)              // keys, histogram, scan
+    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 24)               // keys, histogram, scan, misc
                              : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT));   // keys + scratch
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
