@@ -76,7 +76,7 @@ int64_t row_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64
 size_t index_ws(int B, int Tq, int64_t n_cap, int nslices) {
     if (nslices <= 1) return 0;
     const size_t q = (size_t)B * Tq;
-    return q * ((size_t)3 * row_stride(n_cap) + (size_t)nslices * (csl::IDX_SLOT_W + 1) + csl::IDX_ROWH_W) * 4 + 256;
+    return q * ((size_t)3 * row_stride(n_cap) + (size_t)nslices * (csl::IDX_SLOT_W + 1) + 4) * 4 + 256;
 }
 
 // Split path: slices per filter block, about 256 filter blocks (one per compute unit) in all.
@@ -304,7 +304,7 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
         a.cand_idx = (int32_t*)((uint8_t*)ws + 2 * nr);
         a.hist = (uint32_t*)((uint8_t*)ws + 3 * nr);
         a.seg_cnt = (int32_t*)(a.hist + q * nslices * csl::IDX_SLOT_W);
-        a.row_hist = (uint32_t*)(a.seg_cnt + q * nslices);
+        a.row_bin = (uint32_t*)(a.seg_cnt + q * nslices);
     }
     return launched(csl::launch_index_topk(a, (hipStream_t)stream));
 }

@@ -107,9 +107,11 @@ constexpr int TOPK_BITS = 11;
 constexpr int TOPK_EMAX = 32;
 #define TOPK_SCRATCH(NT) (2 * TOPK_HSZ + 16 + 2 * ((NT) / 64) + 8)
 
+// top_known >= 0: the caller guarantees every key < 2^(top_known + 1), and the
+// min / max phase is skipped.
 template <int NT, int EMAX, typename Emit>
 __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, int n, int want, uint32_t* sh,
-                                           Emit emit) {
+                                           Emit emit, int top_known = -1) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int base = tid * E;
     uint32_t* hist0 = sh;
@@ -120,25 +122,30 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
     int eq_take = 0;
     const bool all = n <= want;
     if (!all) {
-        // ---- min / max over the valid keys; clear the first histogram
-        uint32_t lo = 0xffffffffu, hi = 0u;
+        uint32_t lo = 0u, hi = top_known >= 31 ? 0xffffffffu : (2u << top_known) - 1u;
+        if (top_known < 0) {
+            // ---- min / max over the valid keys; clear the first histogram
+            lo = 0xffffffffu; hi = 0u;
 #pragma unroll
-        for (int x = 0; x < EMAX; ++x) {
-            if (x < E && base + x < n) {
-                lo = kv[x] < lo ? kv[x] : lo;
-                hi = kv[x] > hi ? kv[x] : hi;
+            for (int x = 0; x < EMAX; ++x) {
+                if (x < E && base + x < n) {
+                    lo = kv[x] < lo ? kv[x] : lo;
+                    hi = kv[x] > hi ? kv[x] : hi;
+                }
             }
+            lo = wave_min_u32(lo);
+            hi = wave_max_u32(hi);
+            if (lane == 0) { wsum[wv] = (int)lo; wsum[NT / 64 + wv] = (int)hi; }
         }
-        lo = wave_min_u32(lo);
-        hi = wave_max_u32(hi);
-        if (lane == 0) { wsum[wv] = (int)lo; wsum[NT / 64 + wv] = (int)hi; }
         for (int x = tid; x < TOPK_HSZ; x += NT) hist0[x] = 0;
         __syncthreads();
-        lo = (uint32_t)wsum[0]; hi = (uint32_t)wsum[NT / 64];
-        for (int x = 1; x < NT / 64; ++x) {
-            const uint32_t a = (uint32_t)wsum[x], b = (uint32_t)wsum[NT / 64 + x];
-            lo = a < lo ? a : lo;
-            hi = b > hi ? b : hi;
+        if (top_known < 0) {
+            lo = (uint32_t)wsum[0]; hi = (uint32_t)wsum[NT / 64];
+            for (int x = 1; x < NT / 64; ++x) {
+                const uint32_t a = (uint32_t)wsum[x], b = (uint32_t)wsum[NT / 64 + x];
+                lo = a < lo ? a : lo;
+                hi = b > hi ? b : hi;
+            }
         }
         if (lo == hi) {
             T = lo;                                  // every key ties
@@ -366,7 +373,6 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
 // k_idx_split_filter and k_idx_split_select finish the query.
 constexpr int SLOT_W = IDX_SLOT_W;
 constexpr int MAX_SLICES_PER_ROW = 1024;
-constexpr int ROWH_W = IDX_ROWH_W;
 static_assert(SLOT_W >= TOPK_BINS + 1 && 4 * IDX_NT == TOPK_BINS, "slice lists: 4 bins per scoring thread");
 template <int FMT, int DI, int HB, bool SPLIT>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
@@ -850,11 +856,10 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
 // Split path, step 2: blocks of `spb` consecutive slices (FS = spb * S keys) per
 // query.  Each block sums the query's slice histograms (the score kernel's
 // (bin << 21 | count) lists) into LDS and finds the threshold bin, the one holding
-// the k-th largest key; block 0 stores the summed histogram for the select.  If the
-// keys in that bin or above fit in DSEL_CAP, the block copies its range's such keys,
-// with their entry indices and in entry order, to its segment [f*FS, ..) of the
-// candidate rows, and their count to seg_cnt; otherwise the select refines the
-// threshold over the score row.
+// the k-th largest key; block 0 stores it for the select.  If the keys in that bin or
+// above fit in DSEL_CAP, the block copies its range's such keys, with their entry
+// indices and in entry order, to its segment [f*FS, ..) of the candidate rows, and
+// their count to seg_cnt; otherwise the select refines the threshold over the row.
 constexpr int FLT_NT = 1024;
 constexpr int FLT_CH = 16;        // keys per thread per chunk
 
@@ -862,9 +867,9 @@ __global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t sh[TOPK_HSZ];
     __shared__ uint32_t misc[4];
     __shared__ int wsum[FLT_NT / 64 + 8];
-    __shared__ int soff[MAX_SLICES_PER_ROW];
+    constexpr int NW = FLT_NT / 64;
     const int fb = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bq = (int64_t)b * a.Tq + j;
     const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
     if (n <= a.k) return;                                // the select takes every entry
@@ -884,33 +889,33 @@ __global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
             kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
         }
     };
-    uint32_t kv[FLT_CH];
-    load_chunk(0, kv);                                   // in flight while the histogram is summed
-    // ---- the slices' lists, flattened over the block
+    // ---- histogram: wave w adds the lists of slices w, w + NW, ...; lane l takes entry
+    // l (then l + 64, ...).  The first two slices' count and entry are loaded together
+    // with the first chunk of keys, before the barrier that clears the histogram.
     const uint32_t* slots = a.hist + bq * (int64_t)a.nslices * SLOT_W;
-    const int c = tid < nseg ? (int)slots[(int64_t)tid * SLOT_W] : 0;
+    const int sa = wv, sb = wv + NW;
+    uint32_t ca = 0, ea = 0, cb = 0, eb = 0;
+    if (sa < nseg) { ca = slots[(int64_t)sa * SLOT_W]; ea = slots[(int64_t)sa * SLOT_W + 1 + lane]; }
+    if (sb < nseg) { cb = slots[(int64_t)sb * SLOT_W]; eb = slots[(int64_t)sb * SLOT_W + 1 + lane]; }
+    uint32_t kv[FLT_CH];
+    load_chunk(0, kv);
     for (int x = tid; x < TOPK_HSZ; x += FLT_NT) sh[x] = 0u;
-    int npairs;
-    const int off = block_excl_scan<FLT_NT>(c, wsum, npairs);
-    if (tid < nseg) soff[tid] = off;
     __syncthreads();
-    for (int p = tid; p < npairs; p += FLT_NT) {
-        int l = 0, h = nseg - 1;                         // last slice whose list starts at or before p
-        while (l < h) {
-            const int mid = (l + h + 1) >> 1;
-            if (soff[mid] <= p) l = mid; else h = mid - 1;
+    if ((uint32_t)lane < ca) atomicAdd(&sh[hpad(ea >> 21)], ea & 0x1fffffu);
+    if ((uint32_t)lane < cb) atomicAdd(&sh[hpad(eb >> 21)], eb & 0x1fffffu);
+    for (int sl = wv; sl < nseg; sl += NW) {             // longer lists, further slices
+        const uint32_t* li = slots + (int64_t)sl * SLOT_W;
+        const bool pre = sl == sa || sl == sb;
+        const uint32_t c = sl == sa ? ca : (sl == sb ? cb : li[0]);
+        for (uint32_t e = (pre ? 64u : 0u) + lane; e < c; e += 64) {
+            const uint32_t pr = li[1 + e];
+            atomicAdd(&sh[hpad(pr >> 21)], pr & 0x1fffffu);
         }
-        const uint32_t pr = slots[(int64_t)l * SLOT_W + 1 + (p - soff[l])];
-        atomicAdd(&sh[hpad(pr >> 21)], pr & 0x1fffffu);
     }
     __syncthreads();
     if (wv == 0) find_bin(sh, (uint32_t)a.k, misc);
     __syncthreads();
-    if (fb == 0) {                                       // for the select: the histogram and its threshold bin
-        uint32_t* gh = a.row_hist + bq * ROWH_W;
-        for (int x = tid; x < TOPK_BINS; x += FLT_NT) gh[x] = sh[hpad(x)];
-        if (tid < 3) gh[TOPK_BINS + tid] = misc[tid];
-    }
+    if (fb == 0 && tid < 3) a.row_bin[bq * 4 + tid] = misc[tid];   // for the select
     if (misc[1] + misc[2] > (uint32_t)DSEL_CAP) return;
     // ---- keys in the threshold bin or above, in entry order
     const uint32_t lo = misc[0] << (32 - TOPK_BITS);
@@ -935,49 +940,99 @@ __global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
     if (tid == 0) a.seg_cnt[bq * a.nslices + fb] = cnt;
 }
 
-// Split path, step 3: one block per query.
+// Split path, step 3: one block per query.  Usual case (the keys in and above the
+// threshold bin fit, at most 64 filter blocks): every wave scans the blocks' counts
+// itself, wave w copies segments w, w + 16, ... in entry order, and the exact top k
+// comes from a radix select over the survivors' offsets from the bin's lower edge
+// lo, those above the bin clamped to its upper edge: 22 bits, two passes, no
+// min / max phase.  Otherwise the general row select.
 __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    constexpr int NW = DSEL_NT / 64;
     const int j = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bq = (int64_t)b * a.Tq + j;
-    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    const int nfb_max = (a.nslices + a.spb - 1) / a.spb;
+    // one round of loads: position, threshold bin, counts
+    const int32_t qp = a.q_pos[bq];
+    const uint32_t bin = a.row_bin[bq * 4], above = a.row_bin[bq * 4 + 1], inbin = a.row_bin[bq * 4 + 2];
+    const int craw = lane < nfb_max ? a.seg_cnt[bq * a.nslices + lane] : 0;
+    const int64_t n = n_visible(qp, a.m, a.n_cap);
     const uint32_t* srow = a.scores + bq * a.sstride;
     if (n <= a.k) {
         take_all(a, bq, n, srow, tid, DSEL_NT);
         return;
     }
-    const uint32_t* gh = a.row_hist + bq * ROWH_W;
-    const BinInfo b0{true, gh[TOPK_BINS], gh[TOPK_BINS + 1], gh[TOPK_BINS + 2]};
-    for (int x = tid; x < TOPK_BINS; x += DSEL_NT) smem[hpad(x)] = gh[x];
-    __syncthreads();
     const int nfb = (int)(((n + a.S - 1) / a.S + a.spb - 1) / a.spb);
     const int64_t FS = (int64_t)a.spb * a.S;
+    const uint32_t* ck = a.cand_key + bq * a.sstride;
+    const int32_t* ci = a.cand_idx + bq * a.sstride;
     int* wsum = (int*)(smem + 2 * TOPK_HSZ + 16);
-    select_row(a, bq, n, srow, smem, [&](uint32_t* sk, int* si) {
-        // the filter blocks' segments in block order = entry order
-        int* foff = (int*)(sk + 2 * DSEL_CAP);           // the winner area, free until the final select
-        const int cc = tid < nfb ? a.seg_cnt[bq * a.nslices + tid] : 0;
-        int tot;
-        const int o = block_excl_scan<DSEL_NT>(cc, wsum, tot);
-        tot = tot < DSEL_CAP ? tot : DSEL_CAP;           // equal to the keys in and above the bin
-        if (tid < nfb) foff[tid] = o;
-        __syncthreads();
-        const uint32_t* ck = a.cand_key + bq * a.sstride;
-        const int32_t* ci = a.cand_idx + bq * a.sstride;
-        for (int p = tid; p < tot; p += DSEL_NT) {
-            int l = 0, h = nfb - 1;                      // last block whose segment starts at or before p
-            while (l < h) {
-                const int mid = (l + h + 1) >> 1;
-                if (foff[mid] <= p) l = mid; else h = mid - 1;
+    const BinInfo b0{true, bin, above, inbin};
+    if (above + inbin > (uint32_t)DSEL_CAP || nfb > 64) {
+        select_row(a, bq, n, srow, smem, [&](uint32_t* sk, int* si) {
+            // the filter blocks' segments in block order = entry order
+            int* foff = (int*)(sk + 2 * DSEL_CAP);       // the winner area, free until the final select
+            const int cc = tid < nfb ? a.seg_cnt[bq * a.nslices + tid] : 0;
+            int tot;
+            const int o = block_excl_scan<DSEL_NT>(cc, wsum, tot);
+            tot = tot < DSEL_CAP ? tot : DSEL_CAP;       // equal to the keys in and above the bin
+            if (tid < nfb) foff[tid] = o;
+            __syncthreads();
+            for (int p = tid; p < tot; p += DSEL_NT) {
+                int l = 0, h = nfb - 1;                  // last block whose segment starts at or before p
+                while (l < h) {
+                    const int mid = (l + h + 1) >> 1;
+                    if (foff[mid] <= p) l = mid; else h = mid - 1;
+                }
+                const int64_t src = (int64_t)l * FS + (p - foff[l]);
+                sk[p] = ck[src];
+                si[p] = ci[src];
             }
-            const int64_t src = (int64_t)l * FS + (p - foff[l]);
-            sk[p] = ck[src];
-            si[p] = ci[src];
+            __syncthreads();
+            return tot;
+        }, b0);
+        return;
+    }
+    uint32_t* sh = smem;
+    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);
+    int* si = (int*)(sk + DSEL_CAP);
+    int* win = si + DSEL_CAP;
+    uint32_t* wkey = (uint32_t*)(win + 2048);
+    // ---- gather
+    const int c = lane < nfb ? craw : 0;
+    const int incl = wave_incl_scan(c);
+    const int nsurv = __shfl(incl, 63, 64);               // = above + inbin <= DSEL_CAP
+    for (int f = wv; f < nfb; f += NW) {
+        const int cf = __shfl(c, f, 64), of = __shfl(incl, f, 64) - cf;
+        for (int e = lane; e < cf; e += 64) {
+            sk[of + e] = ck[(int64_t)f * FS + e];
+            si[of + e] = ci[(int64_t)f * FS + e];
         }
-        __syncthreads();
-        return tot;
-    }, b0);
+    }
+    __syncthreads();
+    // ---- exact top k
+    const uint32_t lo = bin << (32 - TOPK_BITS);
+    const uint32_t span = 1u << (32 - TOPK_BITS);         // keys above the bin map to span
+    constexpr int E2MAX = DSEL_CAP / DSEL_NT;
+    const int E2 = (nsurv + DSEL_NT - 1) / DSEL_NT;
+    uint32_t kv2[E2MAX];
+#pragma unroll
+    for (int x = 0; x < E2MAX; ++x) {
+        const uint32_t d = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] - lo : 0u;
+        kv2[x] = d < span ? d : span;
+    }
+    block_topk<DSEL_NT>(kv2, E2, nsurv, a.k, sh, [&](int pos, int i, uint32_t) {
+        win[pos] = si[i];
+        wkey[pos] = sk[i];
+    }, 32 - TOPK_BITS);
+    __syncthreads();
+    int32_t* oi = a.out_idx + bq * a.k;
+    float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
+    for (int p = tid; p < a.k; p += DSEL_NT) {
+        oi[p] = win[p];
+        if (os) os[p] = key_score(wkey[p]);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -7,7 +7,6 @@
 namespace csl {
 
 constexpr int IDX_SLOT_W = 2048 + 8;   // words per slice histogram list: count, then <= 2048 entries
-constexpr int IDX_ROWH_W = 2048 + 4;   // words per row histogram: 2048 bins, threshold bin, above, in bin
 
 struct CompressArgs {
     const uint8_t* x; int x_fmt; int64_t x_bstride; int64_t x_pos0; int64_t n_tok;
@@ -35,7 +34,7 @@ struct IndexArgs {
     uint32_t* cand_key;  // split: [B*Tq][sstride], filter block f's kept keys at [f*spb*S, ..)
     int32_t* cand_idx;   // split: [B*Tq][sstride], their entry indices
     int32_t* seg_cnt;    // split: [B*Tq][nslices] keys kept per filter block
-    uint32_t* row_hist;  // split: [B*Tq][IDX_ROWH_W] the summed histogram of each row, its threshold bin
+    uint32_t* row_bin;   // split: [B*Tq][4] threshold bin of each row, keys above it, keys in it
     // dense path (many queries): queries qc0 .. qc0+Tc-1 per pass
     int dense;           // 1: score every (query, key) pair to HBM, then select per query
     int Tc;              // rows per pass
