@@ -58,11 +58,12 @@ constexpr int MAX_SLICES = 1024;        // slices of one query (the row select s
 constexpr int MAX_S = 16384;            // keys one scoring block holds in LDS
 constexpr int64_t MAX_NCAP = (int64_t)MAX_S * MAX_SLICES;
 
-// Slices of S keys (a power of two in [512, 16384]), about 512 scoring blocks in all
-// (two per compute unit).  One slice per query: the block selects; several: the
-// split path over score rows.
+// Slices of S keys (a power of two in [512, 16384]), about 256 scoring blocks in all
+// (one per compute unit: long contiguous streams; the block's waves balance among
+// themselves).  One slice per query: the block selects; several: the split path over
+// score rows.
 void plan_index(int B, int Tq, int64_t n_cap, int& S, int& nslices) {
-    const int64_t target_blocks = 512;
+    const int64_t target_blocks = 256;
     const int64_t work = (n_cap > 0 ? n_cap : 1) * (int64_t)(B > 0 ? B : 1) * (Tq > 0 ? Tq : 1);
     const int64_t need = (work + target_blocks - 1) / target_blocks;
     S = 512;   // at least one key per thread of the 512-thread scoring block

@@ -373,7 +373,7 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
 // k_idx_split_filter and k_idx_split_select finish the query.
 constexpr int SLOT_W = IDX_SLOT_W;
 constexpr int MAX_SLICES_PER_ROW = 1024;
-static_assert(SLOT_W >= TOPK_BINS + 1 && 4 * IDX_NT == TOPK_BINS, "slice lists: 4 bins per scoring thread");
+static_assert(SLOT_W >= TOPK_BINS + 1 && TOPK_BINS % IDX_NT == 0, "slice lists: whole bins per scoring thread");
 template <int FMT, int DI, int HB, bool SPLIT>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
 k_idx_score(IndexArgs a) {
@@ -386,6 +386,7 @@ k_idx_score(IndexArgs a) {
     uint32_t* keys = smem;
     uint32_t* sh = smem + a.S + (a.S >> le);
     uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the padded histogram
+    uint32_t* ctr = SPLIT ? hs + TOPK_HSZ + 24 : sh + TOPK_SCRATCH(IDX_NT);   // next tile group
 
     const int64_t t = a.q_pos[bq];
     const int64_t n = n_visible(t, a.m, a.n_cap);
@@ -394,8 +395,9 @@ k_idx_score(IndexArgs a) {
     if constexpr (SPLIT) {
         if (ns <= 0) return;
         for (int x = tid; x < TOPK_HSZ; x += IDX_NT) hs[x] = 0u;
-        __syncthreads();
     }
+    if (tid == 0) *ctr = 0u;
+    __syncthreads();
 
     if (ns > 0) {
         // q fragments (A operand: rows = heads) and head weights, kept in registers
@@ -420,12 +422,11 @@ k_idx_score(IndexArgs a) {
         const uint8_t* kbase = a.ki + (int64_t)b * a.ki_bstride;
         const uint8_t* sbase = a.ki_scales ? a.ki_scales + (int64_t)b * a.ks_bstride : nullptr;
         const int ntile = (ns + 15) >> 4;
-        // tiles of this wave: T = wv + 8u + 32k (group k, slot u); a lane's row is
-        // clamped to the slice end, so only the last tile re-reads a valid row and
-        // every load stays in bounds without a per-lane branch
-        // Loads are unconditional (a tile past the end re-reads the last tile, a lane
-        // past the slice end re-reads the last row) so the load stream is straight-line
-        // code and the compiler can wait for exactly the group in use (vmcnt(N)).
+        const int ngr = (ntile + IDX_UNR - 1) / IDX_UNR;     // groups of IDX_UNR consecutive tiles
+        // A lane's row is clamped to the slice end and a group past the end re-reads
+        // the last group, so every load stays in bounds without a per-lane branch and
+        // the load stream is straight-line code: the compiler can wait for exactly the
+        // group in use (vmcnt(N)).
         auto load_tile = [&](int T, KeyFrag<FMT, DI>& f) {
             T = T < ntile ? T : ntile - 1;
             int li = T * 16 + col;
@@ -445,13 +446,18 @@ k_idx_score(IndexArgs a) {
             }
             return part;
         };
-        constexpr int NWV = IDX_NT / 64;
-        const int wvu = __builtin_amdgcn_readfirstlane(wv);           // wave-uniform
-        const int ngroups = wvu < ntile ? (ntile - wvu + NWV * IDX_UNR - 1) / (NWV * IDX_UNR) : 0;
+        // Groups are handed out dynamically: each wave takes the next one from a block
+        // counter in LDS, so the waves finish within about one group of each other.
+        auto grab = [&]() {
+            int v = 0;
+            if (lane == 0) v = (int)atomicAdd(ctr, 1u);
+            return __builtin_amdgcn_readfirstlane(v);
+        };
         KeyFrag<FMT, DI> fa[IDX_UNR], fb[IDX_UNR];
-        auto load_grp = [&](int k, KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
+        auto load_grp = [&](int j, KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
+            j = j < ngr ? j : ngr - 1;
 #pragma unroll
-            for (int u = 0; u < IDX_UNR; ++u) load_tile(wvu + NWV * (u + IDX_UNR * k), f[u]);
+            for (int u = 0; u < IDX_UNR; ++u) load_tile(IDX_UNR * j + u, f[u]);
         };
         // The four tiles' partial sums are reduced across the 4 lane groups together:
         // two 32-lane swaps and one 16-lane swap leave tile u's totals in lane group
@@ -469,7 +475,7 @@ k_idx_score(IndexArgs a) {
             const float s23 = __uint_as_float(a23[0]) + __uint_as_float(a23[1]);
             const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
             const float tot = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-            const int T = wvu + NWV * (((g & 1) << 1 | g >> 1) + IDX_UNR * k);
+            const int T = IDX_UNR * k + ((g & 1) << 1 | g >> 1);
             const int li = T * 16 + col;
             if (T < ntile && li < ns) {
                 const uint32_t u = score_key(tot);
@@ -481,16 +487,18 @@ k_idx_score(IndexArgs a) {
                 }
             }
         };
-        // ping-pong: the next group's fragments load while the current one is scored.
-        // The prefetch is unconditional (past the end it re-reads the last tile, an L2
-        // hit) so every path into the loop body has the same loads in flight.
-        if (ngroups > 0) load_grp(0, fa);
-        for (int k = 0; k < ngroups; k += 2) {
-            load_grp(k + 1, fb);
-            score_grp(k, fa);
-            if (k + 1 >= ngroups) break;
-            load_grp(k + 2, fa);
-            score_grp(k + 1, fb);
+        // ping-pong: the next group's fragments load while the current one is scored
+        int ja = grab();
+        load_grp(ja, fa);
+        int jb = grab();
+        while (ja < ngr) {
+            load_grp(jb, fb);
+            score_grp(ja, fa);
+            if (jb >= ngr) break;
+            ja = grab();
+            load_grp(ja, fa);
+            score_grp(jb, fb);
+            jb = grab();
         }
     }
     __syncthreads();
@@ -511,22 +519,24 @@ k_idx_score(IndexArgs a) {
         // counts at and above it are exact.
         uint32_t* misc = hs + TOPK_HSZ + 16;
         if (wv == 0) find_bin(hs, (uint32_t)(ns < a.k ? ns : a.k), misc);
-        const u32x4 hv = *(const u32x4*)(hs + hpad(4 * tid));    // bins 4t .. 4t+3
+        constexpr int BPT = TOPK_BINS / IDX_NT;          // bins per thread: BPT*t .. BPT*t + BPT-1
+        uint32_t keep[BPT];
+#pragma unroll
+        for (int x = 0; x < BPT; ++x) keep[x] = hs[hpad(BPT * tid + x)];
         __syncthreads();
         const uint32_t bmin = misc[0];
-        uint32_t keep[4];
         int nz = 0;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            keep[x] = (uint32_t)(4 * tid + x) >= bmin ? hv[x] : 0u;
+        for (int x = 0; x < BPT; ++x) {
+            keep[x] = (uint32_t)(BPT * tid + x) >= bmin ? keep[x] : 0u;
             nz += keep[x] != 0;
         }
         int tot;
         int o = 1 + block_excl_scan<IDX_NT>(nz, (int*)(hs + TOPK_HSZ), tot);
         uint32_t* slot = a.hist + (bq * a.nslices + sl) * (int64_t)SLOT_W;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            if (keep[x]) slot[o++] = ((uint32_t)(4 * tid + x) << 21) | keep[x];
+        for (int x = 0; x < BPT; ++x)
+            if (keep[x]) slot[o++] = ((uint32_t)(BPT * tid + x) << 21) | keep[x];
         if (tid == 0) slot[0] = (uint32_t)tot;
         return;
     }
@@ -1041,8 +1051,8 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
 template <int FMT, int DI, int HB, bool SPLIT>
 static void launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
-    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 24)               // keys, histogram, scan, misc
-                             : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT));   // keys + scratch
+    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 32)               // keys, histogram, scan, misc, counter
+                             : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT) + 4);   // keys, scratch, counter
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
 }
