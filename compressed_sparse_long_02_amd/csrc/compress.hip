@@ -14,6 +14,9 @@
 // entry is stored in its format: fp32, bf16, packed bf16 + e4m3fn, or MXFP4 (one
 // e8m0 scale per 32 channels, taken over 4 adjacent threads).  Splitting the rows
 // keeps a 128-row HCA window from becoming a 128-deep dependent loop per thread.
+// With few entries (decode: one per sequence) the channels are also split over
+// gridDim.z blocks of d / gridDim.z channels each, so that the launch still spans
+// a good part of the chip; each block recomputes the (cheap) window softmax.
 #include "device.h"
 #include "launch.h"
 
@@ -31,9 +34,12 @@ __host__ __device__ inline int pow2_at_least(int v) {
     return w;
 }
 
-// Long windows (HCA's 128 rows) get 1024-thread blocks so that each row group
-// walks only a few rows; short windows keep 256-thread blocks.
-__host__ __device__ inline int cmp_threads(int d, int win) { return (d / 8) * pow2_at_least(win) >= 1024 ? 1024 : 256; }
+// Long windows over wide rows (HCA's 128 rows of 512 channels) get 1024-thread
+// blocks so that each row group walks only a few rows; otherwise 256 threads (the
+// row-group merge loops over the groups, so they stay at most 32).
+__host__ __device__ inline int cmp_threads(int d, int win) {
+    return d >= 256 && (d / 8) * pow2_at_least(win) >= 1024 ? 1024 : 256;
+}
 
 __host__ __device__ inline CmpGeom cmp_geom(int d, int win, int nt) {
     CmpGeom g;
@@ -41,6 +47,7 @@ __host__ __device__ inline CmpGeom cmp_geom(int d, int win, int nt) {
     int rg = nt / g.TPR;
     const int w2 = pow2_at_least(win);
     if (rg > w2) rg = w2;
+    if (rg > 32) rg = 32;                  // the merge walks the groups one by one
     if (rg < 1) rg = 1;
     g.RG = rg;
     g.EPB = nt / (g.TPR * g.RG);
@@ -67,12 +74,13 @@ __device__ __forceinline__ void load8(const uint8_t* row, int c0, float* v) {
 template <int XF, int OF, bool ZC1, int CMP_NT>
 __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     const int win = a.overlap ? 2 * a.m : a.m;
-    const CmpGeom G = cmp_geom(a.d, win, CMP_NT);
+    const int dt = a.d / (int)gridDim.z;                // channels of this block
+    const CmpGeom G = cmp_geom(dt, win, CMP_NT);
     const int per_entry = G.TPR * G.RG;
     const int ep = threadIdx.x / per_entry;
     const int rg = (threadIdx.x / G.TPR) % G.RG;
     const int tr = threadIdx.x % G.TPR;
-    const int c0 = tr * 8;
+    const int c0 = (int)blockIdx.z * dt + tr * 8;
     const int b = blockIdx.y;
     const int64_t q = (int64_t)blockIdx.x * G.EPB + ep;
     const bool active = ep < G.EPB && q < a.n_e;
@@ -225,10 +233,18 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     }
 }
 
+// channel splits: halve the block's channels (keeping whole 32-channel groups)
+// while the launch has fewer than 256 entry blocks
+static int cmp_splits(const CompressArgs& a) {
+    int gz = 1;
+    while (a.n_e * (int64_t)a.B * gz < 256 && a.d / (2 * gz) >= 32 && (a.d / (2 * gz)) % 32 == 0) gz *= 2;
+    return gz;
+}
+
 template <int XF, int OF, int NT>
-static hipError_t launch_c3(const CompressArgs& a, hipStream_t s) {
-    const CmpGeom G = cmp_geom(a.d, a.overlap ? 2 * a.m : a.m, NT);
-    dim3 grid((unsigned)((a.n_e + G.EPB - 1) / G.EPB), (unsigned)a.B);
+static hipError_t launch_c3(const CompressArgs& a, hipStream_t s, int gz) {
+    const CmpGeom G = cmp_geom(a.d / gz, a.overlap ? 2 * a.m : a.m, NT);
+    dim3 grid((unsigned)((a.n_e + G.EPB - 1) / G.EPB), (unsigned)a.B, (unsigned)gz);
     if (a.z_ch == 1)
         hipLaunchKernelGGL((k_compress<XF, OF, true, NT>), grid, dim3(NT), 0, s, a);
     else
@@ -238,8 +254,9 @@ static hipError_t launch_c3(const CompressArgs& a, hipStream_t s) {
 
 template <int XF, int OF>
 static hipError_t launch_c2(const CompressArgs& a, hipStream_t s) {
-    return cmp_threads(a.d, a.overlap ? 2 * a.m : a.m) == 1024 ? launch_c3<XF, OF, 1024>(a, s)
-                                                               : launch_c3<XF, OF, 256>(a, s);
+    const int gz = cmp_splits(a);
+    return cmp_threads(a.d / gz, a.overlap ? 2 * a.m : a.m) == 1024 ? launch_c3<XF, OF, 1024>(a, s, gz)
+                                                                    : launch_c3<XF, OF, 256>(a, s, gz);
 }
 
 template <int XF>
