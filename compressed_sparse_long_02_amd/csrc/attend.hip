@@ -642,11 +642,12 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
 
 // Merge of split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One block per (query, 4 heads): the 64 heads of a head block spread over 16
-// blocks so that the merge reads its partials with the whole GPU.  Wave w owns head
-// h0 + w for the weights (lane s holds split s, in passes of 64); the data loop
-// issues the loads of 8 splits before accumulating them, in split order.
+// blocks so that the merge reads its partials with the whole GPU.  Every thread
+// first issues the loads of its first CMB_UNR splits, then waves 0..3 compute the
+// weights of heads h0..h0+3 (lane s holds split s, in passes of 64) while those
+// loads are in flight; the splits are accumulated in split order.
 constexpr int CMB_HEADS = 4;
-constexpr int CMB_UNR = 8;
+constexpr int CMB_UNR = 16;
 constexpr int CMB_NT = 512;
 
 template <int D>
@@ -659,6 +660,22 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
     const int ns = a.nsplit;
     const int64_t base = (bq * a.nhb + hb) * (int64_t)ns;
     float* lse_o = wts + CMB_HEADS * ns;
+    constexpr int C4 = D / 4;
+    constexpr int ITEMS = (CMB_HEADS * C4 + CMB_NT - 1) / CMB_NT;   // float4 items per thread
+    // ---- first loads: splits 0 .. CMB_UNR-1 of this thread's items (clamped: every load in bounds)
+    float4 v[ITEMS][CMB_UNR];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        int item = tid + it * CMB_NT;
+        item = item < CMB_HEADS * C4 ? item : CMB_HEADS * C4 - 1;
+        const int j = item / C4, c = (item - j * C4) * 4;
+        const float* src = a.ws_o + (base * 64 + h0 + j) * D + c;
+#pragma unroll
+        for (int u = 0; u < CMB_UNR; ++u) {
+            const int sc = u < ns ? u : ns - 1;
+            v[it][u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+        }
+    }
     if (wv < CMB_HEADS) {
         const int hh = h0 + wv;
         float M = -INFINITY;
@@ -684,29 +701,33 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
         if (lane == 0) lse_o[wv] = den > 0.f ? M + logf(den) : -INFINITY;
     }
     __syncthreads();
-    constexpr int C4 = D / 4;
-    for (int item = tid; item < CMB_HEADS * C4; item += CMB_NT) {
-        const int j = item / C4, c = (item - j * C4) * 4;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int item = tid + it * CMB_NT;
+        const bool valid = item < CMB_HEADS * C4;
+        const int ic = valid ? item : CMB_HEADS * C4 - 1;
+        const int j = ic / C4, c = (ic - j * C4) * 4;
         const int hh = h0 + j;
         const int h = hb * 64 + hh;
-        if (h >= a.H) continue;
         const float* src = a.ws_o + (base * 64 + hh) * D + c;
         const float* wj = wts + j * ns;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s0 = 0; s0 < ns; s0 += CMB_UNR) {
-            float4 v[CMB_UNR];
+            if (s0 > 0) {
 #pragma unroll
-            for (int u = 0; u < CMB_UNR; ++u) {
-                const int sc = s0 + u < ns ? s0 + u : ns - 1;     // clamped: every load in bounds
-                v[u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+                for (int u = 0; u < CMB_UNR; ++u) {
+                    const int sc = s0 + u < ns ? s0 + u : ns - 1;
+                    v[it][u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+                }
             }
 #pragma unroll
             for (int u = 0; u < CMB_UNR; ++u) {
                 const float w = s0 + u < ns ? wj[s0 + u] : 0.f;
-                acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
-                acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
+                acc.x = fmaf(w, v[it][u].x, acc.x); acc.y = fmaf(w, v[it][u].y, acc.y);
+                acc.z = fmaf(w, v[it][u].z, acc.z); acc.w = fmaf(w, v[it][u].w, acc.w);
             }
         }
+        if (!valid || h >= a.H) continue;
         if (a.out_fmt == F32) {
             *(float4*)((float*)a.out + (bq * a.H + h) * D + c) = acc;
         } else {
