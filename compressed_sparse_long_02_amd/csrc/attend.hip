@@ -366,12 +366,11 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     constexpr int JB = L::JB, J8 = L::J8, NJ = JB + J8;
     constexpr int PF = 3;                               // tiles whose rows are in flight
     constexpr int NSLOT = PF + 1;                       // row-pointer slots
-    __shared__ __attribute__((aligned(16))) uint16_t kl_s[L::TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t kl_s[2][L::TILE_ELEMS];   // tiles it&1
     __shared__ __attribute__((aligned(16))) v4f sx[MQ_NT / 64 * 2 * 64];   // [wave][r2][lane]
     __shared__ const uint8_t* rowptr[NSLOT * ATT_TILE];
     __shared__ uint32_t rowmask[NSLOT];
     __shared__ int sidx[ATT_MAX_SIDX];
-    uint8_t* kl = (uint8_t*)kl_s;
     const int rbf = FMT == BF16 ? D : a.r;              // dims stored as bf16
     const int64_t rb = FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r);
 
@@ -461,10 +460,10 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     u32x4 qb[QH];
     bool ovf = false;
 
-    // one tile: its prefetched rows (Rb) -> LDS, refill Rb with tile it+PF, then
-    // S^T, probabilities and O^T for the tile
-    auto tile = [&](int it, u32x4 (&Rb)[NJ]) {
-        lds_barrier();                                  // the previous tile's K/V and S reads are done
+    // tile `it`: its prefetched rows (Rb) -> LDS buffer it&1 (fp8 -> bf16), invalid
+    // rows zeroed
+    auto write_tile = [&](int it, const u32x4 (&Rb)[NJ]) {
+        uint8_t* kl = (uint8_t*)kl_s[it & 1];
         const uint32_t rmask = rowmask[it % NSLOT];
         const bool full = rmask == 0xffffffffu;         // wave-uniform
 #pragma unroll
@@ -489,12 +488,19 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
                 *(u32x4*)(dst + 16) = hi;
             }
         }
-        if (it + PF < ntiles) resolve(it + PF);
-        lds_barrier();                                  // K tile and the row pointers of tile it+PF visible
-        if (it + PF < ntiles) load_regs(it + PF, Rb);
+    };
+
+    // one tile (it, in LDS buffer it&1): S^T; after the exchange barrier, tile it+1
+    // goes from Rnext into the other buffer (its last readers, tile it-1's P.V, are
+    // past that barrier) while the probabilities and O^T of tile it are computed; the
+    // closing barrier publishes tile it+1, and Rnext is refilled with tile it+1+PF
+    auto tile = [&](int it, u32x4 (&Rnext)[NJ]) {
+        const uint32_t rmask = rowmask[it % NSLOT];
+        const bool full = rmask == 0xffffffffu;         // wave-uniform
+        const uint16_t* kt = kl_s[it & 1];
         // ---- partial S^T over this wave's half of the dims: s[r2] (rows 16*r2 + 4g + i)
         v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-        const uint16_t* k0 = kl_s + (size_t)col * KSTR + 32 * QH * dh + 8 * g;
+        const uint16_t* k0 = kt + (size_t)col * KSTR + 32 * QH * dh + 8 * g;
         const uint16_t* k1 = k0 + 16 * KSTR;
 #pragma unroll
         for (int ks = 0; ks < QH; ++ks) {
@@ -503,7 +509,11 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         }
         sx_mine[0] = s[0];
         sx_mine[64] = s[1];
-        lds_barrier();                                  // both halves of S^T visible
+        lds_barrier();                                  // both halves of S^T visible; tile it-1 done
+        if (it + 1 < ntiles) {
+            write_tile(it + 1, Rnext);
+            if (it + 1 + PF < ntiles) resolve(it + 1 + PF);
+        }
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
             const v4f p = sx_part[64 * r2];
@@ -553,7 +563,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             }
         }
         // ---- O^T += V^T P^T over this wave's dims (one V^T fragment feeds both head blocks)
-        const uint16_t* vp0 = kl_s + (size_t)(4 * g + (col >> 2)) * KSTR + 16 * NDH * dh + 4 * (col & 3);
+        const uint16_t* vp0 = kt + (size_t)(4 * g + (col >> 2)) * KSTR + 16 * NDH * dh + 4 * (col & 3);
         const uint16_t* vp1 = vp0 + 16 * KSTR;
 #pragma unroll
         for (int db = 0; db < NDH; ++db) {
@@ -563,6 +573,8 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             o[db] = mfma_bf16(va, pb, o[db]);
             o[db] = mfma_bf16(va, pl, o[db]);
         }
+        lds_barrier();                                  // tile it+1 and its row pointers visible, S^T reads done
+        if (it + 1 + PF < ntiles) load_regs(it + 1 + PF, Rnext);
     };
 
     // first rows in flight before the query loads, so that the two latencies overlap
@@ -595,10 +607,18 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             __syncthreads();                            // slots and tiles of the first pass are free
             start_rows();
         }
+        // tile 0 into buffer 0, tile PF resolved; R0 then refilled with tile PF
+        if (0 < ntiles) {
+            write_tile(0, R0);
+            if (PF < ntiles) resolve(PF);
+        }
+        lds_barrier();
+        if (PF < ntiles) load_regs(PF, R0);
+        // tile it's successor comes from R[(it+1) % PF]
         for (int it = 0; it < ntiles; it += PF) {
-            tile(it, R0);
-            if (it + 1 < ntiles) tile(it + 1, R1);
-            if (it + 2 < ntiles) tile(it + 2, R2);
+            tile(it, R1);
+            if (it + 1 < ntiles) tile(it + 1, R2);
+            if (it + 2 < ntiles) tile(it + 2, R0);
         }
         // the whole block redoes the split only if some wave overflowed
         if (!__syncthreads_or(ovf ? 1 : 0)) break;
