@@ -70,7 +70,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int incl = wave_incl_scan(v);
     if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
+    lds_barrier();                                   // LDS only: global loads in flight stay in flight
     int base = 0, tot = 0;
 #pragma unroll
     for (int x = 0; x < NT / 64; ++x) {
@@ -654,30 +654,45 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
     lds_barrier();
     for (int t = 0; t < nt; ++t) {
         if (t + 1 < nt) load_tile(t + 1);               // in flight during the MFMA work
-        // eight blocks of 16 keys, one after the other: the epilogue of a block (ReLU,
-        // head weights, the sum over the 4 lane rows) overlaps the next block's MFMAs
+        // eight blocks of 16 keys in two groups of four: per block the MFMAs, ReLU and
+        // head weights (one block's accumulators live at a time); per group the partial
+        // sums are reduced across the 4 lane rows together (two 32-lane swaps and one
+        // 16-lane swap leave block u's totals in lane row 0, 2, 1, 3), so every lane then
+        // stores one key and counts it
         if (n > 0) {
             const uint8_t* tb = &kt[t & 1][col * DNS_KSTR + 16 * g];
 #pragma unroll
-            for (int kb = 0; kb < DNS_KT / 16; ++kb) {
-                v4f acc[HB];
+            for (int k4 = 0; k4 < DNS_KT / 64; ++k4) {
+                float p[4];
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int u = 0; u < 4; ++u) {
+                    const int kb = 4 * k4 + u;
+                    v4f acc[HB];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DNS_KSTR + 64 * ks);
+                    for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16(qa[hb][ks], bf, acc[hb]);
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DNS_KSTR + 64 * ks);
+#pragma unroll
+                        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16(qa[hb][ks], bf, acc[hb]);
+                    }
+                    float part = 0.f;
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(acc[hb][i]), part);
+                    p[u] = part;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                float part = 0.f;
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) part = fmaf(wh[hb][i], relu_bits(acc[hb][i]), part);
-                part = cross4_sum(part);
-                const int64_t sidx = k0 + (int64_t)t * DNS_KT + 16 * kb + col;
-                if (g == 0 && sidx < n) {
-                    const uint32_t key = score_key(part);
+                const auto a01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+                const auto a23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+                const float s01 = __uint_as_float(a01[0]) + __uint_as_float(a01[1]);
+                const float s23 = __uint_as_float(a23[0]) + __uint_as_float(a23[1]);
+                const auto bsw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+                const float tot = __uint_as_float(bsw[0]) + __uint_as_float(bsw[1]);
+                const int64_t sidx = k0 + (int64_t)t * DNS_KT + 16 * (4 * k4 + ((g & 1) << 1 | g >> 1)) + col;
+                if (sidx < n) {
+                    const uint32_t key = score_key(tot);
                     srow[sidx] = key;
                     const uint32_t bin = key >> 21;
                     atomicAdd(&hist[qw * (TOPK_BINS / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -765,8 +780,8 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
     if (!gathered) nsurv = 0;
     int eq_seen = 0;
     constexpr int CH = 16;
-    for (int64_t base = 0; base < n && !gathered; base += (int64_t)DSEL_NT * CH) {
-        uint32_t kv[CH];
+    // chunks of DSEL_NT * CH keys, the next chunk's loads in flight while one is scanned
+    auto load_chunk = [&](int64_t base, uint32_t (&kv)[CH]) {
         const int64_t s0 = base + (int64_t)tid * CH;
 #pragma unroll
         for (int q = 0; q < CH / 4; ++q) {
@@ -775,6 +790,15 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
             const u32x4 v = *(const u32x4*)(srow + sq);
             kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
         }
+    };
+    uint32_t kvn[CH];
+    if (!gathered) load_chunk(0, kvn);
+    for (int64_t base = 0; base < n && !gathered; base += (int64_t)DSEL_NT * CH) {
+        uint32_t kv[CH];
+#pragma unroll
+        for (int x = 0; x < CH; ++x) kv[x] = kvn[x];
+        if (base + (int64_t)DSEL_NT * CH < n) load_chunk(base + (int64_t)DSEL_NT * CH, kvn);
+        const int64_t s0 = base + (int64_t)tid * CH;
         int my_gt = 0, my_eq = 0;
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
@@ -806,7 +830,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
         const int tgt = tot & 0xffff, teq = tot >> 16;
         nsurv += tgt + (exact ? (teq < eq_take ? teq : (eq_take > 0 ? eq_take : 0)) : 0);
         if (exact) eq_seen += teq;
-        __syncthreads();                                 // wsum reuse
+        lds_barrier();                                   // wsum reuse (the next chunk's loads stay in flight)
     }
     nsurv = nsurv < DSEL_CAP ? nsurv : DSEL_CAP;
     // ---- exact top-k among the survivors (in entry order), then the output.  The
