@@ -780,7 +780,10 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
     if (!gathered) nsurv = 0;
     int eq_seen = 0;
     constexpr int CH = 16;
-    // chunks of DSEL_NT * CH keys, the next chunk's loads in flight while one is scanned
+    constexpr int NPF = 3;                               // chunks in flight
+    const int64_t CHUNK = (int64_t)DSEL_NT * CH;
+    // chunks of CHUNK keys; the loads of the next NPF-1 chunks are in flight while one
+    // is scanned (a short scan per chunk would otherwise wait a full memory latency)
     auto load_chunk = [&](int64_t base, uint32_t (&kv)[CH]) {
         const int64_t s0 = base + (int64_t)tid * CH;
 #pragma unroll
@@ -791,13 +794,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
             kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
         }
     };
-    uint32_t kvn[CH];
-    if (!gathered) load_chunk(0, kvn);
-    for (int64_t base = 0; base < n && !gathered; base += (int64_t)DSEL_NT * CH) {
-        uint32_t kv[CH];
-#pragma unroll
-        for (int x = 0; x < CH; ++x) kv[x] = kvn[x];
-        if (base + (int64_t)DSEL_NT * CH < n) load_chunk(base + (int64_t)DSEL_NT * CH, kvn);
+    auto scan_chunk = [&](int64_t base, const uint32_t (&kv)[CH]) {
         const int64_t s0 = base + (int64_t)tid * CH;
         int my_gt = 0, my_eq = 0;
 #pragma unroll
@@ -830,7 +827,22 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
         const int tgt = tot & 0xffff, teq = tot >> 16;
         nsurv += tgt + (exact ? (teq < eq_take ? teq : (eq_take > 0 ? eq_take : 0)) : 0);
         if (exact) eq_seen += teq;
-        lds_barrier();                                   // wsum reuse (the next chunk's loads stay in flight)
+        lds_barrier();                                   // wsum reuse (loads in flight stay in flight)
+    };
+    // The loop body is branch-free (a chunk past the end scans nothing, its loads are
+    // clamped re-reads), so the compiler waits for exactly the chunk in use.
+    const int64_t nch = gathered ? 0 : (n + CHUNK - 1) / CHUNK;
+    uint32_t kr[NPF][CH];
+    if (nch > 0) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) load_chunk(u * CHUNK, kr[u]);
+    }
+    for (int64_t c0 = 0; c0 < nch; c0 += NPF) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            scan_chunk((c0 + u) * CHUNK, kr[u]);
+            load_chunk((c0 + u + NPF) * CHUNK, kr[u]);
+        }
     }
     nsurv = nsurv < DSEL_CAP ? nsurv : DSEL_CAP;
     // ---- exact top-k among the survivors (in entry order), then the output.  The
