@@ -122,6 +122,36 @@ def test_index_topk_clustered_scores_refine_the_threshold(gpu):
     check_topk(host(gi), oi, allsc, k, abs_bound=bound)
 
 
+def test_index_topk_filter_blocks_span_several_slices(gpu):
+    # 16 queries x 300,000 MXFP4 keys: slices of 16,384 keys, 19 per query, two slices per
+    # filter block; rows that end inside a slice, on a slice boundary, below k and empty
+    B, N, H_I, d_I, m, k = 16, 300000, 64, 128, 4, 1024
+    qc, qs = gen.random_mxfp4(B * H_I, d_I, 41)
+    kc, ks = gen.random_mxfp4(B * N, d_I, 42, device="cuda")
+    qc, qs = qc.reshape(B, 1, H_I, -1), qs.reshape(B, 1, H_I, -1)
+    kc, ks = kc.reshape(B, N, -1), ks.reshape(B, N, -1)
+    w = gen.normal((B, 1, H_I), 43, 1 / math.sqrt(H_I))
+    n_of = [N] * B
+    n_of[1], n_of[2], n_of[3], n_of[4] = 17 * 16384 + 5, 2 * 16384, 700, 0
+    qpos = torch.tensor([[n * m - 1 if n > 0 else 1] for n in n_of], dtype=torch.int32)   # n(t) = n
+    gi, _ = ops.index_topk(dev(qc), dev(w), kc, dev(qpos), fmt=O.MXFP4, H_I=H_I, d_I=d_I, m=m, n_cap=N, k=k,
+                           qi_scales=dev(qs), ki_scales=ks)
+    torch.cuda.synchronize()
+    gi_h = host(gi)
+    assert np.all(gi_h[4, 0] == -1)
+    assert np.array_equal(gi_h[3, 0, :700], np.arange(700)) and np.all(gi_h[3, 0, 700:] == -1)
+    for b in (0, 1, 2):
+        sl = slice(b, b + 1)
+        kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
+        oq = dict(qi_scales=host(qs[sl]), ki_scales=host(ks[sl]))
+        oi, _ = O.index_topk(host(qc[sl]), O.MXFP4, host(w[sl]), host(kc[sl]), O.MXFP4, host(qpos[sl]), k=k, **kw, **oq)
+        allsc = oracle_all_scores(host(qc[sl]), O.MXFP4, host(w[sl]), host(kc[sl]), O.MXFP4, host(qpos[sl]), **kw, **oq)
+        qd = BF.decode(host(qc[sl]), BF.MXFP4, d_I, scales=host(qs[sl])).reshape(1, H_I, d_I)
+        kd = BF.decode(host(kc[sl]), BF.MXFP4, d_I, scales=host(ks[sl])).reshape(N, d_I)
+        bound = score_error_bound(qd, host(w[sl])[0].astype(np.float64), kd)
+        check_topk(gi_h[sl], oi, allsc, k, abs_bound=bound[None])
+
+
 def test_index_topk_is_deterministic(gpu):
     B, Tq, H_I, d_I, N, k = 2, 2, 64, 128, 30000, 1024
     qc, qs = gen.random_mxfp4(B * Tq * H_I, d_I, 11)
