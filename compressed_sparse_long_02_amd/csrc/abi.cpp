@@ -89,7 +89,7 @@ int index_spb(int B, int Tq, int nslices) {
 
 constexpr int ATT_STEP = 32;            // rows a block stages per iteration; split lengths are multiples
 constexpr int ATT_TARGET_BLOCKS = 256;  // one block (4 waves, one per SIMD) per compute unit
-constexpr int ATT_MIN_RPS = 128;
+constexpr int ATT_MIN_RPS = 64;
 constexpr int ATT_MAX_SPLIT = 128;
 
 constexpr int ATT_MAX_CSA_RPS = 1536;   // rows of a CSA split whose indices are staged in LDS

@@ -374,8 +374,12 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     const int rbf = FMT == BF16 ? D : a.r;              // dims stored as bf16
     const int64_t rb = FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r);
 
-    const int sp = blockIdx.x, hb = blockIdx.y;
-    const int64_t bq = blockIdx.z;
+    // the splits of one query run on one XCD: its query rows and, later, the combine's
+    // reads of its partials stay in that XCD's L2
+    const unsigned lblk = xcd_local_id(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                       gridDim.x * gridDim.y * gridDim.z);
+    const int sp = (int)(lblk % gridDim.x), hb = (int)((lblk / gridDim.x) % gridDim.y);
+    const int64_t bq = lblk / (gridDim.x * gridDim.y);
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int hg = wv & 3, dh = wv >> 2;
@@ -673,9 +677,12 @@ constexpr int CMB_NT = 512;
 template <int D>
 __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
     extern __shared__ float wts[];   // [CMB_HEADS][nsplit] normalised weights, then lse
-    const int hb = blockIdx.x / (64 / CMB_HEADS);
-    const int h0 = (blockIdx.x % (64 / CMB_HEADS)) * CMB_HEADS;   // first head within the head block
-    const int64_t bq = blockIdx.y;
+    // same XCD assignment of queries as the attention kernel (its partials are in that L2)
+    const unsigned lblk = xcd_local_id(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int bx = (int)(lblk % gridDim.x);
+    const int hb = bx / (64 / CMB_HEADS);
+    const int h0 = (bx % (64 / CMB_HEADS)) * CMB_HEADS;   // first head within the head block
+    const int64_t bq = lblk / gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ns = a.nsplit;
     const int64_t base = (bq * a.nhb + hb) * (int64_t)ns;

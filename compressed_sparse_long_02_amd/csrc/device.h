@@ -196,4 +196,12 @@ __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(
 // compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Work-groups go to the 8 XCDs (each with its own L2) round-robin by linear id.  For
+// a grid of nb blocks (nb a multiple of 8) this maps hardware id `lin` to a logical
+// id such that logical ids [x nb/8, (x+1) nb/8) all run on XCD x: consecutive logical
+// blocks share an L2.  Otherwise the identity.
+__device__ __forceinline__ unsigned xcd_local_id(unsigned lin, unsigned nb) {
+    return (nb & 7u) ? lin : (lin & 7u) * (nb >> 3) + (lin >> 3);
+}
+
 }  // namespace csl
