@@ -10,8 +10,9 @@
 // Streaming, HBM-bound kernel.  A thread owns 8 consecutive channels (one 16-byte
 // bf16 load per row); d/8 adjacent threads cover a row, and RG such groups split
 // the window's rows between them, each running an online softmax over its rows.
-// The RG partial (max, sum, weighted sum) triples are merged through LDS, then the
-// entry is stored in its format: fp32, bf16, packed bf16 + e4m3fn, or MXFP4 (one
+// The RG partial (max, sum, weighted sum) triples are merged -- each rescaled to the
+// entry's maximum, then summed in a pairwise tree over the row groups (lane shuffles
+// within a wave, LDS across waves) -- and the entry is stored in its format: fp32, bf16, packed bf16 + e4m3fn, or MXFP4 (one
 // e8m0 scale per 32 channels, taken over 4 adjacent threads).  Splitting the rows
 // keeps a 128-row HCA window from becoming a 128-deep dependent loop per thread.
 // With few entries (decode: one per sequence) the channels are also split over
@@ -36,7 +37,7 @@ __host__ __device__ inline int pow2_at_least(int v) {
 
 // Long windows over wide rows (HCA's 128 rows of 512 channels) get 1024-thread
 // blocks so that each row group walks only a few rows; otherwise 256 threads (the
-// row-group merge loops over the groups, so they stay at most 32).
+// maximum step of the merge loops over the groups, so they stay at most 32).
 __host__ __device__ inline int cmp_threads(int d, int win) {
     return d >= 256 && (d / 8) * pow2_at_least(win) >= 1024 ? 1024 : 256;
 }
@@ -47,7 +48,7 @@ __host__ __device__ inline CmpGeom cmp_geom(int d, int win, int nt) {
     int rg = nt / g.TPR;
     const int w2 = pow2_at_least(win);
     if (rg > w2) rg = w2;
-    if (rg > 32) rg = 32;                  // the merge walks the groups one by one
+    if (rg > 32) rg = 32;                  // the merge's maximum walks the groups one by one
     if (rg < 1) rg = 1;
     g.RG = rg;
     g.EPB = nt / (g.TPR * g.RG);
@@ -138,49 +139,70 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
         }
     }
 
-    // ---- merge the RG row-group partials (fixed order: deterministic)
+    // ---- merge the RG row-group partials: every group rescales its (sum, weighted
+    // sum) to the entry's maximum logit, then a pairwise tree over rg adds them (level
+    // st joins group rg with rg + st).  The tree depends on RG only, so the result is
+    // deterministic and independent of the channel split; row group 0 ends with the
+    // entry's sums.  A level whose partner is in the same wave reads it by a lane
+    // shuffle, otherwise through LDS.
     __shared__ float s_acc[CMP_NT * 8];
-    __shared__ float s_mx[CMP_NT * NC];
     __shared__ float s_den[CMP_NT * NC];
     float v[8];
     if (G.RG > 1) {
+        float* s_mx = s_acc;                             // the maxima first, then the sums
+        const int base = ep * per_entry + tr;            // row group 0 of this entry and channels
+        const int ng = ep < G.EPB ? G.RG : 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s_acc[threadIdx.x * 8 + c] = acc[c];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) { s_mx[threadIdx.x * NC + c] = mx[c]; s_den[threadIdx.x * NC + c] = den[c]; }
+        for (int c = 0; c < NC; ++c) s_mx[threadIdx.x * NC + c] = mx[c];
         __syncthreads();
-        const int base = ep * per_entry + tr;   // thread of row group 0 for these channels
-        const int ng = ep < G.EPB ? G.RG : 0;    // threads past the last entry merge nothing
-        float M[NC], S[NC], A[8];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            M[c] = -INFINITY;
-            for (int g = 0; g < ng; ++g) M[c] = fmaxf(M[c], s_mx[(base + g * G.TPR) * NC + c]);
-            S[c] = 0.f;
-        }
+            float M = -INFINITY;
+            for (int g = 0; g < ng; ++g) M = fmaxf(M, s_mx[(base + g * G.TPR) * NC + c]);
+            const float f = mx[c] == -INFINITY ? 0.f : expf(mx[c] - M);
+            den[c] *= f;
+            if constexpr (ZC1) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) A[c] = 0.f;
-        for (int g = 0; g < ng; ++g) {
-            const int tg = base + g * G.TPR;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const float m_g = s_mx[tg * NC + c];
-                const float f = m_g == -INFINITY ? 0.f : expf(m_g - M[c]);
-                S[c] = fmaf(s_den[tg * NC + c], f, S[c]);
-                if constexpr (ZC1) {
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) A[cc] = fmaf(s_acc[tg * 8 + cc], f, A[cc]);
-                } else {
-                    A[c] = fmaf(s_acc[tg * 8 + c], f, A[c]);
-                }
+                for (int cc = 0; cc < 8; ++cc) acc[cc] *= f;
+            } else {
+                acc[c] *= f;
             }
         }
+        __syncthreads();                                 // maxima read: s_acc reused below
+        const bool tpr_pow2 = (G.TPR & (G.TPR - 1)) == 0;
+        const int lane = (int)(threadIdx.x & 63);
+        for (int st = 1; st < G.RG; st <<= 1) {          // block-uniform trip count
+            const bool joins = ep < G.EPB && (rg & (2 * st - 1)) == 0 && rg + st < G.RG;
+            float d2[NC], a2[8];
+            if (tpr_pow2 && st * G.TPR < 64) {           // partner lane + st * TPR, same wave
+                const int src = (lane + st * G.TPR) & 63;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = active ? A[c] / S[ZC1 ? 0 : c] : 0.f;
-    } else {
+                for (int c = 0; c < NC; ++c) d2[c] = __shfl(den[c], src, 64);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = active ? acc[c] / den[ZC1 ? 0 : c] : 0.f;
+                for (int c = 0; c < 8; ++c) a2[c] = __shfl(acc[c], src, 64);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s_acc[threadIdx.x * 8 + c] = acc[c];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) s_den[threadIdx.x * NC + c] = den[c];
+                __syncthreads();
+                const int pt = joins ? threadIdx.x + st * G.TPR : threadIdx.x;   // group rg + st
+#pragma unroll
+                for (int c = 0; c < NC; ++c) d2[c] = s_den[pt * NC + c];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) a2[c] = s_acc[pt * 8 + c];
+                __syncthreads();                         // slots free for the next level
+            }
+            if (joins) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) den[c] += d2[c];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] += a2[c];
+            }
+        }
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = active ? acc[c] / den[ZC1 ? 0 : c] : 0.f;   // final in row group 0
     const bool writer = active && rg == 0;
 
     uint8_t* ob = a.out + (int64_t)b * a.out_bstride;
