@@ -337,6 +337,29 @@ def main_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def time_sequence(calls, iters):
+    """Average duration of each call of a repeating sequence, by HIP events recorded
+    between the calls on torch's current stream.  Cycling through the layers of the
+    stack keeps the working set above the 256 MB last-level cache, as in the step."""
+    import torch
+    s = torch.cuda.current_stream()
+    for fn in calls:
+        fn()
+    n = len(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n * iters + 1)]
+    ev[0].record(s)
+    for i in range(iters):
+        for j, fn in enumerate(calls):
+            fn()
+            ev[i * n + j + 1].record(s)
+    ev[-1].synchronize()
+    tot = [0.0] * n
+    for i in range(iters):
+        for j in range(n):
+            tot[j] += ev[i * n + j].elapsed_time(ev[i * n + j + 1])
+    return [t / iters for t in tot]
+
+
 def time_calls(fn, iters):
     """Average duration of fn() on torch's current stream, by HIP events."""
     import torch
@@ -424,11 +447,12 @@ def main():
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     value = args.batch / (ms / 1e3)
-    # per-call durations (HIP events on the launching stream), eager launches
-    csa0, hca1 = st.layers[0], st.layers[1]
-    t_idx = time_calls(lambda: st.index(csa0), args.kernel_iters)
-    t_csa = time_calls(lambda: st.attend(csa0), args.kernel_iters)
-    t_hca = time_calls(lambda: st.attend(hca1), args.kernel_iters)
+    # per-call durations (HIP events on the launching stream), eager launches in step
+    # order through all four layers
+    L0, L1, L2, L3 = st.layers
+    tt = time_sequence([lambda: st.index(L0), lambda: st.attend(L0), lambda: st.attend(L1),
+                        lambda: st.index(L2), lambda: st.attend(L2), lambda: st.attend(L3)], args.kernel_iters)
+    t_idx, t_csa, t_hca = (tt[0] + tt[3]) / 2, (tt[1] + tt[4]) / 2, (tt[2] + tt[5]) / 2
     ib = st.index_bytes()
     ach = ib / (t_idx * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": "index_topk (MXFP4 scores + top-1024 of 262,144 per sequence)",
