@@ -794,15 +794,16 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
             kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
         }
     };
+    // (branch-free count; only a thread with survivors walks its keys again)
     auto scan_chunk = [&](int64_t base, const uint32_t (&kv)[CH]) {
         const int64_t s0 = base + (int64_t)tid * CH;
         int my_gt = 0, my_eq = 0;
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            if (s0 + x < n) {
-                if (exact) { my_gt += kv[x] > lo ? 1 : 0; my_eq += kv[x] == lo ? 1 : 0; }
-                else my_gt += kv[x] >= lo ? 1 : 0;
-            }
+            const bool in = s0 + x < n;
+            const uint32_t u = kv[x];
+            my_gt += (in && (u > lo || (!exact && u == lo))) ? 1 : 0;
+            my_eq += (in && exact && u == lo) ? 1 : 0;
         }
         int tot;
         const uint32_t pre = (uint32_t)block_excl_scan<DSEL_NT>(my_gt | (my_eq << 16), wsum, tot);
@@ -810,17 +811,15 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
         const int eq_take = need - eq_seen;              // exact case: equal keys still to take
         int pos = nsurv + gt_b + (exact ? (eq_b < eq_take ? (eq_b > 0 ? eq_b : 0) : (eq_take > 0 ? eq_take : 0)) : 0);
         int r_eq = eq_b;
+        if (my_gt + my_eq > 0) {
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            if (s0 + x < n) {
+            for (int x = 0; x < CH; ++x) {
+                const bool in = s0 + x < n;
                 const uint32_t u = kv[x];
-                bool keep;
-                if (exact) {
-                    keep = u > lo;
-                    if (u == lo) { keep = r_eq < eq_take; ++r_eq; }
-                } else {
-                    keep = u >= lo;
-                }
+                const bool gt = in && (u > lo || (!exact && u == lo));
+                const bool eq = in && exact && u == lo;
+                const bool keep = gt || (eq && r_eq < eq_take);
+                r_eq += eq ? 1 : 0;
                 if (keep && pos < DSEL_CAP) { sk[pos] = u; si[pos] = (int)(s0 + x); ++pos; }
             }
         }
