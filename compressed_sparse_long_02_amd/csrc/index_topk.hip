@@ -18,13 +18,18 @@
 //    16x16x128 FP4 MFMA, which applies the e8m0 block scales in hardware (the
 //    exact equivalent of the pages' lossless FP4->FP8 upcast).  The ReLU + weighted
 //    head sum runs on the accumulator registers; scores never leave LDS.
-//  * The block then selects its slice's top min(k,S) with a radix select on
-//    order-preserving uint32 keys in LDS (11-bit digits from the highest bit where
-//    the keys differ), and compacts the winners in index order with a block scan
-//    (ties: the first ones in index order).
-//  * k_idx_merge (only when a query spans several slices): one block per query
-//    streams the slices' candidates -- one contiguous array in entry order -- and
-//    repeats the same select; the winners come out ascending by index, no sort.
+//  * One slice per query: the block then selects the top min(k,S) with a radix
+//    select on order-preserving uint32 keys in LDS (11-bit digits from the highest
+//    bit where the keys differ), and compacts the winners in index order with a
+//    block scan (ties: the first ones in index order).
+//  * Several slices per query (long contexts): each block writes its keys to the
+//    query's score row and the histogram of their top 11 bits, from the top down
+//    to the bin of its own min(k,S)-th largest key; k_idx_split_filter finds the
+//    query's threshold bin and copies the keys at or above it (with their indices,
+//    in entry order); k_idx_split_select takes the exact top k among them.
+//  * Many queries (prefill): k_idx_dense_score scores 12 queries per block against
+//    LDS-staged key tiles with bf16 MFMA, writes every score key and a per-query
+//    histogram; k_idx_dense_select selects per query.
 #include "device.h"
 #include "launch.h"
 
