@@ -383,6 +383,19 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int hg = wv & 3, dh = wv >> 2;
+    // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the
+    // dims: loaded first -- they depend on nothing, so their latency overlaps the chain
+    // position -> row indices -> rows
+    u32x4 qb[QH];
+    {
+        const int h = hb * 64 + 16 * hg + col;
+        const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
+#pragma unroll
+        for (int ks = 0; ks < QH; ++ks) {
+            const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
+            qb[ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
+        }
+    }
     const int64_t t = a.q_pos[bq];
     const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
     const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
@@ -461,7 +474,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     v4f* sx_mine = sx + wv * 128 + lane;
     const v4f* sx_part = sx + (wv ^ 4) * 128 + lane;
     u32x4 R0[NJ], R1[NJ], R2[NJ];
-    u32x4 qb[QH];
     bool ovf = false;
 
     // tile `it`: its prefetched rows (Rb) -> LDS buffer it&1 (fp8 -> bf16), invalid
@@ -581,7 +593,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         if (it + 1 + PF < ntiles) load_regs(it + 1 + PF, Rnext);
     };
 
-    // first rows in flight before the query loads, so that the two latencies overlap
+    // the first PF tiles' rows in flight, tile 0 first
     auto start_rows = [&]() {
         for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
         lds_barrier();
@@ -590,16 +602,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         if (2 < ntiles) load_regs(2, R2);
     };
     start_rows();
-    // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the dims
-    {
-        const int h = hb * 64 + 16 * hg + col;
-        const uint8_t* qrow = a.q + (bq * a.H + (h < a.H ? h : 0)) * (int64_t)D * 2;
-#pragma unroll
-        for (int ks = 0; ks < QH; ++ks) {
-            const u32x4 v = *(const u32x4*)(qrow + (32 * (QH * dh + ks) + 8 * g) * 2);
-            qb[ks] = h < a.H ? v : u32x4{0, 0, 0, 0};
-        }
-    }
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
