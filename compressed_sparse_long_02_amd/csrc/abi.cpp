@@ -88,7 +88,7 @@ int index_spb(int B, int Tq, int nslices) {
 }
 
 constexpr int ATT_STEP = 32;            // rows a block stages per iteration; split lengths are multiples
-constexpr int ATT_TARGET_BLOCKS = 256;  // one block (4 waves, one per SIMD) per compute unit
+constexpr int ATT_TARGET_BLOCKS = 256;  // one block (8 waves, two per SIMD) per compute unit
 constexpr int ATT_MIN_RPS = 64;
 constexpr int ATT_MAX_SPLIT = 128;
 

@@ -334,11 +334,12 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / packed rows: register-blocked kernel.  A block (4 waves) owns one query
-// x 64 heads x one split.  Wave w covers heads 32*(w&1) .. +31 as two 16-head MFMA
-// blocks, and the half w>>1 of the head dim: every K or V fragment it reads from
-// LDS feeds two MFMAs (one per head block).  Q (32 heads x d/2, bf16) and O^T (32
-// heads x d/2, fp32) stay in registers (one wave per SIMD holds up to 512).
+// bf16 / packed rows: register-blocked kernel.  A block (8 waves, two per SIMD) owns
+// one query x 64 heads x one split of the attended rows.  Wave w covers the 16 heads
+// 16*(w&3) .. +15 and the half w>>2 of the head dim.  Rows are gathered 32 at a time
+// into registers three tiles ahead and converted once into a padded bf16 LDS tile
+// (double-buffered); Q (16 heads x d/2, bf16) and O^T (16 heads x d/2, fp32) stay in
+// registers.
 //   S^T = K Q^T : 16x16x32 bf16 over the wave's d/2 dims (A = K rows from LDS,
 //   B = Q from registers); the two halves are added through LDS, in the same
 //   order by both waves, so they hold bit-identical scores and softmax state.
