@@ -11,15 +11,19 @@
 //
 // Design (gfx950): a block owns one query token x 64 heads x one split of the
 // attended row list (CSA: the selected indices then the window; HCA: entries
-// 0..n(t)-1 then the window).  Rows are gathered 32 at a time into registers,
-// one tile ahead of the compute, then converted once into a padded bf16 LDS tile
-// (fp8 -> bf16 with the hardware OCP conversion).  Each of the 4 waves owns 16 heads: S = Q.K^T with
-// 16x16x32 bf16 MFMA (Q in registers, K fragments from LDS), an online softmax
-// on the accumulators with a lazy rescale, P staged through LDS, then O += P.V
-// with V fragments read from the same row-major tile by the gfx950 LDS transpose
-// read, so no transposed copy of V is ever written.  fp32 rows take the same path
-// with 16x16x4 f32 MFMA.  Splits write (o, lse) partials that k_attend_combine
-// merges in a fixed order (deterministic, no atomics).
+// 0..n(t)-1 then the window); the splits of one query run on one XCD.  Rows are
+// gathered 32 at a time into registers ahead of the compute, then converted once
+// into a padded bf16 LDS tile (fp8 -> bf16 with the hardware OCP conversion).
+//  * bf16 / packed rows (k_attend_mq, 8 waves): wave w takes 16 heads and half of
+//    the head dim; S^T = K.Q^T with 16x16x32 bf16 MFMA (Q in registers, K fragments
+//    from LDS), the two halves added through LDS; a softmax with a fixed reference
+//    per head (no rescaling, a second pass only if a logit outruns it); P stays in
+//    registers as a bf16 hi + lo pair and O^T += V^T.P^T reads V^T from the same
+//    row-major tile by the gfx950 LDS transpose read.
+//  * fp32 rows (k_attend, 4 waves of 16 heads): 16x16x4 f32 MFMA, an online
+//    softmax with a lazy rescale, P staged through LDS.
+// Splits write (o, lse) partials that k_attend_combine merges in a fixed order
+// (deterministic, no atomics).
 #include <type_traits>
 
 #include "device.h"
