@@ -833,9 +833,96 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
         if (exact) eq_seen += teq;
         lds_barrier();                                   // wsum reuse (loads in flight stay in flight)
     };
+    // Usual case (not exact): every wave streams its own section of the row with its
+    // own ring of chunks in flight and compacts its survivors into its own LDS region
+    // with wave scans -- no block barrier per chunk -- and the regions are then joined
+    // in wave order, which is entry order.  If a region overflows, the block-wide scan
+    // below redoes the row.
+    bool streamed = false;
+    if (!gathered && !exact) {
+        constexpr int NWV = DSEL_NT / 64, WCAP = DSEL_CAP / NWV, WCH = 1024;   // keys per wave chunk
+        const int lane = tid & 63;
+        const int64_t per = ((n + NWV - 1) / NWV + WCH - 1) / WCH * WCH;
+        const int64_t wb = (int64_t)wv * per;
+        const int64_t we = wb + per < n ? wb + per : n;
+        const int nwc = we > wb ? (int)((we - wb + WCH - 1) / WCH) : 0;
+        // lane l of chunk c holds keys wb + c*WCH + q*256 + 4l .. +3, q = 0..3
+        auto wload = [&](int c, u32x4 (&v)[4]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int64_t sq = wb + (int64_t)c * WCH + q * 256 + 4 * lane;
+                sq = sq < n ? sq : ((n - 1) & ~(int64_t)3);   // clamped inside the (4-padded) row
+                v[q] = *(const u32x4*)(srow + sq);
+            }
+        };
+        uint32_t* rk = sk + wv * WCAP;
+        int* ri = si + wv * WCAP;
+        int cnt = 0;
+        auto wscan = [&](int c, const u32x4 (&v)[4]) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t e0 = wb + (int64_t)c * WCH + q * 256 + 4 * lane;
+                int k4 = 0;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) k4 += (e0 + x < we && v[q][x] >= lo) ? 1 : 0;
+                const int incl = wave_incl_scan(k4);
+                if (k4 > 0) {
+                    int pos = cnt + incl - k4;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        if (e0 + x < we && v[q][x] >= lo) {
+                            if (pos < WCAP) { rk[pos] = v[q][x]; ri[pos] = (int)(e0 + x); }
+                            ++pos;
+                        }
+                    }
+                }
+                cnt += __shfl(incl, 63, 64);
+            }
+        };
+        u32x4 wr[NPF][4];
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) wload(u, wr[u]);
+        for (int c = 0; c < nwc; c += NPF) {
+#pragma unroll
+            for (int u = 0; u < NPF; ++u) {
+                if (c + u < nwc) wscan(c + u, wr[u]);
+                wload(c + u + NPF, wr[u]);
+            }
+        }
+        if (lane == 0) wsum[wv] = cnt;
+        __syncthreads();
+        int off = 0, tot = 0;
+        bool ovf = false;
+#pragma unroll
+        for (int x = 0; x < NWV; ++x) {
+            const int cx = wsum[x];
+            off += x < wv ? cx : 0;
+            tot += cx;
+            ovf |= cx > WCAP;
+        }
+        if (!ovf) {                                      // block-uniform
+            uint32_t tk[WCAP / 64];
+            int ti[WCAP / 64];
+#pragma unroll
+            for (int y = 0; y < WCAP / 64; ++y) {
+                const int p = lane + 64 * y;
+                tk[y] = p < cnt ? rk[p] : 0u;
+                ti[y] = p < cnt ? ri[p] : 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int y = 0; y < WCAP / 64; ++y) {
+                const int p = lane + 64 * y;
+                if (p < cnt) { sk[off + p] = tk[y]; si[off + p] = ti[y]; }
+            }
+            nsurv = tot;
+            streamed = true;
+        }
+        __syncthreads();                                 // regions and wsum free again
+    }
     // The loop body is branch-free (a chunk past the end scans nothing, its loads are
     // clamped re-reads), so the compiler waits for exactly the chunk in use.
-    const int64_t nch = gathered ? 0 : (n + CHUNK - 1) / CHUNK;
+    const int64_t nch = (gathered || streamed) ? 0 : (n + CHUNK - 1) / CHUNK;
     uint32_t kr[NPF][CH];
     if (nch > 0) {
 #pragma unroll

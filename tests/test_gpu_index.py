@@ -212,3 +212,29 @@ def test_index_topk_many_queries_all_tied(gpu):
                            H_I=H_I, d_I=d_I, m=4, n_cap=N, k=k)
     torch.cuda.synchronize()
     assert np.array_equal(host(gi)[0], np.tile(np.arange(k), (Tq, 1)))
+
+
+@pytest.mark.parametrize("order", ["rising", "falling"])
+def test_index_topk_many_queries_survivors_in_one_section(gpu, order):
+    # scores that rise (or fall) with the entry index: the keys at and above the first
+    # threshold bin all sit in one end of each query's row, more than one wave's share of
+    # the row select's survivor buffer, so the select takes its block-wide fallback scan
+    B, Tq, H_I, d_I, N, m, k = 1, 64, 16, 128, 24000, 4, 1024
+    v = gen.normal((d_I,), 71, 1 / math.sqrt(d_I))
+    ramp = torch.linspace(0.5, 1.5, N) if order == "rising" else torch.linspace(1.5, 0.5, N)
+    key = (ramp[:, None] * v[None, :]).reshape(1, N, d_I)
+    q = v.reshape(1, 1, 1, d_I).expand(B, Tq, H_I, d_I).contiguous()
+    w = torch.full((B, Tq, H_I), 1.0 / H_I)
+    qi, ki = gen.store(q, O.BF16), gen.store(key, O.BF16)
+    qpos = gen.positions(B, Tq, N * m - 1)
+    kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
+    gi, _ = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=O.BF16, k=k, **kw)
+    torch.cuda.synchronize()
+    oi, _ = O.index_topk(host(qi), O.BF16, host(w), host(ki), O.BF16, host(qpos), k=k, **kw)
+    allsc = oracle_all_scores(host(qi), O.BF16, host(w), host(ki), O.BF16, host(qpos), **kw)
+    qd = BF.decode(host(qi), O.BF16, d_I).reshape(B, Tq, H_I, d_I)
+    kd = BF.decode(host(ki), O.BF16, d_I).reshape(B, N, d_I)
+    bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
+    check_topk(host(gi), oi, allsc, k, abs_bound=bound)
+    sel = host(gi)[0]
+    assert (sel.min(axis=1) > N // 2).all() if order == "rising" else (sel.max(axis=1) < N // 2).all()
