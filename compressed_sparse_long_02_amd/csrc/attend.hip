@@ -13,7 +13,7 @@
 // attended row list (CSA: the selected indices then the window; HCA: entries
 // 0..n(t)-1 then the window); the splits of one query run on one XCD.  Rows are
 // gathered 32 at a time into registers ahead of the compute, then converted once
-// into a padded bf16 LDS tile (fp8 -> bf16 with the hardware OCP conversion).
+// into a bank-skewed bf16 LDS tile (fp8 -> bf16 with the hardware OCP conversion).
 //  * bf16 / packed rows (k_attend_mq, 8 waves): wave w takes 16 heads and half of
 //    the head dim; S^T = K.Q^T with 16x16x32 bf16 MFMA (Q in registers, K fragments
 //    from LDS), the two halves added through LDS; a softmax with a fixed reference
@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 // bf16 / packed rows: register-blocked kernel.  A block (8 waves, two per SIMD) owns
 // one query x 64 heads x one split of the attended rows.  Wave w covers the 16 heads
 // 16*(w&3) .. +15 and the half w>>2 of the head dim.  Rows are gathered 32 at a time
-// into registers three tiles ahead and converted once into a padded bf16 LDS tile
+// into registers three tiles ahead and converted once into a bank-skewed bf16 LDS tile
 // (double-buffered); Q (16 heads x d/2, bf16) and O^T (16 heads x d/2, fp32) stay in
 // registers.
 //   S^T = K Q^T : 16x16x32 bf16 over the wave's d/2 dims (A = K rows from LDS,
@@ -352,9 +352,16 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 //   accumulators sit in the lane, so P never leaves registers; V^T comes from two
 //   LDS transpose reads (rows 4g.. and 16 + 4g..).
 // ---------------------------------------------------------------------------
+// Tile rows in LDS: a stride of D + 128 bf16 (a multiple of the 256-byte bank width
+// for D % 128 == 0) and row r shifted by mq_skew(r) = 16 bytes x f(r), f(r) a
+// bijection of r mod 16 (r mod 8 -> even steps, the next bit -> odd).  The 16 rows a
+// 16-byte K-fragment read touches then start on 16 different bank groups, and so do
+// the 8 rows x 32 bytes of each half of a transposed V^T read.
+__device__ __forceinline__ int mq_skew(int row) { return 8 * (((row & 7) << 1) | ((row >> 3) & 1)); }
+
 template <int D, int FMT>
 struct MqLds {
-    static constexpr int KSTR = D + 8;                           // bf16 per K-tile row
+    static constexpr int KSTR = D + 128;                         // bf16 per K-tile row (with the skew room)
     static constexpr int TILE_ELEMS = ATT_TILE * KSTR;
     // 16-byte chunks per thread and tile: bf16 chunks (RoPE dims, or every dim of a
     // bf16 row) and fp8 chunks (the other dims of a packed row, r <= D/4)
@@ -492,7 +499,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             if (crow[j] < 0) continue;
             u32x4 v = Rb[j];
             if (!full && !((rmask >> crow[j]) & 1u)) v = u32x4{0, 0, 0, 0};
-            uint8_t* rowp = kl + (size_t)crow[j] * KSTR * 2;
+            uint8_t* rowp = kl + (size_t)(crow[j] * KSTR + mq_skew(crow[j])) * 2;
             if (j < JB) {
                 *(u32x4*)(rowp + 16 * cpc[j]) = v;
             } else {
@@ -521,7 +528,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         const uint16_t* kt = kl_s[it & 1];
         // ---- partial S^T over this wave's half of the dims: s[r2] (rows 16*r2 + 4g + i)
         v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-        const uint16_t* k0 = kt + (size_t)col * KSTR + 32 * QH * dh + 8 * g;
+        const uint16_t* k0 = kt + (size_t)(col * KSTR + mq_skew(col)) + 32 * QH * dh + 8 * g;
         const uint16_t* k1 = k0 + 16 * KSTR;
 #pragma unroll
         for (int ks = 0; ks < QH; ++ks) {
@@ -584,7 +591,8 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             }
         }
         // ---- O^T += V^T P^T over this wave's dims (one V^T fragment feeds both head blocks)
-        const uint16_t* vp0 = kt + (size_t)(4 * g + (col >> 2)) * KSTR + 16 * NDH * dh + 4 * (col & 3);
+        const int vr = 4 * g + (col >> 2);
+        const uint16_t* vp0 = kt + (size_t)(vr * KSTR + mq_skew(vr)) + 16 * NDH * dh + 4 * (col & 3);
         const uint16_t* vp1 = vp0 + 16 * KSTR;
 #pragma unroll
         for (int db = 0; db < NDH; ++db) {

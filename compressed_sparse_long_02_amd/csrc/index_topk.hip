@@ -458,9 +458,18 @@ k_idx_score(IndexArgs a) {
             if (lane == 0) v = (int)atomicAdd(ctr, 1u);
             return __builtin_amdgcn_readfirstlane(v);
         };
+        // Every block streams its own slice; started at the same offset, the blocks would
+        // read addresses at the same distance from their slice starts (slices are
+        // multiples of the channel interleave) and crowd the same HBM channels.  Block
+        // i of nb therefore takes its groups in the rotated order starting at group
+        // i*ngr/nb.
+        const unsigned nblk = gridDim.x * gridDim.y * gridDim.z;
+        const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+        const int rot = (int)(((uint64_t)lin * (uint64_t)ngr) / nblk);
+        auto rotg = [&](int j) { return j + rot < ngr ? j + rot : j + rot - ngr; };
         KeyFrag<FMT, DI> fa[IDX_UNR], fb[IDX_UNR];
         auto load_grp = [&](int j, KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
-            j = j < ngr ? j : ngr - 1;
+            j = rotg(j < ngr ? j : ngr - 1);
 #pragma unroll
             for (int u = 0; u < IDX_UNR; ++u) load_tile(IDX_UNR * j + u, f[u]);
         };
@@ -468,6 +477,7 @@ k_idx_score(IndexArgs a) {
         // two 32-lane swaps and one 16-lane swap leave tile u's totals in lane group
         // g(u) = 0, 2, 1, 3, so every lane then finishes one key.
         auto score_grp = [&](int k, const KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
+            k = rotg(k);
             float p[IDX_UNR];
 #pragma unroll
             for (int u = 0; u < IDX_UNR; ++u) {
