@@ -492,7 +492,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     // rows zeroed
     auto write_tile = [&](int it, const u32x4 (&Rb)[NJ]) {
         uint8_t* kl = (uint8_t*)kl_s[it & 1];
-        const uint32_t rmask = rowmask[it % NSLOT];
+        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[it % NSLOT]);   // block-uniform
         const bool full = rmask == 0xffffffffu;         // wave-uniform
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -523,7 +523,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     // past that barrier) while the probabilities and O^T of tile it are computed; the
     // closing barrier publishes tile it+1, and Rnext is refilled with tile it+1+PF
     auto tile = [&](int it, u32x4 (&Rnext)[NJ]) {
-        const uint32_t rmask = rowmask[it % NSLOT];
+        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[it % NSLOT]);   // block-uniform
         const bool full = rmask == 0xffffffffu;         // wave-uniform
         const uint16_t* kt = kl_s[it & 1];
         // ---- partial S^T over this wave's half of the dims: s[r2] (rows 16*r2 + 4g + i)
