@@ -38,6 +38,7 @@ CSA_CASES = [
     ("bf16_small", O.BF16, 2, 5, 8, 128, 0, 600, 64, 16, 100, "ragged"),
     ("f32_cfg1", O.F32, 1, 64, 8, 128, 32, 512, 64, 128, 2048, "cfg1"),
     ("packed_many_q", O.KV_PACKED, 4, 200, 16, 256, 64, 400, 40, 8, 64, "ragged"),  # nsplit = 1 path
+    ("packed_d64", O.KV_PACKED, 2, 3, 16, 64, 16, 700, 128, 32, 64, "ragged"),       # smallest head dim
 ]
 
 
@@ -82,6 +83,9 @@ HCA_CASES = [
     ("packed_ragged", O.KV_PACKED, 2, 4, 64, 512, 64, 700, 128, 128, "ragged"),
     ("bf16_h8", O.BF16, 2, 6, 8, 128, 0, 300, 4, 32, "ragged"),
     ("f32_h8", O.F32, 1, 5, 8, 128, 0, 200, 4, 64, "ragged"),
+    ("bf16_d64", O.BF16, 2, 3, 16, 64, 0, 300, 4, 32, "ragged"),
+    ("f32_d64", O.F32, 1, 4, 8, 64, 0, 150, 4, 16, "ragged"),
+    ("packed_d256_h80", O.KV_PACKED, 2, 2, 80, 256, 64, 400, 16, 128, "end"),   # two head blocks, one partial
 ]
 
 
