@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 // bf16 / packed rows: register-blocked kernel.  A block (8 waves, two per SIMD) owns
 // one query x 64 heads x one split of the attended rows.  Wave w covers the 16 heads
 // 16*(w&3) .. +15 and the half w>>2 of the head dim.  Rows are gathered 32 at a time
-// into registers three tiles ahead and converted once into a bank-skewed bf16 LDS tile
+// into registers two tiles ahead and converted once into a bank-skewed bf16 LDS tile
 // (double-buffered); Q (16 heads x d/2, bf16) and O^T (16 heads x d/2, fp32) stay in
 // registers.
 //   S^T = K Q^T : 16x16x32 bf16 over the wave's d/2 dims (A = K rows from LDS,
@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     constexpr int QH = D / 64;                          // k-steps of 32 dims per half
     constexpr int NDH = D / 32;                         // 16-dim output blocks per half
     constexpr int JB = L::JB, J8 = L::J8, NJ = JB + J8;
-    constexpr int PF = 3;                               // tiles whose rows are in flight
+    constexpr int PF = 2;                               // tiles whose rows are in flight
     constexpr int NSLOT = PF + 1;                       // row-pointer slots
     __shared__ __attribute__((aligned(16))) uint16_t kl_s[2][L::TILE_ELEMS];   // tiles it&1
     __shared__ __attribute__((aligned(16))) v4f sx[MQ_NT / 64 * 2 * 64];   // [wave][r2][lane]
@@ -485,7 +485,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     const float sl2 = a.scale * CSL_LOG2E;
     v4f* sx_mine = sx + wv * 128 + lane;
     const v4f* sx_part = sx + (wv ^ 4) * 128 + lane;
-    u32x4 R0[NJ], R1[NJ], R2[NJ];
+    u32x4 R0[NJ], R1[NJ];
     bool ovf = false;
 
     // tile `it`: its prefetched rows (Rb) -> LDS buffer it&1 (fp8 -> bf16), invalid
@@ -612,7 +612,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         lds_barrier();
         if (0 < ntiles) load_regs(0, R0);
         if (1 < ntiles) load_regs(1, R1);
-        if (2 < ntiles) load_regs(2, R2);
     };
     start_rows();
 
@@ -636,8 +635,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         // tile it's successor comes from R[(it+1) % PF]
         for (int it = 0; it < ntiles; it += PF) {
             tile(it, R1);
-            if (it + 1 < ntiles) tile(it + 1, R2);
-            if (it + 2 < ntiles) tile(it + 2, R0);
+            if (it + 1 < ntiles) tile(it + 1, R0);
         }
         // the whole block redoes the split only if some wave overflowed
         if (!__syncthreads_or(ovf ? 1 : 0)) break;
