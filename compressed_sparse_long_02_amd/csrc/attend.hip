@@ -377,11 +377,12 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     constexpr int NDH = D / 32;                         // 16-dim output blocks per half
     constexpr int JB = L::JB, J8 = L::J8, NJ = JB + J8;
     constexpr int PF = 2;                               // tiles whose rows are in flight
-    constexpr int NSLOT = PF + 1;                       // row-pointer slots
+    constexpr int RCH = 8;                              // tiles whose rows one resolve pass covers
+    static_assert(RCH >= PF + 1, "a chunk's table is rewritten only after its last tile is done");
     __shared__ __attribute__((aligned(16))) uint16_t kl_s[2][L::TILE_ELEMS];   // tiles it&1
     __shared__ __attribute__((aligned(16))) v4f sx[MQ_NT / 64 * 2 * 64];   // [wave][r2][lane]
-    __shared__ const uint8_t* rowptr[NSLOT * ATT_TILE];
-    __shared__ uint32_t rowmask[NSLOT];
+    __shared__ const uint8_t* rowptr[2][RCH * ATT_TILE];   // tile chunk c in table c & 1
+    __shared__ uint32_t rowmask[2][RCH];
     __shared__ int sidx[ATT_MAX_SIDX];
     const int rbf = FMT == BF16 ? D : a.r;              // dims stored as bf16
     const int64_t rb = FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r);
@@ -439,12 +440,15 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     }
     __syncthreads();
 
-    // rows of tile `it` -> rowptr slot it % NSLOT and the validity mask (wave 0)
-    auto resolve = [&](int it) {
-        if (tid < 64) {
+    // Row pointers and validity masks of the RCH tiles of chunk c -> table c & 1, one
+    // row per thread (waves 0..3), once per RCH tiles rather than by one wave on every
+    // tile's critical path.  An empty row points at the query row (an in-bounds dummy
+    // read; its chunks are zeroed when the tile is written).
+    auto resolve_chunk = [&](int c) {
+        for (int rr = tid; rr < RCH * ATT_TILE; rr += MQ_NT) {
             const uint8_t* p = nullptr;
-            if (tid < ATT_TILE) {
-                const int64_t v = v_begin + (int64_t)it * ATT_TILE + tid;
+            {
+                const int64_t v = v_begin + (int64_t)(c * RCH) * ATT_TILE + rr;
                 if (v < v_end) {
                     if (v < n_ent) {
                         const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
@@ -456,17 +460,17 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
                         p = a.kvw + (int64_t)b * a.kvw_bstride + slot * rb;
                     }
                 }
-                rowptr[(it % NSLOT) * ATT_TILE + tid] = p;
+                rowptr[c & 1][rr] = p ? p : a.q;
             }
-            const uint64_t m = __ballot(p != nullptr);
-            if (tid == 0) rowmask[it % NSLOT] = (uint32_t)m;
+            const uint64_t m = __ballot(p != nullptr);       // lanes 0..31: one tile, 32..63: the next
+            if ((rr & (ATT_TILE - 1)) == 0) rowmask[c & 1][rr / ATT_TILE] = (uint32_t)(m >> (lane & 32));
         }
     };
     // Register prefetch, PF tiles deep.  Every load is issued (an empty row re-reads
     // the query row; its chunks are zeroed when the tile is written to LDS), which
     // keeps the load stream branch-free.
     auto load_regs = [&](int it, u32x4 (&Rb)[NJ]) {
-        const uint8_t** rp = rowptr + (it % NSLOT) * ATT_TILE;
+        const uint8_t** rp = rowptr[(it / RCH) & 1] + (it % RCH) * ATT_TILE;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const uint8_t* p = crow[j] >= 0 ? rp[crow[j]] : nullptr;
@@ -492,7 +496,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     // rows zeroed
     auto write_tile = [&](int it, const u32x4 (&Rb)[NJ]) {
         uint8_t* kl = (uint8_t*)kl_s[it & 1];
-        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[it % NSLOT]);   // block-uniform
+        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[(it / RCH) & 1][it % RCH]);   // block-uniform
         const bool full = rmask == 0xffffffffu;         // wave-uniform
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -523,7 +527,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     // past that barrier) while the probabilities and O^T of tile it are computed; the
     // closing barrier publishes tile it+1, and Rnext is refilled with tile it+1+PF
     auto tile = [&](int it, u32x4 (&Rnext)[NJ]) {
-        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[it % NSLOT]);   // block-uniform
+        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[(it / RCH) & 1][it % RCH]);   // block-uniform
         const bool full = rmask == 0xffffffffu;         // wave-uniform
         const uint16_t* kt = kl_s[it & 1];
         // ---- partial S^T over this wave's half of the dims: s[r2] (rows 16*r2 + 4g + i)
@@ -540,8 +544,9 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
         lds_barrier();                                  // both halves of S^T visible; tile it-1 done
         if (it + 1 < ntiles) {
             write_tile(it + 1, Rnext);
-            if (it + 1 + PF < ntiles) resolve(it + 1 + PF);
         }
+        // the next chunk's rows, in time for the load of its first tile after this tile
+        if (it + 1 + PF < ntiles && (it + 1 + PF) % RCH == 0) resolve_chunk((it + 1 + PF) / RCH);
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
             const v4f p = sx_part[64 * r2];
@@ -608,7 +613,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
 
     // the first PF tiles' rows in flight, tile 0 first
     auto start_rows = [&]() {
-        for (int u = 0; u < PF && u < ntiles; ++u) resolve(u);
+        resolve_chunk(0);
         lds_barrier();
         if (0 < ntiles) load_regs(0, R0);
         if (1 < ntiles) load_regs(1, R1);
@@ -625,11 +630,8 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             __syncthreads();                            // slots and tiles of the first pass are free
             start_rows();
         }
-        // tile 0 into buffer 0, tile PF resolved; R0 then refilled with tile PF
-        if (0 < ntiles) {
-            write_tile(0, R0);
-            if (PF < ntiles) resolve(PF);
-        }
+        // tile 0 into buffer 0; R0 then refilled with tile PF (its rows are in chunk 0)
+        if (0 < ntiles) write_tile(0, R0);
         lds_barrier();
         if (PF < ntiles) load_regs(PF, R0);
         // tile it's successor comes from R[(it+1) % PF]
