@@ -681,10 +681,11 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
 
 // Merge of split partials: out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M).
 // One block per (query, 4 heads): the 64 heads of a head block spread over 16
-// blocks so that the merge reads its partials with the whole GPU.  Every thread
-// first issues the loads of its first CMB_UNR splits, then waves 0..3 compute the
-// weights of heads h0..h0+3 (lane s holds split s, in passes of 64) while those
-// loads are in flight; the splits are accumulated in split order.
+// blocks so that the merge reads its partials with the whole GPU.  Waves 0..3 first
+// load the split lse of heads h0..h0+3 (lane s holds split s), then every thread
+// issues the loads of its first CMB_UNR splits; the weights are formed while those
+// are in flight (loads complete in issue order, so waiting for the lse does not wait
+// for the partials), and the splits are accumulated in split order.
 constexpr int CMB_HEADS = 4;
 constexpr int CMB_UNR = 16;
 constexpr int CMB_NT = 512;
@@ -704,6 +705,10 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
     float* lse_o = wts + CMB_HEADS * ns;
     constexpr int C4 = D / 4;
     constexpr int ITEMS = (CMB_HEADS * C4 + CMB_NT - 1) / CMB_NT;   // float4 items per thread
+    // ---- the split lse of this wave's head (waves 0..3, lane s: split s), issued before the
+    //      partials: loads complete in issue order, so the weights need not wait for them
+    const int hw = h0 + (wv < CMB_HEADS ? wv : 0);
+    const float l_first = (wv < CMB_HEADS && lane < ns) ? a.ws_lse[(base + lane) * 64 + hw] : -INFINITY;
     // ---- first loads: splits 0 .. CMB_UNR-1 of this thread's items (clamped: every load in bounds)
     float4 v[ITEMS][CMB_UNR];
 #pragma unroll
@@ -719,20 +724,29 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
         }
     }
     if (wv < CMB_HEADS) {
-        const int hh = h0 + wv;
-        float M = -INFINITY;
-        for (int s0 = 0; s0 < ns; s0 += 64) {
-            const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
-            M = fmaxf(M, l);
+        const int hh = hw;
+        float M = l_first;
+        if (ns > 64) {                                   // more than one pass of 64 splits (rare)
+            for (int s0 = 64; s0 < ns; s0 += 64) {
+                const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
+                M = fmaxf(M, l);
+            }
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float den = 0.f;
-        for (int s0 = 0; s0 < ns; s0 += 64) {
-            const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
-            const float w = M == -INFINITY ? 0.f : expf(l - M);
-            if (s0 + lane < ns) wts[wv * ns + s0 + lane] = w;
-            den += w;
+        float den;
+        {
+            const float w = M == -INFINITY ? 0.f : expf(l_first - M);
+            if (lane < ns) wts[wv * ns + lane] = w;
+            den = w;
+        }
+        if (ns > 64) {
+            for (int s0 = 64; s0 < ns; s0 += 64) {
+                const float l = s0 + lane < ns ? a.ws_lse[(base + s0 + lane) * 64 + hh] : -INFINITY;
+                const float w = M == -INFINITY ? 0.f : expf(l - M);
+                if (s0 + lane < ns) wts[wv * ns + s0 + lane] = w;
+                den += w;
+            }
         }
         // fixed-order sum over the wave (butterfly: every lane gets the same bits)
 #pragma unroll
