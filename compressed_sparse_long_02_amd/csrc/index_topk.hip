@@ -1054,9 +1054,17 @@ __global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
         const uint32_t* li = slots + (int64_t)sl * SLOT_W;
         const bool pre = sl == sa || sl == sb;
         const uint32_t c = sl == sa ? ca : (sl == sb ? cb : li[0]);
-        for (uint32_t e = (pre ? 64u : 0u) + lane; e < c; e += 64) {
-            const uint32_t pr = li[1 + e];
-            atomicAdd(&sh[hpad(pr >> 21)], pr & 0x1fffffu);
+        // four rounds of 64 list entries in flight before their atomics
+        for (uint32_t e0 = pre ? 64u : 0u; e0 < c; e0 += 256) {
+            uint32_t pr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t e = e0 + 64 * u + lane;
+                pr[u] = e < c ? li[1 + e] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e0 + 64 * u + lane < c) atomicAdd(&sh[hpad(pr[u] >> 21)], pr[u] & 0x1fffffu);
         }
     }
     __syncthreads();
@@ -1152,9 +1160,21 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     const int nsurv = __shfl(incl, 63, 64);               // = above + inbin <= DSEL_CAP
     for (int f = wv; f < nfb; f += NW) {
         const int cf = __shfl(c, f, 64), of = __shfl(incl, f, 64) - cf;
-        for (int e = lane; e < cf; e += 64) {
-            sk[of + e] = ck[(int64_t)f * FS + e];
-            si[of + e] = ci[(int64_t)f * FS + e];
+        // four rounds of 64 in flight before the first store (a loop round per element
+        // pair would wait for each pair's loads in turn)
+        for (int e0 = 0; e0 < cf; e0 += 256) {
+            uint32_t kk[4];
+            int32_t ii[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                if (e < cf) { kk[u] = ck[(int64_t)f * FS + e]; ii[u] = ci[(int64_t)f * FS + e]; }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                if (e < cf) { sk[of + e] = kk[u]; si[of + e] = ii[u]; }
+            }
         }
     }
     __syncthreads();
