@@ -396,9 +396,17 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int hg = wv & 3, dh = wv >> 2;
+    // The split's slice of the index list (CSA) first: it depends on nothing but the
+    // split (the k selected entries come first in the row list), and global loads
+    // complete in issue order, so its LDS staging waits for these loads alone.
+    if (a.idx) {
+        const int64_t vb = (int64_t)sp * a.rps;
+        const int64_t e_end = vb + a.rps < a.k ? vb + a.rps : (int64_t)a.k;
+        for (int64_t v = vb + tid; v < e_end; v += MQ_NT) sidx[v - vb] = a.idx[bq * a.k + v];
+    }
     // Q fragments (B operands of S^T = K Q^T) of the wave's 16 heads, its half of the
-    // dims: loaded first -- they depend on nothing, so their latency overlaps the chain
-    // position -> row indices -> rows
+    // dims: they are needed only at the first S^T, so their latency overlaps the chain
+    // row indices -> row pointers -> rows
     u32x4 qb[QH];
     {
         const int h = hb * 64 + 16 * hg + col;
@@ -419,10 +427,6 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     if (v_end > L_all) v_end = L_all;
     const int ntiles = v_end > v_begin ? (int)((v_end - v_begin + ATT_TILE - 1) / ATT_TILE) : 0;
 
-    if (a.idx) {
-        const int64_t e_end = v_end < n_ent ? v_end : n_ent;
-        for (int64_t v = v_begin + tid; v < e_end; v += MQ_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
-    }
     // this thread's chunks of a tile, the same for every tile: j < JB are bf16 chunks
     // (row, 16-byte piece of the first 2*rbf bytes), the others fp8 chunks (row,
     // 16-byte piece of the fp8 part); -1 when beyond the tile
@@ -438,7 +442,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
             cpc[j] = per > 0 ? c - (c / per) * per : 0;
         }
     }
-    __syncthreads();
+    lds_barrier();                                      // the index slice in LDS (not the Q loads)
 
     // Row pointers and validity masks of the RCH tiles of chunk c -> table c & 1, one
     // row per thread (waves 0..3), once per RCH tiles rather than by one wave on every
