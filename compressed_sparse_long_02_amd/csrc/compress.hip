@@ -18,6 +18,8 @@
 // With few entries (decode: one per sequence) the channels are also split over
 // gridDim.z blocks of d / gridDim.z channels each, so that the launch still spans
 // a good part of the chip; each block recomputes the (cheap) window softmax.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -100,43 +102,63 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
         const uint8_t* xb = a.x + (int64_t)b * a.x_bstride;
         const float* zb = (const float*)((const uint8_t*)a.z + (int64_t)b * a.z_bstride);
         const int j0 = p0 < 0 ? (int)(-p0) : 0;
-#pragma unroll 4
-        for (int jw = j0 + ((rg - j0) % G.RG + G.RG) % G.RG; jw < win; jw += G.RG) {
-            const int64_t row = p0 + jw - a.x_pos0;
-            float xv[8];
-            load8<XF>(xb + row * xrb, c0, xv);
-            float lg[NC];
-            if constexpr (ZC1) {
-                lg[0] = zb[row] + a.bias[jw];
-            } else {
-                const float* zr = zb + row * a.z_ch + c0;
-                const float* br = a.bias + (int64_t)jw * a.z_ch + c0;
+        const int jf = j0 + ((rg - j0) % G.RG + G.RG) % G.RG;   // this thread's first row
+        // Rows in batches of CMP_RB: every load of a batch is issued before the first
+        // softmax update (a row past the window re-reads the batch's first row and is
+        // skipped), so a long window costs one memory round trip per batch rather than
+        // per row; the updates run in the same row order as one row at a time.
+        // (CMP_RB = 1 when no thread has a second row: the short CSA windows)
+        auto rows = [&](auto rb_tag) {
+        constexpr int CMP_RB = decltype(rb_tag)::value;
+        for (int jb = jf; jb < win; jb += CMP_RB * G.RG) {
+            float xv[CMP_RB][8], lg[CMP_RB][NC];
+            bool ok[CMP_RB];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) lg[c] = zr[c] + br[c];
+            for (int u = 0; u < CMP_RB; ++u) {
+                const int jw = jb + u * G.RG;
+                ok[u] = jw < win;
+                const int jc = ok[u] ? jw : jb;
+                const int64_t row = p0 + jc - a.x_pos0;
+                load8<XF>(xb + row * xrb, c0, xv[u]);
+                if constexpr (ZC1) {
+                    lg[u][0] = zb[row] + a.bias[jc];
+                } else {
+                    const float* zr = zb + row * a.z_ch + c0;
+                    const float* br = a.bias + (int64_t)jc * a.z_ch + c0;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) lg[u][c] = zr[c] + br[c];
+                }
             }
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                if (lg[c] > mx[c]) {
-                    const float s = expf(mx[c] - lg[c]);
-                    den[c] *= s;
+            for (int u = 0; u < CMP_RB; ++u) {
+                if (!ok[u]) continue;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    if (lg[u][c] > mx[c]) {
+                        const float s = expf(mx[c] - lg[u][c]);
+                        den[c] *= s;
+                        if constexpr (ZC1) {
+#pragma unroll
+                            for (int cc = 0; cc < 8; ++cc) acc[cc] *= s;
+                        } else {
+                            acc[c] *= s;
+                        }
+                        mx[c] = lg[u][c];
+                    }
+                    const float e = expf(lg[u][c] - mx[c]);
+                    den[c] += e;
                     if constexpr (ZC1) {
 #pragma unroll
-                        for (int cc = 0; cc < 8; ++cc) acc[cc] *= s;
+                        for (int cc = 0; cc < 8; ++cc) acc[cc] = fmaf(e, xv[u][cc], acc[cc]);
                     } else {
-                        acc[c] *= s;
+                        acc[c] = fmaf(e, xv[u][c], acc[c]);
                     }
-                    mx[c] = lg[c];
-                }
-                const float e = expf(lg[c] - mx[c]);
-                den[c] += e;
-                if constexpr (ZC1) {
-#pragma unroll
-                    for (int cc = 0; cc < 8; ++cc) acc[cc] = fmaf(e, xv[cc], acc[cc]);
-                } else {
-                    acc[c] = fmaf(e, xv[c], acc[c]);
                 }
             }
         }
+        };
+        if (win <= G.RG) rows(std::integral_constant<int, 1>{});
+        else rows(std::integral_constant<int, 4>{});
     }
 
     // ---- merge the RG row-group partials: every group rescales its (sum, weighted
