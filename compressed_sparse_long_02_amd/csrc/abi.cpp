@@ -144,7 +144,9 @@ int validate_attend(const char* fn, const void* q, int q_fmt, const void* kv_c, 
     if (B * (int64_t)Tq == 0) return CSL_OK;
     if (!q || !q_pos || !out) return fail(CSL_EINVAL, "%s: null q, q_pos or out", fn);
     if (n_cap > 0 && !kv_c) return fail(CSL_EINVAL, "%s: null kv_c with n_cap > 0", fn);
-    if (W > 0 && (!kv_w || kvw_rows < 1)) return fail(CSL_EINVAL, "%s: W > 0 needs kv_w and kvw_rows >= 1", fn);
+    if (W > 0 && !kv_w) return fail(CSL_EINVAL, "%s: W > 0 needs kv_w", fn);
+    if (W > 0 && kvw_rows < W)    // a shorter ring would hand two window positions the same row
+        return fail(CSL_EINVAL, "%s: kvw_rows = %lld is below the window W = %d", fn, (long long)kvw_rows, W);
     if (!al16(q) || !al16(out) || !al16(kv_c) || !al16(kv_w) || !al4(q_pos))
         return fail(CSL_EINVAL, "%s: q/kv_c/kv_w/out must be 16-byte aligned", fn);
     if ((kvc_bstride & 15) || (kvw_bstride & 15)) return fail(CSL_EINVAL, "%s: byte strides must be multiples of 16", fn);
@@ -253,11 +255,12 @@ size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
     return ws;
 }
 
-int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
-               const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
-               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
-               int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
-    const char* fn = "index_topk";
+}  // extern "C"
+
+static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                      const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                      const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
     if (B < 0 || Tq < 0 || n_cap < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
     if (B > 65535 || Tq > 65535) return fail(CSL_EUNSUPPORTED, "%s: B and Tq must be <= 65535", fn);
     if (m < 1) return fail(CSL_EINVAL, "%s: m must be >= 1", fn);
@@ -308,6 +311,16 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
         a.row_bin = (uint32_t*)(a.seg_cnt + q * nslices);
     }
     return launched(csl::launch_index_topk(a, (hipStream_t)stream));
+}
+
+extern "C" {
+
+int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+               const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+               const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+               int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    return index_impl("index_topk", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride, q_pos,
+                      B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, ws, ws_bytes, stream);
 }
 
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max) {

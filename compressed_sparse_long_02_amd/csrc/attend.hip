@@ -41,38 +41,27 @@ __device__ __forceinline__ int64_t att_n_visible(int64_t t, int m, int64_t n_cap
     return n < n_cap ? n : n_cap;
 }
 
-template <int D, int FMT>
-struct AttLds {
-    static constexpr bool F32P = FMT == F32;
-    static constexpr int KSTR = F32P ? D + 4 : D + 8;          // elements per K-tile row (bank padding)
-    static constexpr int KL_ELEMS = ATT_TILE * KSTR;
-    // 16-byte chunks of the longest stored row (packed rows: r <= D/4 RoPE dims)
-    static constexpr int CPR_MAX = F32P ? D / 4 : (FMT == BF16 ? D / 8 : (D + D / 4) / 16);
-    static constexpr int NJ = (ATT_TILE * CPR_MAX + ATT_NT - 1) / ATT_NT;   // chunks per thread per tile
-};
 constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (host plan)
 
 constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
 constexpr float ATT_HEADROOM = 64.0f;   // largest x - m_ref (base 2) accepted without a rescale
 constexpr float ATT_REF_LIFT = 32.0f;   // m_ref starts this far above the first tile's largest logit
 
-// 16x16x16 bf16 MFMA: A lane l = row l%16, k 4*(l/16)..+4; B lane l = col l%16, same k.
-__device__ __forceinline__ v4f mfma_bf16_k16(const u32x2& a, const u32x2& b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);
-}
-
-template <int D, int FMT>
+// ---------------------------------------------------------------------------
+// fp32 rows (the fp32 parity configuration): 4 waves of 16 heads, 16x16x4 f32 MFMA, an
+// online softmax with a lazy rescale.  bf16 and packed rows go to k_attend_mq.
+// ---------------------------------------------------------------------------
+template <int D>
 __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
-    using L = AttLds<D, FMT>;
-    constexpr bool F32P = L::F32P;
-    constexpr int KSTR = L::KSTR;
-    using KT = typename std::conditional<F32P, float, uint16_t>::type;
-    __shared__ __attribute__((aligned(16))) KT kl_s[L::KL_ELEMS];
+    constexpr int KSTR = D + 4;                          // floats per K-tile row (bank padding)
+    constexpr int CPR = D / 4;                           // 16-byte chunks per row
+    constexpr int NCH = ATT_TILE * CPR;
+    constexpr int NJ = (NCH + ATT_NT - 1) / ATT_NT;      // chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) float kl[ATT_TILE * KSTR];
     __shared__ const uint8_t* rowptr[2 * ATT_TILE];
     __shared__ uint32_t rowmask[2];
     __shared__ int sidx[ATT_MAX_SIDX];
-    uint8_t* kl = (uint8_t*)kl_s;
-    const int64_t rb = FMT == F32 ? 4 * (int64_t)D : (FMT == BF16 ? 2 * (int64_t)D : 2 * (int64_t)a.r + (D - a.r));
+    constexpr int64_t rb = 4 * (int64_t)D;
 
     const int sp = blockIdx.x, hb = blockIdx.y;
     const int64_t bq = blockIdx.z;
@@ -87,8 +76,6 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     int64_t v_end = v_begin + a.rps;
     if (v_end > L_all) v_end = L_all;
     const int ntiles = v_end > v_begin ? (int)((v_end - v_begin + ATT_TILE - 1) / ATT_TILE) : 0;
-    const int cpr = (int)(rb / 16);                     // 16-byte chunks per stored row
-    const int nch = ATT_TILE * cpr;
 
     // ---- the split's slice of the index list, staged once (CSA)
     if (a.idx) {
@@ -96,35 +83,14 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         for (int64_t v = v_begin + tid; v < e_end; v += ATT_NT) sidx[v - v_begin] = a.idx[bq * a.k + v];
     }
 
-    // ---- Q fragments (B operand of S^T = K Q^T): head h = hb*64 + wv*16 + col.  The
-    //      first QR k-steps live in registers; for d = 512 the last QL k-steps are
-    //      read from LDS, which keeps the kernel inside 256 registers (two blocks/CU).
+    // ---- Q fragments (B operand of S^T = K Q^T): head h = hb*64 + wv*16 + col
     const int h_a = hb * 64 + wv * 16 + col;
-    constexpr int QKS = F32P ? D / 4 : D / 32;
-    constexpr int QL = (!F32P && D == 512) ? (FMT == BF16 ? 12 : 8) : 0;
-    constexpr int QR = QKS - QL;
-    constexpr int QSTR = QL * 32 + 8;                   // bf16 per head row in LDS (16-byte pad)
-    __shared__ __attribute__((aligned(16))) uint16_t ql_s[QL > 0 ? 64 * QSTR : 8];
-    u32x4 qb[F32P ? 1 : QR];
-    float qf[F32P ? QKS : 1];
-    if constexpr (F32P) {
+    constexpr int QKS = D / 4;
+    float qf[QKS];
+    {
         const float* qrow = (const float*)a.q + (bq * a.H + h_a) * D;
 #pragma unroll
         for (int ks = 0; ks < QKS; ++ks) qf[ks] = h_a < a.H ? qrow[4 * ks + g] : 0.f;
-    } else {
-        const uint8_t* qrow = a.q + (bq * a.H + h_a) * (int64_t)D * 2;
-#pragma unroll
-        for (int ks = 0; ks < QR; ++ks)
-            qb[ks] = h_a < a.H ? *(const u32x4*)(qrow + (32 * ks + 8 * g) * 2) : u32x4{0, 0, 0, 0};
-        if constexpr (QL > 0) {
-            for (int c = tid; c < 64 * QL * 4; c += ATT_NT) {
-                const int hq = c / (QL * 4), pc = c - hq * (QL * 4);
-                const int hg = hb * 64 + hq;
-                const u32x4 v = hg < a.H ? *(const u32x4*)(a.q + ((bq * a.H + hg) * (int64_t)D + 32 * QR + 8 * pc) * 2)
-                                         : u32x4{0, 0, 0, 0};
-                *(u32x4*)(ql_s + hq * QSTR + 8 * pc) = v;
-            }
-        }
     }
     __syncthreads();
 
@@ -152,12 +118,11 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         }
     };
     // Register prefetch of a tile: thread `tid` owns chunks c = tid + ATT_NT*j of the
-    // tile (row c / cpr, 16-byte piece c % cpr), the same for every tile.  The loads
+    // tile (row c / CPR, 16-byte piece c % CPR), the same for every tile.  The loads
     // of tile it+1 are issued right after tile it reaches LDS and are consumed at the
     // top of the next iteration, so a whole tile of MFMA work hides their latency.
     // Every load is issued (an empty row re-reads the query row and is zeroed), which
     // keeps the load stream branch-free.
-    constexpr int NJ = L::NJ;
     u32x4 R[NJ];
     uint32_t okm = 0;
     auto load_regs = [&](int it) {
@@ -166,10 +131,10 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int c = tid + ATT_NT * j;
-            const int rr = c / cpr;
-            const uint8_t* p = c < nch ? rp[rr] : nullptr;
+            const int rr = c / CPR;
+            const uint8_t* p = c < NCH ? rp[rr] : nullptr;
             const bool okc = p != nullptr;
-            R[j] = ld_global<u32x4>(okc ? p + 16 * (c - rr * cpr) : a.q);
+            R[j] = ld_global<u32x4>(okc ? p + 16 * (c - rr * CPR) : a.q);
             okm |= okc ? 1u << j : 0u;
         }
     };
@@ -180,7 +145,6 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     for (int db = 0; db < NDB; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = a.scale * CSL_LOG2E;
-    const int nch_bf = FMT == KV_PACKED ? a.r / 8 : cpr;    // chunks stored as bf16
 
     if (ntiles > 0) {
         resolve(0);
@@ -189,28 +153,14 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     }
     for (int it = 0; it < ntiles; ++it) {
         lds_barrier();                                  // the previous tile's K/V reads are done
-        // ---- the prefetched chunks -> the padded compute-dtype K tile
+        // ---- the prefetched chunks -> the padded K tile
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int c = tid + ATT_NT * j;
-            if (c >= nch) continue;
-            const int rr = c / cpr, pc = c - rr * cpr;
+            if (c >= NCH) continue;
+            const int rr = c / CPR, pc = c - rr * CPR;
             const u32x4 v = ((okm >> j) & 1u) ? R[j] : u32x4{0, 0, 0, 0};
-            if constexpr (F32P) {
-                *(u32x4*)(kl + ((size_t)rr * KSTR + 4 * pc) * 4) = v;
-            } else if (FMT == BF16 || pc < nch_bf) {
-                *(u32x4*)(kl + ((size_t)rr * KSTR + 8 * pc) * 2) = v;
-            } else {
-                const int c8 = pc - nch_bf;
-                uint32_t c0, c1, c2, c3, c4, c5, c6, c7;
-                e4m3x4_to_bf16x4(v[0], c0, c1);
-                e4m3x4_to_bf16x4(v[1], c2, c3);
-                e4m3x4_to_bf16x4(v[2], c4, c5);
-                e4m3x4_to_bf16x4(v[3], c6, c7);
-                uint8_t* dst = kl + ((size_t)rr * KSTR + a.r + 16 * c8) * 2;
-                *(u32x4*)dst = u32x4{c0, c1, c2, c3};
-                *(u32x4*)(dst + 16) = u32x4{c4, c5, c6, c7};
-            }
+            *(u32x4*)(kl + (size_t)rr * KSTR + 4 * pc) = v;
         }
         if (it + 1 < ntiles) resolve(it + 1);
         lds_barrier();                                  // K tile and the next rows' pointers visible
@@ -218,28 +168,13 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         const uint32_t rmask = rowmask[it & 1];
         // ---- S^T = K Q^T: rows 16*r2 + 4g + i of head col, two independent MFMA chains
         v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-        if constexpr (F32P) {
-            const float* k0 = (const float*)kl + (size_t)col * KSTR + g;
+        {
+            const float* k0 = kl + (size_t)col * KSTR + g;
             const float* k1 = k0 + 16 * KSTR;
 #pragma unroll
             for (int ks = 0; ks < QKS; ++ks) {
                 s[0] = mfma_f32(k0[4 * ks], qf[ks], s[0]);
                 s[1] = mfma_f32(k1[4 * ks], qf[ks], s[1]);
-            }
-        } else {
-            const uint8_t* k0 = kl + ((size_t)col * KSTR + 8 * g) * 2;
-            const uint8_t* k1 = k0 + (size_t)16 * KSTR * 2;
-#pragma unroll
-            for (int ks = 0; ks < QR; ++ks) {
-                s[0] = mfma_bf16(*(const u32x4*)(k0 + 64 * ks), qb[ks], s[0]);
-                s[1] = mfma_bf16(*(const u32x4*)(k1 + 64 * ks), qb[ks], s[1]);
-            }
-            const uint16_t* qlp = ql_s + (wv * 16 + col) * QSTR + 8 * g;
-#pragma unroll
-            for (int ks = QR; ks < QKS; ++ks) {
-                const u32x4 qv = *(const u32x4*)(qlp + 32 * (ks - QR));
-                s[0] = mfma_bf16(*(const u32x4*)(k0 + 64 * ks), qv, s[0]);
-                s[1] = mfma_bf16(*(const u32x4*)(k1 + 64 * ks), qv, s[1]);
             }
         }
         // ---- online softmax (base 2) for head col over this tile's 32 rows, lazy rescale
@@ -261,17 +196,13 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
             m_run = mx;
         }
         float rs = 0.f;
-        u32x2 pb[2];
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
+        for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 x[r2][i] = m_run == -INFINITY ? 0.f : exp2f(x[r2][i] - m_run);
                 rs += x[r2][i];
             }
-            pb[r2] = u32x2{f32_to_bf16_rne(x[r2][0]) | (f32_to_bf16_rne(x[r2][1]) << 16),
-                           f32_to_bf16_rne(x[r2][2]) | (f32_to_bf16_rne(x[r2][3]) << 16)};
-        }
         l_run = l_run * corr + cross4_sum(rs);
         if (__builtin_amdgcn_read_exec() & __ballot(need)) {   // wave-uniform: some head rescaled
 #pragma unroll
@@ -281,28 +212,14 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
         }
         // ---- O^T += V^T P^T: P^T (rows x heads) is the S^T accumulator layout, so the
         //      probabilities never leave registers
-        if constexpr (F32P) {
-            const float* kf = (const float*)kl;
 #pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
+        for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float* vr = kf + (size_t)(16 * r2 + 4 * g + i) * KSTR + col;
+            for (int i = 0; i < 4; ++i) {
+                const float* vr = kl + (size_t)(16 * r2 + 4 * g + i) * KSTR + col;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) o[db] = mfma_f32(vr[16 * db], x[r2][i], o[db]);
-                }
-        } else {
-            // V^T fragments by the LDS transpose read: source lane 16g + s reads the four
-            // dims 16*db + 4*(s%4).. of row 16*r2 + 4g + s/4, so lane (g, col) receives
-            // dim 16*db + col of rows 16*r2 + 4g + 0..3
-            const uint16_t* kb = (const uint16_t*)kl;
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2) {
-                const uint16_t* vp = kb + (size_t)(16 * r2 + 4 * g + (col >> 2)) * KSTR + 4 * (col & 3);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] = mfma_bf16_k16(lds_read_tr16(vp + 16 * db), pb[r2], o[db]);
+                for (int db = 0; db < NDB; ++db) o[db] = mfma_f32(vr[16 * db], x[r2][i], o[db]);
             }
-        }
         // the next iteration starts with a barrier before the K tile is rewritten
     }
 
@@ -805,7 +722,7 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq));
     if (a.idx && a.rps > ATT_MAX_SIDX) return hipErrorInvalidValue;
     if constexpr (FMT == F32) {
-        hipLaunchKernelGGL((k_attend<D, FMT>), grid, dim3(ATT_NT), 0, s, a);
+        hipLaunchKernelGGL((k_attend<D>), grid, dim3(ATT_NT), 0, s, a);
     } else {
         hipLaunchKernelGGL((k_attend_mq<D, FMT>), grid, dim3(MQ_NT), 0, s, a);
     }

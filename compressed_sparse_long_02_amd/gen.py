@@ -92,6 +92,14 @@ def random_mxfp4(n_rows: int, d: int, seed: int, scale_lo: int = 124, scale_hi: 
     return codes, scales
 
 
+def random_e8m0(n_rows: int, ranges, seed: int, device="cpu") -> torch.Tensor:
+    """e8m0 block-scale codes [n_rows, len(ranges)]: block j uniform in ranges[j] = (lo, hi)."""
+    g = _gen(seed, device)
+    cols = [torch.randint(lo, hi + 1, (n_rows, 1), generator=g, device=device, dtype=torch.int32)
+            for lo, hi in ranges]
+    return torch.cat(cols, dim=1).to(torch.uint8)
+
+
 def random_logits(shape, seed: int, device="cpu") -> torch.Tensor:
     """Compression logits / biases: plain N(0,1) fp32."""
     return normal(shape, seed, 1.0, device)

@@ -55,13 +55,19 @@ _ws = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor | None:
-    """Per-device scratch tensor reused across calls on the same stream."""
+    """Scratch tensor for the current stream of `device`, reused by later calls on that
+    stream (which run after the previous call's kernels, so they may share it).  Calls on
+    different streams get different buffers, so they may run concurrently.  A buffer is
+    replaced only when a call needs more; it was allocated on that same stream, so the
+    caching allocator hands its memory out again only in that stream's order, after the
+    work already queued there."""
     if nbytes <= 0:
         return None
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     t = _ws.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+        t = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws[key] = t
     return t
 

@@ -73,6 +73,8 @@ def test_attend_rejects_bad_arguments_on_the_host():
     assert _attend(q_fmt=0) == _lib.CSL_EUNSUPPORTED                # f32 q with packed KV
     assert _attend(r=4) == _lib.CSL_EINVAL
     assert _attend(W=4, kv_w=None) == _lib.CSL_EINVAL
+    assert _attend(W=16, kvw_rows=10) == _lib.CSL_EINVAL              # ring shorter than the window
+    assert "below the window" in _lib.last_error()
     assert _attend(m=0) == _lib.CSL_EINVAL
     assert _attend(out=None) == _lib.CSL_EINVAL
     assert _attend(kvc_bstride=8) == _lib.CSL_EINVAL
@@ -110,3 +112,4 @@ def test_valid_call_without_gpu_reports_no_device():
         pass
     rc = _compress(x=16, n_tok=8)
     assert rc in (_lib.CSL_EDEVICE, _lib.CSL_EUNSUPPORTED)
+

@@ -5,15 +5,19 @@ the benchmark uses, checked against the oracle on sampled sequences / queries:
   compression of the completed entry (KV and MXFP4 indexer key), index_topk over
   262,144 MXFP4 keys with 64 heads and k = 1024, csa_attend and hca_attend;
 - CSA decode, batch 8, 131,072 tokens (32,768 entries), bf16 indexer 16 x 128, k = 512;
-- HCA decode, batch 4, 1M tokens (8,192 entries), every sequence checked;
+- HCA decode, batch 4, 1M tokens (8,192 entries);
 - CSA prefill chunk: 8,192 new tokens on 1M cached ones, compression of the chunk's
   2,048 entries, index_topk for all 8,192 queries (64 x 128 bf16 indexer, k = 1024) and
-  csa_attend with 128 heads; four queries (first, two inside, last) checked.
+  csa_attend with 128 heads; 128 evenly spaced queries checked, among them the first and
+  the last query of every pass of the many-query indexer.
+Every sequence of the decode batches is checked.
 
 Sources: x-techcon article, section 2 (CSA steps 1-3, HCA subsection, mixed-precision
 KV); the sizes are the workloads' stated ones.  Tolerances as in the other parity
-tests: max-abs 2e-2 on outputs, index sets equal up to swaps among entries whose
-oracle scores tie with the k-th within the fp32 accumulation bound."""
+tests: max-abs 2e-2 on outputs; index sets equal up to swaps among entries whose oracle
+scores tie with the k-th within max(1e-6 relative, twice the kernel's measured score
+error on that query), at most one query in 64 (plus one) with a swap; quantised entries
+equal except for a few elements one rounding step apart."""
 import math
 import os
 import sys
@@ -25,15 +29,15 @@ import torch
 import oracle as O
 from compressed_sparse_long_02_amd import gen, ops
 from tests import bruteforce as BF
-from tests.gpu_util import check_topk, dev, host, max_abs, oracle_all_scores, score_error_bound
+from tests.gpu_util import cap, check_topk, close_quantised, dev, host, max_abs, oracle_all_scores, score_error_bound
 
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _check_index(gi, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None):
-    """Index sets of the sampled queries against the oracle (ties within the bound)."""
+def _check_index(gi, gs, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None):
+    """Index sets and scores of the sampled queries against the oracle."""
     kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=n_cap)
     oq = dict(qi_scales=qi_scales, ki_scales=ki_scales)
     oi, _ = O.index_topk(qi, qfmt, w, ki, kfmt, qpos, k=k, **kw, **oq)
@@ -42,16 +46,9 @@ def _check_index(gi, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, qi_s
     dec_fmt = BF.MXFP4 if qfmt == O.MXFP4 else qfmt
     qd = BF.decode(qi, dec_fmt, d_I, scales=qi_scales).reshape(B, Tq, H_I, d_I)
     kd = BF.decode(ki, dec_fmt, d_I, scales=ki_scales).reshape(B, -1, d_I)
-    bound = np.stack([score_error_bound(qd[b], w[b].astype(np.float64), kd[b]) for b in range(B)])
-    return check_topk(gi, oi, allsc, k, abs_bound=bound)
-
-
-def _close_quantised(got, ref, fmt, d, r, got_sc=None, ref_sc=None, max_steps=2):
-    """Quantised rows from fp32 (GPU) and fp64 (oracle) arithmetic: equal except for at
-    most `max_steps` elements one rounding step apart (a value on a rounding boundary)."""
-    a = O.decode_rows(got, fmt, d, r, got_sc)
-    b = O.decode_rows(ref, fmt, d, r, ref_sc)
-    assert np.sum(a != b) <= max_steps, np.sum(a != b)
+    bound = np.stack([score_error_bound(qd[b], w[b].astype(np.float64), kd[min(b, kd.shape[0] - 1)])
+                      for b in range(B)])
+    return check_topk(gi, gs, oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
 
 
 # ---------------------------------------------------------------------------
@@ -69,7 +66,7 @@ def stack():
     torch.cuda.empty_cache()
 
 
-SAMPLE = [0, 11]
+SAMPLE = list(range(16))          # every sequence of the batch
 
 
 def test_stack_compress_of_the_completed_entries(gpu, stack):
@@ -80,25 +77,31 @@ def test_stack_compress_of_the_completed_entries(gpu, stack):
     i = (t + 1) // st.m - 1
     ref, _ = O.kv_compress(h(csa["raw"]), O.BF16, h(csa["z"]), host(csa["bias"]), d=st.d, r=st.r, m=st.m,
                            overlap=True, e_begin=i, n_e=1, x_pos0=t - csa["win"] + 1, out_fmt=O.KV_PACKED)
-    _close_quantised(h(csa["cache"][:, i:i + 1]), ref, O.KV_PACKED, st.d, st.r)
+    close_quantised(h(csa["cache"][:, i:i + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
     rk, rs = O.kv_compress(h(csa["raw_i"]), O.BF16, h(csa["z_i"]), host(csa["bias_i"]), d=st.dI, m=st.m,
                            overlap=True, e_begin=i, n_e=1, x_pos0=t - csa["win"] + 1, out_fmt=O.MXFP4)
-    _close_quantised(h(csa["keys"][:, i:i + 1]), rk, O.MXFP4, st.dI, 0, h(csa["kscales"][:, i:i + 1]), rs)
+    close_quantised(h(csa["keys"][:, i:i + 1]), rk, O.MXFP4, st.dI, 0, h(csa["kscales"][:, i:i + 1]), rs,
+                    max_mismatch=len(SAMPLE))
     ih = (t + 1) // st.mh - 1
     ref, _ = O.kv_compress(h(hca["raw"]), O.BF16, h(hca["z"]), host(hca["bias"]), d=st.d, r=st.r, m=st.mh,
                            overlap=False, e_begin=ih, n_e=1, x_pos0=t - hca["win"] + 1, out_fmt=O.KV_PACKED)
-    _close_quantised(h(hca["cache"][:, ih:ih + 1]), ref, O.KV_PACKED, st.d, st.r)
+    close_quantised(h(hca["cache"][:, ih:ih + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
 
 
 def test_stack_index_topk_1M_mxfp4(gpu, stack):
     st = stack
     csa = st.layers[0]
+    # the same call with scores: its indices must equal the step's (deterministic)
+    gi, gs = ops.index_topk(csa["qi"], csa["w"], csa["keys"], st.q_pos, fmt=O.MXFP4, H_I=st.HI, d_I=st.dI, m=st.m,
+                            n_cap=st.N, k=st.k, qi_scales=csa["qis"], ki_scales=csa["kscales"])
+    torch.cuda.synchronize()
+    assert torch.equal(gi, csa["idx"])
     h = lambda x: host(x[SAMPLE])
     qpos = np.full((len(SAMPLE), 1), st.t, np.int32)
-    n_sw, gap = _check_index(h(csa["idx"]), h(csa["qi"]), O.MXFP4, h(csa["w"]), h(csa["keys"]), O.MXFP4, qpos,
-                             H_I=st.HI, d_I=st.dI, m=st.m, n_cap=st.N, k=st.k, qi_scales=h(csa["qis"]),
-                             ki_scales=h(csa["kscales"]))
-    print("stack index: queries with tie swaps %d, largest gap %.3g" % (n_sw, gap))
+    stats = _check_index(h(gi), h(gs), h(csa["qi"]), O.MXFP4, h(csa["w"]), h(csa["keys"]), O.MXFP4, qpos,
+                         H_I=st.HI, d_I=st.dI, m=st.m, n_cap=st.N, k=st.k, qi_scales=h(csa["qis"]),
+                         ki_scales=h(csa["kscales"]))
+    print("stack index: %s" % stats)
 
 
 @pytest.mark.parametrize("kind", ["csa", "hca"])
@@ -144,18 +147,18 @@ def test_csa_decode_b8_128k(gpu):
     w = gen.normal((B, 1, HI), 2005, device="cuda")
     q = gen.normal((B, 1, H, d), 2006, device="cuda").to(torch.bfloat16)
     qpos = torch.full((B, 1), t, dtype=torch.int32, device="cuda")
-    gi, _ = ops.index_topk(qi, w, keys, qpos, fmt=O.BF16, H_I=HI, d_I=dI, m=m, n_cap=N, k=k)
+    gi, gs = ops.index_topk(qi, w, keys, qpos, fmt=O.BF16, H_I=HI, d_I=dI, m=m, n_cap=N, k=k)
     go, gl = ops.csa_attend(q, cache, gi, ring, qpos, kv_fmt=O.KV_PACKED, n_cap=N, kvw_pos0=0, kvw_rows=256, W=W,
                             H=H, d=d, r=r, scale=1 / math.sqrt(d))
     torch.cuda.synchronize()
-    s = [1, 6]
-    h = lambda x: host(x[s])
-    n_sw, gap = _check_index(h(gi), h(qi), O.BF16, h(w), h(keys), O.BF16, h(qpos), H_I=HI, d_I=dI, m=m, n_cap=N, k=k)
+    h = host                                       # every sequence
+    stats = _check_index(h(gi), h(gs), h(qi), O.BF16, h(w), h(keys), O.BF16, h(qpos), H_I=HI, d_I=dI, m=m,
+                         n_cap=N, k=k)
     oo, ol = O.csa_attend(h(q.view(torch.int16)), O.BF16, h(cache), O.KV_PACKED, N, h(gi), h(ring), 0, 256, h(qpos),
                           W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
     err = max_abs(h(go), oo)
     assert err <= 2e-2, err
-    print("csa decode b8 128k: swaps %d, max-abs %.3g" % (n_sw, err))
+    print("csa decode b8 128k: %s; max-abs %.3g" % (stats, err))
 
 
 # ---------------------------------------------------------------------------
@@ -214,26 +217,44 @@ def test_csa_prefill_chunk_8192_on_1m(gpu):
     qi = gen.store(gen.normal((1, C, HI, dI), 2408, device="cuda"), O.BF16)
     w = gen.normal((1, C, HI), 2409, device="cuda")
     q = gen.normal((1, C, H, d), 2410, device="cuda").to(torch.bfloat16)
-    gi, _ = ops.index_topk(qi, w, keys, qpos, fmt=O.BF16, H_I=HI, d_I=dI, m=m, n_cap=N, k=k)
+    gi, gs = ops.index_topk(qi, w, keys, qpos, fmt=O.BF16, H_I=HI, d_I=dI, m=m, n_cap=N, k=k)
     go, gl = ops.csa_attend(q, cache, gi, kvw, qpos, kv_fmt=O.KV_PACKED, n_cap=N, kvw_pos0=pos0, kvw_rows=W + C, W=W,
                             H=H, d=d, r=r, scale=1 / math.sqrt(d))
     torch.cuda.synchronize()
     # compression of the chunk: every new entry (KV and indexer key)
     ref, _ = O.kv_compress(host(xb), O.BF16, host(z), host(bias), d=d, r=r, m=m, overlap=True, e_begin=N0, n_e=ne,
                            x_pos0=T0 - m, out_fmt=O.KV_PACKED)
-    a = O.decode_rows(host(cache[:, N0:N]), O.KV_PACKED, d, r)
-    b = O.decode_rows(ref, O.KV_PACKED, d, r)
-    assert np.mean(a != b) < 1e-4
+    nbad = close_quantised(host(cache[:, N0:N]), ref, O.KV_PACKED, d, r, max_mismatch=ne * d // 10000)
     refk, _ = O.kv_compress(host(xib), O.BF16, host(zi), host(bias_i), d=dI, m=m, overlap=True, e_begin=N0, n_e=ne,
                             x_pos0=T0 - m, out_fmt=O.BF16)
-    assert np.mean(host(keys[:, N0:N]).reshape(-1) != refk.reshape(-1)) < 1e-3
-    # four sampled queries: index sets and attention outputs
-    sq = [0, 1000, 5555, C - 1]
+    nbadk = close_quantised(host(keys[:, N0:N]), refk, O.BF16, dI, max_mismatch=ne * dI // 1000)
+    # 128 evenly spaced queries, and the first and last query of every pass of the
+    # many-query indexer (passes of dense_pass_rows queries)
+    tc = dense_pass_rows(1, C, N)
+    edges = sorted({q for p0 in range(0, C, tc) for q in (p0, min(p0 + tc, C) - 1)})
+    sq = set(edges)
+    for n in range(128 - len(edges), 129):            # 128 distinct queries in all
+        sq = set(edges) | set(np.linspace(0, C - 1, n).astype(int).tolist())
+        if len(sq) >= 128:
+            break
+    sq = sorted(sq)
     hq = lambda x: host(x[:, sq])
-    n_sw, gap = _check_index(hq(gi), hq(qi), O.BF16, hq(w), host(keys), O.BF16, hq(qpos), H_I=HI, d_I=dI, m=m,
-                             n_cap=N, k=k)
+    stats = _check_index(hq(gi), hq(gs), hq(qi), O.BF16, hq(w), host(keys), O.BF16, hq(qpos), H_I=HI, d_I=dI, m=m,
+                         n_cap=N, k=k)
     oo, ol = O.csa_attend(hq(q.view(torch.int16)), O.BF16, host(cache), O.KV_PACKED, N, hq(gi), host(kvw), pos0,
                           W + C, hq(qpos), W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
     err = max_abs(hq(go), oo)
     assert err <= 2e-2, err
-    print("prefill chunk: swaps %d, max-abs %.3g" % (n_sw, err))
+    print("prefill chunk: %d queries checked (pass edges %s); compress mismatches %d + %d; index %s; max-abs %.3g"
+          % (len(sq), edges, nbad, nbadk, stats, err))
+
+
+def dense_pass_rows(B, Tq, n_cap):
+    """Queries per pass of the many-query indexer, as the library plans them: passes of a
+    multiple of 12 queries, as even as possible, each with at most 2 GiB of score rows
+    ((n_cap rounded up to 4) + 2048 histogram words per query)."""
+    per_q = B * (((n_cap + 3) & ~3) + 2048) * 4
+    cap_ = max(12, ((2 << 30) // per_q) // 12 * 12)
+    passes = (Tq + cap_ - 1) // cap_
+    tc = ((Tq + passes - 1) // passes + 11) // 12 * 12
+    return min(tc, cap_)

@@ -1,7 +1,9 @@
 """GPU parity of index_topk against the oracle (lightning indexer + top-k: x-techcon
 article, section 2, CSA step 2; FP4 indexer QK: the mixed-precision paragraph and
 section 4).  Index sets must match except for swaps between entries whose oracle
-scores tie with the k-th score within the fp32 accumulation bound."""
+scores tie with the k-th score within max(1e-6 relative, twice the kernel's measured score
+error on that query), the scores themselves within the fp32 accumulation bound, and at
+most one query in 64 (plus one) with any swap."""
 import math
 
 import numpy as np
@@ -11,7 +13,7 @@ import torch
 import oracle as O
 from compressed_sparse_long_02_amd import gen, ops
 from tests import bruteforce as BF
-from tests.gpu_util import check_topk, dev, host, oracle_all_scores, score_error_bound
+from tests.gpu_util import cap, check_topk, dev, host, oracle_all_scores, score_error_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -69,16 +71,8 @@ def test_index_topk_parity(gpu, case):
     oi, osc = O.index_topk(host(qi), fmt, host(w), host(ki), fmt, host(qpos), k=k, **kw, **oq)
     allsc = oracle_all_scores(host(qi), fmt, host(w), host(ki), fmt, host(qpos), **kw, **oq)
     bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
-    n_sw, gap = check_topk(host(gi), oi, allsc, k, abs_bound=bound)
-    # scores of the selected entries: fp32 vs fp64 within the accumulation bound
-    gi_h, gs_h = host(gi), host(gs)
-    for b in range(B):
-        for j in range(Tq):
-            v = gi_h[b, j] >= 0
-            ref = allsc[b, j, gi_h[b, j, v]]
-            assert np.all(np.abs(gs_h[b, j, v] - ref) <= bound[b, j] + 1e-6 * np.abs(ref)), (b, j)
-            assert np.all(np.isneginf(gs_h[b, j, ~v]))
-    print("case %s: queries with tie swaps %d, largest gap %.3g" % (case[0], n_sw, gap))
+    st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("case %s: %s" % (case[0], st))
 
 
 @pytest.mark.parametrize("N,k", [(3000, 100), (30000, 1024)])
@@ -110,7 +104,7 @@ def test_index_topk_clustered_scores_refine_the_threshold(gpu):
     qpos = gen.positions(B, Tq, 4 * N - 1)
     qs_, ks_ = gen.store(q, O.BF16), gen.store(keys, O.BF16)
     kw = dict(H_I=H_I, d_I=d_I, m=4, n_cap=N)
-    gi, _ = ops.index_topk(dev(qs_), dev(w), dev(ks_), dev(qpos), fmt=O.BF16, k=k, **kw)
+    gi, gs = ops.index_topk(dev(qs_), dev(w), dev(ks_), dev(qpos), fmt=O.BF16, k=k, **kw)
     torch.cuda.synchronize()
     oi, _ = O.index_topk(host(qs_), O.BF16, host(w), host(ks_), O.BF16, host(qpos), k=k, **kw)
     allsc = oracle_all_scores(host(qs_), O.BF16, host(w), host(ks_), O.BF16, host(qpos), **kw)
@@ -119,7 +113,8 @@ def test_index_topk_clustered_scores_refine_the_threshold(gpu):
     bound = np.stack([score_error_bound(qd[0], host(w)[0].astype(np.float64), kd[0])])
     s = np.sort(allsc[0, 0][np.isfinite(allsc[0, 0])])[::-1]
     assert s[-1] > 0.95 * s[0]                                # one narrow band of scores
-    check_topk(host(gi), oi, allsc, k, abs_bound=bound)
+    st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("clustered: %s" % st)
 
 
 def test_index_topk_filter_blocks_span_several_slices(gpu):
@@ -134,10 +129,10 @@ def test_index_topk_filter_blocks_span_several_slices(gpu):
     n_of = [N] * B
     n_of[1], n_of[2], n_of[3], n_of[4] = 17 * 16384 + 5, 2 * 16384, 700, 0
     qpos = torch.tensor([[n * m - 1 if n > 0 else 1] for n in n_of], dtype=torch.int32)   # n(t) = n
-    gi, _ = ops.index_topk(dev(qc), dev(w), kc, dev(qpos), fmt=O.MXFP4, H_I=H_I, d_I=d_I, m=m, n_cap=N, k=k,
-                           qi_scales=dev(qs), ki_scales=ks)
+    gi, gs = ops.index_topk(dev(qc), dev(w), kc, dev(qpos), fmt=O.MXFP4, H_I=H_I, d_I=d_I, m=m, n_cap=N, k=k,
+                            qi_scales=dev(qs), ki_scales=ks)
     torch.cuda.synchronize()
-    gi_h = host(gi)
+    gi_h, gs_h = host(gi), host(gs)
     assert np.all(gi_h[4, 0] == -1)
     assert np.array_equal(gi_h[3, 0, :700], np.arange(700)) and np.all(gi_h[3, 0, 700:] == -1)
     for b in (0, 1, 2):
@@ -149,7 +144,8 @@ def test_index_topk_filter_blocks_span_several_slices(gpu):
         qd = BF.decode(host(qc[sl]), BF.MXFP4, d_I, scales=host(qs[sl])).reshape(1, H_I, d_I)
         kd = BF.decode(host(kc[sl]), BF.MXFP4, d_I, scales=host(ks[sl])).reshape(N, d_I)
         bound = score_error_bound(qd, host(w[sl])[0].astype(np.float64), kd)
-        check_topk(gi_h[sl], oi, allsc, k, abs_bound=bound[None])
+        st = check_topk(gi_h[sl], gs_h[sl], oi, allsc, k, bound=bound[None], max_swapped=cap(1))
+        print("filter blocks, sequence %d: %s" % (b, st))
 
 
 def test_index_topk_is_deterministic(gpu):
@@ -189,15 +185,8 @@ def test_index_topk_many_queries(gpu, case):
     oi, _ = O.index_topk(host(qi), fmt, host(w), host(ki), fmt, host(qpos), k=k, **kw)
     allsc = oracle_all_scores(host(qi), fmt, host(w), host(ki), fmt, host(qpos), **kw)
     bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
-    n_sw, gap = check_topk(host(gi), oi, allsc, k, abs_bound=bound)
-    gi_h, gs_h = host(gi), host(gs)
-    for b in range(B):
-        for j in range(Tq):
-            v = gi_h[b, j] >= 0
-            ref = allsc[b, j, gi_h[b, j, v]]
-            assert np.all(np.abs(gs_h[b, j, v] - ref) <= bound[b, j] + 1e-6 * np.abs(ref)), (b, j)
-            assert np.all(np.isneginf(gs_h[b, j, ~v]))
-    print("case %s: queries with tie swaps %d, largest gap %.3g" % (case[0], n_sw, gap))
+    st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("case %s: %s" % (case[0], st))
 
 
 def test_index_topk_many_queries_all_tied(gpu):
@@ -228,13 +217,50 @@ def test_index_topk_many_queries_survivors_in_one_section(gpu, order):
     qi, ki = gen.store(q, O.BF16), gen.store(key, O.BF16)
     qpos = gen.positions(B, Tq, N * m - 1)
     kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
-    gi, _ = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=O.BF16, k=k, **kw)
+    gi, gs = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=O.BF16, k=k, **kw)
     torch.cuda.synchronize()
     oi, _ = O.index_topk(host(qi), O.BF16, host(w), host(ki), O.BF16, host(qpos), k=k, **kw)
     allsc = oracle_all_scores(host(qi), O.BF16, host(w), host(ki), O.BF16, host(qpos), **kw)
     qd = BF.decode(host(qi), O.BF16, d_I).reshape(B, Tq, H_I, d_I)
     kd = BF.decode(host(ki), O.BF16, d_I).reshape(B, N, d_I)
     bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
-    check_topk(host(gi), oi, allsc, k, abs_bound=bound)
+    st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("survivors %s: %s" % (order, st))
     sel = host(gi)[0]
     assert (sel.min(axis=1) > N // 2).all() if order == "rising" else (sel.max(axis=1) < N // 2).all()
+
+
+def test_index_topk_mxfp4_wide_block_scales(gpu):
+    # e8m0 block scales over almost the whole code range (0 .. 254), paired per block so
+    # that every product of a query scale and a key scale stays inside the fp32 range
+    # (2^-63 .. 2^63): blocks 0 / 1 put codes 0 .. 40 against 214 .. 254, blocks 2 / 3
+    # codes 64 .. 127 against 127 .. 190.  The scaled FP4 MFMA applies both scales of a
+    # block; the scores then span many binades, and the set must still match the oracle.
+    # (Inputs whose exact score leaves the fp32 range are outside the contract: the
+    # kernel accumulates in fp32.)
+    B, Tq, H_I, d_I, N, m, k = 2, 2, 64, 128, 20000, 4, 512
+    qc, _ = gen.random_mxfp4(B * Tq * H_I, d_I, 81)
+    kc, _ = gen.random_mxfp4(B * N, d_I, 82)
+    ranges_q = [(0, 40), (214, 254), (64, 127), (127, 190)]
+    ranges_k = [(214, 254), (0, 40), (127, 190), (64, 127)]
+    qs = gen.random_e8m0(B * Tq * H_I, ranges_q, 83)
+    ks = gen.random_e8m0(B * N, ranges_k, 84)
+    for want in (0, 254):                         # both end codes occur
+        assert (qs == want).any() and (ks == want).any()
+    qc, qs = qc.reshape(B, Tq, H_I, -1), qs.reshape(B, Tq, H_I, -1)
+    kc, ks = kc.reshape(B, N, -1), ks.reshape(B, N, -1)
+    w = gen.normal((B, Tq, H_I), 85, 1 / math.sqrt(H_I))
+    qpos = gen.positions(B, Tq, N * m - 1)
+    kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
+    gi, gs = ops.index_topk(dev(qc), dev(w), dev(kc), dev(qpos), fmt=O.MXFP4, k=k, qi_scales=dev(qs),
+                            ki_scales=dev(ks), **kw)
+    torch.cuda.synchronize()
+    oq = dict(qi_scales=host(qs), ki_scales=host(ks))
+    oi, _ = O.index_topk(host(qc), O.MXFP4, host(w), host(kc), O.MXFP4, host(qpos), k=k, **kw, **oq)
+    allsc = oracle_all_scores(host(qc), O.MXFP4, host(w), host(kc), O.MXFP4, host(qpos), **kw, **oq)
+    assert np.all(np.isfinite(host(gs)))
+    qd = BF.decode(host(qc), BF.MXFP4, d_I, scales=host(qs)).reshape(B, Tq, H_I, d_I)
+    kd = BF.decode(host(kc), BF.MXFP4, d_I, scales=host(ks)).reshape(B, N, d_I)
+    bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
+    st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("wide scales: %s" % st)
