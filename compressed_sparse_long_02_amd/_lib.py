@@ -15,8 +15,9 @@ LIB_PATH = os.path.join(HERE, "libcsl.so")
 CSL_OK, CSL_EINVAL, CSL_EUNSUPPORTED, CSL_EWORKSPACE, CSL_ELAUNCH, CSL_EDEVICE = 0, -1, -2, -3, -4, -5
 
 # every symbol include/csl.h declares
-EXPORTS = ["csl_row_bytes", "kv_compress", "index_topk", "csl_index_topk_workspace", "csa_attend", "hca_attend",
-           "csl_attend_workspace", "csl_status_string", "csl_last_error", "csl_version"]
+EXPORTS = ["csl_row_bytes", "kv_compress", "index_topk", "csl_index_topk_workspace", "index_topk_noalloc",
+           "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend", "csl_attend_workspace", "csl_status_string",
+           "csl_last_error", "csl_version"]
 
 
 class CslError(RuntimeError):
@@ -44,6 +45,11 @@ def lib() -> C.CDLL:
     L.index_topk.restype = i32
     L.index_topk.argtypes = [vp, i32, vp, vp, vp, i32, vp, i64, i64, vp, i32, i32, i32, i32, i32, i64, i32,
                              vp, vp, vp, sz, vp]
+    L.index_topk_noalloc.restype = i32
+    L.index_topk_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, vp, i64, i64, vp, i32, i32, i32, i32, i32, i64, i32,
+                                     vp, vp, vp]
+    L.csl_noalloc_scratch_bytes.restype = sz
+    L.csl_noalloc_scratch_bytes.argtypes = []
     L.csl_index_topk_workspace.restype = sz
     L.csl_index_topk_workspace.argtypes = [i32, i32, i64, i32]
     L.csa_attend.restype = i32

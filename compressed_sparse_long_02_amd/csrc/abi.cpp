@@ -12,6 +12,14 @@
 #include "csl.h"
 #include "launch.h"
 
+// Scratch of index_topk_noalloc (for callers that cannot allocate): a file-scope device
+// array, so each GPU the library runs on holds its own copy from the time the code
+// object is loaded there until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in): it looks up each device's
+// address once with hipGetSymbolAddress and passes that.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -44,6 +52,26 @@ int check_device() {
         g_dev_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     }
     if (g_dev_ok[dev] < 0) return fail(CSL_EUNSUPPORTED, "device %d is not a gfx950 (MI355X)", dev);
+    return CSL_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first call made
+// with that device current and kept per device.
+std::mutex g_scr_mu;
+void* g_scr_ptr[64];
+
+int scratch_ptr(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(CSL_EDEVICE, "no usable HIP device is current");
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if (!g_scr_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CSL_ELAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        g_scr_ptr[dev] = p;
+    }
+    *out = g_scr_ptr[dev];
     return CSL_OK;
 }
 
@@ -257,10 +285,12 @@ size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
 
 }  // extern "C"
 
+// index_topk with a caller workspace (use_scratch false) or with the library's static
+// scratch (use_scratch true, index_topk_noalloc).
 static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
                       const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
-                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
     if (B < 0 || Tq < 0 || n_cap < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
     if (B > 65535 || Tq > 65535) return fail(CSL_EUNSUPPORTED, "%s: B and Tq must be <= 65535", fn);
     if (m < 1) return fail(CSL_EINVAL, "%s: m must be >= 1", fn);
@@ -282,10 +312,20 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
         return fail(CSL_EINVAL, "%s: scale arrays must be given exactly for MXFP4", fn);
     if (!al16(qi) || !al16(ki) || (ki_bstride & 15) || !al4(w) || !al4(q_pos) || !al4(out_idx) || !al4(out_score))
         return fail(CSL_EINVAL, "%s: misaligned pointer or stride", fn);
-    if (need > 0 && (!ws || ws_bytes < need || !al16(ws)))
+    if (use_scratch) {
+        if (need > NOALLOC_SCRATCH_BYTES)
+            return fail(CSL_EWORKSPACE, "%s: this call needs %zu bytes of scratch, more than the %zu bytes the library "
+                        "holds (use index_topk with a workspace)", fn, need, NOALLOC_SCRATCH_BYTES);
+    } else if (need > 0 && (!ws || ws_bytes < need || !al16(ws))) {
         return fail(CSL_EWORKSPACE, "%s: needs %zu bytes of 16-byte aligned workspace", fn, need);
+    }
     int rc = check_device();
     if (rc) return rc;
+    if (use_scratch && need > 0) {
+        rc = scratch_ptr(&ws);
+        if (rc) return rc;
+        ws_bytes = NOALLOC_SCRATCH_BYTES;
+    }
     csl::IndexArgs a{};
     a.qi = (const uint8_t*)qi; a.qi_fmt = qi_fmt; a.qi_scales = qi_scales; a.w = w;
     a.ki = (const uint8_t*)ki; a.ki_fmt = ki_fmt; a.ki_scales = ki_scales; a.ki_bstride = ki_bstride; a.ks_bstride = ks_bstride;
@@ -320,8 +360,18 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
                const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
                int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
     return index_impl("index_topk", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride, q_pos,
-                      B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, ws, ws_bytes, stream);
+                      B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, ws, ws_bytes, false, stream);
 }
+
+int index_topk_noalloc(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                       const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                       int32_t* out_idx, float* out_score, void* stream) {
+    return index_impl("index_topk_noalloc", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride,
+                      q_pos, B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, nullptr, 0, true, stream);
+}
+
+size_t csl_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max) {
     if (B < 0 || Tq < 0 || H < 1) return 0;

@@ -123,6 +123,26 @@ def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, 
     return out_idx, out_score
 
 
+def index_topk_noalloc(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None,
+                       out_idx, out_score=None):
+    """index_topk through the entry point that allocates nothing: the caller passes the
+    outputs (idx int32 [B, Tq, k], scores float32 [B, Tq, k] or None); the staging lives
+    in the library's static device scratch."""
+    _need_cuda(qi, w, ki, q_pos, qi_scales, ki_scales, out_idx, out_score)
+    B, Tq = q_pos.shape
+    if q_pos.dtype != torch.int32 or not q_pos.is_contiguous():
+        raise ValueError("q_pos must be contiguous int32 [B, Tq]")
+    if not qi.is_contiguous() or not w.is_contiguous() or w.dtype != torch.float32:
+        raise ValueError("qi and w must be contiguous (w float32)")
+    _rows_ok(ki, row_bytes(fmt, d_I), "ki")
+    rc = _lib.lib().index_topk_noalloc(_ptr(qi), fmt, _ptr(qi_scales), _ptr(w), _ptr(ki), fmt, _ptr(ki_scales),
+                                       _bstride(ki), _bstride(ki_scales) if ki_scales is not None else 0,
+                                       _ptr(q_pos), B, Tq, H_I, d_I, m, n_cap, k, _ptr(out_idx), _ptr(out_score),
+                                       _stream())
+    check("index_topk_noalloc", rc)
+    return out_idx, out_score
+
+
 def _q_fmt(q):
     if q.dtype == torch.float32:
         return F32

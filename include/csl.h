@@ -132,6 +132,28 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
 size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
 
 /*
+ * index_topk_noalloc -- index_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results as index_topk, without the workspace
+ * arguments.  The staging it needs lives in a static device array of the library,
+ * csl_noalloc_scratch_bytes() bytes (64 MiB) on every GPU the library runs on, held
+ * until the process ends.  A call whose staging would exceed it (the
+ * csl_index_topk_workspace figure of the same sizes, e.g. more than about 5.3 million
+ * (query, entry) pairs per call when entries span several scoring blocks, or a
+ * many-query prefill call) returns CSL_EWORKSPACE and launches nothing.  No call
+ * allocates or frees memory.  All calls on one GPU share that array: calls that may
+ * overlap in time on one GPU (different streams, or graphs replayed concurrently) race
+ * and must be serialised by the caller.  Nothing in the array has to start at zero.
+ */
+int index_topk_noalloc(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                       const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                       int32_t* out_idx, float* out_score, void* stream);
+
+/* Bytes of the static scratch index_topk_noalloc uses on each GPU. */
+size_t csl_noalloc_scratch_bytes(void);
+
+/*
  * csa_attend -- CSA attention ([X] section 2, CSA step 3): shared-KV MQA of each
  * query over the selected compressed entries and its sliding window, in ONE
  * softmax:  S(t) = {idx[b,j,u] : 0 <= idx < n_cap} U {window positions

@@ -113,3 +113,11 @@ def test_valid_call_without_gpu_reports_no_device():
     rc = _compress(x=16, n_tok=8)
     assert rc in (_lib.CSL_EDEVICE, _lib.CSL_EUNSUPPORTED)
 
+
+def test_noalloc_refuses_oversized_calls_on_the_host():
+    L = _lib.lib()
+    assert L.csl_noalloc_scratch_bytes() == 64 << 20
+    # 16 queries x 4M entries would stage ~800 MB: refused before any device work
+    rc = L.index_topk_noalloc(16, 3, 16, 16, 16, 3, 16, 0, 0, 16, 16, 1, 64, 128, 4, 1 << 22, 1024, 16, None, None)
+    assert rc == _lib.CSL_EWORKSPACE
+    assert "scratch" in _lib.last_error()
