@@ -65,16 +65,23 @@ def lib():
         L.orc_encode_rows.restype = None
         L.orc_encode_rows.argtypes = [vp, i32, i32, i32, i64, vp, vp]
         L.orc_kv_compress.restype = i32
-        L.orc_kv_compress.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp,
+        L.orc_kv_compress.argtypes = [vp, i32, i64, i64, i64, i64, i32, vp, i32, i64, vp,
                                       i32, i32, i32, i32, i32, i64, i64, vp, i32, vp, i64, i64]
+        L.orc_kv_compress_step.restype = i32
+        L.orc_kv_compress_step.argtypes = [vp, i32, i64, i64, i32, vp, i32, i64, vp, vp, i32, i32, i32, i32, i32,
+                                           i32, vp, i32, vp, vp]
+        L.orc_paged_gather.restype = None
+        L.orc_paged_gather.argtypes = [vp, i64, vp, i64, i32, i64, i32, i64, vp, i64]
+        L.orc_grouped_out_proj.restype = i32
+        L.orc_grouped_out_proj.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, vp]
         L.orc_index_topk.restype = i32
         L.orc_index_topk.argtypes = [vp, i32, vp, vp, vp, i32, vp, i64, i64,
                                      vp, i32, i32, i32, i32, i32, i64, i32, vp, vp]
         L.orc_csa_attend.restype = i32
-        L.orc_csa_attend.argtypes = [vp, i32, vp, i32, i64, i64, vp, i32, vp, i64, i64, i64,
+        L.orc_csa_attend.argtypes = [vp, i32, vp, i32, i64, i64, vp, i32, vp, i64, i64, i64, vp,
                                      vp, i32, i32, i32, i32, i32, i32, f64, vp, i32, vp]
         L.orc_hca_attend.restype = i32
-        L.orc_hca_attend.argtypes = [vp, i32, vp, i32, i64, i64, i32, vp, i64, i64, i64,
+        L.orc_hca_attend.argtypes = [vp, i32, vp, i32, i64, i64, i32, vp, i64, i64, i64, vp,
                                      vp, i32, i32, i32, i32, i32, i32, f64, vp, i32, vp]
         L.orc_num_threads.restype = i32
         L.orc_num_threads.argtypes = []
@@ -154,10 +161,12 @@ def mx_block_exponent(amax: float) -> int:
 
 # ---- the four operations ------------------------------------------------------
 
-def kv_compress(x, x_fmt, z, bias, *, d, r=0, m, overlap, e_begin, n_e, x_pos0=0, out_fmt=F32):
-    """x: per-sequence raw rows [B, n_tok, rowbytes] (uint8 view) or f32 [B, n_tok, d];
-    z: f32 [B, n_tok, z_ch]; bias: f32 [win, z_ch].  Returns (out [B, n_e, rowbytes]
-    uint8 (f32 [B, n_e, d] for F32), scales [B, n_e, d/32] or None)."""
+def kv_compress(x, x_fmt, z, bias, *, d, r=0, m, overlap, e_begin, n_e, x_pos0=0, out_fmt=F32, x_rows=0, x_roles=1):
+    """x: per-sequence raw rows [B, n_tok, rowbytes] (uint8 view) or f32 [B, n_tok, x_roles*d];
+    z: f32 [B, n_tok, z_ch]; bias: f32 [win, z_ch].  x_rows > 0: x and z are rings of
+    x_rows rows (position p in row (p - x_pos0) mod x_rows).  x_roles = 2: two-role rows
+    (look-back value, then current value).  Returns (out [B, n_e, rowbytes] uint8 (f32
+    [B, n_e, d] for F32), scales [B, n_e, d/32] or None)."""
     B, n_tok = x.shape[0], x.shape[1]
     xb = np.ascontiguousarray(x).view(np.uint8).reshape(B, -1)
     zz = _c(z, np.float32).reshape(B, n_tok, -1)
@@ -166,14 +175,63 @@ def kv_compress(x, x_fmt, z, bias, *, d, r=0, m, overlap, e_begin, n_e, x_pos0=0
     orb = row_bytes(out_fmt, d, r)
     out = np.zeros((B, max(n_e, 0), orb), np.uint8)
     sc = np.zeros((B, max(n_e, 0), d // 32), np.uint8) if out_fmt == MXFP4 else None
-    rc = lib().orc_kv_compress(_p(xb), x_fmt, xb.shape[1], x_pos0, n_tok, _p(zz), z_ch, zz[0].nbytes if B else 0,
-                               _p(bb), B, d, r, m, int(bool(overlap)), e_begin, n_e, _p(out), out_fmt, _p(sc),
-                               out.shape[1] * orb, 0 if sc is None else sc.shape[1] * (d // 32))
+    rc = lib().orc_kv_compress(_p(xb), x_fmt, xb.shape[1], x_pos0, n_tok, x_rows, x_roles, _p(zz), z_ch,
+                               zz[0].nbytes if B else 0, _p(bb), B, d, r, m, int(bool(overlap)), e_begin, n_e, _p(out),
+                               out_fmt, _p(sc), out.shape[1] * orb, 0 if sc is None else sc.shape[1] * (d // 32))
     if rc != 0:
         raise ValueError("orc_kv_compress rejected its arguments (%d)" % rc)
     if out_fmt == F32:
         return out.view(np.float32).reshape(B, max(n_e, 0), d), None
     return out, sc
+
+
+def kv_compress_step(x, x_fmt, z, bias, pos, *, d, r=0, m, overlap, out_fmt=F32, x_roles=1):
+    """Decode-time compression from rings: x [B, x_rows, rowbytes] / f32, z [B, x_rows, z_ch]
+    (position p in row p mod x_rows); pos int32 [B, T] new token positions.  Returns (out
+    [B, T, rowbytes] (f32 [B, T, d]), scales [B, T, d/32] or None, entry int32 [B, T]):
+    the entry a token completes (or -1) and its compressed row."""
+    B, x_rows = x.shape[0], x.shape[1]
+    xb = np.ascontiguousarray(x).view(np.uint8).reshape(B, -1)
+    zz = _c(z, np.float32).reshape(B, x_rows, -1)
+    pp = _c(pos, np.int32)
+    T = pp.shape[1]
+    orb = row_bytes(out_fmt, d, r)
+    out = np.zeros((B, T, orb), np.uint8)
+    sc = np.zeros((B, T, d // 32), np.uint8) if out_fmt == MXFP4 else None
+    ent = np.zeros((B, T), np.int32)
+    rc = lib().orc_kv_compress_step(_p(xb), x_fmt, xb.shape[1], x_rows, x_roles, _p(zz), zz.shape[2],
+                                    zz[0].nbytes if B else 0, _p(_c(bias, np.float32)), _p(pp), B, T, d, r, m,
+                                    int(bool(overlap)), _p(out), out_fmt, _p(sc), _p(ent))
+    if rc != 0:
+        raise ValueError("orc_kv_compress_step rejected its arguments (%d)" % rc)
+    if out_fmt == F32:
+        return out.view(np.float32).reshape(B, T, d), None, ent
+    return out, sc, ent
+
+
+def paged_gather(pool, row_bytes_, block_table, entries_per_block, block_bytes, n):
+    """Rows 0..n-1 of every sequence of a paged pool (uint8 bytes), through the block table
+    int32 [B, max_blocks]: uint8 [B, n, row_bytes_] (zero rows for negative block ids)."""
+    pb = np.ascontiguousarray(pool).view(np.uint8).reshape(-1)
+    bt = _c(block_table, np.int32)
+    B = bt.shape[0]
+    out = np.zeros((B, n, row_bytes_), np.uint8)
+    lib().orc_paged_gather(_p(pb), row_bytes_, _p(bt), bt.shape[1], entries_per_block, block_bytes, B, n, _p(out),
+                           n * row_bytes_)
+    return out
+
+
+def grouped_out_proj(x, x_fmt, w, w_fmt, *, G, K, R):
+    """x: M rows of G*K values (f32, or bf16 bits as uint16/int16); w: [G, R, K] (f32 or bf16
+    bits).  Returns f32 [M, G*R]: group g's outputs = x[:, gK:(g+1)K] @ w[g].T."""
+    xb = np.ascontiguousarray(x).view(np.uint8).reshape(-1)
+    wb = np.ascontiguousarray(w).view(np.uint8).reshape(-1)
+    M = xb.size // row_bytes(x_fmt, G * K)
+    out = np.zeros((M, G * R), np.float32)
+    rc = lib().orc_grouped_out_proj(_p(xb), x_fmt, _p(wb), w_fmt, M, G, K, R, _p(out))
+    if rc != 0:
+        raise ValueError("orc_grouped_out_proj rejected its arguments (%d)" % rc)
+    return out
 
 
 def index_topk(qi, qi_fmt, w, ki, ki_fmt, q_pos, *, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None):
@@ -198,7 +256,7 @@ def index_topk(qi, qi_fmt, w, ki, ki_fmt, q_pos, *, H_I, d_I, m, n_cap, k, qi_sc
 
 
 def _attend(kind, q, q_fmt, kv_c, kv_fmt, n_cap, kv_w, kvw_pos0, kvw_rows, q_pos, *, W, H, d, r, scale,
-            idx=None, m=1, out_fmt=F32):
+            idx=None, m=1, out_fmt=F32, sink=None):
     qp = _c(q_pos, np.int32)
     B, Tq = qp.shape
     qb = np.ascontiguousarray(q).view(np.uint8).reshape(-1)
@@ -206,28 +264,31 @@ def _attend(kind, q, q_fmt, kv_c, kv_fmt, n_cap, kv_w, kvw_pos0, kvw_rows, q_pos
     wb = np.ascontiguousarray(kv_w).view(np.uint8).reshape(B, -1)
     out = np.zeros((B, Tq, H, d), np.float32 if out_fmt == F32 else np.uint16)
     lse = np.zeros((B, Tq, H), np.float32)
+    sk = _c(sink, np.float32)
     if kind == "csa":
         ix = _c(idx, np.int32)
         k = ix.shape[-1]
         rc = lib().orc_csa_attend(_p(qb), q_fmt, _p(cb), kv_fmt, cb.shape[1], n_cap, _p(ix), k, _p(wb), wb.shape[1],
-                                  kvw_pos0, kvw_rows, _p(qp), W, B, Tq, H, d, r, scale, _p(out), out_fmt, _p(lse))
+                                  kvw_pos0, kvw_rows, _p(sk), _p(qp), W, B, Tq, H, d, r, scale, _p(out), out_fmt,
+                                  _p(lse))
     else:
         rc = lib().orc_hca_attend(_p(qb), q_fmt, _p(cb), kv_fmt, cb.shape[1], n_cap, m, _p(wb), wb.shape[1],
-                                  kvw_pos0, kvw_rows, _p(qp), W, B, Tq, H, d, r, scale, _p(out), out_fmt, _p(lse))
+                                  kvw_pos0, kvw_rows, _p(sk), _p(qp), W, B, Tq, H, d, r, scale, _p(out), out_fmt,
+                                  _p(lse))
     if rc != 0:
         raise ValueError("oracle attend rejected its arguments (%d)" % rc)
     return out, lse
 
 
 def csa_attend(q, q_fmt, kv_c, kv_fmt, n_cap, idx, kv_w, kvw_pos0, kvw_rows, q_pos, *, W, H, d, r=0, scale,
-               out_fmt=F32):
+               out_fmt=F32, sink=None):
     """q: [B,Tq,H,d] (f32 or bf16 bits); kv_c: [B, N, rowbytes]; idx int32 [B,Tq,k];
-    kv_w: [B, kvw_rows, rowbytes]; returns (out [B,Tq,H,d], lse [B,Tq,H])."""
+    kv_w: [B, kvw_rows, rowbytes]; sink: f32 [H] or None; returns (out [B,Tq,H,d], lse [B,Tq,H])."""
     return _attend("csa", q, q_fmt, kv_c, kv_fmt, n_cap, kv_w, kvw_pos0, kvw_rows, q_pos, W=W, H=H, d=d, r=r,
-                   scale=scale, idx=idx, out_fmt=out_fmt)
+                   scale=scale, idx=idx, out_fmt=out_fmt, sink=sink)
 
 
 def hca_attend(q, q_fmt, kv_c, kv_fmt, n_cap, m, kv_w, kvw_pos0, kvw_rows, q_pos, *, W, H, d, r=0, scale,
-               out_fmt=F32):
+               out_fmt=F32, sink=None):
     return _attend("hca", q, q_fmt, kv_c, kv_fmt, n_cap, kv_w, kvw_pos0, kvw_rows, q_pos, W=W, H=H, d=d, r=r,
-                   scale=scale, m=m, out_fmt=out_fmt)
+                   scale=scale, m=m, out_fmt=out_fmt, sink=sink)

@@ -35,7 +35,22 @@
  *    t-W+1..t}; key = value = the stored row; logits = scale * q.v;
  *  - MXFP4: e2m1 codes, one e8m0 scale per 32 contiguous elements, scale = the
  *    smallest power of two with 6*2^e >= block max (no clipping), codes by
- *    round-to-nearest-even, low nibble = even element.
+ *    round-to-nearest-even, low nibble = even element;
+ *  - attention sink ([C] table of attention details, "Attention Sink": a head may
+ *    attend to nothing): one extra logit per head that joins the softmax's
+ *    denominator and carries no value;
+ *  - grouped output projection ([X] HCA subsection; [C] "Grouped Output
+ *    Projection": heads are projected group by group before one common output
+ *    projection): group g of G maps the concatenated outputs of its H/G heads
+ *    through its own matrix;
+ *  - two-role values (an alternative compressor input suggested by [B] section 4.2,
+ *    whose projection emits 2*head_dim per token): with overlapping windows a raw
+ *    row may carry two value vectors, the first used when the row sits in the
+ *    look-back half of a window, the second in the current half;
+ *  - two-tier cache ([X] section 4, KV-cache paragraph; [C] KV-cache section):
+ *    raw rows and window rows live in a ring (position p in slot p mod rows),
+ *    compressed entries in fixed blocks reached through a per-sequence block
+ *    table (entry s in block table[s / entries_per_block], row s % entries_per_block).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -259,68 +274,147 @@ void orc_encode_rows(const double* v, int fmt, int d, int r, int64_t n, uint8_t*
  *   win = overlap ? 2m : m;  p_j = (i+1)m - win + j,  j = 0..win-1,  valid iff p_j >= 0
  *   a_j,c  = z[p_j, c] + bias[j, c]                (learned weight + position bias)
  *   w_j,c  = exp(a_j,c) / sum_{valid j'} exp(a_j',c)
- *   e_i[c'] = sum_{valid j} w_{j, c(c')} * x[p_j, c'],  c(c') = 0 if z_ch == 1 else c'
- * Raw row p of sequence b sits at x + b*x_bstride + (p - x_pos0)*rowbytes; its
- * logits at z + b*z_bstride + (p - x_pos0)*z_ch*4 (bytes).  Entry e_begin+q is
- * written at out + b*out_bstride + q*rowbytes(out_fmt) (scales: out_scales +
- * b*sc_bstride + q*d/32).
+ *   e_i[c'] = sum_{valid j} w_{j, c(c')} * v_j[c'],  c(c') = 0 if z_ch == 1 else c'
+ * v_j is the raw row of position p_j; with x_roles == 2 (overlap only) a raw row holds
+ * 2d values and v_j is its first half for the look-back slots j < m, its second half
+ * for the current slots j >= m.
+ * Raw row p of sequence b: linear buffer (x_rows == 0) at x + b*x_bstride +
+ * (p - x_pos0)*rowbytes; ring (x_rows > 0) at slot ((p - x_pos0) mod x_rows).  Its
+ * logits sit at the same row of z (z_ch floats per row, z_bstride bytes per sequence).
  */
-int orc_kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
-                    const float* z, int z_ch, int64_t z_bstride, const float* bias,
+static const uint8_t* ring_or_linear(const uint8_t* base, int64_t pos0, int64_t rows, int64_t rb, int64_t p)
+{
+    int64_t s = p - pos0;
+    if (rows > 0) { s %= rows; if (s < 0) s += rows; }
+    return base + s * rb;
+}
+
+static void compress_entry(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t x_rows, int x_roles,
+                           const float* z, int z_ch, int64_t z_bstride, const float* bias,
+                           int b, int d, int r, int m, int overlap, int64_t i, int out_fmt, uint8_t* o, uint8_t* sc)
+{
+    const int win = overlap ? 2 * m : m;
+    const int64_t xrb = orc_row_bytes(x_fmt, x_roles * d, 0);
+    double* rows = (double*)malloc(sizeof(double) * (size_t)win * x_roles * d);
+    double* wgt = (double*)malloc(sizeof(double) * (size_t)win * z_ch);
+    int* valid = (int*)malloc(sizeof(int) * (size_t)win);
+    double* e = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int j = 0; j < win; ++j) {
+        int64_t p = (i + 1) * m - win + j;
+        valid[j] = p >= 0;
+        if (!valid[j]) continue;
+        const uint8_t* xr = ring_or_linear((const uint8_t*)x + b * x_bstride, x_pos0, x_rows, xrb, p);
+        decode_row(xr, NULL, x_fmt, x_roles * d, r, rows + (size_t)j * x_roles * d);
+        const float* zr = (const float*)ring_or_linear((const uint8_t*)z + b * z_bstride, x_pos0, x_rows,
+                                                       4 * (int64_t)z_ch, p);
+        for (int c = 0; c < z_ch; ++c) wgt[(size_t)j * z_ch + c] = (double)zr[c] + (double)bias[j * z_ch + c];
+    }
+    /* softmax over the valid window positions, per weight channel */
+    for (int c = 0; c < z_ch; ++c) {
+        double mx = -INFINITY, den = 0.0;
+        for (int j = 0; j < win; ++j) if (valid[j] && wgt[(size_t)j * z_ch + c] > mx) mx = wgt[(size_t)j * z_ch + c];
+        for (int j = 0; j < win; ++j) if (valid[j]) den += exp(wgt[(size_t)j * z_ch + c] - mx);
+        for (int j = 0; j < win; ++j)
+            wgt[(size_t)j * z_ch + c] = valid[j] ? exp(wgt[(size_t)j * z_ch + c] - mx) / den : 0.0;
+    }
+    for (int cc = 0; cc < d; ++cc) {
+        double acc = 0.0;
+        int c = (z_ch == 1) ? 0 : cc;
+        for (int j = 0; j < win; ++j) {
+            if (!valid[j]) continue;
+            const int half = (x_roles == 2 && j >= m) ? d : 0;   /* which value of a two-role row */
+            acc += wgt[(size_t)j * z_ch + c] * rows[(size_t)j * x_roles * d + half + cc];
+        }
+        e[cc] = acc;
+    }
+    encode_row(e, out_fmt, d, r, o, sc);
+    free(rows); free(wgt); free(valid); free(e);
+}
+
+static int compress_args_ok(int x_fmt, int x_roles, int overlap, int d, int m, int z_ch)
+{
+    if (d <= 0 || m <= 0 || (z_ch != 1 && z_ch != d)) return 0;
+    if (x_fmt != ORC_F32 && x_fmt != ORC_BF16) return 0;
+    if (x_roles != 1 && x_roles != 2) return 0;
+    if (x_roles == 2 && !overlap) return 0;
+    return 1;
+}
+
+/* Entries e_begin .. e_begin+n_e-1 of every sequence; entry e_begin+q is written at
+ * out + b*out_bstride + q*rowbytes(out_fmt) (scales: out_scales + b*sc_bstride +
+ * q*d/32).  A linear raw buffer must hold every valid window position. */
+int orc_kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t n_tok, int64_t x_rows,
+                    int x_roles, const float* z, int z_ch, int64_t z_bstride, const float* bias,
                     int B, int d, int r, int m, int overlap, int64_t e_begin, int64_t n_e,
                     void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride)
 {
-    if (B < 0 || d <= 0 || m <= 0 || n_e < 0 || (z_ch != 1 && z_ch != d)) return ORC_EINVAL;
-    if (x_fmt != ORC_F32 && x_fmt != ORC_BF16) return ORC_EINVAL;
+    if (B < 0 || n_e < 0 || !compress_args_ok(x_fmt, x_roles, overlap, d, m, z_ch)) return ORC_EINVAL;
     const int win = overlap ? 2 * m : m;
-    const int64_t xrb = orc_row_bytes(x_fmt, d, r), orb = orc_row_bytes(out_fmt, d, r);
-    /* every valid window position must be present in the raw buffer */
-    for (int64_t q = 0; q < n_e; ++q) {
-        int64_t i = e_begin + q;
-        for (int j = 0; j < win; ++j) {
-            int64_t p = (i + 1) * m - win + j;
-            if (p >= 0 && (p < x_pos0 || p >= x_pos0 + n_tok)) return ORC_EINVAL;
+    const int64_t orb = orc_row_bytes(out_fmt, d, r);
+    if (x_rows <= 0) {
+        /* every valid window position must be present in the linear raw buffer */
+        for (int64_t q = 0; q < n_e; ++q) {
+            int64_t i = e_begin + q;
+            for (int j = 0; j < win; ++j) {
+                int64_t p = (i + 1) * m - win + j;
+                if (p >= 0 && (p < x_pos0 || p >= x_pos0 + n_tok)) return ORC_EINVAL;
+            }
         }
     }
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b) {
         for (int64_t q = 0; q < n_e; ++q) {
-            const int64_t i = e_begin + q;
-            double* rows = (double*)malloc(sizeof(double) * (size_t)win * d);
-            double* wgt = (double*)malloc(sizeof(double) * (size_t)win * z_ch);
-            int* valid = (int*)malloc(sizeof(int) * (size_t)win);
-            double* e = (double*)malloc(sizeof(double) * (size_t)d);
-            for (int j = 0; j < win; ++j) {
-                int64_t p = (i + 1) * m - win + j;
-                valid[j] = p >= 0;
-                if (!valid[j]) continue;
-                const uint8_t* xr = (const uint8_t*)x + b * x_bstride + (p - x_pos0) * xrb;
-                decode_row(xr, NULL, x_fmt, d, r, rows + (size_t)j * d);
-                const float* zr = (const float*)((const uint8_t*)z + b * z_bstride) + (p - x_pos0) * z_ch;
-                for (int c = 0; c < z_ch; ++c) wgt[(size_t)j * z_ch + c] = (double)zr[c] + (double)bias[j * z_ch + c];
-            }
-            /* softmax over the valid window positions, per weight channel */
-            for (int c = 0; c < z_ch; ++c) {
-                double mx = -INFINITY, den = 0.0;
-                for (int j = 0; j < win; ++j) if (valid[j] && wgt[(size_t)j * z_ch + c] > mx) mx = wgt[(size_t)j * z_ch + c];
-                for (int j = 0; j < win; ++j) if (valid[j]) den += exp(wgt[(size_t)j * z_ch + c] - mx);
-                for (int j = 0; j < win; ++j)
-                    wgt[(size_t)j * z_ch + c] = valid[j] ? exp(wgt[(size_t)j * z_ch + c] - mx) / den : 0.0;
-            }
-            for (int cc = 0; cc < d; ++cc) {
-                double acc = 0.0;
-                int c = (z_ch == 1) ? 0 : cc;
-                for (int j = 0; j < win; ++j)
-                    if (valid[j]) acc += wgt[(size_t)j * z_ch + c] * rows[(size_t)j * d + cc];
-                e[cc] = acc;
-            }
             uint8_t* o = (uint8_t*)out + b * out_bstride + q * orb;
-            uint8_t* s = out_scales ? out_scales + b * sc_bstride + q * (d / 32) : NULL;
-            encode_row(e, out_fmt, d, r, o, s);
-            free(rows); free(wgt); free(valid); free(e);
+            uint8_t* sc = out_scales ? out_scales + b * sc_bstride + q * (d / 32) : NULL;
+            compress_entry(x, x_fmt, x_bstride, x_pos0, x_rows, x_roles, z, z_ch, z_bstride, bias, b, d, r, m,
+                           overlap, e_begin + q, out_fmt, o, sc);
         }
     }
     return ORC_OK;
+}
+
+/*
+ * Decode-time compression: for every new token (b, j) at position p = pos[b*T + j]
+ * that completes a block ((p + 1) mod m == 0), entry e = (p + 1)/m - 1 is pooled from
+ * the ring of raw rows (slot p mod x_rows, x_pos0 = 0) and written at out +
+ * (b*T + j)*rowbytes (scales at out_scales + (b*T + j)*d/32); out_entry[b*T + j] = e,
+ * or -1 when the token completes no block (nothing written).
+ */
+int orc_kv_compress_step(const void* x, int x_fmt, int64_t x_bstride, int64_t x_rows, int x_roles,
+                         const float* z, int z_ch, int64_t z_bstride, const float* bias,
+                         const int32_t* pos, int B, int T, int d, int r, int m, int overlap,
+                         void* out, int out_fmt, uint8_t* out_scales, int32_t* out_entry)
+{
+    if (B < 0 || T < 0 || x_rows <= 0 || !compress_args_ok(x_fmt, x_roles, overlap, d, m, z_ch)) return ORC_EINVAL;
+    const int64_t orb = orc_row_bytes(out_fmt, d, r);
+    for (int64_t u = 0; u < (int64_t)B * T; ++u) {
+        const int64_t p = pos[u];
+        const int b = (int)(u / (T > 0 ? T : 1));
+        if (p < 0 || (p + 1) % m != 0) { out_entry[u] = -1; continue; }
+        const int64_t e = (p + 1) / m - 1;
+        out_entry[u] = (int32_t)e;
+        compress_entry(x, x_fmt, x_bstride, 0, x_rows, x_roles, z, z_ch, z_bstride, bias, b, d, r, m, overlap, e,
+                       out_fmt, (uint8_t*)out + u * orb, out_scales ? out_scales + u * (d / 32) : NULL);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Plain paged gather: row s of sequence b, stored in block block_table[b*bt_stride +
+ * s / epb] of the pool at byte offset (s % epb)*row_bytes of that block (blocks
+ * block_bytes apart), copied to out + b*out_bstride + s*row_bytes for s < n.  A
+ * negative block id (no block) gives a zero row.
+ */
+void orc_paged_gather(const uint8_t* pool, int64_t row_bytes, const int32_t* block_table, int64_t bt_stride,
+                      int epb, int64_t block_bytes, int B, int64_t n, uint8_t* out, int64_t out_bstride)
+{
+    for (int b = 0; b < B; ++b)
+        for (int64_t s = 0; s < n; ++s) {
+            const int32_t blk = block_table[b * bt_stride + s / epb];
+            uint8_t* dst = out + b * out_bstride + s * row_bytes;
+            if (blk < 0) memset(dst, 0, (size_t)row_bytes);
+            else memcpy(dst, pool + (int64_t)blk * block_bytes + (s % epb) * row_bytes, (size_t)row_bytes);
+        }
 }
 
 /* ------------------------------------------------------------------------- */
@@ -423,10 +517,12 @@ static const uint8_t* window_row(const uint8_t* base, int64_t pos0, int64_t rows
 /*
  * One query (b, j), all heads:  the attended set is a list L of stored rows (K = V),
  * logits l = scale * q_h . v, o_h = sum softmax(l) v, lse_h = log sum exp(l).
- * An empty list gives o = 0 and lse = -inf.
+ * With a sink (sink != NULL) head h's softmax also has the logit sink[h], which has
+ * no value:  o_h = sum exp(l) v / (exp(sink[h]) + sum exp(l)),  lse_h = log(exp(sink[h])
+ * + sum exp(l)).  An empty list gives o = 0 and lse = -inf (= sink[h] with a sink).
  */
 static void attend_list(const double* q, int H, int d, double scale, double* const* rows, int64_t nrows,
-                        float* out_f32, uint16_t* out_bf16, float* lse)
+                        const float* sink, float* out_f32, uint16_t* out_bf16, float* lse)
 {
     double* l = (double*)malloc(sizeof(double) * (size_t)(nrows > 0 ? nrows : 1));
     double* o = (double*)malloc(sizeof(double) * (size_t)d);
@@ -438,8 +534,10 @@ static void attend_list(const double* q, int H, int d, double scale, double* con
             l[a] = scale * dot;
             if (l[a] > mx) mx = l[a];
         }
+        if (sink && (double)sink[h] > mx) mx = sink[h];
         double den = 0.0;
         for (int64_t a = 0; a < nrows; ++a) den += exp(l[a] - mx);
+        if (sink) den += exp((double)sink[h] - mx);
         for (int i = 0; i < d; ++i) o[i] = 0.0;
         for (int64_t a = 0; a < nrows; ++a) {
             double p = exp(l[a] - mx) / den;
@@ -449,7 +547,7 @@ static void attend_list(const double* q, int H, int d, double scale, double* con
             if (out_f32) out_f32[(size_t)h * d + i] = (float)o[i];
             if (out_bf16) out_bf16[(size_t)h * d + i] = orc_bf16_encode(o[i]);
         }
-        if (lse) lse[h] = nrows > 0 ? (float)(mx + log(den)) : -INFINITY;
+        if (lse) lse[h] = den > 0.0 ? (float)(mx + log(den)) : -INFINITY;
     }
     free(l); free(o);
 }
@@ -465,8 +563,8 @@ static void attend_list(const double* q, int H, int d, double scale, double* con
 static int attend_common(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap,
                          const int32_t* idx, int k, int m,
                          const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
-                         const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, double scale,
-                         void* out, int out_fmt, float* out_lse)
+                         const float* sink, const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r,
+                         double scale, void* out, int out_fmt, float* out_lse)
 {
     if (B < 0 || Tq < 0 || H <= 0 || d <= 0 || W < 0 || n_cap < 0) return ORC_EINVAL;
     if (W > 0 && kvw_rows <= 0) return ORC_EINVAL;
@@ -518,7 +616,7 @@ static int attend_common(const void* q, int q_fmt, const void* kv_c, int kv_fmt,
                 decode_row((const uint8_t*)q + (qrow0 + h) * qrb, NULL, q_fmt, d, r, qd + (size_t)h * d);
             float* of = out_fmt == ORC_F32 ? (float*)out + qrow0 * d : NULL;
             uint16_t* ob = out_fmt == ORC_BF16 ? (uint16_t*)out + qrow0 * d : NULL;
-            attend_list(qd, H, d, scale, rows, nrows, of, ob, out_lse ? out_lse + qrow0 : NULL);
+            attend_list(qd, H, d, scale, rows, nrows, sink, of, ob, out_lse ? out_lse + qrow0 : NULL);
             free(qd); free(rows); free(data);
         }
     }
@@ -527,23 +625,55 @@ static int attend_common(const void* q, int q_fmt, const void* kv_c, int kv_fmt,
 
 int orc_csa_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap,
                    const int32_t* idx, int k,
-                   const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+                   const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                    const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, double scale,
                    void* out, int out_fmt, float* out_lse)
 {
     if (!idx || k <= 0) return ORC_EINVAL;
     return attend_common(q, q_fmt, kv_c, kv_fmt, kvc_bstride, n_cap, idx, k, 1, kv_w, kvw_bstride, kvw_pos0,
-                         kvw_rows, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse);
+                         kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse);
 }
 
 int orc_hca_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap, int m,
-                   const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+                   const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                    const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, double scale,
                    void* out, int out_fmt, float* out_lse)
 {
     if (m <= 0) return ORC_EINVAL;
     return attend_common(q, q_fmt, kv_c, kv_fmt, kvc_bstride, n_cap, NULL, 0, m, kv_w, kvw_bstride, kvw_pos0,
-                         kvw_rows, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse);
+                         kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Grouped output projection ([X] HCA subsection; [C] attention details).    */
+/* ------------------------------------------------------------------------- */
+/*
+ * x: M rows of G*K values (row t = the outputs of the H heads of token t, head-major,
+ * so group g holds values g*K .. g*K+K-1); w: G matrices of R rows of K values (row n
+ * of matrix g = the weights of output n of group g).  out[t][g*R + n] =
+ * sum_k x[t][g*K + k] * w[g][n][k], in fp64, stored as fp32.  x_fmt / w_fmt: F32 or BF16.
+ */
+int orc_grouped_out_proj(const void* x, int x_fmt, const void* w, int w_fmt, int M, int G, int K, int R,
+                         float* out)
+{
+    if (M < 0 || G <= 0 || K <= 0 || R <= 0) return ORC_EINVAL;
+    if ((x_fmt != ORC_F32 && x_fmt != ORC_BF16) || (w_fmt != ORC_F32 && w_fmt != ORC_BF16)) return ORC_EINVAL;
+    const int64_t xrb = orc_row_bytes(x_fmt, G * K, 0), wrb = orc_row_bytes(w_fmt, K, 0);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < M; ++t) {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)G * K);
+        double* wr = (double*)malloc(sizeof(double) * (size_t)K);
+        decode_row((const uint8_t*)x + (int64_t)t * xrb, NULL, x_fmt, G * K, 0, xr);
+        for (int g = 0; g < G; ++g)
+            for (int n = 0; n < R; ++n) {
+                decode_row((const uint8_t*)w + ((int64_t)g * R + n) * wrb, NULL, w_fmt, K, 0, wr);
+                double acc = 0.0;
+                for (int k = 0; k < K; ++k) acc += xr[(size_t)g * K + k] * wr[k];
+                out[(int64_t)t * G * R + (int64_t)g * R + n] = (float)acc;
+            }
+        free(xr); free(wr);
+    }
+    return ORC_OK;
 }
 
 int orc_num_threads(void)

@@ -58,9 +58,11 @@ def softmax(a, axis=-1):
     return e / e.sum(axis=axis, keepdims=True)
 
 
-def compress(x, z, bias, m, overlap, entries):
-    """x [n_tok, d] raw rows at positions 0..n_tok-1; z [n_tok, C]; bias [win, C]."""
+def compress(x, z, bias, m, overlap, entries, roles=1):
+    """x [n_tok, roles*d] raw rows at positions 0..n_tok-1; z [n_tok, C]; bias [win, C].
+    roles = 2: window slots j < m take the first d values of a row, the others the last d."""
     win = 2 * m if overlap else m
+    d = x.shape[1] // roles
     out = []
     for i in entries:
         P = np.arange((i + 1) * m - win, (i + 1) * m)
@@ -68,8 +70,12 @@ def compress(x, z, bias, m, overlap, entries):
         logits = z[P[keep]] + bias[keep]          # [nv, C]
         wts = softmax(logits, axis=0)             # normalise over window positions
         if wts.shape[1] == 1:
-            wts = np.broadcast_to(wts, (wts.shape[0], x.shape[1]))
-        out.append((wts * x[P[keep]]).sum(axis=0))
+            wts = np.broadcast_to(wts, (wts.shape[0], d))
+        vals = x[P[keep]]
+        if roles == 2:
+            slot = np.arange(win)[keep]
+            vals = np.where((slot < m)[:, None], vals[:, :d], vals[:, d:])
+        out.append((wts * vals).sum(axis=0))
     return np.array(out)
 
 
@@ -95,6 +101,16 @@ def attend(q, rows, scale):
     p = np.exp(l - mx)
     den = p.sum(axis=1, keepdims=True)
     return (p / den) @ rows, (mx + np.log(den))[:, 0]
+
+
+def attend_sink(q, rows, scale, sink):
+    """attend() with one extra logit per head (sink [H]) in the softmax denominator."""
+    l = scale * (q @ rows.T) if rows.shape[0] else np.zeros((q.shape[0], 0))
+    full = np.concatenate([l, np.asarray(sink, np.float64)[:, None]], axis=1)
+    mx = full.max(axis=1, keepdims=True)
+    p = np.exp(full - mx)
+    den = p.sum(axis=1, keepdims=True)
+    return (p[:, :-1] / den) @ rows if rows.shape[0] else np.zeros_like(q), (mx + np.log(den))[:, 0]
 
 
 def causal_mqa(q, kv, scale, extra=None):

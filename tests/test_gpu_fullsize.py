@@ -258,3 +258,106 @@ def dense_pass_rows(B, Tq, n_cap):
     passes = (Tq + cap_ - 1) // cap_
     tc = ((Tq + passes - 1) // passes + 11) // 12 * 12
     return min(tc, cap_)
+
+
+# ---------------------------------------------------------------------------
+# Other shapes of the same kernels: multi-token decode queries, an SWA-only layer,
+# an HCA prefill chunk
+# ---------------------------------------------------------------------------
+def test_stack_multi_token_decode_tq3(gpu, stack):
+    """Three query tokens per sequence (t-2, t-1, t: multi-token prediction or
+    speculative verification) through a CSA layer and an HCA layer of the 1M-context
+    stack, batch 16: index_topk over the MXFP4 keys and both attention calls, every
+    one of the 48 queries checked."""
+    st = stack
+    csa, hca = st.layers[0], st.layers[1]
+    B, Tq, dev_ = st.B, 3, st.q_pos.device
+    qpos = torch.tensor([[st.t - 2, st.t - 1, st.t]] * B, dtype=torch.int32, device=dev_)
+    qi_raw = gen.with_outliers(gen.normal((B * Tq * st.HI, 1, st.dI), 3301, device=dev_), 3302)
+    z1 = torch.zeros((B * Tq * st.HI, 1, 1), device=dev_)
+    b1 = torch.zeros((1, 1), device=dev_)
+    qic, qis = ops.kv_compress(gen.bf16_bytes(qi_raw), O.BF16, z1, b1, d=st.dI, m=1, overlap=False, e_begin=0, n_e=1,
+                               out_fmt=O.MXFP4)
+    qi = qic.reshape(B, Tq, st.HI, -1).contiguous()
+    qis = qis.reshape(B, Tq, st.HI, -1).contiguous()
+    w = gen.normal((B, Tq, st.HI), 3303, 1 / math.sqrt(st.HI), device=dev_)
+    q = gen.with_outliers(gen.normal((B, Tq, st.H, st.d), 3304, device=dev_), 3305).to(torch.bfloat16)
+    gi, gs = ops.index_topk(qi, w, csa["keys"], qpos, fmt=O.MXFP4, H_I=st.HI, d_I=st.dI, m=st.m, n_cap=st.N, k=st.k,
+                            qi_scales=qis, ki_scales=csa["kscales"])
+    kw = dict(kv_fmt=O.KV_PACKED, kvw_pos0=0, kvw_rows=st.ring, W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
+    oc, lc = ops.csa_attend(q, csa["cache"], gi, csa["ring"], qpos, n_cap=st.N, **kw)
+    oh, lh = ops.hca_attend(q, hca["cache"], hca["ring"], qpos, n_cap=st.Nh, m=st.mh, **kw)
+    torch.cuda.synchronize()
+    stats = _check_index(host(gi), host(gs), host(qi), O.MXFP4, host(w), host(csa["keys"]), O.MXFP4, host(qpos),
+                         H_I=st.HI, d_I=st.dI, m=st.m, n_cap=st.N, k=st.k, qi_scales=host(qis),
+                         ki_scales=host(csa["kscales"]))
+    okw = dict(W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
+    qb = host(q.view(torch.int16))
+    oo, ol = O.csa_attend(qb, O.BF16, host(csa["cache"]), O.KV_PACKED, st.N, host(gi), host(csa["ring"]), 0, st.ring,
+                          host(qpos), **okw)
+    e1 = max_abs(host(oc), oo)
+    oo2, ol2 = O.hca_attend(qb, O.BF16, host(hca["cache"]), O.KV_PACKED, st.Nh, st.mh, host(hca["ring"]), 0, st.ring,
+                            host(qpos), **okw)
+    e2 = max_abs(host(oh), oo2)
+    assert e1 <= 2e-2 and e2 <= 2e-2, (e1, e2)
+    assert max_abs(host(lc), ol) <= 2e-1 and max_abs(host(lh), ol2) <= 2e-1
+    print("multi-token decode (Tq = 3): index %s; csa max-abs %.3g, hca max-abs %.3g" % (stats, e1, e2))
+
+
+def test_swa_only_layer_b16(gpu, stack):
+    """A sliding-window-only layer (the last layer of the stack the pages describe):
+    hca_attend with no compressed entries (n_cap = 0) and the 128-token window, batch 16
+    at 1M context, plus early positions whose window is shorter than 128."""
+    st = stack
+    hca = st.layers[1]
+    B = st.B
+    pos = [st.t] * (B - 4) + [0, 5, 127, 128]
+    qpos = torch.tensor([[p] for p in pos], dtype=torch.int32, device=st.q_pos.device)
+    q = hca["q"]
+    kw = dict(kv_fmt=O.KV_PACKED, kvw_pos0=0, kvw_rows=st.ring, W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
+    go, gl = ops.hca_attend(q, hca["cache"][:, :0], hca["ring"], qpos, n_cap=0, m=st.mh, **kw)
+    torch.cuda.synchronize()
+    okw = dict(W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
+    oo, ol = O.hca_attend(host(q.view(torch.int16)), O.BF16, host(hca["cache"][:, :1]), O.KV_PACKED, 0, st.mh,
+                          host(hca["ring"]), 0, st.ring, host(qpos), **okw)
+    err = max_abs(host(go), oo)
+    assert err <= 2e-2, err
+    assert max_abs(host(gl), ol) <= 2e-1
+    print("swa-only layer: max-abs %.3g" % err)
+
+
+def test_hca_prefill_chunk_8192_on_1m(gpu):
+    """HCA prefill: 8,192 new tokens on 1M cached ones with m' = 128: the chunk's 64 new
+    entries are compressed (no overlap), then every query attends densely to all entries
+    complete at its position plus its 128-token window (causal), 128 heads of 512;
+    128 evenly spaced queries checked, with the first and the last."""
+    H, d, r, m, W, C = 128, 512, 64, 128, 128, 8192
+    T0 = 1 << 20
+    N0, N = T0 // m, (T0 + C) // m
+    cache = torch.empty((1, N, d + r), dtype=torch.uint8, device="cuda")
+    cache[:, :N0] = gen.pack_kv(gen.normal((1, N0, d), 3401, device="cuda"), r)
+    x = gen.normal((1, C, d), 3402, device="cuda")
+    z = gen.random_logits((1, C, 1), 3403, device="cuda")
+    bias = gen.random_logits((m, 1), 3404, device="cuda")
+    xb = gen.bf16_bytes(x)
+    ops.kv_compress(xb, O.BF16, z, bias, d=d, r=r, m=m, overlap=False, e_begin=N0, n_e=C // m, x_pos0=T0,
+                    out_fmt=O.KV_PACKED, out=cache[:, N0:N])
+    xw = torch.cat([gen.normal((1, W, d), 3405, device="cuda"), x], dim=1)
+    kvw = gen.pack_kv(xw, r)
+    pos0 = T0 - W
+    qpos = torch.arange(T0, T0 + C, dtype=torch.int32, device="cuda").view(1, C)
+    q = gen.normal((1, C, H, d), 3406, device="cuda").to(torch.bfloat16)
+    go, gl = ops.hca_attend(q, cache, kvw, qpos, kv_fmt=O.KV_PACKED, n_cap=N, m=m, kvw_pos0=pos0, kvw_rows=W + C,
+                            W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    ref, _ = O.kv_compress(host(xb), O.BF16, host(z), host(bias), d=d, r=r, m=m, overlap=False, e_begin=N0,
+                           n_e=C // m, x_pos0=T0, out_fmt=O.KV_PACKED)
+    nbad = close_quantised(host(cache[:, N0:N]), ref, O.KV_PACKED, d, r, max_mismatch=8)
+    sq = sorted(set(np.linspace(0, C - 1, 128).astype(int).tolist()))
+    hq = lambda t: host(t[:, sq])
+    oo, ol = O.hca_attend(hq(q.view(torch.int16)), O.BF16, host(cache), O.KV_PACKED, N, m, host(kvw), pos0, W + C,
+                          hq(qpos), W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    err = max_abs(hq(go), oo)
+    assert err <= 2e-2, err
+    assert max_abs(hq(gl), ol) <= 2e-1
+    print("hca prefill chunk: %d queries, compress mismatches %d, max-abs %.3g" % (len(sq), nbad, err))
