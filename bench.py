@@ -41,19 +41,32 @@ def parse():
     p.add_argument("--kernel-iters", type=int, default=20)
     p.add_argument("--workload", choices=["stack", "prefill"], default="stack",
                    help="stack: the 4-layer decode stack (default); prefill: one CSA prefill chunk")
+    p.add_argument("--layout", choices=["linear", "paged"], default="linear",
+                   help="compressed cache of the stack: dense per sequence, or 128-token blocks behind a block table")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="also run a plain device copy of this many MiB (the reference kernel for HBM counters)")
     return p.parse_args()
 
 
 class Stack:
-    """Device-resident caches and inputs of the 4-layer decode step."""
+    """Device-resident caches and inputs of the 4-layer decode step.
 
-    def __init__(self, B, ctx, device):
+    Per layer, the two tiers of the cache: a state ring per sequence (the last RING raw
+    rows -- bf16, with their compression logits -- and the window rows, packed) and the
+    compressed cache.  layout "linear": one dense array of entries per sequence; layout
+    "paged": blocks of BLOCK_TOKENS = lcm(4, 128) = 128 raw tokens behind one block
+    table shared by all layers (a CSA block holds 32 packed entries, their 32 MXFP4
+    indexer keys and the keys' scales; an HCA block 1 entry), the physical blocks in a
+    seeded random order."""
+
+    RING = 128
+    BLOCK_TOKENS = 128
+
+    def __init__(self, B, ctx, device, layout="linear"):
         import torch
         from compressed_sparse_long_02_amd import gen, ops
         F = ops
-        self.B, self.ctx, self.dev = B, ctx, device
+        self.B, self.ctx, self.dev, self.layout = B, ctx, device, layout
         self.t = ctx - 1
         self.H, self.d, self.r, self.W = 64, 512, 64, 128
         self.m, self.mh = 4, 128
@@ -64,6 +77,21 @@ class Stack:
         self.scale = 1.0 / math.sqrt(self.d)
         B, d, r = self.B, self.d, self.r
         rb = F.row_bytes(F.KV_PACKED, d, r)
+        self.rb = rb
+        # paged layout: one block table for every layer, physical blocks shuffled
+        self.nblk = ctx // self.BLOCK_TOKENS
+        self.epb_csa = self.BLOCK_TOKENS // self.m
+        self.epb_hca = self.BLOCK_TOKENS // self.mh
+        self.csa_key_off = self.epb_csa * rb                       # bytes of a CSA block: entries, keys, scales
+        self.csa_sc_off = self.csa_key_off + self.epb_csa * self.dI // 2
+        self.csa_blk = self.csa_sc_off + self.epb_csa * self.dI // 32
+        self.csa_blk = (self.csa_blk + 15) // 16 * 16
+        self.hca_blk = self.epb_hca * rb
+        self.n_phys = B * self.nblk
+        if layout == "paged":
+            g = torch.Generator(device="cpu")
+            g.manual_seed(77)
+            self.bt = torch.randperm(self.n_phys, generator=g).to(torch.int32).reshape(B, self.nblk).to(device)
         self.layers = []
         seed = 1000
         for li, kind in enumerate(["csa", "hca", "csa", "hca"]):
@@ -78,17 +106,16 @@ class Stack:
                 x = gen.with_outliers(gen.normal((B, c, d), seed + s0, device=device), seed)
                 cache[:, s0:s0 + c] = gen.pack_kv(x, r)
             L["cache"] = cache
-            # sliding-window state: ring of packed rows
+            # the state ring: window rows (packed) and the raw rows + logits of the last RING
+            # positions (row p % RING), from which the completed entries are compressed
             xw = gen.with_outliers(gen.normal((B, self.ring, d), seed + 1, device=device), seed)
             L["ring"] = gen.pack_kv(xw, r)
-            # raw tail of the new block (bf16) + compression logits and slot biases
             mm = self.m if kind == "csa" else self.mh
-            win = 2 * mm if kind == "csa" else mm
-            L["win"] = win
-            xr = gen.with_outliers(gen.normal((B, win, d), seed + 2, device=device), seed)
+            L["win"] = 2 * mm if kind == "csa" else mm
+            xr = gen.with_outliers(gen.normal((B, self.RING, d), seed + 2, device=device), seed)
             L["raw"] = gen.bf16_bytes(xr)
-            L["z"] = gen.random_logits((B, win, 1), seed + 3, device=device)
-            L["bias"] = gen.random_logits((win, 1), seed + 4, device=device)
+            L["z"] = gen.random_logits((B, self.RING, 1), seed + 3, device=device)
+            L["bias"] = gen.random_logits((L["win"], 1), seed + 4, device=device)
             L["q"] = gen.with_outliers(gen.normal((B, 1, self.H, d), seed + 5, device=device), seed).to(torch.bfloat16)
             L["out"] = torch.empty((B, 1, self.H, d), dtype=torch.bfloat16, device=device)
             if kind == "csa":
@@ -103,10 +130,10 @@ class Stack:
                     F.kv_compress(gen.bf16_bytes(x), F.BF16, z1[:, :c], b1, d=self.dI, m=1, overlap=False, e_begin=0,
                                   n_e=c, out_fmt=F.MXFP4, out=keys[:, s0:s0 + c], out_scales=ksc[:, s0:s0 + c])
                 L["keys"], L["kscales"] = keys, ksc
-                xi = gen.with_outliers(gen.normal((B, win, self.dI), seed + 8, device=device), seed + 1)
+                xi = gen.with_outliers(gen.normal((B, self.RING, self.dI), seed + 8, device=device), seed + 1)
                 L["raw_i"] = gen.bf16_bytes(xi)
-                L["z_i"] = gen.random_logits((B, win, 1), seed + 9, device=device)
-                L["bias_i"] = gen.random_logits((win, 1), seed + 10, device=device)
+                L["z_i"] = gen.random_logits((B, self.RING, 1), seed + 9, device=device)
+                L["bias_i"] = gen.random_logits((L["win"], 1), seed + 10, device=device)
                 qi = gen.with_outliers(gen.normal((B * self.HI, 1, self.dI), seed + 11, device=device), seed + 1)
                 qic, qis = F.kv_compress(gen.bf16_bytes(qi), F.BF16, torch.zeros((B * self.HI, 1, 1), device=device),
                                          b1, d=self.dI, m=1, overlap=False, e_begin=0, n_e=1, out_fmt=F.MXFP4)
@@ -114,42 +141,116 @@ class Stack:
                 L["qis"] = qis.reshape(B, 1, self.HI, self.dI // 32).contiguous()
                 L["w"] = gen.normal((B, 1, self.HI), seed + 12, 1 / math.sqrt(self.HI), device=device)
                 L["idx"] = torch.empty((B, 1, self.k), dtype=torch.int32, device=device)
+            if layout == "paged":
+                self._to_pool(L)
             self.layers.append(L)
         self.q_pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
         torch.cuda.synchronize()
 
-    # -- the ABI calls of one layer ------------------------------------------
-    def compress(self, L):
-        from compressed_sparse_long_02_amd import ops as F
-        t = self.t
+    def _to_pool(self, L):
+        """Move a layer's linear cache into its block pool (physical block bt[b, j] holds the
+        entries of raw tokens 128 j .. 128 j + 127 of sequence b); the linear arrays are
+        dropped, and `cache` / `keys` / `kscales` become views of the pool's blocks."""
+        import torch
+        B, rb = self.B, self.rb
+        bt = self.bt.long()
         if L["kind"] == "csa":
-            i = (t + 1) // self.m - 1          # the entry completed by token t
-            F.kv_compress(L["raw"], F.BF16, L["z"], L["bias"], d=self.d, r=self.r, m=self.m, overlap=True,
-                          e_begin=i, n_e=1, x_pos0=t - L["win"] + 1, out_fmt=F.KV_PACKED,
-                          out=L["cache"][:, i:i + 1])
-            F.kv_compress(L["raw_i"], F.BF16, L["z_i"], L["bias_i"], d=self.dI, m=self.m, overlap=True,
-                          e_begin=i, n_e=1, x_pos0=t - L["win"] + 1, out_fmt=F.MXFP4,
-                          out=L["keys"][:, i:i + 1], out_scales=L["kscales"][:, i:i + 1])
+            epb, blk = self.epb_csa, self.csa_blk
+            pool = torch.zeros((self.n_phys, blk), dtype=torch.uint8, device=self.dev)
+            for b in range(B):
+                ids = bt[b]
+                pool[ids, :self.csa_key_off] = L["cache"][b].reshape(self.nblk, epb * rb)
+                pool[ids, self.csa_key_off:self.csa_sc_off] = L["keys"][b].reshape(self.nblk, -1)
+                pool[ids, self.csa_sc_off:self.csa_sc_off + epb * self.dI // 32] = L["kscales"][b].reshape(self.nblk, -1)
+            del L["keys"], L["kscales"]
+            L["pool"] = pool
         else:
-            i = (t + 1) // self.mh - 1
-            F.kv_compress(L["raw"], F.BF16, L["z"], L["bias"], d=self.d, r=self.r, m=self.mh, overlap=False,
-                          e_begin=i, n_e=1, x_pos0=t - L["win"] + 1, out_fmt=F.KV_PACKED,
-                          out=L["cache"][:, i:i + 1])
+            epb, blk = self.epb_hca, self.hca_blk
+            pool = torch.zeros((self.n_phys, blk), dtype=torch.uint8, device=self.dev)
+            for b in range(B):
+                pool[bt[b]] = L["cache"][b].reshape(self.nblk, epb * rb)
+            L["pool"] = pool
+        del L["cache"]
+        torch.cuda.synchronize()
 
-    def index(self, L):
+    # -- views of the compressed cache ----------------------------------------------
+    def entries(self, L):
+        """Linear [B, n, row] entries of a layer (gathered through the block table when
+        paged: a host-side copy for the oracle, not part of the step)."""
+        import torch
+        if self.layout != "paged":
+            return L["cache"]
+        epb = self.epb_csa if L["kind"] == "csa" else self.epb_hca
+        bt = self.bt.long()
+        rows = L["pool"][:, :epb * self.rb]
+        return torch.stack([rows[bt[b]].reshape(-1, self.rb) for b in range(self.B)])
+
+    def index_keys(self, L):
+        """Linear MXFP4 keys and scales of a CSA layer ([B, N, 64], [B, N, 4])."""
+        import torch
+        if self.layout != "paged":
+            return L["keys"], L["kscales"]
+        bt = self.bt.long()
+        p = L["pool"]
+        k = torch.stack([p[bt[b], self.csa_key_off:self.csa_sc_off].reshape(-1, self.dI // 2) for b in range(self.B)])
+        s = torch.stack([p[bt[b], self.csa_sc_off:self.csa_sc_off + self.epb_csa * self.dI // 32]
+                         .reshape(-1, self.dI // 32) for b in range(self.B)])
+        return k, s
+
+    # -- the ABI calls of one layer ------------------------------------------------
+    def compress(self, L):
+        """The entries completed by the new token, pooled from the state ring into the cache."""
         from compressed_sparse_long_02_amd import ops as F
-        F.index_topk(L["qi"], L["w"], L["keys"], self.q_pos, fmt=F.MXFP4, H_I=self.HI, d_I=self.dI, m=self.m,
-                     n_cap=self.N, k=self.k, qi_scales=L["qis"], ki_scales=L["kscales"], out_idx=L["idx"],
-                     with_scores=False)
+        paged = self.layout == "paged"
+        if L["kind"] == "csa":
+            kw = dict(m=self.m, overlap=True)
+            if paged:
+                pg = (self.bt, self.epb_csa, self.csa_blk, self.csa_blk, self.n_phys)
+                p = L["pool"]
+                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, d=self.d, r=self.r,
+                                   out=p, out_fmt=F.KV_PACKED, pages=pg, **kw)
+                F.kv_compress_step(L["raw_i"], F.BF16, L["z_i"], L["bias_i"], self.q_pos, d=self.dI,
+                                   out=p[:, self.csa_key_off:], out_fmt=F.MXFP4, out_scales=p[:, self.csa_sc_off:],
+                                   pages=pg, **kw)
+            else:
+                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, d=self.d, r=self.r,
+                                   out=L["cache"], out_fmt=F.KV_PACKED, **kw)
+                F.kv_compress_step(L["raw_i"], F.BF16, L["z_i"], L["bias_i"], self.q_pos, d=self.dI,
+                                   out=L["keys"], out_fmt=F.MXFP4, out_scales=L["kscales"], **kw)
+        else:
+            kw = dict(m=self.mh, overlap=False, d=self.d, r=self.r, out_fmt=F.KV_PACKED)
+            if paged:
+                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, out=L["pool"],
+                                   pages=(self.bt, self.epb_hca, self.hca_blk, self.hca_blk, self.n_phys), **kw)
+            else:
+                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, out=L["cache"], **kw)
 
-    def attend(self, L):
+    def index(self, L, with_scores=False, out_idx=None):
+        from compressed_sparse_long_02_amd import ops as F
+        kw = dict(fmt=F.MXFP4, H_I=self.HI, d_I=self.dI, m=self.m, n_cap=self.N, k=self.k, qi_scales=L["qis"],
+                  out_idx=L["idx"] if out_idx is None else out_idx, with_scores=with_scores)
+        if self.layout == "paged":
+            p = L["pool"]
+            return F.index_topk(L["qi"], L["w"], p[:, self.csa_key_off:], self.q_pos, ki_scales=p[:, self.csa_sc_off:],
+                                pages=(self.bt, self.epb_csa, self.csa_blk, self.csa_blk, self.n_phys), **kw)
+        return F.index_topk(L["qi"], L["w"], L["keys"], self.q_pos, ki_scales=L["kscales"], **kw)
+
+    def attend(self, L, out=None, out_fmt=None, with_lse=False):
         from compressed_sparse_long_02_amd import ops as F
         kw = dict(kv_fmt=F.KV_PACKED, kvw_pos0=0, kvw_rows=self.ring, W=self.W, H=self.H, d=self.d, r=self.r,
-                  scale=self.scale, out_fmt=F.BF16, out=L["out"], with_lse=False)
+                  scale=self.scale, out_fmt=F.BF16 if out_fmt is None else out_fmt,
+                  out=L["out"] if out is None and out_fmt is None else out, with_lse=with_lse)
+        if self.layout == "paged":
+            if L["kind"] == "csa":
+                return F.csa_attend_paged(L["q"], L["pool"], self.bt, L["idx"], L["ring"], self.q_pos,
+                                          entries_per_block=self.epb_csa, block_bytes=self.csa_blk,
+                                          n_blocks=self.n_phys, n_cap=self.N, **kw)
+            return F.hca_attend_paged(L["q"], L["pool"], self.bt, L["ring"], self.q_pos,
+                                      entries_per_block=self.epb_hca, block_bytes=self.hca_blk, n_blocks=self.n_phys,
+                                      n_cap=self.Nh, m=self.mh, **kw)
         if L["kind"] == "csa":
-            F.csa_attend(L["q"], L["cache"], L["idx"], L["ring"], self.q_pos, n_cap=self.N, **kw)
-        else:
-            F.hca_attend(L["q"], L["cache"], L["ring"], self.q_pos, n_cap=self.Nh, m=self.mh, **kw)
+            return F.csa_attend(L["q"], L["cache"], L["idx"], L["ring"], self.q_pos, n_cap=self.N, **kw)
+        return F.hca_attend(L["q"], L["cache"], L["ring"], self.q_pos, n_cap=self.Nh, m=self.mh, **kw)
 
     def step(self):
         for L in self.layers:
@@ -386,11 +487,12 @@ def cpu_baseline(st, nseq, min_s=10.0):
     h = lambda x: x[:nseq].detach().cpu().numpy()
     csa, hca = st.layers[0], st.layers[1]
     t, d, r = st.t, st.d, st.r
+    keys, kscales = st.index_keys(csa)
     arrs = dict(c_raw=h(csa["raw"]), c_z=h(csa["z"]), c_bias=csa["bias"].cpu().numpy(), c_rawi=h(csa["raw_i"]),
                 c_zi=h(csa["z_i"]), c_biasi=csa["bias_i"].cpu().numpy(), qi=h(csa["qi"]), qis=h(csa["qis"]),
-                w=h(csa["w"]), keys=h(csa["keys"]), ksc=h(csa["kscales"]), c_cache=h(csa["cache"]),
+                w=h(csa["w"]), keys=h(keys), ksc=h(kscales), c_cache=h(st.entries(csa)),
                 c_ring=h(csa["ring"]), c_q=h(csa["q"].view(torch.int16)), h_raw=h(hca["raw"]), h_z=h(hca["z"]),
-                h_bias=hca["bias"].cpu().numpy(), h_cache=h(hca["cache"]), h_ring=h(hca["ring"]),
+                h_bias=hca["bias"].cpu().numpy(), h_cache=h(st.entries(hca)), h_ring=h(hca["ring"]),
                 h_q=h(hca["q"].view(torch.int16)))
     qpos = np.full((nseq, 1), t, np.int32)
     a = arrs
@@ -414,16 +516,16 @@ def _oracle_pass(st, a, qpos):
     t0 = time.perf_counter()
     i = (t + 1) // st.m - 1
     O.kv_compress(a["c_raw"], O.BF16, a["c_z"], a["c_bias"], d=d, r=r, m=st.m, overlap=True, e_begin=i, n_e=1,
-                  x_pos0=t - 7, out_fmt=O.KV_PACKED)
+                  x_rows=st.RING, out_fmt=O.KV_PACKED)
     O.kv_compress(a["c_rawi"], O.BF16, a["c_zi"], a["c_biasi"], d=st.dI, m=st.m, overlap=True, e_begin=i, n_e=1,
-                  x_pos0=t - 7, out_fmt=O.MXFP4)
+                  x_rows=st.RING, out_fmt=O.MXFP4)
     idx, _ = O.index_topk(a["qi"], O.MXFP4, a["w"], a["keys"], O.MXFP4, qpos, H_I=st.HI, d_I=st.dI, m=st.m,
                           n_cap=st.N, k=st.k, qi_scales=a["qis"], ki_scales=a["ksc"])
     O.csa_attend(a["c_q"], O.BF16, a["c_cache"], O.KV_PACKED, st.N, idx, a["c_ring"], 0, st.ring, qpos, W=st.W,
                  H=st.H, d=d, r=r, scale=st.scale)
     ih = (t + 1) // st.mh - 1
     O.kv_compress(a["h_raw"], O.BF16, a["h_z"], a["h_bias"], d=d, r=r, m=st.mh, overlap=False, e_begin=ih, n_e=1,
-                  x_pos0=t - 127, out_fmt=O.KV_PACKED)
+                  x_rows=st.RING, out_fmt=O.KV_PACKED)
     O.hca_attend(a["h_q"], O.BF16, a["h_cache"], O.KV_PACKED, st.Nh, st.mh, a["h_ring"], 0, st.ring, qpos,
                  W=st.W, H=st.H, d=d, r=r, scale=st.scale)
     return time.perf_counter() - t0
@@ -440,7 +542,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] building inputs (B=%d, ctx=%d)" % (args.batch, args.ctx), file=sys.stderr, flush=True)
-    st = Stack(args.batch, args.ctx, dev)
+    st = Stack(args.batch, args.ctx, dev, layout=args.layout)
     st.step()                       # eager warm-up: allocates workspaces before capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -507,6 +609,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4+bf16", "data": "synthetic",
         "config": {"workload": "4-layer CSA,HCA,CSA,HCA decode at 1M ctx (t=2^20-1), batch %d" % args.batch,
+                   "cache_layout": args.layout,
                    "global_batch": args.batch, "seq_len": args.ctx, "heads": 64, "head_dim": 512,
                    "kv": "bf16 rope64 + fp8 e4m3 (576 B)", "indexer": "MXFP4 64x128, top-k 1024", "m": 4,
                    "m_hca": 128, "window": 128, "parallelism": "single GPU"},

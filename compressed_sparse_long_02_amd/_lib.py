@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(HERE, "libcsl.so")
 CSL_OK, CSL_EINVAL, CSL_EUNSUPPORTED, CSL_EWORKSPACE, CSL_ELAUNCH, CSL_EDEVICE = 0, -1, -2, -3, -4, -5
 
 # every symbol include/csl.h declares
-EXPORTS = ["csl_row_bytes", "kv_compress", "index_topk", "csl_index_topk_workspace", "index_topk_noalloc",
-           "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend", "csl_attend_workspace", "csl_status_string",
-           "csl_last_error", "csl_version"]
+EXPORTS = ["csl_row_bytes", "kv_compress", "kv_compress_step", "index_topk", "index_topk_paged",
+           "csl_index_topk_workspace", "index_topk_noalloc", "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend",
+           "csa_attend_paged", "hca_attend_paged", "csl_attend_workspace", "csl_status_string", "csl_last_error",
+           "csl_version"]
 
 
 class CslError(RuntimeError):
@@ -40,8 +41,14 @@ def lib() -> C.CDLL:
     L.csl_row_bytes.restype = i64
     L.csl_row_bytes.argtypes = [i32, i32, i32]
     L.kv_compress.restype = i32
-    L.kv_compress.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, i32, i32, i32, i32, i64, i64,
+    L.kv_compress.argtypes = [vp, i32, i32, i64, i64, i64, vp, i32, i64, vp, i32, i32, i32, i32, i32, i64, i64,
                               vp, i32, vp, i64, i64, vp]
+    L.kv_compress_step.restype = i32
+    L.kv_compress_step.argtypes = [vp, i32, i32, i64, i64, vp, i32, i64, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   vp, i32, vp, i64, i64, i64, vp, i64, i32, i64, i64, i64, vp]
+    L.index_topk_paged.restype = i32
+    L.index_topk_paged.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, i64, i32, i64, i64, i64, vp, i32, i32, i32,
+                                   i32, i32, i64, i32, vp, vp, vp, sz, vp]
     L.index_topk.restype = i32
     L.index_topk.argtypes = [vp, i32, vp, vp, vp, i32, vp, i64, i64, vp, i32, i32, i32, i32, i32, i64, i32,
                              vp, vp, vp, sz, vp]
@@ -53,11 +60,17 @@ def lib() -> C.CDLL:
     L.csl_index_topk_workspace.restype = sz
     L.csl_index_topk_workspace.argtypes = [i32, i32, i64, i32]
     L.csa_attend.restype = i32
-    L.csa_attend.argtypes = [vp, i32, vp, i32, i64, i64, vp, i32, vp, i64, i64, i64, vp, i32, i32, i32, i32, i32,
-                             i32, f32, vp, i32, vp, vp, sz, vp]
+    L.csa_attend.argtypes = [vp, i32, vp, i32, i64, i64, vp, i32, vp, i64, i64, i64, vp, vp, i32, i32, i32, i32,
+                             i32, i32, f32, vp, i32, vp, vp, sz, vp]
     L.hca_attend.restype = i32
-    L.hca_attend.argtypes = [vp, i32, vp, i32, i64, i64, i32, vp, i64, i64, i64, vp, i32, i32, i32, i32, i32,
+    L.hca_attend.argtypes = [vp, i32, vp, i32, i64, i64, i32, vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, i32,
                              i32, f32, vp, i32, vp, vp, sz, vp]
+    L.csa_attend_paged.restype = i32
+    L.csa_attend_paged.argtypes = [vp, i32, vp, i32, vp, i64, i32, i64, i64, i64, vp, i32, vp, i64, i64, i64, vp,
+                                   vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, sz, vp]
+    L.hca_attend_paged.restype = i32
+    L.hca_attend_paged.argtypes = [vp, i32, vp, i32, vp, i64, i32, i64, i64, i64, i32, vp, i64, i64, i64, vp,
+                                   vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, sz, vp]
     L.csl_attend_workspace.restype = sz
     L.csl_attend_workspace.argtypes = [i32, i32, i32, i32, i64]
     L.csl_status_string.restype = C.c_char_p

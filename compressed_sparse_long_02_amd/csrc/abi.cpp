@@ -153,6 +153,30 @@ int64_t row_bytes(int fmt, int d, int r) {
     }
 }
 
+// Paged compressed entries (csa_attend_paged / hca_attend_paged, index_topk_paged,
+// kv_compress_step): entry s of sequence b is row s % epb of physical block
+// bt[b * bt_stride + s / epb]; blocks are blk_bytes apart; the pool holds n_blocks.
+struct Paged {
+    const int32_t* bt = nullptr;
+    int64_t bt_stride = 0;
+    int epb = 0;
+    int64_t blk_bytes = 0, n_blocks = 0;
+    int64_t sblk_bytes = 0;     // index_topk_paged: block stride of the MXFP4 scale rows
+};
+
+int validate_paged(const char* fn, const Paged& pg, int64_t n_cap, int64_t rb) {
+    if (!pg.bt || !al4(pg.bt)) return fail(CSL_EINVAL, "%s: null or misaligned block table", fn);
+    if (pg.epb < 1 || pg.n_blocks < 1 || pg.n_blocks > INT32_MAX)
+        return fail(CSL_EINVAL, "%s: need entries_per_block >= 1 and 1 <= n_blocks < 2^31", fn);
+    if (pg.bt_stride < (n_cap + pg.epb - 1) / pg.epb)
+        return fail(CSL_EINVAL, "%s: block-table rows of %lld ids cannot cover %lld entries of %d per block", fn,
+                    (long long)pg.bt_stride, (long long)n_cap, pg.epb);
+    if (pg.blk_bytes < pg.epb * rb || (pg.blk_bytes & 15))
+        return fail(CSL_EINVAL, "%s: block_bytes must be a multiple of 16 holding entries_per_block rows", fn);
+    if (n_cap > INT32_MAX) return fail(CSL_EUNSUPPORTED, "%s: paged n_cap must be < 2^31", fn);
+    return CSL_OK;
+}
+
 int validate_attend(const char* fn, const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride,
                     int64_t n_cap, const void* kv_w, int64_t kvw_bstride, int64_t kvw_rows, const int32_t* q_pos,
                     int W, int B, int Tq, int H, int d, int r, void* out, int out_fmt) {
@@ -210,29 +234,49 @@ int csl_last_error(char* buf, size_t n) {
 
 int csl_version(void) { return 100; }
 
-int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
-                const float* z, int z_ch, int64_t z_bstride, const float* bias,
-                int B, int d, int r, int m, int overlap, int64_t e_begin, int64_t n_e,
-                void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
-                void* stream) {
-    const char* fn = "kv_compress";
-    if (B < 0 || n_e < 0 || n_tok < 0 || e_begin < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
+// Checks shared by kv_compress and kv_compress_step (everything but the raw-row range).
+static int compress_common(const char* fn, const void* x, int x_fmt, int x_roles, int64_t x_bstride, const float* z,
+                           int z_ch, int64_t z_bstride, const float* bias, int B, int d, int r, int m, int overlap,
+                           const void* out, int out_fmt, const uint8_t* out_scales, int64_t out_bstride) {
+    if (B < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
     if (B > 65535) return fail(CSL_EUNSUPPORTED, "%s: B > 65535", fn);
     if (m < 1) return fail(CSL_EINVAL, "%s: m must be >= 1", fn);
     if (d < 32 || d > 1024 || d % 32) return fail(CSL_EUNSUPPORTED, "%s: d = %d must be a multiple of 32 in [32, 1024]", fn, d);
     if (x_fmt != CSL_F32 && x_fmt != CSL_BF16) return fail(CSL_EINVAL, "%s: x_fmt must be F32 or BF16", fn);
+    if (x_roles != 1 && x_roles != 2) return fail(CSL_EINVAL, "%s: x_roles must be 1 or 2", fn);
+    if (x_roles == 2 && !overlap) return fail(CSL_EINVAL, "%s: two-role rows need overlapping windows", fn);
     if (out_fmt < CSL_F32 || out_fmt > CSL_MXFP4) return fail(CSL_EINVAL, "%s: unknown out_fmt %d", fn, out_fmt);
     if (out_fmt == CSL_KV_PACKED && (r < 0 || r > d || r % 8 || (d + r) % 16))
         return fail(CSL_EINVAL, "%s: packed output needs r %% 8 == 0, (d + r) %% 16 == 0, 0 <= r <= d", fn);
     if (z_ch != 1 && z_ch != d) return fail(CSL_EINVAL, "%s: z_ch must be 1 or d", fn);
-    if ((int64_t)n_e * m > ((int64_t)1 << 40)) return fail(CSL_EINVAL, "%s: entry range too large", fn);
-    if (B == 0 || n_e == 0) { g_err.clear(); return CSL_OK; }
+    if (B == 0) return CSL_OK;
     if (!x || !z || !bias || !out) return fail(CSL_EINVAL, "%s: null x, z, bias or out", fn);
     if ((out_fmt == CSL_MXFP4) != (out_scales != nullptr)) return fail(CSL_EINVAL, "%s: out_scales must be given exactly for MXFP4", fn);
     if (!al16(x) || (x_bstride & 15) || !al16(out) || (out_bstride & 15))
         return fail(CSL_EINVAL, "%s: x/out and their strides must be 16-byte aligned", fn);
     if (z_ch == d ? (!al16(z) || (z_bstride & 15) || !al16(bias)) : (!al4(z) || (z_bstride & 3) || !al4(bias)))
         return fail(CSL_EINVAL, "%s: z/bias misaligned", fn);
+    return CSL_OK;
+}
+
+int kv_compress(const void* x, int x_fmt, int x_roles, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
+                const float* z, int z_ch, int64_t z_bstride, const float* bias,
+                int B, int d, int r, int m, int overlap, int64_t e_begin, int64_t n_e,
+                void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
+                void* stream) {
+    const char* fn = "kv_compress";
+    if (n_e < 0 || n_tok < 0 || e_begin < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
+    if ((int64_t)n_e * m > ((int64_t)1 << 40)) return fail(CSL_EINVAL, "%s: entry range too large", fn);
+    if (B == 0 || n_e == 0) {
+        int rc = compress_common(fn, x, x_fmt, x_roles, x_bstride, z, z_ch, z_bstride, bias, 0, d, r, m, overlap, out,
+                                 out_fmt, out_scales, out_bstride);
+        if (rc) return rc;
+        g_err.clear();
+        return CSL_OK;
+    }
+    int rc = compress_common(fn, x, x_fmt, x_roles, x_bstride, z, z_ch, z_bstride, bias, B, d, r, m, overlap, out,
+                             out_fmt, out_scales, out_bstride);
+    if (rc) return rc;
     const int win = overlap ? 2 * m : m;
     int64_t lo = (e_begin + 1) * m - win;
     if (lo < 0) lo = 0;
@@ -240,11 +284,60 @@ int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int
     if (lo < x_pos0 || hi >= x_pos0 + n_tok)
         return fail(CSL_EINVAL, "%s: raw positions %lld..%lld are not all in the buffer [%lld, %lld)", fn,
                     (long long)lo, (long long)hi, (long long)x_pos0, (long long)(x_pos0 + n_tok));
-    int rc = check_device();
+    rc = check_device();
     if (rc) return rc;
-    csl::CompressArgs a{(const uint8_t*)x, x_fmt, x_bstride, x_pos0, n_tok, z, z_ch, z_bstride, bias,
-                        B, d, r, m, overlap ? 1 : 0, e_begin, n_e,
-                        (uint8_t*)out, out_fmt, out_scales, out_bstride, sc_bstride};
+    csl::CompressArgs a{};
+    a.x = (const uint8_t*)x; a.x_fmt = x_fmt; a.x_bstride = x_bstride; a.x_pos0 = x_pos0; a.n_tok = n_tok;
+    a.x_rows = 0; a.x_roles = x_roles;
+    a.z = z; a.z_ch = z_ch; a.z_bstride = z_bstride; a.bias = bias;
+    a.B = B; a.d = d; a.r = r; a.m = m; a.overlap = overlap ? 1 : 0; a.e_begin = e_begin; a.n_e = n_e;
+    a.out = (uint8_t*)out; a.out_fmt = out_fmt; a.out_scales = out_scales; a.out_bstride = out_bstride;
+    a.sc_bstride = sc_bstride;
+    return launched(csl::launch_compress(a, (hipStream_t)stream));
+}
+
+int kv_compress_step(const void* x_ring, int x_fmt, int x_roles, int64_t x_bstride, int64_t x_rows,
+                     const float* z_ring, int z_ch, int64_t z_bstride, const float* bias,
+                     const int32_t* pos, int B, int T, int d, int r, int m, int overlap,
+                     void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
+                     int64_t n_cap, const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                     int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks, void* stream) {
+    const char* fn = "kv_compress_step";
+    if (T < 0) return fail(CSL_EINVAL, "%s: negative T", fn);
+    if (T > 65535) return fail(CSL_EUNSUPPORTED, "%s: T > 65535", fn);
+    int rc = compress_common(fn, x_ring, x_fmt, x_roles, x_bstride, z_ring, z_ch, z_bstride, bias, B, d, r, m,
+                             overlap, out, out_fmt, out_scales, block_table ? 0 : out_bstride);
+    if (rc) return rc;
+    const int win = overlap ? 2 * m : m;
+    if (x_rows < win + T - 1)
+        return fail(CSL_EINVAL, "%s: a ring of %lld rows cannot hold the %d-row window of T = %d new tokens", fn,
+                    (long long)x_rows, win, T);
+    if (B * (int64_t)T == 0) { g_err.clear(); return CSL_OK; }
+    if (!pos || !al4(pos)) return fail(CSL_EINVAL, "%s: null or misaligned pos", fn);
+    Paged pg;
+    if (block_table) {
+        pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+        pg.sblk_bytes = scale_block_bytes; pg.n_blocks = n_blocks;
+        if ((rc = validate_paged(fn, pg, (int64_t)bt_stride * (entries_per_block > 0 ? entries_per_block : 1),
+                                 row_bytes(out_fmt, d, r))))
+            return rc;
+        if (out_fmt == CSL_MXFP4 && scale_block_bytes < (int64_t)entries_per_block * (d / 32))
+            return fail(CSL_EINVAL, "%s: scale_block_bytes cannot hold entries_per_block scale rows", fn);
+    } else if (n_cap < 0) {
+        return fail(CSL_EINVAL, "%s: negative n_cap", fn);
+    }
+    rc = check_device();
+    if (rc) return rc;
+    csl::CompressArgs a{};
+    a.x = (const uint8_t*)x_ring; a.x_fmt = x_fmt; a.x_bstride = x_bstride; a.x_pos0 = 0; a.n_tok = x_rows;
+    a.x_rows = x_rows; a.x_roles = x_roles;
+    a.z = z_ring; a.z_ch = z_ch; a.z_bstride = z_bstride; a.bias = bias;
+    a.B = B; a.d = d; a.r = r; a.m = m; a.overlap = overlap ? 1 : 0; a.e_begin = 0; a.n_e = T;
+    a.out = (uint8_t*)out; a.out_fmt = out_fmt; a.out_scales = out_scales; a.out_bstride = out_bstride;
+    a.sc_bstride = sc_bstride;
+    a.pos = pos; a.n_cap = n_cap;
+    if (block_table) { a.bt = pg.bt; a.bt_stride = pg.bt_stride; a.epb = pg.epb; a.blk_bytes = pg.blk_bytes;
+                       a.sblk_bytes = pg.sblk_bytes; a.n_blocks = pg.n_blocks; }
     return launched(csl::launch_compress(a, (hipStream_t)stream));
 }
 
@@ -289,6 +382,7 @@ size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k) {
 // scratch (use_scratch true, index_topk_noalloc).
 static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
                       const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                      const Paged* pg,
                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
                       int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
     if (B < 0 || Tq < 0 || n_cap < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
@@ -312,6 +406,12 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
         return fail(CSL_EINVAL, "%s: scale arrays must be given exactly for MXFP4", fn);
     if (!al16(qi) || !al16(ki) || (ki_bstride & 15) || !al4(w) || !al4(q_pos) || !al4(out_idx) || !al4(out_score))
         return fail(CSL_EINVAL, "%s: misaligned pointer or stride", fn);
+    if (pg) {
+        if (int rc = validate_paged(fn, *pg, n_cap, row_bytes(ki_fmt, d_I, 0))) return rc;
+        if (pg->epb % 16) return fail(CSL_EUNSUPPORTED, "%s: entries_per_block must be a multiple of 16", fn);
+        if (ki_fmt == CSL_MXFP4 && pg->sblk_bytes < (int64_t)pg->epb * (d_I / 32))
+            return fail(CSL_EINVAL, "%s: scale_block_bytes cannot hold entries_per_block scale rows", fn);
+    }
     if (use_scratch) {
         if (need > NOALLOC_SCRATCH_BYTES)
             return fail(CSL_EWORKSPACE, "%s: this call needs %zu bytes of scratch, more than the %zu bytes the library "
@@ -329,6 +429,8 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
     csl::IndexArgs a{};
     a.qi = (const uint8_t*)qi; a.qi_fmt = qi_fmt; a.qi_scales = qi_scales; a.w = w;
     a.ki = (const uint8_t*)ki; a.ki_fmt = ki_fmt; a.ki_scales = ki_scales; a.ki_bstride = ki_bstride; a.ks_bstride = ks_bstride;
+    if (pg) { a.bt = pg->bt; a.bt_stride = pg->bt_stride; a.epb = pg->epb; a.blk_bytes = pg->blk_bytes;
+              a.sblk_bytes = pg->sblk_bytes; a.n_blocks = pg->n_blocks; }
     a.q_pos = q_pos; a.B = B; a.Tq = Tq; a.H_I = H_I; a.d_I = d_I; a.m = m; a.n_cap = n_cap; a.k = k;
     a.out_idx = out_idx; a.out_score = out_score;
     a.S = S; a.nslices = nslices;
@@ -359,7 +461,20 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
                const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
                const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
                int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
-    return index_impl("index_topk", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride, q_pos,
+    return index_impl("index_topk", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride, nullptr,
+                      q_pos, B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, ws, ws_bytes, false, stream);
+}
+
+int index_topk_paged(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                     const void* ki_pool, int ki_fmt, const uint8_t* ki_scale_pool,
+                     const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                     int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks,
+                     const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                     int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    Paged pg;
+    pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+    pg.sblk_bytes = scale_block_bytes; pg.n_blocks = n_blocks;
+    return index_impl("index_topk_paged", qi, qi_fmt, qi_scales, w, ki_pool, ki_fmt, ki_scale_pool, 0, 0, &pg, q_pos,
                       B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, ws, ws_bytes, false, stream);
 }
 
@@ -368,7 +483,7 @@ int index_topk_noalloc(const void* qi, int qi_fmt, const uint8_t* qi_scales, con
                        const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
                        int32_t* out_idx, float* out_score, void* stream) {
     return index_impl("index_topk_noalloc", qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, ki_bstride, ks_bstride,
-                      q_pos, B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, nullptr, 0, true, stream);
+                      nullptr, q_pos, B, Tq, H_I, d_I, m, n_cap, k, out_idx, out_score, nullptr, 0, true, stream);
 }
 
 size_t csl_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
@@ -380,20 +495,24 @@ size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max) {
     return attend_ws(B, Tq, d, nhb, nsplit);
 }
 
+}  // extern "C"
+
 static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride,
-                       int64_t n_cap, const int32_t* idx, int k, int m, const void* kv_w, int64_t kvw_bstride,
-                       int64_t kvw_pos0, int64_t kvw_rows, const int32_t* q_pos, int W, int B, int Tq, int H, int d,
-                       int r, float scale, void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes,
-                       void* stream) {
-    int rc = validate_attend(fn, q, q_fmt, kv_c, kv_fmt, kvc_bstride, n_cap, kv_w, kvw_bstride, kvw_rows, q_pos, W,
-                             B, Tq, H, d, r, out, out_fmt);
+                       const Paged* pg, int64_t n_cap, const int32_t* idx, int k, int m, const void* kv_w,
+                       int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
+                       const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale, void* out,
+                       int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate_attend(fn, q, q_fmt, kv_c, kv_fmt, pg ? 0 : kvc_bstride, n_cap, kv_w, kvw_bstride, kvw_rows,
+                             q_pos, W, B, Tq, H, d, r, out, out_fmt);
     if (rc) return rc;
+    if (pg && (rc = validate_paged(fn, *pg, n_cap, row_bytes(kv_fmt, d, r)))) return rc;
     const int64_t rows_max = (idx ? (int64_t)k : n_cap) + W;
     int nhb, nsplit, rps;
     plan_attend(B, Tq, H, rows_max, true, nhb, nsplit, rps);
     const size_t need = attend_ws(B, Tq, d, nhb, nsplit);
     if (B * (int64_t)Tq == 0) { g_err.clear(); return CSL_OK; }
     if (out_lse && !al4(out_lse)) return fail(CSL_EINVAL, "%s: out_lse misaligned", fn);
+    if (sink && !al4(sink)) return fail(CSL_EINVAL, "%s: sink misaligned", fn);
     if (need > 0 && (!ws || ws_bytes < need || !al16(ws)))
         return fail(CSL_EWORKSPACE, "%s: needs %zu bytes of 16-byte aligned workspace", fn, need);
     rc = check_device();
@@ -401,8 +520,10 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
     csl::AttendArgs a{};
     a.q = (const uint8_t*)q; a.q_fmt = q_fmt;
     a.kvc = (const uint8_t*)kv_c; a.kv_fmt = kv_fmt; a.kvc_bstride = kvc_bstride; a.n_cap = n_cap;
+    if (pg) { a.bt = pg->bt; a.bt_stride = pg->bt_stride; a.epb = pg->epb; a.blk_bytes = pg->blk_bytes; a.n_blocks = pg->n_blocks; }
     a.idx = idx; a.k = k; a.m = m;
     a.kvw = (const uint8_t*)kv_w; a.kvw_bstride = kvw_bstride; a.kvw_pos0 = kvw_pos0; a.kvw_rows = kvw_rows > 0 ? kvw_rows : 1;
+    a.sink = sink;
     a.q_pos = q_pos; a.W = W; a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.r = r; a.scale = scale;
     a.out = (uint8_t*)out; a.out_fmt = out_fmt; a.lse = out_lse;
     a.nhb = nhb; a.nsplit = nsplit; a.rps = rps;
@@ -414,24 +535,62 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
     return launched(csl::launch_attend(a, (hipStream_t)stream));
 }
 
+static int csa_check(const char* fn, const int32_t* idx, int k, int B, int Tq) {
+    if (k < 1) return fail(CSL_EINVAL, "%s: k must be >= 1", fn);
+    if (B * (int64_t)Tq > 0 && (!idx || !al4(idx))) return fail(CSL_EINVAL, "%s: null or misaligned idx", fn);
+    return CSL_OK;
+}
+
+extern "C" {
+
 int csa_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap,
                const int32_t* idx, int k,
-               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
                void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
-    if (k < 1) return fail(CSL_EINVAL, "csa_attend: k must be >= 1");
-    if (B * (int64_t)Tq > 0 && (!idx || !al4(idx))) return fail(CSL_EINVAL, "csa_attend: null or misaligned idx");
-    return attend_impl("csa_attend", q, q_fmt, kv_c, kv_fmt, kvc_bstride, n_cap, idx, k, 1, kv_w, kvw_bstride,
-                       kvw_pos0, kvw_rows, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse, ws, ws_bytes, stream);
+    if (int rc = csa_check("csa_attend", idx, k, B, Tq)) return rc;
+    return attend_impl("csa_attend", q, q_fmt, kv_c, kv_fmt, kvc_bstride, nullptr, n_cap, idx, k, 1, kv_w,
+                       kvw_bstride, kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse,
+                       ws, ws_bytes, stream);
 }
 
 int hca_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap, int m,
-               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
                void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
     if (m < 1) return fail(CSL_EINVAL, "hca_attend: m must be >= 1");
-    return attend_impl("hca_attend", q, q_fmt, kv_c, kv_fmt, kvc_bstride, n_cap, nullptr, 0, m, kv_w, kvw_bstride,
-                       kvw_pos0, kvw_rows, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse, ws, ws_bytes, stream);
+    return attend_impl("hca_attend", q, q_fmt, kv_c, kv_fmt, kvc_bstride, nullptr, n_cap, nullptr, 0, m, kv_w,
+                       kvw_bstride, kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse,
+                       ws, ws_bytes, stream);
+}
+
+int csa_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, const int32_t* block_table,
+                     int64_t bt_stride, int entries_per_block, int64_t block_bytes, int64_t n_blocks, int64_t n_cap,
+                     const int32_t* idx, int k,
+                     const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
+                     const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                     void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+    if (int rc = csa_check("csa_attend_paged", idx, k, B, Tq)) return rc;
+    Paged pg;
+    pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+    pg.n_blocks = n_blocks;
+    return attend_impl("csa_attend_paged", q, q_fmt, kv_pool, kv_fmt, 0, &pg, n_cap, idx, k, 1, kv_w, kvw_bstride,
+                       kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse, ws, ws_bytes,
+                       stream);
+}
+
+int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, const int32_t* block_table,
+                     int64_t bt_stride, int entries_per_block, int64_t block_bytes, int64_t n_blocks, int64_t n_cap,
+                     int m, const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+                     const float* sink, const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                     void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+    if (m < 1) return fail(CSL_EINVAL, "hca_attend_paged: m must be >= 1");
+    Paged pg;
+    pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+    pg.n_blocks = n_blocks;
+    return attend_impl("hca_attend_paged", q, q_fmt, kv_pool, kv_fmt, 0, &pg, n_cap, nullptr, 0, m, kv_w,
+                       kvw_bstride, kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse,
+                       ws, ws_bytes, stream);
 }
 
 }  // extern "C"

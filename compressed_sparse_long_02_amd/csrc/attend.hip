@@ -41,6 +41,36 @@ __device__ __forceinline__ int64_t att_n_visible(int64_t t, int m, int64_t n_cap
     return n < n_cap ? n : n_cap;
 }
 
+// Stored row of compressed entry s (0 <= s < n_cap) of sequence b: dense rows per
+// sequence, or, with a block table, row s % epb of physical block bt[b][s / epb] (a
+// block id outside [0, n_blocks) is an absent block: nullptr, the row is skipped).
+__device__ __forceinline__ const uint8_t* att_entry_row(const AttendArgs& a, int b, int64_t s, int64_t rb) {
+    if (!a.bt) return a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+    const uint32_t su = (uint32_t)s, ep = (uint32_t)a.epb;
+    const uint32_t lb = su / ep;
+    const int32_t blk = a.bt[(int64_t)b * a.bt_stride + lb];
+    if (blk < 0 || blk >= a.n_blocks) return nullptr;
+    return a.kvc + (int64_t)blk * a.blk_bytes + (int64_t)(su - lb * ep) * rb;
+}
+
+// Final normalisation of a query's (unsplit) softmax, base 2: the accumulated rows give
+// lse2 = m_ref + log2(l); a sink logit s (natural units) joins the denominator.
+// Returns the factor that turns the accumulated output into the result, and the lse
+// (natural log).  Without a sink the factor is 1/l, as before.
+__device__ __forceinline__ void att_finish(float m_ref, float l, const float* sink, int h, float& inv, float& lse) {
+    if (!sink) {
+        inv = l > 0.f ? 1.f / l : 0.f;
+        lse = l > 0.f ? (m_ref + log2f(l)) * CSL_LN2 : -INFINITY;
+        return;
+    }
+    const float s2 = sink[h] * CSL_LOG2E;
+    const float L2 = l > 0.f ? m_ref + log2f(l) : -INFINITY;
+    const float T = fmaxf(L2, s2);
+    const float lse2 = T + log2f(exp2f(L2 - T) + exp2f(s2 - T));
+    inv = l > 0.f ? exp2f(m_ref - lse2) : 0.f;
+    lse = lse2 * CSL_LN2;
+}
+
 constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (host plan)
 
 constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
@@ -103,7 +133,7 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
                 if (v < v_end) {
                     if (v < n_ent) {
                         const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
-                        if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+                        if (s >= 0 && s < a.n_cap) p = att_entry_row(a, b, s, rb);
                     } else {
                         const int64_t pos = w0 + (v - n_ent);
                         int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
@@ -226,8 +256,13 @@ __global__ void __launch_bounds__(ATT_NT, 2) k_attend(AttendArgs a) {
     // ---- finish: normalise, write output or the split's partial
     const int hh = wv * 16 + col;                  // head within the block
     const int h = hb * 64 + hh;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
+    float inv, lse;
+    if (a.nsplit == 1) {
+        att_finish(m_run, l_run, h < a.H ? a.sink : nullptr, h, inv, lse);
+    } else {                                        // a split's partial: no sink (the combine adds it)
+        inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
+    }
     if (a.nsplit == 1) {
         if (h < a.H) {
             if (a.out_fmt == F32) {
@@ -373,7 +408,7 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
                 if (v < v_end) {
                     if (v < n_ent) {
                         const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
-                        if (s >= 0 && s < a.n_cap) p = a.kvc + (int64_t)b * a.kvc_bstride + s * rb;
+                        if (s >= 0 && s < a.n_cap) p = att_entry_row(a, b, s, rb);
                     } else {
                         const int64_t pos = w0 + (v - n_ent);
                         int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
@@ -569,8 +604,13 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
     {
         const int hh = 16 * hg + col;                   // head within the block
         const int h = hb * 64 + hh;
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
+        float inv, lse;
+        if (a.nsplit == 1) {
+            att_finish(m_run, l_run, h < a.H ? a.sink : nullptr, h, inv, lse);
+        } else {                                    // a split's partial: no sink (the combine adds it)
+            inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            lse = l_run > 0.f ? (m_run + log2f(l_run)) * CSL_LN2 : -INFINITY;
+        }
         const int d0 = 16 * NDH * dh + 4 * g;
         if (a.nsplit == 1) {
             if (h < a.H) {
@@ -655,6 +695,10 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        // a sink logit joins the denominator (once per query, not per split)
+        const bool has_sink = a.sink != nullptr && hb * 64 + hh < a.H;
+        const float sk = has_sink ? a.sink[hb * 64 + hh] : -INFINITY;
+        M = fmaxf(M, sk);
         float den;
         {
             const float w = M == -INFINITY ? 0.f : expf(l_first - M);
@@ -672,6 +716,7 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
         // fixed-order sum over the wave (butterfly: every lane gets the same bits)
 #pragma unroll
         for (int o = 1; o <= 32; o <<= 1) den += __shfl_xor(den, o, 64);
+        if (has_sink) den += expf(sk - M);
         const float inv = den > 0.f ? 1.f / den : 0.f;
         for (int s0 = 0; s0 < ns; s0 += 64)
             if (s0 + lane < ns) wts[wv * ns + s0 + lane] *= inv;

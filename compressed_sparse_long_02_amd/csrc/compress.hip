@@ -86,10 +86,25 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     const int c0 = (int)blockIdx.z * dt + tr * 8;
     const int b = blockIdx.y;
     const int64_t q = (int64_t)blockIdx.x * G.EPB + ep;
-    const bool active = ep < G.EPB && q < a.n_e;
-    const int64_t i = a.e_begin + (active ? q : 0);
+    bool active = ep < G.EPB && q < a.n_e;
+    int64_t i;
+    if (a.pos) {                                         // decode-time step: the entry token q completes
+        const int64_t p = active ? a.pos[(int64_t)b * a.n_e + q] : -1;
+        active = active && p >= 0 && (p + 1) % a.m == 0;
+        i = active ? (p + 1) / a.m - 1 : 0;
+    } else {
+        i = a.e_begin + (active ? q : 0);
+    }
     const int64_t p0 = (i + 1) * a.m - win;
-    const int64_t xrb = XF == F32 ? 4 * (int64_t)a.d : 2 * (int64_t)a.d;
+    const int64_t xrb = (XF == F32 ? 4 * (int64_t)a.d : 2 * (int64_t)a.d) * a.x_roles;
+    // raw row of window slot j: linear buffer or ring; a two-role row's current half
+    // (slots j >= m) starts d values in
+    auto xrow = [&](int jc) {
+        int64_t row = p0 + jc - a.x_pos0;
+        if (a.x_rows > 0) { row %= a.x_rows; if (row < 0) row += a.x_rows; }
+        return row;
+    };
+    const int role_off = a.x_roles == 2 ? a.d : 0;
     constexpr int NC = ZC1 ? 1 : 8;   // softmax channels carried per thread
 
     float acc[8], mx[NC], den[NC];
@@ -118,8 +133,8 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
                 const int jw = jb + u * G.RG;
                 ok[u] = jw < win;
                 const int jc = ok[u] ? jw : jb;
-                const int64_t row = p0 + jc - a.x_pos0;
-                load8<XF>(xb + row * xrb, c0, xv[u]);
+                const int64_t row = xrow(jc);
+                load8<XF>(xb + row * xrb, c0 + (jc >= a.m ? role_off : 0), xv[u]);
                 if constexpr (ZC1) {
                     lg[u][0] = zb[row] + a.bias[jc];
                 } else {
@@ -225,12 +240,32 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) v[c] = active ? acc[c] / den[ZC1 ? 0 : c] : 0.f;   // final in row group 0
-    const bool writer = active && rg == 0;
+    bool writer = active && rg == 0;
 
-    uint8_t* ob = a.out + (int64_t)b * a.out_bstride;
+    // this entry's output row (and MXFP4 scale row)
+    const int64_t orb = OF == F32 ? 4 * (int64_t)a.d : (OF == BF16 ? 2 * (int64_t)a.d :
+                        (OF == KV_PACKED ? 2 * (int64_t)a.r + (a.d - a.r) : (int64_t)a.d / 2));
+    uint8_t* orow = nullptr;
+    uint8_t* osc = nullptr;
+    if (!a.pos) {
+        orow = a.out + (int64_t)b * a.out_bstride + q * orb;
+        if (OF == MXFP4) osc = a.out_scales + (int64_t)b * a.sc_bstride + q * (a.d / 32);
+    } else if (!a.bt) {
+        writer = writer && i < a.n_cap;
+        orow = a.out + (int64_t)b * a.out_bstride + i * orb;
+        if (OF == MXFP4) osc = a.out_scales + (int64_t)b * a.sc_bstride + i * (a.d / 32);
+    } else {
+        const int64_t lb = i / a.epb;
+        const int32_t blk = (writer && lb < a.bt_stride) ? a.bt[(int64_t)b * a.bt_stride + lb] : -1;
+        writer = writer && blk >= 0 && blk < a.n_blocks;
+        const int64_t off = i - lb * a.epb;
+        orow = a.out + (int64_t)blk * a.blk_bytes + off * orb;
+        if (OF == MXFP4) osc = a.out_scales + (int64_t)blk * a.sblk_bytes + off * (a.d / 32);
+    }
+
     if (OF == F32) {
         if (writer) {
-            float* o = (float*)(ob + q * 4 * (int64_t)a.d) + c0;
+            float* o = (float*)orow + c0;
             *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
             *(float4*)(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
         }
@@ -239,12 +274,11 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
             u32x4 o;
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) o[k2] = f32_to_bf16_rne(v[2 * k2]) | (f32_to_bf16_rne(v[2 * k2 + 1]) << 16);
-            *(u32x4*)(ob + q * 2 * (int64_t)a.d + (int64_t)c0 * 2) = o;
+            *(u32x4*)(orow + (int64_t)c0 * 2) = o;
         }
     } else if (OF == KV_PACKED) {
         if (writer) {
-            const int64_t rb = 2 * (int64_t)a.r + (a.d - a.r);
-            uint8_t* row = ob + q * rb;
+            uint8_t* row = orow;
             if (c0 < a.r) {
                 u32x4 o;
 #pragma unroll
@@ -271,8 +305,8 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) w |= f32_to_e2m1_rne_sat(ldexpf(v[c], -e)) << (4 * c);
         if (writer) {
-            *(uint32_t*)(ob + q * (int64_t)(a.d / 2) + c0 / 2) = w;
-            if ((c0 & 31) == 0) a.out_scales[(int64_t)b * a.sc_bstride + q * (a.d / 32) + c0 / 32] = (uint8_t)(e + 127);
+            *(uint32_t*)(orow + c0 / 2) = w;
+            if ((c0 & 31) == 0) osc[c0 / 32] = (uint8_t)(e + 127);
         }
     }
 }

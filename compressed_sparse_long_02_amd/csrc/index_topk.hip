@@ -392,6 +392,7 @@ k_idx_score(IndexArgs a) {
     uint32_t* sh = smem + a.S + (a.S >> le);
     uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the padded histogram
     uint32_t* ctr = SPLIT ? hs + TOPK_HSZ + 24 : sh + TOPK_SCRATCH(IDX_NT);   // next tile group
+    int32_t* ids = (int32_t*)(ctr + 4);                  // paged keys: the slice's block ids
 
     const int64_t t = a.q_pos[bq];
     const int64_t n = n_visible(t, a.m, a.n_cap);
@@ -402,6 +403,15 @@ k_idx_score(IndexArgs a) {
         for (int x = tid; x < TOPK_HSZ; x += IDX_NT) hs[x] = 0u;
     }
     if (tid == 0) *ctr = 0u;
+    // paged keys: the block ids of the slice's keys (a 16-key tile lies in one block)
+    const int64_t blk0 = a.bt ? s0 / a.epb : 0;
+    if (a.bt && ns > 0) {
+        const int nid = (int)((s0 + ns - 1) / a.epb - blk0 + 1);
+        for (int x = tid; x < nid; x += IDX_NT) {
+            const int32_t v = a.bt[(int64_t)b * a.bt_stride + blk0 + x];
+            ids[x] = (v >= 0 && v < a.n_blocks) ? v : -1;
+        }
+    }
     __syncthreads();
 
     if (ns > 0) {
@@ -437,7 +447,18 @@ k_idx_score(IndexArgs a) {
             int li = T * 16 + col;
             li = li < ns ? li : ns - 1;
             const int64_t row = s0 + li;
-            f.load(kbase + row * rb, sbase ? sbase + row * (DI / 32) : nullptr, g);
+            if (!a.bt) {
+                f.load(kbase + row * rb, sbase ? sbase + row * (DI / 32) : nullptr, g);
+            } else {
+                const uint32_t rl = (uint32_t)(row - blk0 * a.epb), ep = (uint32_t)a.epb;
+                const uint32_t lb = rl / ep;
+                const int32_t blk = ids[lb];
+                // an absent block reads the query's own row (in bounds); its keys score -inf
+                const int64_t off = (int64_t)(rl - lb * ep);
+                f.load(blk >= 0 ? a.ki + (int64_t)blk * a.blk_bytes + off * rb : a.qi,
+                       a.ki_scales ? (blk >= 0 ? a.ki_scales + (int64_t)blk * a.sblk_bytes + off * (DI / 32)
+                                               : a.qi_scales) : nullptr, g);
+            }
         };
         // per lane: the 16 heads of its row group for its key, ReLU-gated and weighted
         auto head_sum = [&](const KeyFrag<FMT, DI>& f) {
@@ -493,7 +514,8 @@ k_idx_score(IndexArgs a) {
             const int T = IDX_UNR * k + ((g & 1) << 1 | g >> 1);
             const int li = T * 16 + col;
             if (T < ntile && li < ns) {
-                const uint32_t u = score_key(tot);
+                const bool absent = a.bt && ids[(uint32_t)(s0 + li - blk0 * a.epb) / (uint32_t)a.epb] < 0;
+                const uint32_t u = absent ? score_key(-INFINITY) : score_key(tot);
                 if constexpr (SPLIT) {
                     keys[li] = u;
                     atomicAdd(&hs[hpad(u >> (32 - TOPK_BITS))], 1u);
@@ -653,7 +675,12 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
             const int c = tid + DNS_NT * j < DNS_KT * 16 ? tid + DNS_NT * j : DNS_KT * 16 - 1;
             int64_t key = k0 + (int64_t)t * DNS_KT + (c >> 4);
             key = key < k1 ? key : k1 - 1;
-            R[j] = ld_global<u32x4>(kbase + key * 256 + 16 * (c & 15));
+            const uint8_t* kp = kbase + key * 256;
+            if (a.bt) {                                  // paged keys (an absent block reads key 0 of the query)
+                const int32_t blk = a.bt[(int64_t)b * a.bt_stride + key / a.epb];
+                kp = (blk >= 0 && blk < a.n_blocks) ? a.ki + (int64_t)blk * a.blk_bytes + (key % a.epb) * 256 : a.qi;
+            }
+            R[j] = ld_global<u32x4>(kp + 16 * (c & 15));
         }
     };
     auto store_tile = [&](int buf) {
@@ -707,7 +734,12 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
                 const float tot = __uint_as_float(bsw[0]) + __uint_as_float(bsw[1]);
                 const int64_t sidx = k0 + (int64_t)t * DNS_KT + 16 * (4 * k4 + ((g & 1) << 1 | g >> 1)) + col;
                 if (sidx < n) {
-                    const uint32_t key = score_key(tot);
+                    bool absent = false;
+                    if (a.bt) {
+                        const int32_t blk = a.bt[(int64_t)b * a.bt_stride + sidx / a.epb];
+                        absent = blk < 0 || blk >= a.n_blocks;
+                    }
+                    const uint32_t key = score_key(absent ? -INFINITY : tot);
                     srow[sidx] = key;
                     const uint32_t bin = key >> 21;
                     atomicAdd(&hist[qw * (TOPK_BINS / 2) + (bin >> 1)], 1u << (16 * (bin & 1)));
@@ -1208,8 +1240,9 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
 template <int FMT, int DI, int HB, bool SPLIT>
 static void launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
-    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 32)               // keys, histogram, scan, misc, counter
-                             : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT) + 4);   // keys, scratch, counter
+    const size_t nid = a.bt ? (size_t)a.S / 16 + 2 : 0;                                         // paged: block ids
+    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 32 + nid)         // keys, histogram, scan, misc, counter
+                             : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT) + 4 + nid);   // keys, scratch, counter
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
 }

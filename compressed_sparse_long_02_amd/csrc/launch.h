@@ -10,15 +10,27 @@ constexpr int IDX_SLOT_W = 2048 + 8;   // words per slice histogram list: count,
 
 struct CompressArgs {
     const uint8_t* x; int x_fmt; int64_t x_bstride; int64_t x_pos0; int64_t n_tok;
+    int64_t x_rows;              // > 0: x and z are rings (position p in row (p - x_pos0) mod x_rows)
+    int x_roles;                 // 2: a raw row holds a look-back value, then a current value
     const float* z; int z_ch; int64_t z_bstride;
     const float* bias;
     int B, d, r, m, overlap; int64_t e_begin, n_e;
     uint8_t* out; int out_fmt; uint8_t* out_scales; int64_t out_bstride, sc_bstride;
+    // decode-time step (pos != nullptr): token q of sequence b at pos[b*n_e + q] compresses
+    // entry (pos+1)/m - 1 when (pos+1) % m == 0, written at its absolute index in the cache:
+    // out + b*out_bstride + e*row (e < n_cap), or, with a block table, row e % epb of block
+    // bt[b*bt_stride + e/epb] (blocks blk_bytes apart; scales sblk_bytes apart)
+    const int32_t* pos; int64_t n_cap;
+    const int32_t* bt; int64_t bt_stride; int epb; int64_t blk_bytes, sblk_bytes, n_blocks;
 };
 
 struct IndexArgs {
     const uint8_t* qi; int qi_fmt; const uint8_t* qi_scales; const float* w;
     const uint8_t* ki; int ki_fmt; const uint8_t* ki_scales; int64_t ki_bstride, ks_bstride;
+    // paged keys (bt != nullptr): key s of sequence b is row s % epb of block bt[b * bt_stride
+    // + s / epb], blocks blk_bytes apart from ki (its scales: sblk_bytes apart from ki_scales);
+    // ids outside [0, n_blocks) are absent blocks (their keys score -inf); epb % 16 == 0
+    const int32_t* bt; int64_t bt_stride; int epb; int64_t blk_bytes, sblk_bytes, n_blocks;
     const int32_t* q_pos;
     int B, Tq, H_I, d_I, m; int64_t n_cap; int k;
     int32_t* out_idx; float* out_score;
@@ -47,6 +59,11 @@ struct AttendArgs {
     const int32_t* idx; int k;   // CSA: selected entries (idx != nullptr)
     int m;                       // HCA: entries visible at t are s < floor((t+1)/m)
     const uint8_t* kvw; int64_t kvw_bstride, kvw_pos0, kvw_rows;
+    const float* sink;           // [H] sink logits, or nullptr
+    // paged entries (bt != nullptr): entry s of sequence b is row s % epb of block
+    // bt[b * bt_stride + s / epb], blocks blk_bytes apart from kvc; ids outside
+    // [0, n_blocks) are absent blocks
+    const int32_t* bt; int64_t bt_stride; int epb; int64_t blk_bytes, n_blocks;
     const int32_t* q_pos; int W, B, Tq, H, d, r; float scale;
     uint8_t* out; int out_fmt; float* lse;
     // plan

@@ -41,13 +41,19 @@ def _need_cuda(*ts):
             raise ValueError("tensors must live on the GPU")
 
 
+def _check_table(bt):
+    _need_cuda(bt)
+    if bt.dtype != torch.int32 or not bt.is_contiguous() or bt.dim() != 2:
+        raise ValueError("block table must be contiguous int32 [B, max_blocks]")
+
+
 def _rows_ok(t: torch.Tensor, rb: int, name: str):
     """Rows of one sequence must be dense: dim-1 stride == row bytes."""
     if t.dim() < 2:
         raise ValueError("%s must be [B, N, ...]" % name)
     if t.shape[1] > 1 and t.stride(1) * t.element_size() != rb:
         raise ValueError("%s: rows of a sequence must be dense (%d bytes each)" % (name, rb))
-    if t.dim() > 2 and not t[0, 0].is_contiguous():
+    if t.dim() > 2 and t.shape[0] > 0 and t.shape[1] > 0 and not t[0, 0].is_contiguous():
         raise ValueError("%s: a row must be contiguous" % name)
 
 
@@ -73,12 +79,13 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
 
 
 def kv_compress(x, x_fmt, z, bias, *, d, m, overlap, e_begin, n_e, r=0, x_pos0=0, out_fmt=F32, out=None,
-                out_scales=None):
-    """Compress raw rows x [B, n_tok, .] (F32 or BF16) into entries e_begin..e_begin+n_e-1.
-    z: float32 [B, n_tok, z_ch]; bias float32 [win, z_ch].  Returns (out, out_scales)."""
+                out_scales=None, x_roles=1):
+    """Compress raw rows x [B, n_tok, .] (F32 or BF16; x_roles*d values per row) into entries
+    e_begin..e_begin+n_e-1.  z: float32 [B, n_tok, z_ch]; bias float32 [win, z_ch].
+    Returns (out, out_scales)."""
     _need_cuda(x, z, bias, out, out_scales)
     B, n_tok = x.shape[0], x.shape[1]
-    _rows_ok(x, row_bytes(x_fmt, d), "x")
+    _rows_ok(x, row_bytes(x_fmt, x_roles * d), "x")
     if z.dtype != torch.float32 or bias.dtype != torch.float32:
         raise ValueError("z and bias must be float32")
     z_ch = z.shape[-1]
@@ -89,17 +96,50 @@ def kv_compress(x, x_fmt, z, bias, *, d, m, overlap, e_begin, n_e, r=0, x_pos0=0
     if out_fmt == MXFP4 and out_scales is None:
         out_scales = torch.empty((B, n_e, d // 32), dtype=torch.uint8, device=x.device)
     _rows_ok(out, orb, "out")
-    rc = _lib.lib().kv_compress(_ptr(x), x_fmt, _bstride(x), x_pos0, n_tok, _ptr(z), z_ch, _bstride(z), _ptr(bias),
-                                B, d, r, m, int(bool(overlap)), e_begin, n_e, _ptr(out), out_fmt,
+    rc = _lib.lib().kv_compress(_ptr(x), x_fmt, x_roles, _bstride(x), x_pos0, n_tok, _ptr(z), z_ch, _bstride(z),
+                                _ptr(bias), B, d, r, m, int(bool(overlap)), e_begin, n_e, _ptr(out), out_fmt,
                                 _ptr(out_scales) if out_fmt == MXFP4 else None, _bstride(out),
                                 _bstride(out_scales) if out_fmt == MXFP4 else 0, _stream())
     check("kv_compress", rc)
     return out, out_scales
 
 
+def kv_compress_step(x_ring, x_fmt, z_ring, bias, pos, *, d, m, overlap, out, out_fmt, r=0, out_scales=None,
+                     x_roles=1, pages=None):
+    """Decode-time compression from the state rings: x_ring [B, x_rows, .], z_ring float32
+    [B, x_rows, z_ch] (position p in row p % x_rows); pos int32 [B, T] new token positions.
+    out: the compressed cache -- linear [B, n_cap, row] (out_scales [B, n_cap, d/32]) or, with
+    pages = (block_table int32 [B, max_blocks], entries_per_block, block_bytes,
+    scale_block_bytes, n_blocks), a pool of blocks (out / out_scales point at the first
+    block's rows)."""
+    _need_cuda(x_ring, z_ring, bias, pos, out, out_scales)
+    B, x_rows = x_ring.shape[0], x_ring.shape[1]
+    if pos.dtype != torch.int32 or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32 [B, T]")
+    _rows_ok(x_ring, row_bytes(x_fmt, x_roles * d), "x_ring")
+    T = pos.shape[1]
+    sc = _ptr(out_scales) if out_fmt == MXFP4 else None
+    if pages is None:
+        _rows_ok(out, row_bytes(out_fmt, d, r), "out")
+        tail = (out.shape[1], None, 0, 0, 0, 0, 0)
+        ob, sb = _bstride(out), (_bstride(out_scales) if out_fmt == MXFP4 else 0)
+    else:
+        bt, epb, blk, sblk, nblk = pages
+        _check_table(bt)
+        tail = (0, _ptr(bt), bt.shape[1], epb, blk, sblk, nblk)
+        ob, sb = 0, 0
+    rc = _lib.lib().kv_compress_step(_ptr(x_ring), x_fmt, x_roles, _bstride(x_ring), x_rows, _ptr(z_ring),
+                                     z_ring.shape[-1], _bstride(z_ring), _ptr(bias), _ptr(pos), B, T, d, r, m,
+                                     int(bool(overlap)), _ptr(out), out_fmt, sc, ob, sb, *tail, _stream())
+    check("kv_compress_step", rc)
+    return out, out_scales
+
+
 def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None, out_idx=None,
-               out_score=None, with_scores=True):
+               out_score=None, with_scores=True, pages=None):
     """qi [B, Tq, H_I, .] in `fmt`; w float32 [B, Tq, H_I]; ki [B, N, .]; q_pos int32 [B, Tq].
+    pages = (block_table int32 [B, max_blocks], entries_per_block, block_bytes,
+    scale_block_bytes, n_blocks): ki / ki_scales point into pools of blocks (index_topk_paged).
     Returns (idx int32 [B, Tq, k], scores float32 [B, Tq, k] or None)."""
     _need_cuda(qi, w, ki, q_pos, qi_scales, ki_scales)
     B, Tq = q_pos.shape
@@ -107,7 +147,8 @@ def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, 
         raise ValueError("q_pos must be contiguous int32 [B, Tq]")
     if not qi.is_contiguous() or not w.is_contiguous() or w.dtype != torch.float32:
         raise ValueError("qi and w must be contiguous (w float32)")
-    _rows_ok(ki, row_bytes(fmt, d_I), "ki")
+    if pages is None:
+        _rows_ok(ki, row_bytes(fmt, d_I), "ki")
     dev = q_pos.device
     if out_idx is None:
         out_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
@@ -115,11 +156,20 @@ def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, 
         out_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
     nb = int(_lib.lib().csl_index_topk_workspace(B, Tq, n_cap, k))
     ws = workspace(nb, dev)
-    rc = _lib.lib().index_topk(_ptr(qi), fmt, _ptr(qi_scales), _ptr(w), _ptr(ki), fmt, _ptr(ki_scales),
-                               _bstride(ki), _bstride(ki_scales) if ki_scales is not None else 0, _ptr(q_pos),
-                               B, Tq, H_I, d_I, m, n_cap, k, _ptr(out_idx), _ptr(out_score), _ptr(ws),
-                               0 if ws is None else ws.numel(), _stream())
-    check("index_topk", rc)
+    wsn = 0 if ws is None else ws.numel()
+    if pages is None:
+        rc = _lib.lib().index_topk(_ptr(qi), fmt, _ptr(qi_scales), _ptr(w), _ptr(ki), fmt, _ptr(ki_scales),
+                                   _bstride(ki), _bstride(ki_scales) if ki_scales is not None else 0, _ptr(q_pos),
+                                   B, Tq, H_I, d_I, m, n_cap, k, _ptr(out_idx), _ptr(out_score), _ptr(ws), wsn,
+                                   _stream())
+        check("index_topk", rc)
+    else:
+        bt, epb, blk, sblk, nblk = pages
+        _check_table(bt)
+        rc = _lib.lib().index_topk_paged(_ptr(qi), fmt, _ptr(qi_scales), _ptr(w), _ptr(ki), fmt, _ptr(ki_scales),
+                                         _ptr(bt), bt.shape[1], epb, blk, sblk, nblk, _ptr(q_pos), B, Tq, H_I, d_I,
+                                         m, n_cap, k, _ptr(out_idx), _ptr(out_score), _ptr(ws), wsn, _stream())
+        check("index_topk_paged", rc)
     return out_idx, out_score
 
 
@@ -152,13 +202,16 @@ def _q_fmt(q):
 
 
 def _attend(name, q, kv_c, kv_w, q_pos, idx, *, kv_fmt, n_cap, m, kvw_pos0, kvw_rows, W, H, d, r, scale, out_fmt,
-            out, lse, with_lse):
-    _need_cuda(q, kv_c, kv_w, q_pos, idx, out, lse)
+            out, lse, with_lse, sink=None, pages=None):
+    _need_cuda(q, kv_c, kv_w, q_pos, idx, out, lse, sink)
     B, Tq = q_pos.shape
     if q_pos.dtype != torch.int32 or not q_pos.is_contiguous() or not q.is_contiguous():
         raise ValueError("q and q_pos must be contiguous (q_pos int32)")
+    if sink is not None and (sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < H):
+        raise ValueError("sink must be contiguous float32 [H]")
     rb = row_bytes(kv_fmt, d, r)
-    _rows_ok(kv_c, rb, "kv_c")
+    if pages is None:
+        _rows_ok(kv_c, rb, "kv_c")
     _rows_ok(kv_w, rb, "kv_w")
     dev = q.device
     if out is None:
@@ -169,31 +222,59 @@ def _attend(name, q, kv_c, kv_w, q_pos, idx, *, kv_fmt, n_cap, m, kvw_pos0, kvw_
     nb = int(_lib.lib().csl_attend_workspace(B, Tq, H, d, rows_max))
     ws = workspace(nb, dev)
     L = _lib.lib()
-    if name == "csa_attend":
-        if idx.dtype != torch.int32 or not idx.is_contiguous():
-            raise ValueError("idx must be contiguous int32 [B, Tq, k]")
-        rc = L.csa_attend(_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _bstride(kv_c), n_cap, _ptr(idx), idx.shape[-1],
-                          _ptr(kv_w), _bstride(kv_w), kvw_pos0, kvw_rows, _ptr(q_pos), W, B, Tq, H, d, r, scale,
-                          _ptr(out), out_fmt, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    tail = (_ptr(kv_w), _bstride(kv_w), kvw_pos0, kvw_rows, _ptr(sink), _ptr(q_pos), W, B, Tq, H, d, r, scale,
+            _ptr(out), out_fmt, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()):
+        raise ValueError("idx must be contiguous int32 [B, Tq, k]")
+    if pages is None:
+        if name == "csa_attend":
+            rc = L.csa_attend(_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _bstride(kv_c), n_cap, _ptr(idx),
+                              idx.shape[-1], *tail)
+        else:
+            rc = L.hca_attend(_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _bstride(kv_c), n_cap, m, *tail)
     else:
-        rc = L.hca_attend(_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _bstride(kv_c), n_cap, m, _ptr(kv_w),
-                          _bstride(kv_w), kvw_pos0, kvw_rows, _ptr(q_pos), W, B, Tq, H, d, r, scale, _ptr(out),
-                          out_fmt, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+        bt, epb, blk_bytes, n_blocks = pages
+        _check_table(bt)
+        head = (_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _ptr(bt), bt.shape[1], epb, blk_bytes, n_blocks, n_cap)
+        if name == "csa_attend":
+            rc = L.csa_attend_paged(*head, _ptr(idx), idx.shape[-1], *tail)
+        else:
+            rc = L.hca_attend_paged(*head, m, *tail)
+        name += "_paged"
     check(name, rc)
     return out, lse
 
 
 def csa_attend(q, kv_c, idx, kv_w, q_pos, *, kv_fmt, n_cap, kvw_pos0, kvw_rows, W, H, d, r=0, scale,
-               out_fmt=F32, out=None, lse=None, with_lse=True):
-    """q [B, Tq, H, d] (bf16 for BF16/packed KV, f32 for F32 KV); idx int32 [B, Tq, k].
-    Returns (out [B, Tq, H, d], lse float32 [B, Tq, H] or None)."""
+               out_fmt=F32, out=None, lse=None, with_lse=True, sink=None):
+    """q [B, Tq, H, d] (bf16 for BF16/packed KV, f32 for F32 KV); idx int32 [B, Tq, k];
+    sink float32 [H] or None.  Returns (out [B, Tq, H, d], lse float32 [B, Tq, H] or None)."""
     return _attend("csa_attend", q, kv_c, kv_w, q_pos, idx, kv_fmt=kv_fmt, n_cap=n_cap, m=1, kvw_pos0=kvw_pos0,
                    kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out, lse=lse,
-                   with_lse=with_lse)
+                   with_lse=with_lse, sink=sink)
 
 
 def hca_attend(q, kv_c, kv_w, q_pos, *, kv_fmt, n_cap, m, kvw_pos0, kvw_rows, W, H, d, r=0, scale, out_fmt=F32,
-               out=None, lse=None, with_lse=True):
+               out=None, lse=None, with_lse=True, sink=None):
     return _attend("hca_attend", q, kv_c, kv_w, q_pos, None, kv_fmt=kv_fmt, n_cap=n_cap, m=m, kvw_pos0=kvw_pos0,
                    kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out, lse=lse,
-                   with_lse=with_lse)
+                   with_lse=with_lse, sink=sink)
+
+
+def csa_attend_paged(q, pool, block_table, idx, kv_w, q_pos, *, entries_per_block, block_bytes, n_blocks, kv_fmt,
+                     n_cap, kvw_pos0, kvw_rows, W, H, d, r=0, scale, out_fmt=F32, out=None, lse=None, with_lse=True,
+                     sink=None):
+    """csa_attend over a paged pool (`pool` points at block 0's first entry row; blocks are
+    block_bytes apart, n_blocks of them) with block_table int32 [B, max_blocks]: entry s of
+    sequence b is row s % entries_per_block of block block_table[b, s // entries_per_block]."""
+    return _attend("csa_attend", q, pool, kv_w, q_pos, idx, kv_fmt=kv_fmt, n_cap=n_cap, m=1, kvw_pos0=kvw_pos0,
+                   kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out, lse=lse,
+                   with_lse=with_lse, sink=sink, pages=(block_table, entries_per_block, block_bytes, n_blocks))
+
+
+def hca_attend_paged(q, pool, block_table, kv_w, q_pos, *, entries_per_block, block_bytes, n_blocks, kv_fmt, n_cap,
+                     m, kvw_pos0, kvw_rows, W, H, d, r=0, scale, out_fmt=F32, out=None, lse=None, with_lse=True,
+                     sink=None):
+    return _attend("hca_attend", q, pool, kv_w, q_pos, None, kv_fmt=kv_fmt, n_cap=n_cap, m=m, kvw_pos0=kvw_pos0,
+                   kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out, lse=lse,
+                   with_lse=with_lse, sink=sink, pages=(block_table, entries_per_block, block_bytes, n_blocks))

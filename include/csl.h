@@ -76,13 +76,17 @@ int64_t csl_row_bytes(int fmt, int d, int r);
  * Entry i of each sequence pools raw rows with a softmax over learned per-token
  * logits plus a per-slot position bias:
  *   win = overlap ? 2m : m;   p_j = (i+1)*m - win + j,  j = 0..win-1 (p_j >= 0 only)
- *   w_j,c = softmax_j(z[p_j, c] + bias[j, c]),  e_i[c'] = sum_j w_{j,c(c')} x[p_j, c']
+ *   w_j,c = softmax_j(z[p_j, c] + bias[j, c]),  e_i[c'] = sum_j w_{j,c(c')} v_j[c']
  *   (c(c') = 0 when z_ch == 1, c' when z_ch == d).
  * CSA uses overlap = 1 (adjacent blocks overlap), HCA overlap = 0.
- *  x          raw rows, x_fmt CSL_F32 or CSL_BF16; row of position p of sequence b
- *             at x + b*x_bstride + (p - x_pos0)*csl_row_bytes(x_fmt, d, 0).  The
- *             buffer holds positions x_pos0 .. x_pos0 + n_tok - 1 and must hold
+ *  x          raw rows, x_fmt CSL_F32 or CSL_BF16, x_roles*d values each; row of
+ *             position p of sequence b at x + b*x_bstride + (p - x_pos0)*row bytes.
+ *             The buffer holds positions x_pos0 .. x_pos0 + n_tok - 1 and must hold
  *             every window position >= 0 of entries e_begin .. e_begin+n_e-1.
+ *  x_roles    1: v_j is the row.  2 (overlap only): two-role rows ([B] section 4.2
+ *             projects 2*head_dim per token for the compressor): v_j is the row's
+ *             first d values in the look-back slots j < m and its last d values in
+ *             the current slots j >= m.
  *  z          fp32 logits, z_ch (1 or d) per position, same position indexing:
  *             z + b*z_bstride (bytes) + (p - x_pos0)*z_ch floats.
  *  bias       fp32 [win][z_ch], one bias per window slot (host-checked count).
@@ -96,11 +100,39 @@ int64_t csl_row_bytes(int fmt, int d, int r);
  *  multiple of 8 with 0 <= r <= d and d + r a multiple of 16 (16-byte rows);
  *  m >= 1; e_begin >= 0.
  */
-int kv_compress(const void* x, int x_fmt, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
+int kv_compress(const void* x, int x_fmt, int x_roles, int64_t x_bstride, int64_t x_pos0, int64_t n_tok,
                 const float* z, int z_ch, int64_t z_bstride, const float* bias,
                 int B, int d, int r, int m, int overlap, int64_t e_begin, int64_t n_e,
                 void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
                 void* stream);
+
+/*
+ * kv_compress_step -- decode-time compression driven from the state ring, the other
+ * half of the two-tier cache ([X] section 4, KV-cache paragraph: a per-request state
+ * cache holds the window and the not yet compressed tail; [C] KV-cache section).
+ * Each sequence b appended T new tokens at positions pos[b*T + 0 .. T-1] (ragged
+ * across the batch).  A token at p with (p + 1) % m == 0 completes entry
+ * e = (p + 1)/m - 1, which is pooled as in kv_compress from the raw rows and logits
+ * in the rings and written into the cache; other tokens do nothing (one launch serves
+ * the whole batch).
+ *  x_ring     raw rows (x_fmt, x_roles*d values): position p of sequence b in row
+ *             p mod x_rows of x_ring + b*x_bstride; z_ring the logits, same rows.  The
+ *             ring must hold the window of every completed entry: x_rows >= win + T - 1
+ *             (checked) with the newest x_rows positions resident (the caller's part).
+ *  out        the compressed cache: linear (block_table NULL) -- entry e of sequence b
+ *             at out + b*out_bstride + e*row bytes, scales out_scales + b*sc_bstride +
+ *             e*(d/32), entries e >= n_cap skipped -- or paged: row e % entries_per_block
+ *             of block block_table[b*bt_stride + e / entries_per_block] (out +
+ *             block*block_bytes; scales out_scales + block*scale_block_bytes); absent
+ *             blocks (ids outside [0, n_blocks)) and entries beyond the table are skipped.
+ *  Other arguments as in kv_compress.
+ */
+int kv_compress_step(const void* x_ring, int x_fmt, int x_roles, int64_t x_bstride, int64_t x_rows,
+                     const float* z_ring, int z_ch, int64_t z_bstride, const float* bias,
+                     const int32_t* pos, int B, int T, int d, int r, int m, int overlap,
+                     void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
+                     int64_t n_cap, const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                     int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks, void* stream);
 
 /*
  * index_topk -- lightning indexer + top-k selection ([X] section 2, CSA step 2;
@@ -130,6 +162,26 @@ int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float
                int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 size_t csl_index_topk_workspace(int B, int Tq, int64_t n_cap, int k);
+
+/*
+ * index_topk_paged -- index_topk over paged indexer keys, the classical half of the
+ * two-tier cache ([X] section 4, KV-cache paragraph; [C] KV-cache section: the CSA
+ * cache also holds the indexer's keys).  Key s of sequence b is row (s %
+ * entries_per_block) of block block_table[b*bt_stride + s / entries_per_block]: its
+ * bytes at ki_pool + block*block_bytes + (s % entries_per_block)*row bytes, its MXFP4
+ * scales at ki_scale_pool + block*scale_block_bytes + (s % entries_per_block)*(d_I/32).
+ * The key rows may share their blocks with the compressed KV entries (one block per
+ * lcm(m, m') raw tokens holding both: pass pointers into the block and the block's full
+ * stride).  entries_per_block must be a multiple of 16.  Keys of an absent block (id
+ * outside [0, n_blocks)) are never read and score -inf.  Other arguments, results and
+ * the workspace (csl_index_topk_workspace) as in index_topk.
+ */
+int index_topk_paged(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                     const void* ki_pool, int ki_fmt, const uint8_t* ki_scale_pool,
+                     const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                     int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks,
+                     const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                     int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * index_topk_noalloc -- index_topk for callers that cannot allocate device memory
@@ -170,6 +222,11 @@ size_t csl_noalloc_scratch_bytes(void);
  *             buffer (kvw_pos0 = its first position) or a ring (kvw_pos0 = 0).  The
  *             caller keeps positions t-W+1 .. t resident; kvw_rows >= W is required
  *             (CSL_EINVAL otherwise), so W consecutive positions never share a row.
+ *  sink       fp32 [H] attention-sink logits, or NULL for none ([C] table of attention
+ *             details, "Attention Sink": a head may attend to nothing).  Head h's
+ *             softmax then has the extra logit sink[h] with no value:
+ *             o_h = sum_S exp(l) v / (exp(sink[h]) + sum_S exp(l)),
+ *             lse_h = log(exp(sink[h]) + sum_S exp(l))  (an empty S: o = 0, lse = sink[h]).
  *  out        [B][Tq][H][d], out_fmt CSL_F32 or CSL_BF16;  out_lse fp32 [B][Tq][H] or NULL.
  *  Limits: d in {64, 128, 256, 512}; packed: r multiple of 8, d-r multiple of 16,
  *  r <= d/4 (CSL_EUNSUPPORTED beyond).
@@ -178,21 +235,50 @@ size_t csl_noalloc_scratch_bytes(void);
  */
 int csa_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap,
                const int32_t* idx, int k,
-               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
                void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * hca_attend -- HCA attention ([X] section 2, HCA subsection): as csa_attend, but
  * over EVERY complete entry, S(t) = {s < min(floor((t+1)/m), n_cap)} U window.
+ * n_cap = 0 with W > 0 is a sliding-window-only layer.
  */
 int hca_attend(const void* q, int q_fmt, const void* kv_c, int kv_fmt, int64_t kvc_bstride, int64_t n_cap, int m,
-               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+               const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
                void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for csa_attend (rows_max = k + W) or hca_attend (rows_max =
- * n_cap + W) with these sizes; 0 when no split partials are needed. */
+/*
+ * csa_attend_paged / hca_attend_paged -- the same attention over a PAGED compressed
+ * cache, the classical half of the two-tier cache ([X] section 4, KV-cache paragraph:
+ * compressed CSA/HCA entries in blocks, each block covering lcm(m, m') raw tokens;
+ * [C] KV-cache section).  Compressed entry s of sequence b is row
+ * (s % entries_per_block) of physical block block_table[b*bt_stride + s /
+ * entries_per_block] of the pool, blocks block_bytes apart from kv_pool (a block may
+ * hold other data after its rows).  For blocks of lcm(4, 128) = 128 raw tokens a CSA
+ * layer has entries_per_block = 32 and an HCA layer 1, and both layers can share one
+ * block table.  A block id outside [0, n_blocks) is an absent block: its rows are
+ * skipped (never read).  Requires bt_stride >= ceil(n_cap / entries_per_block),
+ * block_bytes >= entries_per_block * row bytes and a multiple of 16, n_cap < 2^31.
+ * The window (the other tier: a ring per sequence) and every other argument as in
+ * csa_attend / hca_attend.
+ */
+int csa_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, const int32_t* block_table,
+                     int64_t bt_stride, int entries_per_block, int64_t block_bytes, int64_t n_blocks, int64_t n_cap,
+                     const int32_t* idx, int k,
+                     const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
+                     const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                     void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
+
+int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, const int32_t* block_table,
+                     int64_t bt_stride, int entries_per_block, int64_t block_bytes, int64_t n_blocks, int64_t n_cap,
+                     int m, const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows,
+                     const float* sink, const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                     void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for csa_attend[_paged] (rows_max = k + W) or hca_attend[_paged]
+ * (rows_max = n_cap + W) with these sizes; 0 when no split partials are needed. */
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max);
 
 /* Text of a status code; text of the calling thread's last error (copied into

@@ -40,7 +40,7 @@ def test_helpers():
 
 
 def _compress(**over):
-    a = dict(x=16, x_fmt=1, x_bstride=0, x_pos0=0, n_tok=8, z=16, z_ch=1, z_bstride=0, bias=16, B=1, d=512, r=64,
+    a = dict(x=16, x_fmt=1, x_roles=1, x_bstride=0, x_pos0=0, n_tok=8, z=16, z_ch=1, z_bstride=0, bias=16, B=1, d=512, r=64,
              m=4, overlap=1, e_begin=0, n_e=1, out=16, out_fmt=2, out_scales=None, out_bstride=0, sc_bstride=0,
              stream=None)
     a.update(over)
@@ -56,13 +56,15 @@ def test_compress_rejects_bad_arguments_on_the_host():
     assert _compress(n_tok=3) == _lib.CSL_EINVAL                    # window not resident
     assert _compress(out_fmt=3) == _lib.CSL_EINVAL                  # MXFP4 without scales
     assert _compress(r=4) == _lib.CSL_EINVAL                        # packed needs r % 8 == 0
+    assert _compress(x_roles=3) == _lib.CSL_EINVAL
+    assert _compress(x_roles=2, overlap=0) == _lib.CSL_EINVAL       # two roles need overlapping windows
     assert _compress(n_e=0) == _lib.CSL_OK                          # nothing to do, no device needed
     assert "window" in _lib.last_error() or _lib.last_error() == ""
 
 
 def _attend(fn="hca", **over):
     a = dict(q=16, q_fmt=1, kv_c=16, kv_fmt=2, kvc_bstride=0, n_cap=10, m=4, kv_w=16, kvw_bstride=0, kvw_pos0=0,
-             kvw_rows=10, q_pos=16, W=4, B=1, Tq=1, H=64, d=512, r=64, scale=0.1, out=16, out_fmt=0, out_lse=None,
+             kvw_rows=10, sink=None, q_pos=16, W=4, B=1, Tq=1, H=64, d=512, r=64, scale=0.1, out=16, out_fmt=0, out_lse=None,
              ws=None, ws_bytes=0, stream=None)
     a.update(over)
     return _lib.lib().hca_attend(*a.values())
@@ -81,6 +83,27 @@ def test_attend_rejects_bad_arguments_on_the_host():
     assert _attend(ws=None, n_cap=10000) == _lib.CSL_EWORKSPACE     # one query: split partials needed
     assert "workspace" in _lib.last_error()
     assert _attend(B=0) == _lib.CSL_OK
+    assert _attend(sink=18) == _lib.CSL_EINVAL                      # misaligned sink
+
+
+def test_paged_attend_rejects_bad_tables_on_the_host():
+    L = _lib.lib()
+
+    def call(**over):
+        a = dict(q=16, q_fmt=1, pool=16, kv_fmt=2, bt=16, bt_stride=8, epb=32, block_bytes=32 * 576, n_blocks=100,
+                 n_cap=256, m=128, kv_w=16, kvw_bstride=0, kvw_pos0=0, kvw_rows=128, sink=None, q_pos=16, W=128,
+                 B=1, Tq=1, H=64, d=512, r=64, scale=0.1, out=16, out_fmt=0, out_lse=None, ws=16, ws_bytes=1 << 30,
+                 stream=None)
+        a.update(over)
+        return L.hca_attend_paged(*a.values())
+
+    assert call(bt=None) == _lib.CSL_EINVAL
+    assert call(epb=0) == _lib.CSL_EINVAL
+    assert call(bt_stride=7) == _lib.CSL_EINVAL                     # 8 blocks of 32 needed for 256 entries
+    assert "block-table" in _lib.last_error()
+    assert call(block_bytes=32 * 576 - 16) == _lib.CSL_EINVAL       # a block cannot hold its rows
+    assert call(n_blocks=0) == _lib.CSL_EINVAL
+    assert call(B=0) == _lib.CSL_OK
 
 
 def test_index_rejects_bad_arguments_on_the_host():
@@ -121,3 +144,21 @@ def test_noalloc_refuses_oversized_calls_on_the_host():
     rc = L.index_topk_noalloc(16, 3, 16, 16, 16, 3, 16, 0, 0, 16, 16, 1, 64, 128, 4, 1 << 22, 1024, 16, None, None)
     assert rc == _lib.CSL_EWORKSPACE
     assert "scratch" in _lib.last_error()
+
+
+def test_compress_step_rejects_bad_arguments_on_the_host():
+    L = _lib.lib()
+
+    def call(**over):
+        a = dict(x=16, x_fmt=1, x_roles=1, x_bstride=0, x_rows=16, z=16, z_ch=1, z_bstride=0, bias=16, pos=16, B=2,
+                 T=1, d=512, r=64, m=4, overlap=1, out=16, out_fmt=2, out_scales=None, out_bstride=0, sc_bstride=0,
+                 n_cap=100, bt=None, bt_stride=0, epb=0, block_bytes=0, sblk=0, n_blocks=0, stream=None)
+        a.update(over)
+        return L.kv_compress_step(*a.values())
+
+    assert call(x_rows=7) == _lib.CSL_EINVAL                        # ring shorter than the 8-row window
+    assert "ring" in _lib.last_error()
+    assert call(x_rows=8, T=2) == _lib.CSL_EINVAL                   # two new tokens need 9 rows
+    assert call(pos=None) == _lib.CSL_EINVAL
+    assert call(bt=16, bt_stride=4, epb=32, block_bytes=100, n_blocks=10) == _lib.CSL_EINVAL   # block too small
+    assert call(T=0) == _lib.CSL_OK

@@ -176,3 +176,62 @@ def test_logits_far_above_the_first_tile_are_recomputed(gpu):
     err = max_abs(host(go), oo)
     assert np.all(np.isfinite(host(go))) and err <= TOL[fmt], "max-abs %.3g" % err
     assert max_abs(host(gl), ol) <= 10 * TOL[fmt]
+
+
+SINK_CASES = [
+    # (name, fmt, kind, B, Tq, H, d, r, N, k or m, W): split and unsplit paths, both kernels
+    ("csa_decode_split", O.KV_PACKED, "csa", 2, 1, 64, 512, 64, 5000, 512, 128),
+    ("hca_decode_split", O.KV_PACKED, "hca", 2, 1, 64, 512, 64, 1500, 128, 128),
+    ("hca_many_q", O.KV_PACKED, "hca", 4, 200, 16, 256, 64, 400, 4, 8),
+    ("csa_f32", O.F32, "csa", 1, 8, 8, 128, 32, 512, 64, 128),
+    ("hca_f32_split", O.F32, "hca", 1, 1, 8, 128, 32, 800, 4, 16),
+]
+
+
+@pytest.mark.parametrize("case", SINK_CASES, ids=[c[0] for c in SINK_CASES])
+def test_attention_sink_parity(gpu, case):
+    """An attention sink per head (CSDN explainer, table of attention details): one
+    extra logit in the softmax's denominator, counted once per query whether or not the
+    attended rows are split across blocks."""
+    name, fmt, kind, B, Tq, H, d, r, N, km, W = case
+    kvc = _kv(fmt, B, N, d, r, 620 + d)
+    L = 4 * N if kind == "csa" else N * km
+    kvw = _kv(fmt, B, min(L, 4096), d, r, 621 + d)
+    q = _q(fmt, B, Tq, H, d, 622 + d)
+    qpos = gen.positions(B, Tq, min(L, 4096) - 1).to(torch.int32)
+    sink = gen.normal((H,), 623, 2.0)
+    kw = dict(W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    okw = dict(kw)
+    qf = O.F32 if fmt == O.F32 else O.BF16
+    nw = min(L, 4096)
+    if kind == "csa":
+        rng = np.random.default_rng(624)
+        idx = np.sort(rng.integers(0, N, size=(B, Tq, km)), axis=-1).astype(np.int32)
+        go, gl = ops.csa_attend(dev(q), dev(kvc), dev(idx), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, kvw_pos0=0,
+                                kvw_rows=nw, sink=dev(sink), **kw)
+        oo, ol = O.csa_attend(_oracle_q(q), qf, host(kvc), fmt, N, idx, host(kvw), 0, nw, host(qpos),
+                              sink=host(sink), **okw)
+    else:
+        go, gl = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), kv_fmt=fmt, n_cap=N, m=km, kvw_pos0=0,
+                                kvw_rows=nw, sink=dev(sink), **kw)
+        oo, ol = O.hca_attend(_oracle_q(q), qf, host(kvc), fmt, N, km, host(kvw), 0, nw, host(qpos),
+                              sink=host(sink), **okw)
+    torch.cuda.synchronize()
+    err = max_abs(host(go), oo)
+    assert err <= TOL[fmt], "%s: max-abs %.3g" % (name, err)
+    assert max_abs(host(gl), ol) <= 10 * TOL[fmt]
+    print("%s: max-abs %.3g" % (name, err))
+
+
+def test_attention_sink_with_nothing_attended(gpu):
+    fmt, B, H, d = O.KV_PACKED, 1, 64, 512
+    kvc = _kv(fmt, B, 10, d, 64, 631)
+    q = _q(fmt, B, 2, H, d, 632)
+    idx = torch.full((B, 2, 16), -1, dtype=torch.int32)
+    qpos = torch.tensor([[5, 9]], dtype=torch.int32)
+    sink = gen.normal((H,), 633)
+    o, l = ops.csa_attend(dev(q), dev(kvc), dev(idx), dev(kvc), dev(qpos), kv_fmt=fmt, n_cap=10, kvw_pos0=0,
+                          kvw_rows=10, W=0, H=H, d=d, r=64, scale=0.1, sink=dev(sink))
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert torch.allclose(l.detach().cpu(), sink.expand(B, 2, H), rtol=1e-6, atol=1e-6)

@@ -94,3 +94,99 @@ def test_compress_writes_into_a_cache_slice(gpu):
     c = host(cache)
     assert np.all(c[:, :10] == 7) and np.all(c[:, 26:] == 7)
     assert np.mean(c[:, 10:26] != ref) < 1e-3
+
+
+@pytest.mark.parametrize("x_fmt,d,r,m,per_channel", [(O.F32, 128, 32, 4, False), (O.BF16, 512, 64, 4, False),
+                                                     (O.BF16, 128, 0, 4, True)])
+def test_compress_two_role_rows(gpu, x_fmt, d, r, m, per_channel):
+    """Two-role raw rows (look-back value, then current value; chenxutan.com article,
+    section 4.2 projects 2 x head_dim per token) against the oracle: fp32 entries within
+    fp32 rounding, quantised entries byte-equal to the oracle's encoder on them."""
+    B, n_e = 2, 33
+    n_tok = n_e * m
+    z_ch = d if per_channel else 1
+    xs = gen.store(gen.normal((B, n_tok, 2 * d), 900 + d), x_fmt)
+    z = gen.random_logits((B, n_tok, z_ch), 901)
+    bias = gen.random_logits((2 * m, z_ch), 902)
+    kw = dict(d=d, r=r, m=m, overlap=True, e_begin=0, n_e=n_e, x_roles=2)
+    ref, _ = O.kv_compress(host(xs), x_fmt, host(z), host(bias), **kw, out_fmt=O.F32)
+    got, _ = ops.kv_compress(dev(xs), x_fmt, dev(z), dev(bias), **kw, out_fmt=O.F32)
+    torch.cuda.synchronize()
+    g = host(got).astype(np.float64)
+    assert np.all(np.abs(g - ref) <= 2e-6 * (1.0 + np.abs(ref)))
+    for fmt in [O.MXFP4] + ([O.KV_PACKED] if r > 0 else [O.BF16]):
+        q, sc = ops.kv_compress(dev(xs), x_fmt, dev(z), dev(bias), **kw, out_fmt=fmt)
+        torch.cuda.synchronize()
+        enc, enc_sc = O.encode_rows(g.reshape(-1, d), fmt, d, r)
+        assert np.array_equal(host(q).reshape(enc.shape), enc)
+        if fmt == O.MXFP4:
+            assert np.array_equal(host(sc).reshape(enc_sc.shape), enc_sc)
+
+
+@pytest.mark.parametrize("roles,out_fmt,m,overlap", [(1, O.KV_PACKED, 4, True), (2, O.KV_PACKED, 4, True),
+                                                     (1, O.MXFP4, 4, True), (1, O.KV_PACKED, 128, False)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_compress_step_from_the_ring(gpu, roles, out_fmt, m, overlap, paged):
+    """Decode-time compression driven from the state ring: a ragged batch appends T = 2
+    tokens per sequence; the tokens that complete a block compress their entry from the
+    ring (row p mod R) into the cache -- dense, or through a block table of shuffled
+    blocks of 128 raw tokens -- and nothing else in the cache changes.  Checked against
+    the oracle's step and, byte for byte, against kv_compress on the same rows."""
+    B, T, d, r, R = 4, 2, 512 if out_fmt == O.KV_PACKED else 128, 64 if out_fmt == O.KV_PACKED else 0, 256
+    n_cap = 4096 // m
+    pos = torch.tensor([[5, 6], [2 * m - 2, 2 * m - 1], [4095 - m, 4096 - m], [4094, 4095]], dtype=torch.int32)
+    xr = gen.store(gen.normal((B, R, roles * d), 910 + m), O.BF16)
+    zr = gen.random_logits((B, R, 1), 911)
+    bias = gen.random_logits((2 * m if overlap else m, 1), 912)
+    rb = O.row_bytes(out_fmt, d, r)
+    fill = 0xA5
+    kw = dict(d=d, r=r, m=m, overlap=overlap, x_roles=roles)
+    if not paged:
+        cache = torch.full((B, n_cap, rb), fill, dtype=torch.uint8)
+        scales = torch.full((B, n_cap, d // 32), fill, dtype=torch.uint8) if out_fmt == O.MXFP4 else None
+        out, sc = ops.kv_compress_step(dev(xr), O.BF16, dev(zr), dev(bias), dev(pos), out=dev(cache),
+                                       out_scales=dev(scales) if scales is not None else None, out_fmt=out_fmt, **kw)
+        torch.cuda.synchronize()
+        got, got_sc = host(out), (host(sc) if sc is not None else None)
+    else:
+        epb = 128 // m
+        nblk = n_cap // epb
+        blk_bytes = (epb * rb + 15) // 16 * 16 + 16 * epb      # rows, then the scales (and slack)
+        g = torch.Generator().manual_seed(5)
+        bt = torch.randperm(B * nblk, generator=g).to(torch.int32).reshape(B, nblk)
+        pool = torch.full((B * nblk, blk_bytes), fill, dtype=torch.uint8)
+        sc_off = (epb * rb + 15) // 16 * 16
+        pool_d = dev(pool)
+        pg = (dev(bt), epb, blk_bytes, blk_bytes, B * nblk)
+        ops.kv_compress_step(dev(xr), O.BF16, dev(zr), dev(bias), dev(pos), out=pool_d, out_fmt=out_fmt,
+                             out_scales=pool_d[:, sc_off:] if out_fmt == O.MXFP4 else None, pages=pg, **kw)
+        torch.cuda.synchronize()
+        ph = host(pool_d)
+        got = O.paged_gather(ph, rb, host(bt), epb, blk_bytes, n_cap)
+        got_sc = (O.paged_gather(ph.reshape(-1)[sc_off:], d // 32, host(bt), epb, blk_bytes, n_cap)
+                  if out_fmt == O.MXFP4 else None)
+    want, want_sc, ent = O.kv_compress_step(host(xr), O.BF16, host(zr), host(bias), host(pos), out_fmt=out_fmt, **kw)
+    assert (ent >= 0).sum() >= 3
+    touched = set()
+    for b in range(B):
+        for j in range(T):
+            e = int(ent[b, j])
+            if e < 0:
+                continue
+            touched.add((b, e))
+            assert np.array_equal(got[b, e], want[b, j]), (b, j, e)
+            if out_fmt == O.MXFP4:
+                assert np.array_equal(got_sc[b, e], want_sc[b, j])
+            # byte-equal to kv_compress over the same ring rows, as a linear buffer
+            p_hi = int(pos[b, j])
+            lin = np.stack([host(xr)[b, p % R] for p in range(p_hi - (2 * m if overlap else m) + 1, p_hi + 1)])
+            zl = np.stack([host(zr)[b, p % R] for p in range(p_hi - (2 * m if overlap else m) + 1, p_hi + 1)])
+            one, one_sc = ops.kv_compress(dev(lin[None]), O.BF16, dev(zl[None]), dev(bias), e_begin=e, n_e=1,
+                                          x_pos0=p_hi - (2 * m if overlap else m) + 1, out_fmt=out_fmt, **kw)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(one)[0, 0], got[b, e])
+    # every other cache row is untouched
+    for b in range(B):
+        for e in range(n_cap):
+            if (b, e) not in touched:
+                assert np.all(got[b, e] == fill), (b, e)

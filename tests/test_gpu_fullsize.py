@@ -54,13 +54,26 @@ def _check_index(gi, gs, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, 
 # ---------------------------------------------------------------------------
 # the 4-layer decode stack, exactly as the benchmark builds and launches it
 # ---------------------------------------------------------------------------
-@pytest.fixture(scope="module")
-def stack():
+def _make_stack(layout):
     sys.path.insert(0, ROOT)
     import bench
-    st = bench.Stack(16, 1 << 20, torch.device("cuda:0"))
+    st = bench.Stack(16, 1 << 20, torch.device("cuda:0"), layout=layout)
     st.step()
     torch.cuda.synchronize()
+    return st
+
+
+@pytest.fixture(scope="module")
+def stack():
+    st = _make_stack("linear")
+    yield st
+    del st
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def paged_stack():
+    st = _make_stack("paged")
     yield st
     del st
     torch.cuda.empty_cache()
@@ -69,68 +82,84 @@ def stack():
 SAMPLE = list(range(16))          # every sequence of the batch
 
 
-def test_stack_compress_of_the_completed_entries(gpu, stack):
-    st = stack
+@pytest.mark.parametrize("layout", ["linear", "paged"])
+def test_stack_compress_of_the_completed_entries(gpu, layout, request):
+    """The entries completed by the token at 2^20 - 1, pooled by kv_compress_step from
+    the 128-row state ring (row p % 128) into the compressed cache (dense, or the block
+    the block table names)."""
+    st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
     t = st.t
     csa, hca = st.layers[0], st.layers[1]
     h = lambda x: host(x[SAMPLE])
     i = (t + 1) // st.m - 1
+    ring = dict(x_rows=st.RING, x_pos0=0)
     ref, _ = O.kv_compress(h(csa["raw"]), O.BF16, h(csa["z"]), host(csa["bias"]), d=st.d, r=st.r, m=st.m,
-                           overlap=True, e_begin=i, n_e=1, x_pos0=t - csa["win"] + 1, out_fmt=O.KV_PACKED)
-    close_quantised(h(csa["cache"][:, i:i + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
+                           overlap=True, e_begin=i, n_e=1, out_fmt=O.KV_PACKED, **ring)
+    close_quantised(h(st.entries(csa)[:, i:i + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
+    keys, ksc = st.index_keys(csa)
     rk, rs = O.kv_compress(h(csa["raw_i"]), O.BF16, h(csa["z_i"]), host(csa["bias_i"]), d=st.dI, m=st.m,
-                           overlap=True, e_begin=i, n_e=1, x_pos0=t - csa["win"] + 1, out_fmt=O.MXFP4)
-    close_quantised(h(csa["keys"][:, i:i + 1]), rk, O.MXFP4, st.dI, 0, h(csa["kscales"][:, i:i + 1]), rs,
-                    max_mismatch=len(SAMPLE))
+                           overlap=True, e_begin=i, n_e=1, out_fmt=O.MXFP4, **ring)
+    close_quantised(h(keys[:, i:i + 1]), rk, O.MXFP4, st.dI, 0, h(ksc[:, i:i + 1]), rs, max_mismatch=len(SAMPLE))
     ih = (t + 1) // st.mh - 1
     ref, _ = O.kv_compress(h(hca["raw"]), O.BF16, h(hca["z"]), host(hca["bias"]), d=st.d, r=st.r, m=st.mh,
-                           overlap=False, e_begin=ih, n_e=1, x_pos0=t - hca["win"] + 1, out_fmt=O.KV_PACKED)
-    close_quantised(h(hca["cache"][:, ih:ih + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
+                           overlap=False, e_begin=ih, n_e=1, out_fmt=O.KV_PACKED, **ring)
+    close_quantised(h(st.entries(hca)[:, ih:ih + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
 
 
-def test_stack_index_topk_1M_mxfp4(gpu, stack):
-    st = stack
+@pytest.mark.parametrize("layout", ["linear", "paged"])
+def test_stack_index_topk_1M_mxfp4(gpu, layout, request):
+    st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
     csa = st.layers[0]
     # the same call with scores: its indices must equal the step's (deterministic)
-    gi, gs = ops.index_topk(csa["qi"], csa["w"], csa["keys"], st.q_pos, fmt=O.MXFP4, H_I=st.HI, d_I=st.dI, m=st.m,
-                            n_cap=st.N, k=st.k, qi_scales=csa["qis"], ki_scales=csa["kscales"])
+    gi = torch.empty_like(csa["idx"])
+    _, gs = st.index(csa, with_scores=True, out_idx=gi)
     torch.cuda.synchronize()
     assert torch.equal(gi, csa["idx"])
+    keys, ksc = st.index_keys(csa)
     h = lambda x: host(x[SAMPLE])
     qpos = np.full((len(SAMPLE), 1), st.t, np.int32)
-    stats = _check_index(h(gi), h(gs), h(csa["qi"]), O.MXFP4, h(csa["w"]), h(csa["keys"]), O.MXFP4, qpos,
+    stats = _check_index(h(gi), h(gs), h(csa["qi"]), O.MXFP4, h(csa["w"]), h(keys), O.MXFP4, qpos,
                          H_I=st.HI, d_I=st.dI, m=st.m, n_cap=st.N, k=st.k, qi_scales=h(csa["qis"]),
-                         ki_scales=h(csa["kscales"]))
-    print("stack index: %s" % stats)
+                         ki_scales=h(ksc))
+    print("stack index (%s): %s" % (layout, stats))
 
 
+@pytest.mark.parametrize("layout", ["linear", "paged"])
 @pytest.mark.parametrize("kind", ["csa", "hca"])
-def test_stack_attend(gpu, stack, kind):
-    st = stack
+def test_stack_attend(gpu, kind, layout, request):
+    st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
     L = st.layers[0] if kind == "csa" else st.layers[1]
-    kw = dict(kv_fmt=O.KV_PACKED, kvw_pos0=0, kvw_rows=st.ring, W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
-    if kind == "csa":
-        go, gl = ops.csa_attend(L["q"], L["cache"], L["idx"], L["ring"], st.q_pos, n_cap=st.N, **kw)
-    else:
-        go, gl = ops.hca_attend(L["q"], L["cache"], L["ring"], st.q_pos, n_cap=st.Nh, m=st.mh, **kw)
+    go, gl = st.attend(L, out_fmt=O.F32, with_lse=True)
     torch.cuda.synchronize()
     h = lambda x: host(x[SAMPLE])
     q = h(L["q"].view(torch.int16))
     qpos = h(st.q_pos)
     okw = dict(W=st.W, H=st.H, d=st.d, r=st.r, scale=st.scale)
+    ent = h(st.entries(L))
     if kind == "csa":
-        oo, ol = O.csa_attend(q, O.BF16, h(L["cache"]), O.KV_PACKED, st.N, h(L["idx"]), h(L["ring"]), 0, st.ring,
-                              qpos, **okw)
+        oo, ol = O.csa_attend(q, O.BF16, ent, O.KV_PACKED, st.N, h(L["idx"]), h(L["ring"]), 0, st.ring, qpos, **okw)
     else:
-        oo, ol = O.hca_attend(q, O.BF16, h(L["cache"]), O.KV_PACKED, st.Nh, st.mh, h(L["ring"]), 0, st.ring, qpos,
-                              **okw)
+        oo, ol = O.hca_attend(q, O.BF16, ent, O.KV_PACKED, st.Nh, st.mh, h(L["ring"]), 0, st.ring, qpos, **okw)
     err = max_abs(h(go), oo)
     assert err <= 2e-2, "%s: max-abs %.3g" % (kind, err)
     assert max_abs(h(gl), ol) <= 2e-1
     # the benchmark's own bf16 output agrees with the fp32 one up to bf16 rounding
     ob = host(L["out"][SAMPLE].float())
     assert np.all(np.abs(ob - h(go)) <= 2.0 ** -8 * np.abs(h(go)) + 1e-6)
-    print("stack %s: max-abs %.3g" % (kind, err))
+    print("stack %s (%s): max-abs %.3g" % (kind, layout, err))
+
+
+def test_paged_stack_equals_linear_stack(gpu, stack, paged_stack):
+    """The same seeded data in both layouts: the paged step's compressed entries, index
+    sets and outputs are bit-identical to the linear step's (only the addressing differs)."""
+    for La, Lb in zip(stack.layers, paged_stack.layers):
+        if La["kind"] == "csa":
+            assert torch.equal(La["idx"], Lb["idx"])
+            ka, sa = stack.index_keys(La)
+            kb, sb = paged_stack.index_keys(Lb)
+            assert torch.equal(ka, kb) and torch.equal(sa, sb)
+        assert torch.equal(stack.entries(La), paged_stack.entries(Lb))
+        assert torch.equal(La["out"], Lb["out"])
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,143 @@
+"""The paged (classical) tier of the two-tier KV cache (x-techcon article, section 4,
+KV-cache paragraph: compressed CSA/HCA entries in blocks of lcm(m, m') raw tokens;
+CSDN explainer, KV-cache section): attention and the indexer read compressed entries
+through a block table.  Checked against the oracle on the plainly gathered cache, and
+byte for byte against the linear layout on the same data; blocks missing from the table
+are skipped by the attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_sparse_long_02_amd import gen, ops
+from tests.gpu_util import cap, check_topk, dev, host, max_abs, oracle_all_scores, score_error_bound
+from tests import bruteforce as BF
+
+pytestmark = pytest.mark.gpu
+
+
+def _paged(lin, epb, extra, seed, spare=5):
+    """Scatter a linear cache [B, n, row] into a pool of shuffled blocks of epb rows (+ extra
+    bytes of other data per block).  Returns (pool [n_phys, block_bytes], bt [B, nblk])."""
+    B, n, rb = lin.shape
+    nblk = (n + epb - 1) // epb
+    bb = epb * rb + extra
+    n_phys = B * nblk + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n_phys, generator=g)[:B * nblk].to(torch.int32).reshape(B, nblk)
+    pool = torch.randint(0, 256, (n_phys, bb), generator=g, dtype=torch.int32).to(torch.uint8)
+    padded = torch.zeros((B, nblk * epb, rb), dtype=torch.uint8)
+    padded[:, :n] = lin
+    for b in range(B):
+        pool[perm[b].long(), :epb * rb] = padded[b].reshape(nblk, epb * rb)
+    return pool, perm
+
+
+@pytest.mark.parametrize("kind,epb,N,m", [("csa", 32, 3000, 4), ("hca", 1, 600, 128), ("hca", 16, 700, 4)])
+def test_paged_attention_equals_linear_and_oracle(gpu, kind, epb, N, m):
+    fmt, B, H, d, r, W = O.KV_PACKED, 3, 64, 512, 64, 128
+    lin = gen.pack_kv(gen.normal((B, N, d), 700 + epb), r)
+    pool, bt = _paged(lin, epb, 48, 701 + epb)
+    ring = gen.pack_kv(gen.normal((B, 256, d), 702), r)
+    q = gen.normal((B, 1, H, d), 703).to(torch.bfloat16)
+    qpos = torch.tensor([[N * m - 1], [N * m // 2], [N * m - 7]], dtype=torch.int32)
+    sink = gen.normal((H,), 704)
+    kw = dict(kv_fmt=fmt, kvw_pos0=0, kvw_rows=256, W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d), sink=dev(sink))
+    pg = dict(entries_per_block=epb, block_bytes=pool.shape[1], n_blocks=pool.shape[0])
+    if kind == "csa":
+        rng = np.random.default_rng(705)
+        idx = dev(np.sort(rng.integers(-1, N, size=(B, 1, 512)), axis=-1).astype(np.int32))
+        a, la = ops.csa_attend(dev(q), dev(lin), idx, dev(ring), dev(qpos), n_cap=N, **kw)
+        p, lp = ops.csa_attend_paged(dev(q), dev(pool), dev(bt), idx, dev(ring), dev(qpos), n_cap=N, **pg, **kw)
+    else:
+        a, la = ops.hca_attend(dev(q), dev(lin), dev(ring), dev(qpos), n_cap=N, m=m, **kw)
+        p, lp = ops.hca_attend_paged(dev(q), dev(pool), dev(bt), dev(ring), dev(qpos), n_cap=N, m=m, **pg, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, p) and torch.equal(la, lp)
+    gathered = O.paged_gather(host(pool), lin.shape[2], host(bt), epb, pool.shape[1], N)
+    assert np.array_equal(gathered, host(lin))
+    okw = dict(W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d), sink=host(sink))
+    qb = host(q.view(torch.int16))
+    if kind == "csa":
+        oo, ol = O.csa_attend(qb, O.BF16, gathered, fmt, N, host(idx), host(ring), 0, 256, host(qpos), **okw)
+    else:
+        oo, ol = O.hca_attend(qb, O.BF16, gathered, fmt, N, m, host(ring), 0, 256, host(qpos), **okw)
+    assert max_abs(host(p), oo) <= 2e-2 and max_abs(host(lp), ol) <= 2e-1
+
+
+def test_paged_attention_skips_missing_blocks(gpu):
+    """Blocks missing from the table (negative ids, or ids past the pool) hold no rows:
+    HCA over the rest equals CSA selecting exactly the present entries (oracle)."""
+    fmt, B, H, d, r, W, m, N, epb = O.KV_PACKED, 2, 64, 512, 64, 128, 4, 1000, 32
+    lin = gen.pack_kv(gen.normal((B, N, d), 711), r)
+    pool, bt = _paged(lin, epb, 0, 712)
+    bt[0, 3] = -1
+    bt[1, 10] = pool.shape[0] + 7
+    ring = gen.pack_kv(gen.normal((B, 256, d), 713), r)
+    q = gen.normal((B, 1, H, d), 714).to(torch.bfloat16)
+    qpos = torch.full((B, 1), N * m - 1, dtype=torch.int32)
+    o, l = ops.hca_attend_paged(dev(q), dev(pool), dev(bt), dev(ring), dev(qpos), entries_per_block=epb,
+                                block_bytes=pool.shape[1], n_blocks=pool.shape[0], kv_fmt=fmt, n_cap=N, m=m,
+                                kvw_pos0=0, kvw_rows=256, W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    present = np.ones((B, N), bool)
+    present[0, 3 * epb:4 * epb] = False
+    present[1, 10 * epb:11 * epb] = False
+    idx = np.full((B, 1, N), -1, np.int32)
+    for b in range(B):
+        s = np.nonzero(present[b])[0]
+        idx[b, 0, :len(s)] = s
+    oo, ol = O.csa_attend(host(q.view(torch.int16)), O.BF16, host(lin), fmt, N, idx, host(ring), 0, 256, host(qpos),
+                          W=W, H=H, d=d, r=r, scale=1 / math.sqrt(d))
+    assert max_abs(host(o), oo) <= 2e-2 and max_abs(host(l), ol) <= 2e-1
+
+
+@pytest.mark.parametrize("fmt,N,Tq", [(O.MXFP4, 40000, 1), (O.BF16, 20000, 2), (O.BF16, 6000, 64)])
+def test_paged_index_equals_linear_and_oracle(gpu, fmt, N, Tq):
+    """index_topk_paged over keys that share their blocks with other data (as in a CSA
+    block of 32 entries + 32 keys + scales): identical to index_topk on the linear keys,
+    and the oracle's on the gathered keys.  Tq = 64 takes the many-query path."""
+    B, H_I, d_I, m, k, epb = 2, 64, 128, 4, 512, 32
+    if fmt == O.MXFP4:
+        kc, ks = gen.random_mxfp4(B * N, d_I, 721)
+        keys, scales = kc.reshape(B, N, -1), ks.reshape(B, N, -1)
+        qc, qs = gen.random_mxfp4(B * Tq * H_I, d_I, 722)
+        qi, qis = qc.reshape(B, Tq, H_I, -1), qs.reshape(B, Tq, H_I, -1)
+    else:
+        keys = gen.store(gen.normal((B, N, d_I), 721, 1 / math.sqrt(d_I)), fmt)
+        scales, qis = None, None
+        qi = gen.store(gen.normal((B, Tq, H_I, d_I), 722, 1 / math.sqrt(d_I)), fmt)
+    w = gen.normal((B, Tq, H_I), 723, 1 / math.sqrt(H_I))
+    qpos = gen.positions(B, Tq, N * m - 1).to(torch.int32)
+    krb = keys.shape[2]
+    # one pool holding keys then scales per block (offset sc_off), plus slack
+    sc_off = epb * krb
+    blk = ((sc_off + epb * (d_I // 32) + 16) + 15) // 16 * 16
+    pool, bt = _paged(keys, epb, blk - epb * krb, 724)
+    if scales is not None:                            # the scale rows of each block, after its keys
+        for b in range(B):
+            for j in range(bt.shape[1]):
+                rows = scales[b, j * epb:(j + 1) * epb].reshape(-1)
+                pool[int(bt[b, j]), sc_off:sc_off + rows.numel()] = rows
+    kw = dict(fmt=fmt, H_I=H_I, d_I=d_I, m=m, n_cap=N, k=k)
+    pd = dev(pool)
+    a, sa = ops.index_topk(dev(qi), dev(w), dev(keys), dev(qpos), qi_scales=dev(qis) if qis is not None else None,
+                           ki_scales=dev(scales) if scales is not None else None, **kw)
+    p, sp = ops.index_topk(dev(qi), dev(w), pd, dev(qpos), qi_scales=dev(qis) if qis is not None else None,
+                           ki_scales=pd[:, sc_off:] if scales is not None else None,
+                           pages=(dev(bt), epb, blk, blk, pool.shape[0]), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, p) and torch.equal(sa, sp)
+    gk = O.paged_gather(host(pool), krb, host(bt), epb, blk, N)
+    assert np.array_equal(gk, host(keys))
+    oq = dict(qi_scales=host(qis) if qis is not None else None, ki_scales=host(scales) if scales is not None else None)
+    oi, _ = O.index_topk(host(qi), fmt, host(w), gk, fmt, host(qpos), k=k, H_I=H_I, d_I=d_I, m=m, n_cap=N, **oq)
+    allsc = oracle_all_scores(host(qi), fmt, host(w), gk, fmt, host(qpos), H_I=H_I, d_I=d_I, m=m, n_cap=N, **oq)
+    dfmt = BF.MXFP4 if fmt == O.MXFP4 else fmt
+    qd = BF.decode(host(qi), dfmt, d_I, scales=oq["qi_scales"]).reshape(B, Tq, H_I, d_I)
+    kd = BF.decode(gk, dfmt, d_I, scales=oq["ki_scales"]).reshape(B, N, d_I)
+    bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
+    st = check_topk(host(p), host(sp), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+    print("paged index %d/%d: %s" % (fmt, Tq, st))
