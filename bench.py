@@ -592,6 +592,19 @@ def main():
         "step_ms": step_ms,
         "step_bytes": st.step_bytes(),
     }
+    # the grouped output projection after each layer's attention (not part of the
+    # configured step): 64 heads x 512 in 8 groups -> 8 x 1024, the batch's 16 tokens
+    G, R = 8, 1024
+    K = st.H * st.d // G
+    xo = st.layers[0]["out"].reshape(st.B, st.H * st.d)
+    wo = torch.randn((G, R, K), device=dev, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+    yo = torch.empty((st.B, G * R), dtype=torch.bfloat16, device=dev)
+    from compressed_sparse_long_02_amd import ops as F
+    t_op = time_calls(lambda: F.grouped_out_proj(xo, wo, G=G, out_fmt=F.BF16, out=yo), args.kernel_iters)
+    op_bytes = G * R * K * 2 + st.B * st.H * st.d * 2 + st.B * G * R * 2
+    kernels["grouped_out_proj (decode, not in the step)"] = {"ms": round(t_op, 4),
+                                                             "GB/s": round(op_bytes / (t_op * 1e-3) / 1e9, 1)}
+    del wo
     if args.copy_mb > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev).fill_(1)

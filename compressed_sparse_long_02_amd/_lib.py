@@ -17,8 +17,8 @@ CSL_OK, CSL_EINVAL, CSL_EUNSUPPORTED, CSL_EWORKSPACE, CSL_ELAUNCH, CSL_EDEVICE =
 # every symbol include/csl.h declares
 EXPORTS = ["csl_row_bytes", "kv_compress", "kv_compress_step", "index_topk", "index_topk_paged",
            "csl_index_topk_workspace", "index_topk_noalloc", "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend",
-           "csa_attend_paged", "hca_attend_paged", "csl_attend_workspace", "csl_status_string", "csl_last_error",
-           "csl_version"]
+           "csa_attend_paged", "hca_attend_paged", "csl_attend_workspace", "grouped_out_proj", "csl_status_string",
+           "csl_last_error", "csl_version"]
 
 
 class CslError(RuntimeError):
@@ -73,6 +73,8 @@ def lib() -> C.CDLL:
                                    vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, sz, vp]
     L.csl_attend_workspace.restype = sz
     L.csl_attend_workspace.argtypes = [i32, i32, i32, i32, i64]
+    L.grouped_out_proj.restype = i32
+    L.grouped_out_proj.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, vp, i32, vp]
     L.csl_status_string.restype = C.c_char_p
     L.csl_status_string.argtypes = [i32]
     L.csl_last_error.restype = i32

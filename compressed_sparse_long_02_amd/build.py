@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsl.so")
-SOURCES = ["compress.hip", "index_topk.hip", "attend.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "index_topk.hip", "attend.hip", "oproj.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

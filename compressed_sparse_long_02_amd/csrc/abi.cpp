@@ -593,4 +593,22 @@ int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, 
                        ws, ws_bytes, stream);
 }
 
+int grouped_out_proj(const void* x, int x_fmt, const void* w, int w_fmt, int M, int G, int K, int R,
+                     void* out, int out_fmt, void* stream) {
+    const char* fn = "grouped_out_proj";
+    if (M < 0 || G < 1 || K < 1 || R < 1) return fail(CSL_EINVAL, "%s: need M >= 0 and G, K, R >= 1", fn);
+    if (x_fmt != CSL_BF16 || w_fmt != CSL_BF16) return fail(CSL_EUNSUPPORTED, "%s: x and w must be CSL_BF16", fn);
+    if (out_fmt != CSL_F32 && out_fmt != CSL_BF16) return fail(CSL_EINVAL, "%s: out_fmt must be F32 or BF16", fn);
+    if (K % 128 || R % 128) return fail(CSL_EUNSUPPORTED, "%s: K and R must be multiples of 128", fn);
+    if ((int64_t)G * K > INT32_MAX || (int64_t)G * R > INT32_MAX || M > 65535 * 128)
+        return fail(CSL_EUNSUPPORTED, "%s: sizes too large", fn);
+    if (M == 0) { g_err.clear(); return CSL_OK; }
+    if (!x || !w || !out) return fail(CSL_EINVAL, "%s: null x, w or out", fn);
+    if (!al16(x) || !al16(w) || !al16(out)) return fail(CSL_EINVAL, "%s: x, w and out must be 16-byte aligned", fn);
+    int rc = check_device();
+    if (rc) return rc;
+    csl::GprojArgs a{(const uint8_t*)x, (const uint8_t*)w, M, G, K, R, (uint8_t*)out, out_fmt};
+    return launched(csl::launch_grouped_out_proj(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -74,8 +74,16 @@ struct AttendArgs {
     float* ws_lse;  // [B*Tq][nhb][nsplit][64]
 };
 
+struct GprojArgs {
+    const uint8_t* x;   // bf16 [M][G*K]
+    const uint8_t* w;   // bf16 [G][R][K]
+    int M, G, K, R;
+    uint8_t* out; int out_fmt;   // [M][G*R], F32 or BF16
+};
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_grouped_out_proj(const GprojArgs& a, hipStream_t s);
 
 }  // namespace csl

@@ -278,3 +278,21 @@ def hca_attend_paged(q, pool, block_table, kv_w, q_pos, *, entries_per_block, bl
     return _attend("hca_attend", q, pool, kv_w, q_pos, None, kv_fmt=kv_fmt, n_cap=n_cap, m=m, kvw_pos0=kvw_pos0,
                    kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out, lse=lse,
                    with_lse=with_lse, sink=sink, pages=(block_table, entries_per_block, block_bytes, n_blocks))
+
+
+def grouped_out_proj(x, w, *, G, out_fmt=F32, out=None):
+    """x bf16 [M, G*K] (e.g. the attention output [B, Tq, H, d] viewed as [B*Tq, H*d]);
+    w bf16 [G, R, K].  Returns out [M, G*R] (float32 or bfloat16): group g's outputs are
+    x[:, g*K:(g+1)*K] @ w[g].T."""
+    _need_cuda(x, w, out)
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("x and w must be contiguous bfloat16")
+    G_, R, K = w.shape
+    if G_ != G or x.shape[-1] != G * K:
+        raise ValueError("x must be [M, G*K] and w [G, R, K]")
+    M = x.numel() // (G * K)
+    if out is None:
+        out = torch.empty((M, G * R), dtype=torch.float32 if out_fmt == F32 else torch.bfloat16, device=x.device)
+    rc = _lib.lib().grouped_out_proj(_ptr(x), BF16, _ptr(w), BF16, M, G, K, R, _ptr(out), out_fmt, _stream())
+    check("grouped_out_proj", rc)
+    return out

@@ -281,6 +281,24 @@ int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, 
  * (rows_max = n_cap + W) with these sizes; 0 when no split partials are needed. */
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max);
 
+/*
+ * grouped_out_proj -- grouped output projection after the attention ([X] section 2,
+ * HCA subsection: both branches project their outputs group by group; [C] table of
+ * attention details, "Grouped Output Projection": compress per group, then combine).
+ * With the attention output of M tokens laid out [M][H][d] and G groups of H/G heads,
+ * group g's input is the K = (H/G)*d contiguous values g*K .. g*K+K-1 of a token:
+ *   out[t][g*R + n] = sum_k x[t][g*K + k] * w[g][n][k]      (fp32 accumulation)
+ * G = 1 is a plain projection (the common projection that combines the groups).
+ *  x      bf16 [M][G*K] (dense);  w  bf16 [G][R][K] (dense; row n of group g's matrix
+ *         is output n's weights, the layout of a [out][in] linear weight).
+ *  out    [M][G*R], CSL_F32 or CSL_BF16 (round to nearest even).
+ *  Limits: K and R multiples of 128 (CSL_EUNSUPPORTED otherwise); 16-byte aligned
+ *  pointers.  The pages give no sizes; the benchmark uses H = 64, d = 512, G = 8,
+ *  R = 1024.
+ */
+int grouped_out_proj(const void* x, int x_fmt, const void* w, int w_fmt, int M, int G, int K, int R,
+                     void* out, int out_fmt, void* stream);
+
 /* Text of a status code; text of the calling thread's last error (copied into
  * buf, NUL-terminated; returns the full length); library version (major*10000 +
  * minor*100 + patch). */

@@ -162,3 +162,19 @@ def test_compress_step_rejects_bad_arguments_on_the_host():
     assert call(pos=None) == _lib.CSL_EINVAL
     assert call(bt=16, bt_stride=4, epb=32, block_bytes=100, n_blocks=10) == _lib.CSL_EINVAL   # block too small
     assert call(T=0) == _lib.CSL_OK
+
+
+def test_grouped_out_proj_rejects_bad_arguments_on_the_host():
+    L = _lib.lib()
+
+    def call(**over):
+        a = dict(x=16, x_fmt=1, w=16, w_fmt=1, M=16, G=8, K=4096, R=1024, out=16, out_fmt=0, stream=None)
+        a.update(over)
+        return L.grouped_out_proj(*a.values())
+
+    assert call(K=4000) == _lib.CSL_EUNSUPPORTED                     # K a multiple of 128
+    assert call(R=100) == _lib.CSL_EUNSUPPORTED
+    assert call(x_fmt=0) == _lib.CSL_EUNSUPPORTED
+    assert call(x=None) == _lib.CSL_EINVAL
+    assert call(out_fmt=2) == _lib.CSL_EINVAL
+    assert call(M=0) == _lib.CSL_OK
