@@ -39,8 +39,9 @@ def parse():
     p.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle CPU sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=20)
-    p.add_argument("--workload", choices=["stack", "prefill"], default="stack",
-                   help="stack: the 4-layer decode stack (default); prefill: one CSA prefill chunk")
+    p.add_argument("--workload", choices=["stack", "prefill", "csa_decode", "hca_decode"], default="stack",
+                   help="stack: the 4-layer decode stack (default); prefill: one CSA prefill chunk; csa_decode: one "
+                        "CSA layer, batch 8 at 128K; hca_decode: one HCA layer, batch 4 at 1M")
     p.add_argument("--layout", choices=["linear", "paged"], default="linear",
                    help="compressed cache of the stack: dense per sequence, or 128-token blocks behind a block table")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -438,6 +439,210 @@ def main_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+class Layer:
+    """One decode layer on its own, with its inputs in `copies` independent sets so that the
+    timed steps cycle through more data than the 256 MB last-level cache holds.
+      csa_decode: batch 8, context 131,072 (t = 131,071), 32,768 packed entries per sequence,
+                  bf16 indexer keys (16 heads x 128, top-512), 64 heads x 512, window 128.
+      hca_decode: batch 4, context 1,048,576, m' = 128: 8,192 packed entries per sequence,
+                  64 heads x 512, window 128.
+    A step: compress the entry the new token completes (from the 128-row state ring), then
+    index + csa_attend, or hca_attend."""
+
+    RING = 128
+
+    def __init__(self, kind, device, copies):
+        import torch
+        from compressed_sparse_long_02_amd import gen, ops as F
+        self.kind, self.dev = kind, device
+        self.H, self.d, self.r, self.W = 64, 512, 64, 128
+        if kind == "csa_decode":
+            self.B, self.ctx, self.m, self.HI, self.dI, self.k = 8, 1 << 17, 4, 16, 128, 512
+        else:
+            self.B, self.ctx, self.m = 4, 1 << 20, 128
+        self.t = self.ctx - 1
+        self.N = self.ctx // self.m
+        self.win = 2 * self.m if kind == "csa_decode" else self.m
+        self.scale = 1.0 / math.sqrt(self.d)
+        B, d, r = self.B, self.d, self.r
+        self.rb = F.row_bytes(F.KV_PACKED, d, r)
+        self.q_pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
+        self.sets = []
+        for c in range(copies):
+            seed = 9000 + 100 * c
+            S = {}
+            S["cache"] = torch.empty((B, self.N, self.rb), dtype=torch.uint8, device=device)
+            for s0 in range(0, self.N, 16384):
+                n = min(16384, self.N - s0)
+                S["cache"][:, s0:s0 + n] = gen.pack_kv(gen.normal((B, n, d), seed + s0, device=device), r)
+            S["ring"] = gen.pack_kv(gen.normal((B, 256, d), seed + 1, device=device), r)
+            S["raw"] = gen.bf16_bytes(gen.normal((B, self.RING, d), seed + 2, device=device))
+            S["z"] = gen.random_logits((B, self.RING, 1), seed + 3, device=device)
+            S["bias"] = gen.random_logits((self.win, 1), seed + 4, device=device)
+            S["q"] = gen.normal((B, 1, self.H, d), seed + 5, device=device).to(torch.bfloat16)
+            S["out"] = torch.empty((B, 1, self.H, d), dtype=torch.bfloat16, device=device)
+            if kind == "csa_decode":
+                S["keys"] = gen.bf16_bytes(gen.normal((B, self.N, self.dI), seed + 6, device=device))
+                S["raw_i"] = gen.bf16_bytes(gen.normal((B, self.RING, self.dI), seed + 7, device=device))
+                S["z_i"] = gen.random_logits((B, self.RING, 1), seed + 8, device=device)
+                S["bias_i"] = gen.random_logits((self.win, 1), seed + 9, device=device)
+                S["qi"] = gen.bf16_bytes(gen.normal((B, 1, self.HI, self.dI), seed + 10, device=device))
+                S["w"] = gen.normal((B, 1, self.HI), seed + 11, device=device)
+                S["idx"] = torch.empty((B, 1, self.k), dtype=torch.int32, device=device)
+            self.sets.append(S)
+        torch.cuda.synchronize()
+
+    def compress(self, S):
+        from compressed_sparse_long_02_amd import ops as F
+        ov = self.kind == "csa_decode"
+        F.kv_compress_step(S["raw"], F.BF16, S["z"], S["bias"], self.q_pos, d=self.d, r=self.r, m=self.m, overlap=ov,
+                           out=S["cache"], out_fmt=F.KV_PACKED)
+        if ov:
+            F.kv_compress_step(S["raw_i"], F.BF16, S["z_i"], S["bias_i"], self.q_pos, d=self.dI, m=self.m,
+                               overlap=True, out=S["keys"], out_fmt=F.BF16)
+
+    def index(self, S, with_scores=False):
+        from compressed_sparse_long_02_amd import ops as F
+        return F.index_topk(S["qi"], S["w"], S["keys"], self.q_pos, fmt=F.BF16, H_I=self.HI, d_I=self.dI, m=self.m,
+                            n_cap=self.N, k=self.k, out_idx=S["idx"], with_scores=with_scores)
+
+    def attend(self, S, out_fmt=None, with_lse=False):
+        from compressed_sparse_long_02_amd import ops as F
+        kw = dict(kv_fmt=F.KV_PACKED, kvw_pos0=0, kvw_rows=256, W=self.W, H=self.H, d=self.d, r=self.r,
+                  scale=self.scale, out_fmt=F.BF16 if out_fmt is None else out_fmt,
+                  out=S["out"] if out_fmt is None else None, with_lse=with_lse)
+        if self.kind == "csa_decode":
+            return F.csa_attend(S["q"], S["cache"], S["idx"], S["ring"], self.q_pos, n_cap=self.N, **kw)
+        return F.hca_attend(S["q"], S["cache"], S["ring"], self.q_pos, n_cap=self.N, m=self.m, **kw)
+
+    def step(self, S):
+        self.compress(S)
+        if self.kind == "csa_decode":
+            self.index(S)
+        self.attend(S)
+
+    def index_bytes(self):
+        B = self.B
+        return B * self.N * self.dI * 2 + B * self.HI * (self.dI * 2 + 4) + B * self.k * 4
+
+    def attend_bytes(self):
+        rows = (self.k if self.kind == "csa_decode" else self.N) + self.W
+        idx = self.k * 4 if self.kind == "csa_decode" else 0
+        return self.B * (rows * self.rb + idx + self.H * self.d * 2 * 2)
+
+    def compress_bytes(self):
+        kv = self.win * (self.d * 2 + 4) + self.rb
+        ik = self.win * (self.dI * 2 + 4) + self.dI * 2 if self.kind == "csa_decode" else 0
+        return self.B * (kv + ik)
+
+    def step_bytes(self):
+        return (self.index_bytes() if self.kind == "csa_decode" else 0) + self.attend_bytes() + self.compress_bytes()
+
+
+def layer_cpu_baseline(ly, min_s=10.0):
+    """The oracle on the whole batch of one input set (compress the new entry, index, attend),
+    repeated until about min_s seconds have passed; the median pass counts."""
+    import numpy as np
+    import torch
+    import oracle as O
+    S = ly.sets[0]
+    h = lambda x: x.detach().cpu().numpy()
+    a = {k: h(v) for k, v in S.items() if k not in ("out", "idx", "q")}
+    a["q"] = h(S["q"].view(torch.int16))
+    qpos = np.full((ly.B, 1), ly.t, np.int32)
+    i = (ly.t + 1) // ly.m - 1
+    okw = dict(W=ly.W, H=ly.H, d=ly.d, r=ly.r, scale=ly.scale)
+    reps, total = [], 0.0
+    while not reps or (total < min_s and len(reps) < 50):
+        t0 = time.perf_counter()
+        O.kv_compress(a["raw"], O.BF16, a["z"], a["bias"], d=ly.d, r=ly.r, m=ly.m, overlap=ly.kind == "csa_decode",
+                      e_begin=i, n_e=1, x_rows=ly.RING, out_fmt=O.KV_PACKED)
+        if ly.kind == "csa_decode":
+            O.kv_compress(a["raw_i"], O.BF16, a["z_i"], a["bias_i"], d=ly.dI, m=ly.m, overlap=True, e_begin=i, n_e=1,
+                          x_rows=ly.RING, out_fmt=O.BF16)
+            idx, _ = O.index_topk(a["qi"], O.BF16, a["w"], a["keys"], O.BF16, qpos, H_I=ly.HI, d_I=ly.dI, m=ly.m,
+                                  n_cap=ly.N, k=ly.k)
+            O.csa_attend(a["q"], O.BF16, a["cache"], O.KV_PACKED, ly.N, idx, a["ring"], 0, 256, qpos, **okw)
+        else:
+            O.hca_attend(a["q"], O.BF16, a["cache"], O.KV_PACKED, ly.N, ly.m, a["ring"], 0, 256, qpos, **okw)
+        dt = time.perf_counter() - t0
+        reps.append(dt)
+        total += dt
+    dt = float(np.median(reps))
+    return {"value": round(ly.B / dt, 4), "unit": "tokens/s", "cores": min(ly.B, O.num_threads()), "kind": "oracle",
+            "sample": "the whole batch (%d sequences) of one input set through the layer (compress + %s), median of "
+                      "%d passes (%.2f s each) on the host" % (ly.B, "index + attend" if ly.kind == "csa_decode"
+                                                               else "attend", len(reps), dt)}
+
+
+def main_layer(args):
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = 3 if args.workload == "csa_decode" else 28
+    print("[bench] building %s inputs (%d copies)" % (args.workload, copies), file=sys.stderr, flush=True)
+    ly = Layer(args.workload, dev, copies)
+    for S in ly.sets:
+        ly.step(S)
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    for S in ly.sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                ly.step(S)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    print("[bench] graphs captured; warmup %d, timed %d" % (args.warmup, args.steps), file=sys.stderr, flush=True)
+    n = len(graphs)
+    for i in range(args.warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-call durations, cycling through the input sets
+    if args.workload == "csa_decode":
+        calls = [f for S in ly.sets for f in (lambda S=S: ly.index(S), lambda S=S: ly.attend(S))]
+        tt = time_sequence(calls, args.kernel_iters)
+        t_idx = sum(tt[0::2]) / n
+        t_att = sum(tt[1::2]) / n
+    else:
+        tt = time_sequence([lambda S=S: ly.attend(S) for S in ly.sets], args.kernel_iters)
+        t_idx, t_att = None, sum(tt) / n
+    tc = time_sequence([lambda S=S: ly.compress(S) for S in ly.sets], max(3, args.kernel_iters // 4))
+    t_cmp = sum(tc) / n
+    kernels = {"csa_attend" if args.workload == "csa_decode" else "hca_attend":
+               {"ms": round(t_att, 4), "GB/s": round(ly.attend_bytes() / (t_att * 1e-3) / 1e9, 1)},
+               "kv_compress_step": {"ms": round(t_cmp, 4)},
+               "step_GB/s": round(ly.step_bytes() / (ms * 1e-3) / 1e9, 1), "step_bytes": ly.step_bytes(),
+               "input_sets": n}
+    if t_idx is not None:
+        kernels["index_topk"] = {"ms": round(t_idx, 4), "GB/s": round(ly.index_bytes() / (t_idx * 1e-3) / 1e9, 1)}
+        dom, db, dt = "index_topk (bf16 16x128 scores + top-512 of 32,768 per sequence)", ly.index_bytes(), t_idx
+    else:
+        dom, db, dt = "hca_attend (64 heads x 512 over 8,192 entries + 128-token window)", ly.attend_bytes(), t_att
+    ach = db / (dt * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": db, "ms_per_launch": round(dt, 4)}
+    cpu = None if args.no_cpu_baseline else layer_cpu_baseline(ly)
+    wl = ("CSA decode layer: batch 8 at 131,072 tokens (32,768 entries), bf16 indexer 16x128 top-512"
+          if args.workload == "csa_decode" else "HCA decode layer: batch 4 at 1,048,576 tokens (8,192 entries)")
+    line = {
+        "metric": METRIC, "value": round(ly.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "global_batch": ly.B, "seq_len": ly.ctx, "heads": ly.H, "head_dim": ly.d,
+                   "kv": "bf16 rope64 + fp8 e4m3 (576 B)", "m": ly.m, "window": ly.W, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def time_sequence(calls, iters):
     """Average duration of each call of a repeating sequence, by HIP events recorded
     between the calls on torch's current stream.  Cycling through the layers of the
@@ -538,6 +743,8 @@ def main():
         sys.exit(2)
     if args.workload == "prefill":
         return main_prefill(args)
+    if args.workload in ("csa_decode", "hca_decode"):
+        return main_layer(args)
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -584,8 +791,12 @@ def main():
     roof = {"bound": "hbm", "kernel": "index_topk (MXFP4 scores + top-1024 of 262,144 per sequence)",
             "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(args.batch, args.ctx), "bytes_per_launch": ib, "ms_per_launch": round(t_idx, 4)}
+    # the indexer's contraction as MFMA work: 2 * H_I * d_I flops per (query, entry), on the
+    # scaled FP4 MFMA (dense fp4 peak 10.1 PFLOP/s)
+    idx_tf = 2.0 * st.HI * st.dI * st.N * st.B / (t_idx * 1e-3) / 1e12
     kernels = {
-        "index_topk": {"ms": round(t_idx, 4), "GB/s": round(ach, 1)},
+        "index_topk": {"ms": round(t_idx, 4), "GB/s": round(ach, 1), "TFLOP/s": round(idx_tf, 1),
+                       "mfma_frac_fp4": round(idx_tf / 10100.0, 4)},
         "csa_attend": {"ms": round(t_csa, 4), "GB/s": round(st.csa_bytes() / (t_csa * 1e-3) / 1e9, 1)},
         "hca_attend": {"ms": round(t_hca, 4), "GB/s": round(st.hca_bytes() / (t_hca * 1e-3) / 1e9, 1)},
         "step_GB/s": round(st.step_bytes() / (ms * 1e-3) / 1e9, 1),

@@ -17,7 +17,7 @@
 // object is loaded there until the process ends.  Host code never passes the array's
 // name to a kernel (on the host it is only a stand-in): it looks up each device's
 // address once with hipGetSymbolAddress and passes that.
-constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)96 << 20;
 static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
@@ -105,14 +105,7 @@ int64_t row_stride(int64_t n_cap) { return n_cap < 4 ? 4 : (n_cap + 3) & ~(int64
 size_t index_ws(int B, int Tq, int64_t n_cap, int nslices) {
     if (nslices <= 1) return 0;
     const size_t q = (size_t)B * Tq;
-    return q * ((size_t)3 * row_stride(n_cap) + (size_t)nslices * (csl::IDX_SLOT_W + 1) + 4) * 4 + 256;
-}
-
-// Split path: slices per filter block, about 256 filter blocks (one per compute unit) in all.
-int index_spb(int B, int Tq, int nslices) {
-    const int64_t q = (int64_t)(B > 0 ? B : 1) * (Tq > 0 ? Tq : 1);
-    int64_t spb = ((int64_t)nslices * q + 255) / 256;
-    return (int)(spb < 1 ? 1 : (spb > nslices ? nslices : spb));
+    return q * ((size_t)4 * row_stride(n_cap) + (size_t)nslices * (csl::IDX_SLOT_W + 1)) * 4 + 256;
 }
 
 constexpr int ATT_STEP = 32;            // rows a block stages per iteration; split lengths are multiples
@@ -441,16 +434,15 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
         a.scores = (uint32_t*)ws;
         a.hist = (uint32_t*)((uint8_t*)ws + (size_t)B * a.Tc * a.sstride * 4);
     } else if (nslices > 1) {
-        a.spb = index_spb(B, Tq, nslices);
         a.sstride = row_stride(n_cap);
         const size_t q = (size_t)B * Tq;
         const size_t nr = q * a.sstride * 4;           // bytes of one [B*Tq][sstride] array
-        a.scores = (uint32_t*)ws;
-        a.cand_key = (uint32_t*)((uint8_t*)ws + nr);
-        a.cand_idx = (int32_t*)((uint8_t*)ws + 2 * nr);
-        a.hist = (uint32_t*)((uint8_t*)ws + 3 * nr);
+        a.cand_key = (uint32_t*)ws;
+        a.cand_idx = (int32_t*)((uint8_t*)ws + nr);
+        a.scores = (uint32_t*)((uint8_t*)ws + 2 * nr);
+        a.fb_idx = (int32_t*)((uint8_t*)ws + 3 * nr);
+        a.hist = (uint32_t*)((uint8_t*)ws + 4 * nr);
         a.seg_cnt = (int32_t*)(a.hist + q * nslices * csl::IDX_SLOT_W);
-        a.row_bin = (uint32_t*)(a.seg_cnt + q * nslices);
     }
     return launched(csl::launch_index_topk(a, (hipStream_t)stream));
 }

@@ -388,9 +388,9 @@ k_idx_score(IndexArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int E = a.S / IDX_NT;
     const int le = 31 - __builtin_clz(E);
-    uint32_t* keys = smem;
+    uint32_t* keys = smem;                               // key li at li + li / E (E + 1 words per thread)
     uint32_t* sh = smem + a.S + (a.S >> le);
-    uint32_t* hs = smem + a.S;                           // SPLIT: keys (unpadded), then the padded histogram
+    uint32_t* hs = sh;                                   // SPLIT: the padded histogram after the keys
     uint32_t* ctr = SPLIT ? hs + TOPK_HSZ + 24 : sh + TOPK_SCRATCH(IDX_NT);   // next tile group
     int32_t* ids = (int32_t*)(ctr + 4);                  // paged keys: the slice's block ids
 
@@ -516,12 +516,8 @@ k_idx_score(IndexArgs a) {
             if (T < ntile && li < ns) {
                 const bool absent = a.bt && ids[(uint32_t)(s0 + li - blk0 * a.epb) / (uint32_t)a.epb] < 0;
                 const uint32_t u = absent ? score_key(-INFINITY) : score_key(tot);
-                if constexpr (SPLIT) {
-                    keys[li] = u;
-                    atomicAdd(&hs[hpad(u >> (32 - TOPK_BITS))], 1u);
-                } else {
-                    keys[li + (li >> le)] = u;
-                }
+                keys[li + (li >> le)] = u;
+                if constexpr (SPLIT) atomicAdd(&hs[hpad(u >> (32 - TOPK_BITS))], 1u);
             }
         };
         // ping-pong: the next group's fragments load while the current one is scored
@@ -540,20 +536,12 @@ k_idx_score(IndexArgs a) {
     }
     __syncthreads();
     if constexpr (SPLIT) {
-        // the slice's keys to its part of the score row in 16-byte stores (s0 and the
-        // row stride are multiples of 4), the histogram into the query's
-        uint32_t* srow = a.scores + bq * a.sstride + s0;
-        for (int i = 4 * tid; i < ns; i += 4 * IDX_NT) {
-            if (i + 4 <= ns) {
-                *(u32x4*)(srow + i) = *(const u32x4*)(keys + i);
-            } else {
-                for (int x = i; x < ns; ++x) srow[x] = keys[x];
-            }
-        }
-        // The list keeps the nonzero bins from the top down to the one holding the
-        // slice's min(k, ns)-th largest key: that key is at most the query's k-th
-        // largest, so the bins left out lie below the query's threshold bin, and the
-        // counts at and above it are exact.
+        // The slice's threshold bin: the one holding its min(k, ns)-th largest key.  That
+        // key is at most the query's k-th largest, so every key of the query's top k lies
+        // in this bin or above: the slice keeps only those keys (with their entry indices,
+        // in entry order, at its segment [s0, s0 + S) of the candidate rows) and the list
+        // of its nonzero bins from the top down to this one -- the counts at and above
+        // the query's threshold bin are then exact.
         uint32_t* misc = hs + TOPK_HSZ + 16;
         if (wv == 0) find_bin(hs, (uint32_t)(ns < a.k ? ns : a.k), misc);
         constexpr int BPT = TOPK_BINS / IDX_NT;          // bins per thread: BPT*t .. BPT*t + BPT-1
@@ -575,6 +563,27 @@ k_idx_score(IndexArgs a) {
         for (int x = 0; x < BPT; ++x)
             if (keep[x]) slot[o++] = ((uint32_t)(BPT * tid + x) << 21) | keep[x];
         if (tid == 0) slot[0] = (uint32_t)tot;
+        __syncthreads();                                 // the scan's words are reused below
+        // candidates: thread t takes keys t*E .. t*E + E-1 (entry order)
+        const uint32_t lo = bmin << (32 - TOPK_BITS);
+        uint32_t kv[TOPK_EMAX];
+        int my = 0;
+#pragma unroll
+        for (int x = 0; x < TOPK_EMAX; ++x) {
+            const int i = tid * E + x;
+            kv[x] = (x < E && i < ns) ? keys[i + (i >> le)] : 0u;
+            my += (x < E && i < ns && kv[x] >= lo) ? 1 : 0;
+        }
+        int ctot;
+        int pos = block_excl_scan<IDX_NT>(my, (int*)(hs + TOPK_HSZ), ctot);
+        uint32_t* ck = a.cand_key + bq * a.sstride + s0;
+        int32_t* ci = a.cand_idx + bq * a.sstride + s0;
+#pragma unroll
+        for (int x = 0; x < TOPK_EMAX; ++x) {
+            const int i = tid * E + x;
+            if (x < E && i < ns && kv[x] >= lo) { ck[pos] = kv[x]; ci[pos] = (int32_t)(s0 + i); ++pos; }
+        }
+        if (tid == 0) a.seg_cnt[bq * a.nslices + sl] = ctot;
         return;
     }
 
@@ -767,7 +776,8 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
 // survivor keys [DSEL_CAP] | their entry indices [DSEL_CAP] | winners [2048] |
 // winner keys [2048].
 // The threshold is refined 11 + 11 + 10 key bits at a time (one pass over the row per
-// extra level) until the keys at or above it fit in DSEL_CAP.  If the first level
+// extra level) until the keys at or above it fit in DSEL_CAP.  The row's positions are
+// its entry indices, or map to them through imap (a gathered row, in entry order).  If the first level
 // fits and gather(sk, si) returns the survivor count (>= 0), the survivors come from
 // there (the split path filtered them already); otherwise one pass over the row
 // collects them.  Then an exact radix select among the survivors, in entry order.
@@ -778,7 +788,8 @@ struct BinInfo {          // the first level's threshold bin, when already known
 
 template <typename Gather>
 __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64_t n, const uint32_t* srow,
-                                           uint32_t* smem, Gather gather, BinInfo b0 = BinInfo{false, 0, 0, 0}) {
+                                           uint32_t* smem, Gather gather, BinInfo b0 = BinInfo{false, 0, 0, 0},
+                                           const int32_t* imap = nullptr) {
     const int tid = threadIdx.x, wv = tid >> 6;
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
@@ -999,7 +1010,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
     });
     __syncthreads();
     for (int p = tid; p < a.k; p += DSEL_NT) {
-        oi[p] = win[p];
+        oi[p] = imap ? imap[win[p]] : win[p];        // a gathered row: position -> entry index
         if (os) os[p] = key_score(wkey[p]);
     }
 }
@@ -1032,206 +1043,218 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
     select_row(a, bq, n, srow, smem, [](uint32_t*, int*) { return -1; });
 }
 
-// Split path, step 2: blocks of `spb` consecutive slices (FS = spb * S keys) per
-// query.  Each block sums the query's slice histograms (the score kernel's
-// (bin << 21 | count) lists) into LDS and finds the threshold bin, the one holding
-// the k-th largest key; block 0 stores it for the select.  If the keys in that bin or
-// above fit in DSEL_CAP, the block copies its range's such keys, with their entry
-// indices and in entry order, to its segment [f*FS, ..) of the candidate rows, and
-// their count to seg_cnt; otherwise the select refines the threshold over the row.
-constexpr int FLT_NT = 1024;
-constexpr int FLT_CH = 16;        // keys per thread per chunk
+// Split path, step 2: one block per query; wave w owns slices w, w + 16, ...  At the
+// start every wave issues the loads of its first slice's list and of up to SEL_PF
+// candidates of its segment, all at once (one memory round trip).  The lists are added
+// into an LDS histogram, which gives the query's threshold bin (the one holding its
+// k-th largest key) and the exact count of keys in it and above.  Every such key is in
+// some slice's candidate segment (a slice kept all keys at or above its own threshold
+// bin, which is at most the query's).  Usual case: each wave compacts its segment's
+// keys at or above the bin (the prefetched part, then the rest) into its own LDS region, the regions are joined in wave
+// order (= entry order), and a radix select over their offsets from the bin's lower
+// edge, the keys above the bin clamped to its upper edge (22 bits, two passes, no
+// min / max phase), gives the exact top k.  Otherwise (a region overflows: ties,
+// clustered scores, or more slices than waves) the keys at or above the bin are
+// gathered, in entry order, into the workspace row and the general row select refines
+// the threshold over them.  n(t) <= k: the segments hold every key, all are taken.
+constexpr int SEL_PF = 1024;                         // candidates a wave prefetches (16 rounds of 64)
 
-__global__ void __launch_bounds__(FLT_NT) k_idx_split_filter(IndexArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t sh[TOPK_HSZ];
-    __shared__ uint32_t misc[4];
-    __shared__ int wsum[FLT_NT / 64 + 8];
-    constexpr int NW = FLT_NT / 64;
-    const int fb = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+__global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    constexpr int NW = DSEL_NT / 64, WCAP = DSEL_CAP / NW, NR = SEL_PF / 64;
+    const int j = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bq = (int64_t)b * a.Tq + j;
-    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
-    if (n <= a.k) return;                                // the select takes every entry
-    const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
-    const int nfb = (nseg + a.spb - 1) / a.spb;          // filter blocks with keys
-    if (fb >= nfb) return;
-    const uint32_t* srow = a.scores + bq * a.sstride;
-    const int64_t FS = (int64_t)a.spb * a.S;
-    const int64_t f0 = (int64_t)fb * FS;
-    const int nf = (int)(n - f0 < FS ? n - f0 : FS);     // keys of this block
-    auto load_chunk = [&](int c0, uint32_t (&kv)[FLT_CH]) {
-#pragma unroll
-        for (int q = 0; q < FLT_CH / 4; ++q) {
-            int64_t sq = f0 + c0 + tid * FLT_CH + 4 * q;
-            sq = sq < n ? sq : ((n - 1) & ~(int64_t)3);  // clamped inside the (4-padded) row
-            const u32x4 v = *(const u32x4*)(srow + sq);
-            kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
-        }
-    };
-    // ---- histogram: wave w adds the lists of slices w, w + NW, ...; lane l takes entry
-    // l (then l + 64, ...).  The first two slices' count and entry are loaded together
-    // with the first chunk of keys, before the barrier that clears the histogram.
+    const uint32_t* ckr = a.cand_key + bq * a.sstride;
+    const int32_t* cir = a.cand_idx + bq * a.sstride;
     const uint32_t* slots = a.hist + bq * (int64_t)a.nslices * SLOT_W;
-    const int sa = wv, sb = wv + NW;
-    uint32_t ca = 0, ea = 0, cb = 0, eb = 0;
-    if (sa < nseg) { ca = slots[(int64_t)sa * SLOT_W]; ea = slots[(int64_t)sa * SLOT_W + 1 + lane]; }
-    if (sb < nseg) { cb = slots[(int64_t)sb * SLOT_W]; eb = slots[(int64_t)sb * SLOT_W + 1 + lane]; }
-    uint32_t kv[FLT_CH];
-    load_chunk(0, kv);
-    for (int x = tid; x < TOPK_HSZ; x += FLT_NT) sh[x] = 0u;
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
+    // ---- prefetch: this wave's first slice: list head, its first 64 list entries, its count
+    // and its first SEL_PF candidates (indices only where a key is present)
+    const bool mine = wv < nseg && n > a.k;
+    uint32_t lc = 0, le = 0, pk[NR];
+    int32_t pi[NR];
+    int cnt = 0;
+    if (mine) {
+        const uint32_t* li = slots + (int64_t)wv * SLOT_W;
+        lc = li[0];
+        le = li[1 + lane];                               // read within the slot (lists hold <= 2048 entries)
+        cnt = a.seg_cnt[bq * a.nslices + wv];
+    }
+    {
+        const uint32_t* kk = ckr + (int64_t)wv * a.S;
+        const int32_t* ii = cir + (int64_t)wv * a.S;
+        const int64_t nsw = mine ? (n - (int64_t)wv * a.S < a.S ? n - (int64_t)wv * a.S : a.S) : 0;   // the slice's keys
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int e = 64 * r + lane;
+            pk[r] = e < nsw ? kk[e] : 0u;                // within the slice's segment (entries < n)
+            pi[r] = e < nsw ? ii[e] : 0;
+        }
+    }
+    if (n <= a.k) {
+        take_all(a, bq, n, ckr, tid, DSEL_NT);
+        return;
+    }
+    uint32_t* sh = smem;
+    uint32_t* misc = sh + 2 * TOPK_HSZ;
+    int* wsum = (int*)(sh + 2 * TOPK_HSZ + 16);
+    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);
+    int* si = (int*)(sk + DSEL_CAP);
+    int* win = si + DSEL_CAP;
+    uint32_t* wkey = (uint32_t*)(win + 2048);
+    int* segoff = (int*)(wkey + 2048);                   // fallback: per slice, keys at or above the bin
+    // ---- the query's histogram from the slices' lists
+    for (int x = tid; x < TOPK_HSZ; x += DSEL_NT) sh[x] = 0u;
     __syncthreads();
-    if ((uint32_t)lane < ca) atomicAdd(&sh[hpad(ea >> 21)], ea & 0x1fffffu);
-    if ((uint32_t)lane < cb) atomicAdd(&sh[hpad(eb >> 21)], eb & 0x1fffffu);
-    for (int sl = wv; sl < nseg; sl += NW) {             // longer lists, further slices
+    if (mine && (uint32_t)lane < lc) atomicAdd(&sh[hpad(le >> 21)], le & 0x1fffffu);
+    for (int sl = wv; sl < nseg; sl += NW) {             // the rest of the lists (long ones, further slices)
         const uint32_t* li = slots + (int64_t)sl * SLOT_W;
-        const bool pre = sl == sa || sl == sb;
-        const uint32_t c = sl == sa ? ca : (sl == sb ? cb : li[0]);
-        // four rounds of 64 list entries in flight before their atomics
-        for (uint32_t e0 = pre ? 64u : 0u; e0 < c; e0 += 256) {
-            uint32_t pr[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t e = e0 + 64 * u + lane;
-                pr[u] = e < c ? li[1 + e] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (e0 + 64 * u + lane < c) atomicAdd(&sh[hpad(pr[u] >> 21)], pr[u] & 0x1fffffu);
+        const uint32_t c = sl == wv ? lc : li[0];
+        for (uint32_t e0 = sl == wv ? 64u : 0u; e0 < c; e0 += 64) {
+            const uint32_t e = e0 + lane;
+            const uint32_t v = e < c ? li[1 + e] : 0u;
+            if (e < c) atomicAdd(&sh[hpad(v >> 21)], v & 0x1fffffu);
         }
     }
     __syncthreads();
     if (wv == 0) find_bin(sh, (uint32_t)a.k, misc);
     __syncthreads();
-    if (fb == 0 && tid < 3) a.row_bin[bq * 4 + tid] = misc[tid];   // for the select
-    if (misc[1] + misc[2] > (uint32_t)DSEL_CAP) return;
-    // ---- keys in the threshold bin or above, in entry order
-    const uint32_t lo = misc[0] << (32 - TOPK_BITS);
-    uint32_t* ck = a.cand_key + bq * a.sstride + f0;
-    int32_t* ci = a.cand_idx + bq * a.sstride + f0;
-    int cnt = 0;
-    for (int c0 = 0; c0 < nf; c0 += FLT_NT * FLT_CH) {
-        if (c0 > 0) load_chunk(c0, kv);
-        const int e0 = c0 + tid * FLT_CH;                // block offset of kv[0]
-        int my = 0;
-#pragma unroll
-        for (int x = 0; x < FLT_CH; ++x) my += (e0 + x < nf && kv[x] >= lo) ? 1 : 0;
-        int tot;
-        int pos = cnt + block_excl_scan<FLT_NT>(my, wsum, tot);
-#pragma unroll
-        for (int x = 0; x < FLT_CH; ++x) {
-            if (e0 + x < nf && kv[x] >= lo) { ck[pos] = kv[x]; ci[pos] = (int32_t)(f0 + e0 + x); ++pos; }
-        }
-        cnt += tot;
-        __syncthreads();                                 // wsum reuse
-    }
-    if (tid == 0) a.seg_cnt[bq * a.nslices + fb] = cnt;
-}
-
-// Split path, step 3: one block per query.  Usual case (the keys in and above the
-// threshold bin fit, at most 64 filter blocks): every wave scans the blocks' counts
-// itself, wave w copies segments w, w + 16, ... in entry order, and the exact top k
-// comes from a radix select over the survivors' offsets from the bin's lower edge
-// lo, those above the bin clamped to its upper edge: 22 bits, two passes, no
-// min / max phase.  Otherwise the general row select.
-__global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-    constexpr int NW = DSEL_NT / 64;
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t bq = (int64_t)b * a.Tq + j;
-    const int nfb_max = (a.nslices + a.spb - 1) / a.spb;
-    // one round of loads: position, threshold bin, counts
-    const int32_t qp = a.q_pos[bq];
-    const uint32_t bin = a.row_bin[bq * 4], above = a.row_bin[bq * 4 + 1], inbin = a.row_bin[bq * 4 + 2];
-    const int craw = lane < nfb_max ? a.seg_cnt[bq * a.nslices + lane] : 0;
-    const int64_t n = n_visible(qp, a.m, a.n_cap);
-    const uint32_t* srow = a.scores + bq * a.sstride;
-    if (n <= a.k) {
-        take_all(a, bq, n, srow, tid, DSEL_NT);
-        return;
-    }
-    const int nfb = (int)(((n + a.S - 1) / a.S + a.spb - 1) / a.spb);
-    const int64_t FS = (int64_t)a.spb * a.S;
-    const uint32_t* ck = a.cand_key + bq * a.sstride;
-    const int32_t* ci = a.cand_idx + bq * a.sstride;
-    int* wsum = (int*)(smem + 2 * TOPK_HSZ + 16);
-    const BinInfo b0{true, bin, above, inbin};
-    if (above + inbin > (uint32_t)DSEL_CAP || nfb > 64) {
-        select_row(a, bq, n, srow, smem, [&](uint32_t* sk, int* si) {
-            // the filter blocks' segments in block order = entry order
-            int* foff = (int*)(sk + 2 * DSEL_CAP);       // the winner area, free until the final select
-            const int cc = tid < nfb ? a.seg_cnt[bq * a.nslices + tid] : 0;
-            int tot;
-            const int o = block_excl_scan<DSEL_NT>(cc, wsum, tot);
-            tot = tot < DSEL_CAP ? tot : DSEL_CAP;       // equal to the keys in and above the bin
-            if (tid < nfb) foff[tid] = o;
-            __syncthreads();
-            for (int p = tid; p < tot; p += DSEL_NT) {
-                int l = 0, h = nfb - 1;                  // last block whose segment starts at or before p
-                while (l < h) {
-                    const int mid = (l + h + 1) >> 1;
-                    if (foff[mid] <= p) l = mid; else h = mid - 1;
-                }
-                const int64_t src = (int64_t)l * FS + (p - foff[l]);
-                sk[p] = ck[src];
-                si[p] = ci[src];
-            }
-            __syncthreads();
-            return tot;
-        }, b0);
-        return;
-    }
-    uint32_t* sh = smem;
-    uint32_t* sk = sh + TOPK_SCRATCH(DSEL_NT);
-    int* si = (int*)(sk + DSEL_CAP);
-    int* win = si + DSEL_CAP;
-    uint32_t* wkey = (uint32_t*)(win + 2048);
-    // ---- gather
-    const int c = lane < nfb ? craw : 0;
-    const int incl = wave_incl_scan(c);
-    const int nsurv = __shfl(incl, 63, 64);               // = above + inbin <= DSEL_CAP
-    for (int f = wv; f < nfb; f += NW) {
-        const int cf = __shfl(c, f, 64), of = __shfl(incl, f, 64) - cf;
-        // four rounds of 64 in flight before the first store (a loop round per element
-        // pair would wait for each pair's loads in turn)
-        for (int e0 = 0; e0 < cf; e0 += 256) {
-            uint32_t kk[4];
-            int32_t ii[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + 64 * u + lane;
-                if (e < cf) { kk[u] = ck[(int64_t)f * FS + e]; ii[u] = ci[(int64_t)f * FS + e]; }
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + 64 * u + lane;
-                if (e < cf) { sk[of + e] = kk[u]; si[of + e] = ii[u]; }
-            }
-        }
-    }
-    __syncthreads();
-    // ---- exact top k
+    const uint32_t bin = misc[0], above = misc[1], inbin = misc[2];
     const uint32_t lo = bin << (32 - TOPK_BITS);
-    const uint32_t span = 1u << (32 - TOPK_BITS);         // keys above the bin map to span
-    constexpr int E2MAX = DSEL_CAP / DSEL_NT;
-    const int E2 = (nsurv + DSEL_NT - 1) / DSEL_NT;
-    uint32_t kv2[E2MAX];
+    const uint32_t nsurv = above + inbin;
+    // ---- usual case: per-wave compaction of the prefetched segment into its LDS region
+    int got = 0;
+    bool ovf = nseg > NW || nsurv > (uint32_t)DSEL_CAP;
+    if (!ovf && mine) {
+        uint32_t* rk = sk + wv * WCAP;
+        int* ri = si + wv * WCAP;
+        auto put = [&](bool keep, uint32_t key, int32_t idx) {
+            const uint64_t m = __ballot(keep);
+            if (keep) {
+                const int p = got + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                if (p < WCAP) { rk[p] = key; ri[p] = idx; }
+            }
+            got += __builtin_popcountll(m);
+        };
 #pragma unroll
-    for (int x = 0; x < E2MAX; ++x) {
-        const uint32_t d = (x < E2 && tid * E2 + x < nsurv) ? sk[tid * E2 + x] - lo : 0u;
-        kv2[x] = d < span ? d : span;
+        for (int r = 0; r < NR; ++r) put(64 * r + lane < cnt && pk[r] >= lo, pk[r], pi[r]);
+        // the rest of the segment (beyond the prefetched part), four rounds at a time
+        const uint32_t* kk = ckr + (int64_t)wv * a.S;
+        const int32_t* ii = cir + (int64_t)wv * a.S;
+        for (int e0 = SEL_PF; e0 < cnt; e0 += 256) {
+            uint32_t kr[4];
+            int32_t ir[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                kr[u] = e < cnt ? kk[e] : 0u;
+                ir[u] = e < cnt ? ii[e] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) put(e0 + 64 * u + lane < cnt && kr[u] >= lo, kr[u], ir[u]);
+        }
     }
-    block_topk<DSEL_NT>(kv2, E2, nsurv, a.k, sh, [&](int pos, int i, uint32_t) {
-        win[pos] = si[i];
-        wkey[pos] = sk[i];
-    }, 32 - TOPK_BITS);
-    __syncthreads();
+    if (lane == 0) wsum[wv] = got;
+    ovf = __syncthreads_or((ovf || got > WCAP) ? 1 : 0);
     int32_t* oi = a.out_idx + bq * a.k;
     float* os = a.out_score ? a.out_score + bq * a.k : nullptr;
-    for (int p = tid; p < a.k; p += DSEL_NT) {
-        oi[p] = win[p];
-        if (os) os[p] = key_score(wkey[p]);
+    if (!ovf) {
+        // join the regions in wave order (= entry order) at the front of sk / si
+        int off = 0;
+        for (int x = 0; x < wv; ++x) off += wsum[x];
+        uint32_t tk[WCAP / 64];
+        int ti[WCAP / 64];
+#pragma unroll
+        for (int y = 0; y < WCAP / 64; ++y) {
+            const int p = lane + 64 * y;
+            tk[y] = p < got ? sk[wv * WCAP + p] : 0u;
+            ti[y] = p < got ? si[wv * WCAP + p] : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int y = 0; y < WCAP / 64; ++y) {
+            const int p = lane + 64 * y;
+            if (p < got) { sk[off + p] = tk[y]; si[off + p] = ti[y]; }
+        }
+        __syncthreads();
+        // ---- exact top k among the survivors
+        const uint32_t span = 1u << (32 - TOPK_BITS);     // keys above the bin map to span
+        constexpr int E2MAX = DSEL_CAP / DSEL_NT;
+        const int E2 = ((int)nsurv + DSEL_NT - 1) / DSEL_NT;
+        uint32_t kv2[E2MAX];
+#pragma unroll
+        for (int x = 0; x < E2MAX; ++x) {
+            const uint32_t d = (x < E2 && tid * E2 + x < (int)nsurv) ? sk[tid * E2 + x] - lo : 0u;
+            kv2[x] = d < span ? d : span;
+        }
+        block_topk<DSEL_NT>(kv2, E2, (int)nsurv, a.k, sh, [&](int pos, int i, uint32_t) {
+            win[pos] = si[i];
+            wkey[pos] = sk[i];
+        }, 32 - TOPK_BITS);
+        __syncthreads();
+        for (int p = tid; p < a.k; p += DSEL_NT) {
+            oi[p] = win[p];
+            if (os) os[p] = key_score(wkey[p]);
+        }
+        return;
     }
+    // ---- fallback: gather the keys at or above the bin into the workspace row, in entry
+    // order (per-slice counts from the lists give the offsets), then the row select
+    for (int sl = wv; sl < nseg; sl += NW) {
+        const uint32_t* li = slots + (int64_t)sl * SLOT_W;
+        const uint32_t c = li[0];
+        uint32_t cn = 0;
+        for (uint32_t e = lane; e < c; e += 64) {
+            const uint32_t v = li[1 + e];
+            cn += (v >> 21) >= bin ? (v & 0x1fffffu) : 0u;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) cn += __shfl_xor(cn, o, 64);
+        if (lane == 0) segoff[sl] = (int)cn;
+    }
+    __syncthreads();
+    {
+        const int c = tid < nseg ? segoff[tid] : 0;
+        int tot;
+        const int o = block_excl_scan<DSEL_NT>(c, wsum, tot);
+        __syncthreads();
+        if (tid < nseg) segoff[tid] = o;
+    }
+    __syncthreads();
+    uint32_t* gk = a.scores + bq * a.sstride;
+    int32_t* gi = a.fb_idx + bq * a.sstride;
+    for (int sl = wv; sl < nseg; sl += NW) {
+        const int c = a.seg_cnt[bq * a.nslices + sl];
+        int o = segoff[sl];
+        const uint32_t* kk = ckr + (int64_t)sl * a.S;
+        const int32_t* ii = cir + (int64_t)sl * a.S;
+        for (int e0 = 0; e0 < c; e0 += 256) {
+            uint32_t kr[4];
+            int32_t ir[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + 64 * u + lane;
+                kr[u] = e < c ? kk[e] : 0u;
+                ir[u] = e < c ? ii[e] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool keep = e0 + 64 * u + lane < c && kr[u] >= lo;
+                const uint64_t m = __ballot(keep);
+                if (keep) {
+                    const int p = o + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                    gk[p] = kr[u];
+                    gi[p] = ir[u];
+                }
+                o += __builtin_popcountll(m);
+            }
+        }
+    }
+    __syncthreads();
+    const BinInfo b0{true, bin, above, inbin};
+    select_row(a, bq, (int64_t)nsurv, gk, smem, [](uint32_t*, int*) { return -1; }, b0, gi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1241,7 +1264,7 @@ template <int FMT, int DI, int HB, bool SPLIT>
 static void launch_score(const IndexArgs& a, hipStream_t s) {
     const int E = a.S / IDX_NT;
     const size_t nid = a.bt ? (size_t)a.S / 16 + 2 : 0;                                         // paged: block ids
-    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + TOPK_HSZ + 32 + nid)         // keys, histogram, scan, misc, counter
+    const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_HSZ + 32 + nid)   // keys, histogram, scan, misc, counter
                              : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT) + 4 + nid);   // keys, scratch, counter
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
@@ -1298,11 +1321,10 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
         launch_fmt<false>(a, s);
         return hipGetLastError();
     }
-    // split: score rows + slice histograms, filter, select
+    // split: per-slice candidates + histogram lists, then one select per query
     launch_fmt<true>(a, s);
-    const int nfb = (a.nslices + a.spb - 1) / a.spb;
-    hipLaunchKernelGGL(k_idx_split_filter, dim3((unsigned)nfb, (unsigned)a.Tq, (unsigned)a.B), dim3(FLT_NT), 0, s, a);
-    hipLaunchKernelGGL(k_idx_split_select, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(DSEL_NT), sel_lds(), s, a);
+    hipLaunchKernelGGL(k_idx_split_select, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(DSEL_NT),
+                       sel_lds() + sizeof(int) * MAX_SLICES_PER_ROW, s, a);
     return hipGetLastError();
 }
 

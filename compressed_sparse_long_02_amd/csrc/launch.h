@@ -37,16 +37,16 @@ struct IndexArgs {
     // plan
     int S;          // keys per slice (power of two in [512, 16384])
     int nslices;    // slices per query (<= 1024)
-    int spb;        // split path: slices per filter block
     // rows of the split (nslices > 1) and dense paths, in the workspace
     int64_t sstride;     // row stride (n_cap rounded up to a multiple of 4)
-    uint32_t* scores;    // order-preserving score keys: split [B*Tq][sstride], dense [B][Tc][sstride]
+    uint32_t* scores;    // order-preserving score keys: dense [B][Tc][sstride]; split: [B*Tq][sstride],
+                         // the keys at or above the query's threshold bin when too many for LDS
     uint32_t* hist;      // dense: [B][Tc][2048] histograms of the keys' top 11 bits;
                          // split: [B*Tq][nslices][IDX_SLOT_W] per-slice lists of nonzero bins
-    uint32_t* cand_key;  // split: [B*Tq][sstride], filter block f's kept keys at [f*spb*S, ..)
+    uint32_t* cand_key;  // split: [B*Tq][sstride], slice s's kept keys at [s*S, ..), in entry order
     int32_t* cand_idx;   // split: [B*Tq][sstride], their entry indices
-    int32_t* seg_cnt;    // split: [B*Tq][nslices] keys kept per filter block
-    uint32_t* row_bin;   // split: [B*Tq][4] threshold bin of each row, keys above it, keys in it
+    int32_t* seg_cnt;    // split: [B*Tq][nslices] keys kept per slice
+    int32_t* fb_idx;     // split: [B*Tq][sstride], entry indices of the `scores` keys (when used)
     // dense path (many queries): queries qc0 .. qc0+Tc-1 per pass
     int dense;           // 1: score every (query, key) pair to HBM, then select per query
     int Tc;              // rows per pass

@@ -152,9 +152,9 @@ int kv_compress_step(const void* x_ring, int x_fmt, int x_roles, int64_t x_bstri
  *  or 128), CSL_MXFP4 (d_I 128; scales applied by the scaled FP4 MFMA).
  *  Limits: H_I <= 128, 1 <= k <= 2048, n_cap <= 2^24 (CSL_EUNSUPPORTED beyond).
  *  ws         device workspace of at least csl_index_topk_workspace(...) bytes
- *             (0 for small calls; a little over 12 * B * Tq * n_cap bytes when a query's
- *             entries span several scoring blocks: score rows and filtered
- *             candidates are staged there).
+ *             (0 for small calls; a little over 16 * B * Tq * n_cap bytes when a query's
+ *             entries span several scoring blocks: the blocks' candidates and, for
+ *             queries with many tied keys, their gathered rows are staged there).
  */
 int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
                const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
@@ -188,9 +188,9 @@ int index_topk_paged(const void* qi, int qi_fmt, const uint8_t* qi_scales, const
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments and results as index_topk, without the workspace
  * arguments.  The staging it needs lives in a static device array of the library,
- * csl_noalloc_scratch_bytes() bytes (64 MiB) on every GPU the library runs on, held
+ * csl_noalloc_scratch_bytes() bytes (96 MiB) on every GPU the library runs on, held
  * until the process ends.  A call whose staging would exceed it (the
- * csl_index_topk_workspace figure of the same sizes, e.g. more than about 5.3 million
+ * csl_index_topk_workspace figure of the same sizes, e.g. more than about 6 million
  * (query, entry) pairs per call when entries span several scoring blocks, or a
  * many-query prefill call) returns CSL_EWORKSPACE and launches nothing.  No call
  * allocates or frees memory.  All calls on one GPU share that array: calls that may

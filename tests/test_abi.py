@@ -139,7 +139,7 @@ def test_valid_call_without_gpu_reports_no_device():
 
 def test_noalloc_refuses_oversized_calls_on_the_host():
     L = _lib.lib()
-    assert L.csl_noalloc_scratch_bytes() == 64 << 20
+    assert L.csl_noalloc_scratch_bytes() == 96 << 20
     # 16 queries x 4M entries would stage ~800 MB: refused before any device work
     rc = L.index_topk_noalloc(16, 3, 16, 16, 16, 3, 16, 0, 0, 16, 16, 1, 64, 128, 4, 1 << 22, 1024, 16, None, None)
     assert rc == _lib.CSL_EWORKSPACE
