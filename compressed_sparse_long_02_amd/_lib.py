@@ -15,10 +15,21 @@ LIB_PATH = os.path.join(HERE, "libcsl.so")
 CSL_OK, CSL_EINVAL, CSL_EUNSUPPORTED, CSL_EWORKSPACE, CSL_ELAUNCH, CSL_EDEVICE = 0, -1, -2, -3, -4, -5
 
 # every symbol include/csl.h declares
-EXPORTS = ["csl_row_bytes", "kv_compress", "kv_compress_step", "index_topk", "index_topk_paged",
+EXPORTS = ["csl_row_bytes", "kv_compress", "kv_compress_step", "kv_compress_step_pair", "index_topk", "index_topk_paged",
            "csl_index_topk_workspace", "index_topk_noalloc", "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend",
            "csa_attend_paged", "hca_attend_paged", "csl_attend_workspace", "grouped_out_proj", "csl_status_string",
            "csl_last_error", "csl_version"]
+
+
+class CompressJob(C.Structure):
+    """csl_compress_job: one decode-time compression job (kv_compress_step's arguments)."""
+    _fields_ = [("x_ring", C.c_void_p), ("x_fmt", C.c_int), ("x_roles", C.c_int), ("x_bstride", C.c_int64),
+                ("x_rows", C.c_int64), ("z_ring", C.c_void_p), ("z_ch", C.c_int), ("z_bstride", C.c_int64),
+                ("bias", C.c_void_p), ("d", C.c_int), ("r", C.c_int), ("m", C.c_int), ("overlap", C.c_int),
+                ("out", C.c_void_p), ("out_fmt", C.c_int), ("out_scales", C.c_void_p), ("out_bstride", C.c_int64),
+                ("sc_bstride", C.c_int64), ("n_cap", C.c_int64), ("block_table", C.c_void_p),
+                ("bt_stride", C.c_int64), ("entries_per_block", C.c_int), ("block_bytes", C.c_int64),
+                ("scale_block_bytes", C.c_int64), ("n_blocks", C.c_int64)]
 
 
 class CslError(RuntimeError):
@@ -46,6 +57,8 @@ def lib() -> C.CDLL:
     L.kv_compress_step.restype = i32
     L.kv_compress_step.argtypes = [vp, i32, i32, i64, i64, vp, i32, i64, vp, vp, i32, i32, i32, i32, i32, i32,
                                    vp, i32, vp, i64, i64, i64, vp, i64, i32, i64, i64, i64, vp]
+    L.kv_compress_step_pair.restype = i32
+    L.kv_compress_step_pair.argtypes = [C.POINTER(CompressJob), C.POINTER(CompressJob), vp, i32, i32, vp]
     L.index_topk_paged.restype = i32
     L.index_topk_paged.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp, i64, i32, i64, i64, i64, vp, i32, i32, i32,
                                    i32, i32, i64, i32, vp, vp, vp, sz, vp]

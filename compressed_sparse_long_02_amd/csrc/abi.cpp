@@ -289,49 +289,78 @@ int kv_compress(const void* x, int x_fmt, int x_roles, int64_t x_bstride, int64_
     return launched(csl::launch_compress(a, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+// Validation and argument block of one decode-time compression job.
+static int step_job(const char* fn, const csl_compress_job& j, const int32_t* pos, int B, int T, csl::CompressArgs& a) {
+    if (T < 0) return fail(CSL_EINVAL, "%s: negative T", fn);
+    if (T > 65535) return fail(CSL_EUNSUPPORTED, "%s: T > 65535", fn);
+    int rc = compress_common(fn, j.x_ring, j.x_fmt, j.x_roles, j.x_bstride, j.z_ring, j.z_ch, j.z_bstride, j.bias, B,
+                             j.d, j.r, j.m, j.overlap, j.out, j.out_fmt, j.out_scales, j.block_table ? 0 : j.out_bstride);
+    if (rc) return rc;
+    const int win = j.overlap ? 2 * j.m : j.m;
+    if (j.x_rows < win + T - 1)
+        return fail(CSL_EINVAL, "%s: a ring of %lld rows cannot hold the %d-row window of T = %d new tokens", fn,
+                    (long long)j.x_rows, win, T);
+    Paged pg;
+    if (j.block_table) {
+        pg.bt = j.block_table; pg.bt_stride = j.bt_stride; pg.epb = j.entries_per_block; pg.blk_bytes = j.block_bytes;
+        pg.sblk_bytes = j.scale_block_bytes; pg.n_blocks = j.n_blocks;
+        if ((rc = validate_paged(fn, pg, (int64_t)j.bt_stride * (j.entries_per_block > 0 ? j.entries_per_block : 1),
+                                 row_bytes(j.out_fmt, j.d, j.r))))
+            return rc;
+        if (j.out_fmt == CSL_MXFP4 && j.scale_block_bytes < (int64_t)j.entries_per_block * (j.d / 32))
+            return fail(CSL_EINVAL, "%s: scale_block_bytes cannot hold entries_per_block scale rows", fn);
+    } else if (j.n_cap < 0) {
+        return fail(CSL_EINVAL, "%s: negative n_cap", fn);
+    }
+    if (B * (int64_t)T > 0 && (!pos || !al4(pos))) return fail(CSL_EINVAL, "%s: null or misaligned pos", fn);
+    a = csl::CompressArgs{};
+    a.x = (const uint8_t*)j.x_ring; a.x_fmt = j.x_fmt; a.x_bstride = j.x_bstride; a.x_pos0 = 0; a.n_tok = j.x_rows;
+    a.x_rows = j.x_rows; a.x_roles = j.x_roles;
+    a.z = j.z_ring; a.z_ch = j.z_ch; a.z_bstride = j.z_bstride; a.bias = j.bias;
+    a.B = B; a.d = j.d; a.r = j.r; a.m = j.m; a.overlap = j.overlap ? 1 : 0; a.e_begin = 0; a.n_e = T;
+    a.out = (uint8_t*)j.out; a.out_fmt = j.out_fmt; a.out_scales = j.out_scales; a.out_bstride = j.out_bstride;
+    a.sc_bstride = j.sc_bstride;
+    a.pos = pos; a.n_cap = j.n_cap;
+    if (j.block_table) { a.bt = pg.bt; a.bt_stride = pg.bt_stride; a.epb = pg.epb; a.blk_bytes = pg.blk_bytes;
+                         a.sblk_bytes = pg.sblk_bytes; a.n_blocks = pg.n_blocks; }
+    return CSL_OK;
+}
+
+extern "C" {
+
 int kv_compress_step(const void* x_ring, int x_fmt, int x_roles, int64_t x_bstride, int64_t x_rows,
                      const float* z_ring, int z_ch, int64_t z_bstride, const float* bias,
                      const int32_t* pos, int B, int T, int d, int r, int m, int overlap,
                      void* out, int out_fmt, uint8_t* out_scales, int64_t out_bstride, int64_t sc_bstride,
                      int64_t n_cap, const int32_t* block_table, int64_t bt_stride, int entries_per_block,
                      int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks, void* stream) {
-    const char* fn = "kv_compress_step";
-    if (T < 0) return fail(CSL_EINVAL, "%s: negative T", fn);
-    if (T > 65535) return fail(CSL_EUNSUPPORTED, "%s: T > 65535", fn);
-    int rc = compress_common(fn, x_ring, x_fmt, x_roles, x_bstride, z_ring, z_ch, z_bstride, bias, B, d, r, m,
-                             overlap, out, out_fmt, out_scales, block_table ? 0 : out_bstride);
+    const csl_compress_job j{x_ring, x_fmt, x_roles, x_bstride, x_rows, z_ring, z_ch, z_bstride, bias, d, r, m, overlap,
+                             out, out_fmt, out_scales, out_bstride, sc_bstride, n_cap, block_table, bt_stride,
+                             entries_per_block, block_bytes, scale_block_bytes, n_blocks};
+    csl::CompressArgs a;
+    int rc = step_job("kv_compress_step", j, pos, B, T, a);
     if (rc) return rc;
-    const int win = overlap ? 2 * m : m;
-    if (x_rows < win + T - 1)
-        return fail(CSL_EINVAL, "%s: a ring of %lld rows cannot hold the %d-row window of T = %d new tokens", fn,
-                    (long long)x_rows, win, T);
     if (B * (int64_t)T == 0) { g_err.clear(); return CSL_OK; }
-    if (!pos || !al4(pos)) return fail(CSL_EINVAL, "%s: null or misaligned pos", fn);
-    Paged pg;
-    if (block_table) {
-        pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
-        pg.sblk_bytes = scale_block_bytes; pg.n_blocks = n_blocks;
-        if ((rc = validate_paged(fn, pg, (int64_t)bt_stride * (entries_per_block > 0 ? entries_per_block : 1),
-                                 row_bytes(out_fmt, d, r))))
-            return rc;
-        if (out_fmt == CSL_MXFP4 && scale_block_bytes < (int64_t)entries_per_block * (d / 32))
-            return fail(CSL_EINVAL, "%s: scale_block_bytes cannot hold entries_per_block scale rows", fn);
-    } else if (n_cap < 0) {
-        return fail(CSL_EINVAL, "%s: negative n_cap", fn);
-    }
     rc = check_device();
     if (rc) return rc;
-    csl::CompressArgs a{};
-    a.x = (const uint8_t*)x_ring; a.x_fmt = x_fmt; a.x_bstride = x_bstride; a.x_pos0 = 0; a.n_tok = x_rows;
-    a.x_rows = x_rows; a.x_roles = x_roles;
-    a.z = z_ring; a.z_ch = z_ch; a.z_bstride = z_bstride; a.bias = bias;
-    a.B = B; a.d = d; a.r = r; a.m = m; a.overlap = overlap ? 1 : 0; a.e_begin = 0; a.n_e = T;
-    a.out = (uint8_t*)out; a.out_fmt = out_fmt; a.out_scales = out_scales; a.out_bstride = out_bstride;
-    a.sc_bstride = sc_bstride;
-    a.pos = pos; a.n_cap = n_cap;
-    if (block_table) { a.bt = pg.bt; a.bt_stride = pg.bt_stride; a.epb = pg.epb; a.blk_bytes = pg.blk_bytes;
-                       a.sblk_bytes = pg.sblk_bytes; a.n_blocks = pg.n_blocks; }
     return launched(csl::launch_compress(a, (hipStream_t)stream));
+}
+
+int kv_compress_step_pair(const csl_compress_job* first, const csl_compress_job* second, const int32_t* pos, int B,
+                          int T, void* stream) {
+    const char* fn = "kv_compress_step_pair";
+    if (!first || !second) return fail(CSL_EINVAL, "%s: null job", fn);
+    csl::CompressArgs a0, a1;
+    int rc = step_job(fn, *first, pos, B, T, a0);
+    if (rc) return rc;
+    rc = step_job(fn, *second, pos, B, T, a1);
+    if (rc) return rc;
+    if (B * (int64_t)T == 0) { g_err.clear(); return CSL_OK; }
+    rc = check_device();
+    if (rc) return rc;
+    return launched(csl::launch_compress_pair(a0, a1, (hipStream_t)stream));
 }
 
 // Many queries per call (prefill): the dense path scores every (query, key) pair into

@@ -74,16 +74,18 @@ __device__ __forceinline__ void load8(const uint8_t* row, int c0, float* v) {
     }
 }
 
+// One block's share of a compression: channel part zi of gz (the grid's z index and
+// extent for a single job; a fused launch of two jobs splits its z range between them).
 template <int XF, int OF, bool ZC1, int CMP_NT>
-__global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
+__device__ __forceinline__ void compress_body(const CompressArgs& a, int zi, int gz) {
     const int win = a.overlap ? 2 * a.m : a.m;
-    const int dt = a.d / (int)gridDim.z;                // channels of this block
+    const int dt = a.d / gz;                            // channels of this block
     const CmpGeom G = cmp_geom(dt, win, CMP_NT);
     const int per_entry = G.TPR * G.RG;
     const int ep = threadIdx.x / per_entry;
     const int rg = (threadIdx.x / G.TPR) % G.RG;
     const int tr = threadIdx.x % G.TPR;
-    const int c0 = (int)blockIdx.z * dt + tr * 8;
+    const int c0 = zi * dt + tr * 8;
     const int b = blockIdx.y;
     const int64_t q = (int64_t)blockIdx.x * G.EPB + ep;
     bool active = ep < G.EPB && q < a.n_e;
@@ -311,6 +313,19 @@ __global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
     }
 }
 
+template <int XF, int OF, bool ZC1, int CMP_NT>
+__global__ void __launch_bounds__(CMP_NT) k_compress(CompressArgs a) {
+    compress_body<XF, OF, ZC1, CMP_NT>(a, (int)blockIdx.z, (int)gridDim.z);
+}
+
+// Two compressions of the same new tokens in one launch (a CSA layer's KV entry and its
+// indexer key): z indices [0, gz0) run the first job, [gz0, gz0 + gz1) the second.
+template <int OF0, int OF1>
+__global__ void __launch_bounds__(256) k_compress_pair(CompressArgs a0, CompressArgs a1, int gz0, int gz1) {
+    if ((int)blockIdx.z < gz0) compress_body<BF16, OF0, true, 256>(a0, (int)blockIdx.z, gz0);
+    else compress_body<BF16, OF1, true, 256>(a1, (int)blockIdx.z - gz0, gz1);
+}
+
 // channel splits: halve the block's channels (keeping whole 32-channel groups)
 // while the launch has fewer than 256 entry blocks
 static int cmp_splits(const CompressArgs& a) {
@@ -350,6 +365,30 @@ static hipError_t launch_c1(const CompressArgs& a, hipStream_t s) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     if (a.n_e <= 0 || a.B <= 0) return hipSuccess;
     return a.x_fmt == F32 ? launch_c1<F32>(a, s) : launch_c1<BF16>(a, s);
+}
+
+// Both jobs in one launch when they take the fused kernel's shape (bf16 raw rows, one
+// logit per token, 256-thread blocks, a packed KV entry plus an MXFP4 or bf16 key);
+// otherwise one launch after the other.
+hipError_t launch_compress_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t s) {
+    if (a0.B <= 0 || a0.n_e <= 0) return hipSuccess;
+    const int gz0 = cmp_splits(a0), gz1 = cmp_splits(a1);
+    const int w0 = a0.overlap ? 2 * a0.m : a0.m, w1 = a1.overlap ? 2 * a1.m : a1.m;
+    const bool shape = a0.B == a1.B && a0.n_e == a1.n_e && a0.x_fmt == BF16 && a1.x_fmt == BF16 && a0.z_ch == 1 &&
+                       a1.z_ch == 1 && cmp_threads(a0.d / gz0, w0) == 256 && cmp_threads(a1.d / gz1, w1) == 256 &&
+                       a0.out_fmt == KV_PACKED && (a1.out_fmt == MXFP4 || a1.out_fmt == BF16);
+    if (!shape) {
+        hipError_t e = launch_compress(a0, s);
+        return e != hipSuccess ? e : launch_compress(a1, s);
+    }
+    const CmpGeom G0 = cmp_geom(a0.d / gz0, w0, 256), G1 = cmp_geom(a1.d / gz1, w1, 256);
+    const int64_t x0 = (a0.n_e + G0.EPB - 1) / G0.EPB, x1 = (a1.n_e + G1.EPB - 1) / G1.EPB;
+    const dim3 grid((unsigned)(x0 > x1 ? x0 : x1), (unsigned)a0.B, (unsigned)(gz0 + gz1));
+    if (a1.out_fmt == MXFP4)
+        hipLaunchKernelGGL((k_compress_pair<KV_PACKED, MXFP4>), grid, dim3(256), 0, s, a0, a1, gz0, gz1);
+    else
+        hipLaunchKernelGGL((k_compress_pair<KV_PACKED, BF16>), grid, dim3(256), 0, s, a0, a1, gz0, gz1);
+    return hipGetLastError();
 }
 
 }  // namespace csl

@@ -82,6 +82,7 @@ struct GprojArgs {
 };
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+hipError_t launch_compress_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t s);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_grouped_out_proj(const GprojArgs& a, hipStream_t s);

@@ -11,6 +11,8 @@ Layouts (B = batch, rows dense inside a sequence):
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
 from . import _lib
@@ -104,6 +106,34 @@ def kv_compress(x, x_fmt, z, bias, *, d, m, overlap, e_begin, n_e, r=0, x_pos0=0
     return out, out_scales
 
 
+def _step_job(x_ring, x_fmt, z_ring, bias, *, d, m, overlap, out, out_fmt, r=0, out_scales=None, x_roles=1,
+              pages=None):
+    """One decode-time compression job as the C struct csl_compress_job."""
+    _need_cuda(x_ring, z_ring, bias, out, out_scales)
+    _rows_ok(x_ring, row_bytes(x_fmt, x_roles * d), "x_ring")
+    sc = _ptr(out_scales) if out_fmt == MXFP4 else None
+    if pages is None:
+        _rows_ok(out, row_bytes(out_fmt, d, r), "out")
+        ob, sb = _bstride(out), (_bstride(out_scales) if out_fmt == MXFP4 else 0)
+        tail = dict(n_cap=out.shape[1])
+    else:
+        bt, epb, blk, sblk, nblk = pages
+        _check_table(bt)
+        ob, sb = 0, 0
+        tail = dict(block_table=_ptr(bt), bt_stride=bt.shape[1], entries_per_block=epb, block_bytes=blk,
+                    scale_block_bytes=sblk, n_blocks=nblk)
+    return _lib.CompressJob(x_ring=_ptr(x_ring), x_fmt=x_fmt, x_roles=x_roles, x_bstride=_bstride(x_ring),
+                            x_rows=x_ring.shape[1], z_ring=_ptr(z_ring), z_ch=z_ring.shape[-1],
+                            z_bstride=_bstride(z_ring), bias=_ptr(bias), d=d, r=r, m=m, overlap=int(bool(overlap)),
+                            out=_ptr(out), out_fmt=out_fmt, out_scales=sc, out_bstride=ob, sc_bstride=sb, **tail)
+
+
+def _check_pos(pos, B):
+    _need_cuda(pos)
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or pos.dim() != 2 or pos.shape[0] != B:
+        raise ValueError("pos must be contiguous int32 [B, T]")
+
+
 def kv_compress_step(x_ring, x_fmt, z_ring, bias, pos, *, d, m, overlap, out, out_fmt, r=0, out_scales=None,
                      x_roles=1, pages=None):
     """Decode-time compression from the state rings: x_ring [B, x_rows, .], z_ring float32
@@ -112,27 +142,28 @@ def kv_compress_step(x_ring, x_fmt, z_ring, bias, pos, *, d, m, overlap, out, ou
     pages = (block_table int32 [B, max_blocks], entries_per_block, block_bytes,
     scale_block_bytes, n_blocks), a pool of blocks (out / out_scales point at the first
     block's rows)."""
-    _need_cuda(x_ring, z_ring, bias, pos, out, out_scales)
-    B, x_rows = x_ring.shape[0], x_ring.shape[1]
-    if pos.dtype != torch.int32 or not pos.is_contiguous():
-        raise ValueError("pos must be contiguous int32 [B, T]")
-    _rows_ok(x_ring, row_bytes(x_fmt, x_roles * d), "x_ring")
-    T = pos.shape[1]
-    sc = _ptr(out_scales) if out_fmt == MXFP4 else None
-    if pages is None:
-        _rows_ok(out, row_bytes(out_fmt, d, r), "out")
-        tail = (out.shape[1], None, 0, 0, 0, 0, 0)
-        ob, sb = _bstride(out), (_bstride(out_scales) if out_fmt == MXFP4 else 0)
-    else:
-        bt, epb, blk, sblk, nblk = pages
-        _check_table(bt)
-        tail = (0, _ptr(bt), bt.shape[1], epb, blk, sblk, nblk)
-        ob, sb = 0, 0
-    rc = _lib.lib().kv_compress_step(_ptr(x_ring), x_fmt, x_roles, _bstride(x_ring), x_rows, _ptr(z_ring),
-                                     z_ring.shape[-1], _bstride(z_ring), _ptr(bias), _ptr(pos), B, T, d, r, m,
-                                     int(bool(overlap)), _ptr(out), out_fmt, sc, ob, sb, *tail, _stream())
+    j = _step_job(x_ring, x_fmt, z_ring, bias, d=d, m=m, overlap=overlap, out=out, out_fmt=out_fmt, r=r,
+                  out_scales=out_scales, x_roles=x_roles, pages=pages)
+    B = x_ring.shape[0]
+    _check_pos(pos, B)
+    rc = _lib.lib().kv_compress_step(j.x_ring, j.x_fmt, j.x_roles, j.x_bstride, j.x_rows, j.z_ring, j.z_ch,
+                                     j.z_bstride, j.bias, _ptr(pos), B, pos.shape[1], d, r, m, j.overlap, j.out,
+                                     j.out_fmt, j.out_scales, j.out_bstride, j.sc_bstride, j.n_cap, j.block_table,
+                                     j.bt_stride, j.entries_per_block, j.block_bytes, j.scale_block_bytes,
+                                     j.n_blocks, _stream())
     check("kv_compress_step", rc)
     return out, out_scales
+
+
+def kv_compress_step_pair(first, second, pos):
+    """Two kv_compress_step jobs over the same new tokens in one launch (a CSA layer's KV
+    entry and its indexer key).  `first` and `second` are dicts of kv_compress_step's
+    keyword arguments plus x_ring, x_fmt, z_ring and bias."""
+    j0, j1 = _step_job(**first), _step_job(**second)
+    B = first["x_ring"].shape[0]
+    _check_pos(pos, B)
+    rc = _lib.lib().kv_compress_step_pair(C.byref(j0), C.byref(j1), _ptr(pos), B, pos.shape[1], _stream())
+    check("kv_compress_step_pair", rc)
 
 
 def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None, out_idx=None,

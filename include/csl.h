@@ -135,6 +135,28 @@ int kv_compress_step(const void* x_ring, int x_fmt, int x_roles, int64_t x_bstri
                      int64_t block_bytes, int64_t scale_block_bytes, int64_t n_blocks, void* stream);
 
 /*
+ * kv_compress_step_pair -- two kv_compress_step jobs over the same new tokens (pos, B,
+ * T) in one launch: a CSA layer's KV entry and its indexer key, both pooled from their
+ * rings when a token completes a block.  Each job's fields mean what kv_compress_step's
+ * arguments of the same names mean, and each job is validated as that call would
+ * validate it; on any error nothing is launched.  Results are identical to two
+ * kv_compress_step calls (jobs whose shapes the fused kernel does not take -- other
+ * than bf16 raw rows, one logit per token, a packed KV entry then an MXFP4 or bf16
+ * key -- are run as two launches).
+ */
+typedef struct {
+    const void* x_ring; int x_fmt; int x_roles; int64_t x_bstride; int64_t x_rows;
+    const float* z_ring; int z_ch; int64_t z_bstride; const float* bias;
+    int d; int r; int m; int overlap;
+    void* out; int out_fmt; uint8_t* out_scales; int64_t out_bstride; int64_t sc_bstride; int64_t n_cap;
+    const int32_t* block_table; int64_t bt_stride; int entries_per_block;
+    int64_t block_bytes; int64_t scale_block_bytes; int64_t n_blocks;
+} csl_compress_job;
+
+int kv_compress_step_pair(const csl_compress_job* first, const csl_compress_job* second, const int32_t* pos, int B,
+                          int T, void* stream);
+
+/*
  * index_topk -- lightning indexer + top-k selection ([X] section 2, CSA step 2;
  * FP4 indexer QK: [X] mixed-precision paragraph and section 4).
  * For query j of sequence b at position t = q_pos[b*Tq + j]:

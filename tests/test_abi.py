@@ -164,6 +164,30 @@ def test_compress_step_rejects_bad_arguments_on_the_host():
     assert call(T=0) == _lib.CSL_OK
 
 
+def test_compress_step_pair_rejects_bad_jobs_on_the_host():
+    L = _lib.lib()
+
+    def job(**over):
+        a = dict(x_ring=16, x_fmt=1, x_roles=1, x_bstride=0, x_rows=16, z_ring=16, z_ch=1, z_bstride=0, bias=16,
+                 d=512, r=64, m=4, overlap=1, out=16, out_fmt=2, out_scales=None, n_cap=100)
+        a.update(over)
+        return _lib.CompressJob(**a)
+
+    def call(j0, j1, pos=16, B=2, T=1):
+        return L.kv_compress_step_pair(C.byref(j0), C.byref(j1), pos, B, T, None)
+
+    key = dict(d=128, r=0, out_fmt=3, out_scales=16)
+    assert call(job(), job(**key), T=0) == _lib.CSL_OK
+    assert call(job(), job(x_rows=7, **key)) == _lib.CSL_EINVAL           # the second job's ring is too short
+    assert "kv_compress_step_pair" in _lib.last_error() and "ring" in _lib.last_error()
+    assert call(job(out=None), job(**key)) == _lib.CSL_EINVAL             # the first job has no output
+    assert call(job(), job(**key), pos=None) == _lib.CSL_EINVAL
+    assert call(job(), job(**dict(key, out_scales=None))) == _lib.CSL_EINVAL   # MXFP4 needs its scales
+    assert call(job(), job(block_table=16, bt_stride=4, entries_per_block=32, block_bytes=100, n_blocks=10,
+                           **key)) == _lib.CSL_EINVAL                      # block too small for 32 keys
+    assert L.kv_compress_step_pair(None, C.byref(job()), 16, 2, 1, None) == _lib.CSL_EINVAL
+
+
 def test_grouped_out_proj_rejects_bad_arguments_on_the_host():
     L = _lib.lib()
 

@@ -190,3 +190,81 @@ def test_compress_step_from_the_ring(gpu, roles, out_fmt, m, overlap, paged):
         for e in range(n_cap):
             if (b, e) not in touched:
                 assert np.all(got[b, e] == fill), (b, e)
+
+
+def _pair_jobs(B, R, roles, key_fmt, m0, seed, paged, n_cap0):
+    """A CSA-layer pair: the packed KV entry (d = 512, r = 64, window m0 / overlap when
+    m0 = 4) and the indexer key (d = 128, m = 4, overlap) in `key_fmt`, their rings, and
+    their caches filled with 0xA5 -- linear, or one pool of shuffled blocks of 128 raw
+    tokens holding both (KV rows, then key rows, then key scales)."""
+    fill = 0xA5
+    ov0 = m0 == 4
+    xr0 = gen.store(gen.normal((B, R, roles * 512), seed), O.BF16)
+    zr0 = gen.random_logits((B, R, 1), seed + 1)
+    b0 = gen.random_logits((2 * m0 if ov0 else m0, 1), seed + 2)
+    xr1 = gen.store(gen.normal((B, R, 128), seed + 3), O.BF16)
+    zr1 = gen.random_logits((B, R, 1), seed + 4)
+    b1 = gen.random_logits((8, 1), seed + 5)
+    rb0, rb1 = O.row_bytes(O.KV_PACKED, 512, 64), O.row_bytes(key_fmt, 128, 0)
+    j0 = dict(x_ring=dev(xr0), x_fmt=O.BF16, z_ring=dev(zr0), bias=dev(b0), d=512, r=64, m=m0, overlap=ov0,
+              out_fmt=O.KV_PACKED, x_roles=roles)
+    j1 = dict(x_ring=dev(xr1), x_fmt=O.BF16, z_ring=dev(zr1), bias=dev(b1), d=128, m=4, overlap=True,
+              out_fmt=key_fmt)
+    if not paged:
+        n_cap1 = n_cap0 * m0 // 4                 # both cover the same raw tokens
+        j0["out"] = dev(torch.full((B, n_cap0, rb0), fill, dtype=torch.uint8))
+        j1["out"] = dev(torch.full((B, n_cap1, rb1), fill, dtype=torch.uint8))
+        if key_fmt == O.MXFP4:
+            j1["out_scales"] = dev(torch.full((B, n_cap1, 4), fill, dtype=torch.uint8))
+        return j0, j1, None
+    epb0, epb1 = 128 // m0, 32
+    nblk = max(n_cap0 // epb0, 1)
+    o1 = epb0 * rb0
+    o2 = o1 + epb1 * rb1
+    blk = o2 + epb1 * 4
+    g = torch.Generator().manual_seed(seed)
+    bt = dev(torch.randperm(B * nblk + 3, generator=g)[:B * nblk].to(torch.int32).reshape(B, nblk))
+    pool = dev(torch.full((B * nblk + 3, blk), fill, dtype=torch.uint8))
+    j0.update(out=pool, pages=(bt, epb0, blk, blk, B * nblk + 3))
+    j1.update(out=pool[:, o1:], pages=(bt, epb1, blk, blk, B * nblk + 3))
+    if key_fmt == O.MXFP4:
+        j1["out_scales"] = pool[:, o2:]
+    return j0, j1, (pool, o1)
+
+
+def _pair_state(j0, j1, pool):
+    if pool is not None:                       # the block's KV rows, then its keys and scales
+        p, o1 = pool
+        h = host(p)
+        return [h[:, :o1], h[:, o1:]]
+    return [host(j0["out"]), host(j1["out"])] + ([host(j1["out_scales"])] if "out_scales" in j1 else [])
+
+
+@pytest.mark.parametrize("roles,key_fmt,m0", [(1, O.MXFP4, 4), (2, O.MXFP4, 4), (1, O.BF16, 4),
+                                              (1, O.MXFP4, 128)])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("B,T", [(8, 1), (3, 2)])
+def test_compress_step_pair_equals_two_steps(gpu, roles, key_fmt, m0, paged, B, T):
+    """kv_compress_step_pair (one launch for a CSA layer's KV entry and indexer key; the
+    m = 128 first job takes the two-launch route) leaves the caches byte-identical to two
+    kv_compress_step calls, and writes the entries the new tokens complete."""
+    R, n_cap0 = 256, (8192 // m0)
+    rng = np.random.default_rng(B * 10 + T)
+    base = rng.integers(0, 8192 - T, size=B)
+    base[0] = 8 * m0 - T                            # completes an entry of both jobs
+    pos = dev(torch.tensor(base[:, None] + np.arange(T)[None, :], dtype=torch.int32))
+    s0 = 40 + 7 * roles + m0
+    j0, j1, pool = _pair_jobs(B, R, roles, key_fmt, m0, s0, paged, n_cap0)
+    before = [a.copy() for a in _pair_state(j0, j1, pool)]
+    ops.kv_compress_step(pos=pos, **j0)
+    ops.kv_compress_step(pos=pos, **j1)
+    torch.cuda.synchronize()
+    want = _pair_state(j0, j1, pool)
+    k0, k1, pool2 = _pair_jobs(B, R, roles, key_fmt, m0, s0, paged, n_cap0)
+    ops.kv_compress_step_pair(k0, k1, pos)
+    torch.cuda.synchronize()
+    got = _pair_state(k0, k1, pool2)
+    # both jobs wrote something (a KV entry and a key)
+    assert (want[0] != before[0]).any() and (want[1] != before[1]).any()
+    for w, g_ in zip(want, got):
+        assert np.array_equal(w, g_)
