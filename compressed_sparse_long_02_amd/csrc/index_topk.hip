@@ -1043,20 +1043,20 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
     select_row(a, bq, n, srow, smem, [](uint32_t*, int*) { return -1; });
 }
 
-// Split path, step 2: one block per query; wave w owns slices w, w + 16, ...  At the
-// start every wave issues the loads of its first slice's list and of up to SEL_PF
-// candidates of its segment, all at once (one memory round trip).  The lists are added
-// into an LDS histogram, which gives the query's threshold bin (the one holding its
-// k-th largest key) and the exact count of keys in it and above.  Every such key is in
-// some slice's candidate segment (a slice kept all keys at or above its own threshold
-// bin, which is at most the query's).  Usual case: each wave compacts its segment's
-// keys at or above the bin (the prefetched part, then the rest) into its own LDS region, the regions are joined in wave
-// order (= entry order), and a radix select over their offsets from the bin's lower
-// edge, the keys above the bin clamped to its upper edge (22 bits, two passes, no
-// min / max phase), gives the exact top k.  Otherwise (a region overflows: ties,
-// clustered scores, or more slices than waves) the keys at or above the bin are
-// gathered, in entry order, into the workspace row and the general row select refines
-// the threshold over them.  n(t) <= k: the segments hold every key, all are taken.
+// Split path, step 2: one block per query.  At the start every wave issues the loads of
+// one slice's histogram list and of up to SEL_PF candidates of the first of its slices,
+// all at once (one memory round trip).  The lists are added into an LDS histogram, which
+// gives the query's threshold bin (the one holding its k-th largest key) and the exact
+// count of keys in it and above.  Every such key is in some slice's candidate segment (a
+// slice kept all keys at or above its own threshold bin, which is at most the query's).
+// Usual case: wave w compacts the keys at or above the bin of its contiguous run of
+// slices (the prefetched part, then the rest) into its own LDS region, the regions are
+// joined in wave order (= entry order), and a radix select over their offsets from the
+// bin's lower edge, the keys above the bin clamped to its upper edge (22 bits, two
+// passes, no min / max phase), gives the exact top k.  Otherwise (a region overflows:
+// ties or clustered scores) the keys at or above the bin are gathered, in entry order,
+// into the workspace row and the general row select refines the threshold over them.
+// n(t) <= k: the segments hold every key, all are taken.
 constexpr int SEL_PF = 1024;                         // candidates a wave prefetches (16 rounds of 64)
 
 __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
@@ -1070,22 +1070,28 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     const uint32_t* slots = a.hist + bq * (int64_t)a.nslices * SLOT_W;
     const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
     const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
-    // ---- prefetch: this wave's first slice: list head, its first 64 list entries, its count
-    // and its first SEL_PF candidates (indices only where a key is present)
-    const bool mine = wv < nseg && n > a.k;
+    // Wave w compacts the contiguous slices [w q, w q + q) (q = ceil(nseg / 16)), so that
+    // its region, and the regions joined in wave order, keep entry order.
+    const int q = (nseg + NW - 1) / NW;
+    const int s_lo = wv * q, s_hi = s_lo + q < nseg ? s_lo + q : nseg;
+    // ---- prefetch: slice wv's list head and first 64 list entries (for the histogram),
+    // and the count and first SEL_PF candidates of slice s_lo (indices only where a key is
+    // present)
+    const bool lmine = wv < nseg && n > a.k;
+    const bool mine = s_lo < nseg && n > a.k;
     uint32_t lc = 0, le = 0, pk[NR];
     int32_t pi[NR];
     int cnt = 0;
-    if (mine) {
+    if (lmine) {
         const uint32_t* li = slots + (int64_t)wv * SLOT_W;
         lc = li[0];
         le = li[1 + lane];                               // read within the slot (lists hold <= 2048 entries)
-        cnt = a.seg_cnt[bq * a.nslices + wv];
     }
+    if (mine) cnt = a.seg_cnt[bq * a.nslices + s_lo];
     {
-        const uint32_t* kk = ckr + (int64_t)wv * a.S;
-        const int32_t* ii = cir + (int64_t)wv * a.S;
-        const int64_t nsw = mine ? (n - (int64_t)wv * a.S < a.S ? n - (int64_t)wv * a.S : a.S) : 0;   // the slice's keys
+        const uint32_t* kk = ckr + (int64_t)s_lo * a.S;
+        const int32_t* ii = cir + (int64_t)s_lo * a.S;
+        const int64_t nsw = mine ? (n - (int64_t)s_lo * a.S < a.S ? n - (int64_t)s_lo * a.S : a.S) : 0;   // the slice's keys
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int e = 64 * r + lane;
@@ -1108,7 +1114,7 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     // ---- the query's histogram from the slices' lists
     for (int x = tid; x < TOPK_HSZ; x += DSEL_NT) sh[x] = 0u;
     __syncthreads();
-    if (mine && (uint32_t)lane < lc) atomicAdd(&sh[hpad(le >> 21)], le & 0x1fffffu);
+    if (lmine && (uint32_t)lane < lc) atomicAdd(&sh[hpad(le >> 21)], le & 0x1fffffu);
     for (int sl = wv; sl < nseg; sl += NW) {             // the rest of the lists (long ones, further slices)
         const uint32_t* li = slots + (int64_t)sl * SLOT_W;
         const uint32_t c = sl == wv ? lc : li[0];
@@ -1124,9 +1130,9 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     const uint32_t bin = misc[0], above = misc[1], inbin = misc[2];
     const uint32_t lo = bin << (32 - TOPK_BITS);
     const uint32_t nsurv = above + inbin;
-    // ---- usual case: per-wave compaction of the prefetched segment into its LDS region
+    // ---- usual case: per-wave compaction of its slices' segments into its LDS region
     int got = 0;
-    bool ovf = nseg > NW || nsurv > (uint32_t)DSEL_CAP;
+    bool ovf = nsurv > (uint32_t)DSEL_CAP;
     if (!ovf && mine) {
         uint32_t* rk = sk + wv * WCAP;
         int* ri = si + wv * WCAP;
@@ -1138,23 +1144,27 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
             }
             got += __builtin_popcountll(m);
         };
+        // segment entries [e_from, c) of slice sl, four rounds of 64 at a time
+        auto stream = [&](int sl, int e_from, int c) {
+            const uint32_t* kk = ckr + (int64_t)sl * a.S;
+            const int32_t* ii = cir + (int64_t)sl * a.S;
+            for (int e0 = e_from; e0 < c; e0 += 256) {
+                uint32_t kr[4];
+                int32_t ir[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = e0 + 64 * u + lane;
+                    kr[u] = e < c ? kk[e] : 0u;
+                    ir[u] = e < c ? ii[e] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) put(e0 + 64 * u + lane < c && kr[u] >= lo, kr[u], ir[u]);
+            }
+        };
 #pragma unroll
         for (int r = 0; r < NR; ++r) put(64 * r + lane < cnt && pk[r] >= lo, pk[r], pi[r]);
-        // the rest of the segment (beyond the prefetched part), four rounds at a time
-        const uint32_t* kk = ckr + (int64_t)wv * a.S;
-        const int32_t* ii = cir + (int64_t)wv * a.S;
-        for (int e0 = SEL_PF; e0 < cnt; e0 += 256) {
-            uint32_t kr[4];
-            int32_t ir[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + 64 * u + lane;
-                kr[u] = e < cnt ? kk[e] : 0u;
-                ir[u] = e < cnt ? ii[e] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) put(e0 + 64 * u + lane < cnt && kr[u] >= lo, kr[u], ir[u]);
-        }
+        stream(s_lo, SEL_PF, cnt);                       // the rest of the first segment
+        for (int sl = s_lo + 1; sl < s_hi; ++sl) stream(sl, 0, a.seg_cnt[bq * a.nslices + sl]);
     }
     if (lane == 0) wsum[wv] = got;
     ovf = __syncthreads_or((ovf || got > WCAP) ? 1 : 0);
