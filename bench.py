@@ -286,7 +286,7 @@ class Stack:
         return 2 * self.index_bytes() + 2 * self.csa_bytes() + 2 * self.hca_bytes() + self.compress_bytes()
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "index_topk_hbm_counters_stack_1M_b16.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_stack_1M_b16.txt")
 INDEX_SOURCES = ["compressed_sparse_long_02_amd/csrc/index_topk.hip", "compressed_sparse_long_02_amd/csrc/device.h",
                  "compressed_sparse_long_02_amd/csrc/launch.h"]
 
