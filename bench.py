@@ -49,243 +49,6 @@ def parse():
     return p.parse_args()
 
 
-class Stack:
-    """Device-resident caches and inputs of the 4-layer decode step.
-
-    Per layer, the two tiers of the cache: a state ring per sequence (the last RING raw
-    rows -- bf16, with their compression logits -- and the window rows, packed) and the
-    compressed cache.  layout "linear": one dense array of entries per sequence; layout
-    "paged": blocks of BLOCK_TOKENS = lcm(4, 128) = 128 raw tokens behind one block
-    table shared by all layers (a CSA block holds 32 packed entries, their 32 MXFP4
-    indexer keys and the keys' scales; an HCA block 1 entry), the physical blocks in a
-    seeded random order."""
-
-    RING = 128
-    BLOCK_TOKENS = 128
-
-    def __init__(self, B, ctx, device, layout="linear"):
-        import torch
-        from compressed_sparse_long_02_amd import gen, ops
-        F = ops
-        self.B, self.ctx, self.dev, self.layout = B, ctx, device, layout
-        self.t = ctx - 1
-        self.H, self.d, self.r, self.W = 64, 512, 64, 128
-        self.m, self.mh = 4, 128
-        self.HI, self.dI, self.k = 64, 128, 1024
-        self.N = ctx // self.m
-        self.Nh = ctx // self.mh
-        self.ring = 256
-        self.scale = 1.0 / math.sqrt(self.d)
-        B, d, r = self.B, self.d, self.r
-        rb = F.row_bytes(F.KV_PACKED, d, r)
-        self.rb = rb
-        # paged layout: one block table for every layer, physical blocks shuffled
-        self.nblk = ctx // self.BLOCK_TOKENS
-        self.epb_csa = self.BLOCK_TOKENS // self.m
-        self.epb_hca = self.BLOCK_TOKENS // self.mh
-        self.csa_key_off = self.epb_csa * rb                       # bytes of a CSA block: entries, keys, scales
-        self.csa_sc_off = self.csa_key_off + self.epb_csa * self.dI // 2
-        self.csa_blk = self.csa_sc_off + self.epb_csa * self.dI // 32
-        self.csa_blk = (self.csa_blk + 15) // 16 * 16
-        self.hca_blk = self.epb_hca * rb
-        self.n_phys = B * self.nblk
-        if layout == "paged":
-            g = torch.Generator(device="cpu")
-            g.manual_seed(77)
-            self.bt = torch.randperm(self.n_phys, generator=g).to(torch.int32).reshape(B, self.nblk).to(device)
-        self.layers = []
-        seed = 1000
-        for li, kind in enumerate(["csa", "hca", "csa", "hca"]):
-            L = {"kind": kind}
-            seed += 100
-            n = self.N if kind == "csa" else self.Nh
-            # compressed KV cache: packed rows of N(0,1) values with outlier channels
-            cache = torch.empty((B, n, rb), dtype=torch.uint8, device=device)
-            chunk = 16384
-            for s0 in range(0, n, chunk):
-                c = min(chunk, n - s0)
-                x = gen.with_outliers(gen.normal((B, c, d), seed + s0, device=device), seed)
-                cache[:, s0:s0 + c] = gen.pack_kv(x, r)
-            L["cache"] = cache
-            # the state ring: window rows (packed) and the raw rows + logits of the last RING
-            # positions (row p % RING), from which the completed entries are compressed
-            xw = gen.with_outliers(gen.normal((B, self.ring, d), seed + 1, device=device), seed)
-            L["ring"] = gen.pack_kv(xw, r)
-            mm = self.m if kind == "csa" else self.mh
-            L["win"] = 2 * mm if kind == "csa" else mm
-            xr = gen.with_outliers(gen.normal((B, self.RING, d), seed + 2, device=device), seed)
-            L["raw"] = gen.bf16_bytes(xr)
-            L["z"] = gen.random_logits((B, self.RING, 1), seed + 3, device=device)
-            L["bias"] = gen.random_logits((L["win"], 1), seed + 4, device=device)
-            L["q"] = gen.with_outliers(gen.normal((B, 1, self.H, d), seed + 5, device=device), seed).to(torch.bfloat16)
-            L["out"] = torch.empty((B, 1, self.H, d), dtype=torch.bfloat16, device=device)
-            if kind == "csa":
-                # MXFP4 indexer keys, quantised through kv_compress with m = 1 (identity pooling)
-                keys = torch.empty((B, n, self.dI // 2), dtype=torch.uint8, device=device)
-                ksc = torch.empty((B, n, self.dI // 32), dtype=torch.uint8, device=device)
-                z1 = torch.zeros((B, chunk, 1), device=device)
-                b1 = torch.zeros((1, 1), device=device)
-                for s0 in range(0, n, chunk):
-                    c = min(chunk, n - s0)
-                    x = gen.with_outliers(gen.normal((B, c, self.dI), seed + 7 + s0, device=device), seed + 1)
-                    F.kv_compress(gen.bf16_bytes(x), F.BF16, z1[:, :c], b1, d=self.dI, m=1, overlap=False, e_begin=0,
-                                  n_e=c, out_fmt=F.MXFP4, out=keys[:, s0:s0 + c], out_scales=ksc[:, s0:s0 + c])
-                L["keys"], L["kscales"] = keys, ksc
-                xi = gen.with_outliers(gen.normal((B, self.RING, self.dI), seed + 8, device=device), seed + 1)
-                L["raw_i"] = gen.bf16_bytes(xi)
-                L["z_i"] = gen.random_logits((B, self.RING, 1), seed + 9, device=device)
-                L["bias_i"] = gen.random_logits((L["win"], 1), seed + 10, device=device)
-                qi = gen.with_outliers(gen.normal((B * self.HI, 1, self.dI), seed + 11, device=device), seed + 1)
-                qic, qis = F.kv_compress(gen.bf16_bytes(qi), F.BF16, torch.zeros((B * self.HI, 1, 1), device=device),
-                                         b1, d=self.dI, m=1, overlap=False, e_begin=0, n_e=1, out_fmt=F.MXFP4)
-                L["qi"] = qic.reshape(B, 1, self.HI, self.dI // 2).contiguous()
-                L["qis"] = qis.reshape(B, 1, self.HI, self.dI // 32).contiguous()
-                L["w"] = gen.normal((B, 1, self.HI), seed + 12, 1 / math.sqrt(self.HI), device=device)
-                L["idx"] = torch.empty((B, 1, self.k), dtype=torch.int32, device=device)
-            if layout == "paged":
-                self._to_pool(L)
-            self.layers.append(L)
-        self.q_pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
-        torch.cuda.synchronize()
-
-    def _to_pool(self, L):
-        """Move a layer's linear cache into its block pool (physical block bt[b, j] holds the
-        entries of raw tokens 128 j .. 128 j + 127 of sequence b); the linear arrays are
-        dropped, and `cache` / `keys` / `kscales` become views of the pool's blocks."""
-        import torch
-        B, rb = self.B, self.rb
-        bt = self.bt.long()
-        if L["kind"] == "csa":
-            epb, blk = self.epb_csa, self.csa_blk
-            pool = torch.zeros((self.n_phys, blk), dtype=torch.uint8, device=self.dev)
-            for b in range(B):
-                ids = bt[b]
-                pool[ids, :self.csa_key_off] = L["cache"][b].reshape(self.nblk, epb * rb)
-                pool[ids, self.csa_key_off:self.csa_sc_off] = L["keys"][b].reshape(self.nblk, -1)
-                pool[ids, self.csa_sc_off:self.csa_sc_off + epb * self.dI // 32] = L["kscales"][b].reshape(self.nblk, -1)
-            del L["keys"], L["kscales"]
-            L["pool"] = pool
-        else:
-            epb, blk = self.epb_hca, self.hca_blk
-            pool = torch.zeros((self.n_phys, blk), dtype=torch.uint8, device=self.dev)
-            for b in range(B):
-                pool[bt[b]] = L["cache"][b].reshape(self.nblk, epb * rb)
-            L["pool"] = pool
-        del L["cache"]
-        torch.cuda.synchronize()
-
-    # -- views of the compressed cache ----------------------------------------------
-    def entries(self, L):
-        """Linear [B, n, row] entries of a layer (gathered through the block table when
-        paged: a host-side copy for the oracle, not part of the step)."""
-        import torch
-        if self.layout != "paged":
-            return L["cache"]
-        epb = self.epb_csa if L["kind"] == "csa" else self.epb_hca
-        bt = self.bt.long()
-        rows = L["pool"][:, :epb * self.rb]
-        return torch.stack([rows[bt[b]].reshape(-1, self.rb) for b in range(self.B)])
-
-    def index_keys(self, L):
-        """Linear MXFP4 keys and scales of a CSA layer ([B, N, 64], [B, N, 4])."""
-        import torch
-        if self.layout != "paged":
-            return L["keys"], L["kscales"]
-        bt = self.bt.long()
-        p = L["pool"]
-        k = torch.stack([p[bt[b], self.csa_key_off:self.csa_sc_off].reshape(-1, self.dI // 2) for b in range(self.B)])
-        s = torch.stack([p[bt[b], self.csa_sc_off:self.csa_sc_off + self.epb_csa * self.dI // 32]
-                         .reshape(-1, self.dI // 32) for b in range(self.B)])
-        return k, s
-
-    # -- the ABI calls of one layer ------------------------------------------------
-    def compress(self, L):
-        """The entries completed by the new token, pooled from the state ring into the cache."""
-        from compressed_sparse_long_02_amd import ops as F
-        paged = self.layout == "paged"
-        if L["kind"] == "csa":
-            # the KV entry and the indexer key of the same new tokens, one launch
-            kv = dict(x_ring=L["raw"], x_fmt=F.BF16, z_ring=L["z"], bias=L["bias"], d=self.d, r=self.r, m=self.m,
-                      overlap=True, out_fmt=F.KV_PACKED)
-            key = dict(x_ring=L["raw_i"], x_fmt=F.BF16, z_ring=L["z_i"], bias=L["bias_i"], d=self.dI, m=self.m,
-                       overlap=True, out_fmt=F.MXFP4)
-            if paged:
-                pg = (self.bt, self.epb_csa, self.csa_blk, self.csa_blk, self.n_phys)
-                p = L["pool"]
-                kv.update(out=p, pages=pg)
-                key.update(out=p[:, self.csa_key_off:], out_scales=p[:, self.csa_sc_off:], pages=pg)
-            else:
-                kv.update(out=L["cache"])
-                key.update(out=L["keys"], out_scales=L["kscales"])
-            F.kv_compress_step_pair(kv, key, self.q_pos)
-        else:
-            kw = dict(m=self.mh, overlap=False, d=self.d, r=self.r, out_fmt=F.KV_PACKED)
-            if paged:
-                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, out=L["pool"],
-                                   pages=(self.bt, self.epb_hca, self.hca_blk, self.hca_blk, self.n_phys), **kw)
-            else:
-                F.kv_compress_step(L["raw"], F.BF16, L["z"], L["bias"], self.q_pos, out=L["cache"], **kw)
-
-    def index(self, L, with_scores=False, out_idx=None):
-        from compressed_sparse_long_02_amd import ops as F
-        kw = dict(fmt=F.MXFP4, H_I=self.HI, d_I=self.dI, m=self.m, n_cap=self.N, k=self.k, qi_scales=L["qis"],
-                  out_idx=L["idx"] if out_idx is None else out_idx, with_scores=with_scores)
-        if self.layout == "paged":
-            p = L["pool"]
-            return F.index_topk(L["qi"], L["w"], p[:, self.csa_key_off:], self.q_pos, ki_scales=p[:, self.csa_sc_off:],
-                                pages=(self.bt, self.epb_csa, self.csa_blk, self.csa_blk, self.n_phys), **kw)
-        return F.index_topk(L["qi"], L["w"], L["keys"], self.q_pos, ki_scales=L["kscales"], **kw)
-
-    def attend(self, L, out=None, out_fmt=None, with_lse=False):
-        from compressed_sparse_long_02_amd import ops as F
-        kw = dict(kv_fmt=F.KV_PACKED, kvw_pos0=0, kvw_rows=self.ring, W=self.W, H=self.H, d=self.d, r=self.r,
-                  scale=self.scale, out_fmt=F.BF16 if out_fmt is None else out_fmt,
-                  out=L["out"] if out is None and out_fmt is None else out, with_lse=with_lse)
-        if self.layout == "paged":
-            if L["kind"] == "csa":
-                return F.csa_attend_paged(L["q"], L["pool"], self.bt, L["idx"], L["ring"], self.q_pos,
-                                          entries_per_block=self.epb_csa, block_bytes=self.csa_blk,
-                                          n_blocks=self.n_phys, n_cap=self.N, **kw)
-            return F.hca_attend_paged(L["q"], L["pool"], self.bt, L["ring"], self.q_pos,
-                                      entries_per_block=self.epb_hca, block_bytes=self.hca_blk, n_blocks=self.n_phys,
-                                      n_cap=self.Nh, m=self.mh, **kw)
-        if L["kind"] == "csa":
-            return F.csa_attend(L["q"], L["cache"], L["idx"], L["ring"], self.q_pos, n_cap=self.N, **kw)
-        return F.hca_attend(L["q"], L["cache"], L["ring"], self.q_pos, n_cap=self.Nh, m=self.mh, **kw)
-
-    def step(self):
-        for L in self.layers:
-            self.compress(L)
-            if L["kind"] == "csa":
-                self.index(L)
-            self.attend(L)
-
-    # -- algorithmic bytes -----------------------------------------------------
-    def index_bytes(self):
-        B = self.B
-        keys = B * self.N * (self.dI // 2 + self.dI // 32)
-        q = B * self.HI * (self.dI // 2 + self.dI // 32 + 4)
-        out = B * self.k * 4
-        return keys + q + out
-
-    def csa_bytes(self):
-        B, rb = self.B, 2 * self.r + (self.d - self.r)
-        return B * ((self.k + self.W) * rb + self.k * 4 + self.H * self.d * 2 * 2)
-
-    def hca_bytes(self):
-        B, rb = self.B, 2 * self.r + (self.d - self.r)
-        return B * ((self.Nh + self.W) * rb + self.H * self.d * 2 * 2)
-
-    def compress_bytes(self):
-        B = self.B
-        csa = B * (2 * self.m * (self.d * 2 + 4) + 576 + 2 * self.m * (self.dI * 2 + 4) + 68)
-        hca = B * (self.mh * (self.d * 2 + 4) + 576)
-        return 2 * csa + 2 * hca
-
-    def step_bytes(self):
-        return 2 * self.index_bytes() + 2 * self.csa_bytes() + 2 * self.hca_bytes() + self.compress_bytes()
-
-
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_stack_1M_b16.txt")
 INDEX_SOURCES = ["compressed_sparse_long_02_amd/csrc/index_topk.hip", "compressed_sparse_long_02_amd/csrc/device.h",
                  "compressed_sparse_long_02_amd/csrc/launch.h"]
@@ -308,75 +71,6 @@ def recorded_traffic(B, ctx):
     if fields.get("source_sha256_16") != h.hexdigest()[:16] or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
-
-
-class Prefill:
-    """One CSA layer appending a chunk of 8,192 tokens to 1,048,576 cached ones: compress the
-    chunk's 2,048 entries (KV and bf16 indexer keys, with the 4 look-back rows), index the
-    8,192 queries against the 264,192 entries (64 heads x 128, bf16, top-1024, causal) and
-    attend with 128 heads of 512 over the selected entries plus a 128-token window."""
-
-    def __init__(self, device):
-        import torch
-        from compressed_sparse_long_02_amd import gen
-        self.H, self.d, self.r, self.m, self.HI, self.dI, self.k, self.W, self.C = 128, 512, 64, 4, 64, 128, 1024, 128, 8192
-        self.T0 = 1 << 20
-        self.N0 = self.T0 // self.m
-        self.N = (self.T0 + self.C) // self.m
-        d, r, dI, m, C, W = self.d, self.r, self.dI, self.m, self.C, self.W
-        self.cache = torch.empty((1, self.N, d + r), dtype=torch.uint8, device=device)
-        self.keys = torch.empty((1, self.N, dI * 2), dtype=torch.uint8, device=device)
-        for s0 in range(0, self.N0, 32768):
-            c = min(32768, self.N0 - s0)
-            self.cache[:, s0:s0 + c] = gen.pack_kv(gen.normal((1, c, d), 5000 + s0, device=device), r)
-            self.keys[:, s0:s0 + c] = gen.bf16_bytes(gen.normal((1, c, dI), 6000 + s0, device=device))
-        self.x = gen.bf16_bytes(gen.normal((1, C + m, d), 7001, device=device))
-        self.xi = gen.bf16_bytes(gen.normal((1, C + m, dI), 7002, device=device))
-        self.z = gen.random_logits((1, C + m, 1), 7003, device=device)
-        self.zi = gen.random_logits((1, C + m, 1), 7004, device=device)
-        self.bias = gen.random_logits((2 * m, 1), 7005, device=device)
-        self.bias_i = gen.random_logits((2 * m, 1), 7006, device=device)
-        self.kvw = gen.pack_kv(gen.normal((1, W + C, d), 7007, device=device), r)
-        self.q_pos = torch.arange(self.T0, self.T0 + C, dtype=torch.int32, device=device).view(1, C)
-        self.qi = gen.bf16_bytes(gen.normal((1, C, self.HI, dI), 7008, device=device))
-        self.w = gen.normal((1, C, self.HI), 7009, 1 / math.sqrt(self.HI), device=device)
-        self.q = gen.normal((1, C, self.H, d), 7010, device=device).to(torch.bfloat16)
-        self.idx = torch.empty((1, C, self.k), dtype=torch.int32, device=device)
-        self.out = torch.empty((1, C, self.H, d), dtype=torch.bfloat16, device=device)
-        torch.cuda.synchronize()
-
-    def compress(self):
-        from compressed_sparse_long_02_amd import ops as F
-        ne = self.C // self.m
-        kw = dict(m=self.m, overlap=True, e_begin=self.N0, n_e=ne, x_pos0=self.T0 - self.m)
-        F.kv_compress(self.x, F.BF16, self.z, self.bias, d=self.d, r=self.r, out_fmt=F.KV_PACKED,
-                      out=self.cache[:, self.N0:self.N], **kw)
-        F.kv_compress(self.xi, F.BF16, self.zi, self.bias_i, d=self.dI, out_fmt=F.BF16,
-                      out=self.keys[:, self.N0:self.N], **kw)
-
-    def index(self):
-        from compressed_sparse_long_02_amd import ops as F
-        F.index_topk(self.qi, self.w, self.keys, self.q_pos, fmt=F.BF16, H_I=self.HI, d_I=self.dI, m=self.m,
-                     n_cap=self.N, k=self.k, out_idx=self.idx, with_scores=False)
-
-    def attend(self):
-        from compressed_sparse_long_02_amd import ops as F
-        F.csa_attend(self.q, self.cache, self.idx, self.kvw, self.q_pos, kv_fmt=F.KV_PACKED, n_cap=self.N,
-                     kvw_pos0=self.T0 - self.W, kvw_rows=self.W + self.C, W=self.W, H=self.H, d=self.d, r=self.r,
-                     scale=1 / math.sqrt(self.d), out_fmt=F.BF16, out=self.out, with_lse=False)
-
-    def step(self):
-        self.compress()
-        self.index()
-        self.attend()
-
-    def index_flops(self):
-        """2 * H_I * d_I per visible (query, entry) pair."""
-        pairs = sum(min((self.T0 + j + 1) // self.m, self.N) for j in range(self.C))
-        return 2 * self.HI * self.dI * pairs
-
-    def attend_flops(self):
-        return 4 * self.C * self.H * (self.k + self.W) * self.d
 
 
 def prefill_cpu_baseline(pf, nq):
@@ -403,6 +97,7 @@ def main_prefill(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] building the prefill-chunk inputs", file=sys.stderr, flush=True)
+    from compressed_sparse_long_02_amd.workloads import Prefill
     pf = Prefill(dev)
     pf.step()
     torch.cuda.synchronize()
@@ -437,109 +132,6 @@ def main_prefill(args):
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
-
-
-class Layer:
-    """One decode layer on its own, with its inputs in `copies` independent sets so that the
-    timed steps cycle through more data than the 256 MB last-level cache holds.
-      csa_decode: batch 8, context 131,072 (t = 131,071), 32,768 packed entries per sequence,
-                  bf16 indexer keys (16 heads x 128, top-512), 64 heads x 512, window 128.
-      hca_decode: batch 4, context 1,048,576, m' = 128: 8,192 packed entries per sequence,
-                  64 heads x 512, window 128.
-    A step: compress the entry the new token completes (from the 128-row state ring), then
-    index + csa_attend, or hca_attend."""
-
-    RING = 128
-
-    def __init__(self, kind, device, copies):
-        import torch
-        from compressed_sparse_long_02_amd import gen, ops as F
-        self.kind, self.dev = kind, device
-        self.H, self.d, self.r, self.W = 64, 512, 64, 128
-        if kind == "csa_decode":
-            self.B, self.ctx, self.m, self.HI, self.dI, self.k = 8, 1 << 17, 4, 16, 128, 512
-        else:
-            self.B, self.ctx, self.m = 4, 1 << 20, 128
-        self.t = self.ctx - 1
-        self.N = self.ctx // self.m
-        self.win = 2 * self.m if kind == "csa_decode" else self.m
-        self.scale = 1.0 / math.sqrt(self.d)
-        B, d, r = self.B, self.d, self.r
-        self.rb = F.row_bytes(F.KV_PACKED, d, r)
-        self.q_pos = torch.full((B, 1), self.t, dtype=torch.int32, device=device)
-        self.sets = []
-        for c in range(copies):
-            seed = 9000 + 100 * c
-            S = {}
-            S["cache"] = torch.empty((B, self.N, self.rb), dtype=torch.uint8, device=device)
-            for s0 in range(0, self.N, 16384):
-                n = min(16384, self.N - s0)
-                S["cache"][:, s0:s0 + n] = gen.pack_kv(gen.normal((B, n, d), seed + s0, device=device), r)
-            S["ring"] = gen.pack_kv(gen.normal((B, 256, d), seed + 1, device=device), r)
-            S["raw"] = gen.bf16_bytes(gen.normal((B, self.RING, d), seed + 2, device=device))
-            S["z"] = gen.random_logits((B, self.RING, 1), seed + 3, device=device)
-            S["bias"] = gen.random_logits((self.win, 1), seed + 4, device=device)
-            S["q"] = gen.normal((B, 1, self.H, d), seed + 5, device=device).to(torch.bfloat16)
-            S["out"] = torch.empty((B, 1, self.H, d), dtype=torch.bfloat16, device=device)
-            if kind == "csa_decode":
-                S["keys"] = gen.bf16_bytes(gen.normal((B, self.N, self.dI), seed + 6, device=device))
-                S["raw_i"] = gen.bf16_bytes(gen.normal((B, self.RING, self.dI), seed + 7, device=device))
-                S["z_i"] = gen.random_logits((B, self.RING, 1), seed + 8, device=device)
-                S["bias_i"] = gen.random_logits((self.win, 1), seed + 9, device=device)
-                S["qi"] = gen.bf16_bytes(gen.normal((B, 1, self.HI, self.dI), seed + 10, device=device))
-                S["w"] = gen.normal((B, 1, self.HI), seed + 11, device=device)
-                S["idx"] = torch.empty((B, 1, self.k), dtype=torch.int32, device=device)
-            self.sets.append(S)
-        torch.cuda.synchronize()
-
-    def compress(self, S):
-        from compressed_sparse_long_02_amd import ops as F
-        ov = self.kind == "csa_decode"
-        kv = dict(x_ring=S["raw"], x_fmt=F.BF16, z_ring=S["z"], bias=S["bias"], d=self.d, r=self.r, m=self.m,
-                  overlap=ov, out=S["cache"], out_fmt=F.KV_PACKED)
-        if ov:   # the KV entry and the indexer key, one launch
-            F.kv_compress_step_pair(kv, dict(x_ring=S["raw_i"], x_fmt=F.BF16, z_ring=S["z_i"], bias=S["bias_i"],
-                                             d=self.dI, m=self.m, overlap=True, out=S["keys"], out_fmt=F.BF16),
-                                    self.q_pos)
-        else:
-            F.kv_compress_step(pos=self.q_pos, **kv)
-
-    def index(self, S, with_scores=False):
-        from compressed_sparse_long_02_amd import ops as F
-        return F.index_topk(S["qi"], S["w"], S["keys"], self.q_pos, fmt=F.BF16, H_I=self.HI, d_I=self.dI, m=self.m,
-                            n_cap=self.N, k=self.k, out_idx=S["idx"], with_scores=with_scores)
-
-    def attend(self, S, out_fmt=None, with_lse=False):
-        from compressed_sparse_long_02_amd import ops as F
-        kw = dict(kv_fmt=F.KV_PACKED, kvw_pos0=0, kvw_rows=256, W=self.W, H=self.H, d=self.d, r=self.r,
-                  scale=self.scale, out_fmt=F.BF16 if out_fmt is None else out_fmt,
-                  out=S["out"] if out_fmt is None else None, with_lse=with_lse)
-        if self.kind == "csa_decode":
-            return F.csa_attend(S["q"], S["cache"], S["idx"], S["ring"], self.q_pos, n_cap=self.N, **kw)
-        return F.hca_attend(S["q"], S["cache"], S["ring"], self.q_pos, n_cap=self.N, m=self.m, **kw)
-
-    def step(self, S):
-        self.compress(S)
-        if self.kind == "csa_decode":
-            self.index(S)
-        self.attend(S)
-
-    def index_bytes(self):
-        B = self.B
-        return B * self.N * self.dI * 2 + B * self.HI * (self.dI * 2 + 4) + B * self.k * 4
-
-    def attend_bytes(self):
-        rows = (self.k if self.kind == "csa_decode" else self.N) + self.W
-        idx = self.k * 4 if self.kind == "csa_decode" else 0
-        return self.B * (rows * self.rb + idx + self.H * self.d * 2 * 2)
-
-    def compress_bytes(self):
-        kv = self.win * (self.d * 2 + 4) + self.rb
-        ik = self.win * (self.dI * 2 + 4) + self.dI * 2 if self.kind == "csa_decode" else 0
-        return self.B * (kv + ik)
-
-    def step_bytes(self):
-        return (self.index_bytes() if self.kind == "csa_decode" else 0) + self.attend_bytes() + self.compress_bytes()
 
 
 def layer_cpu_baseline(ly, min_s=10.0):
@@ -584,6 +176,7 @@ def main_layer(args):
     torch.cuda.set_device(dev)
     copies = 3 if args.workload == "csa_decode" else 28
     print("[bench] building %s inputs (%d copies)" % (args.workload, copies), file=sys.stderr, flush=True)
+    from compressed_sparse_long_02_amd.workloads import Layer
     ly = Layer(args.workload, dev, copies)
     for S in ly.sets:
         ly.step(S)
@@ -752,6 +345,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] building inputs (B=%d, ctx=%d)" % (args.batch, args.ctx), file=sys.stderr, flush=True)
+    from compressed_sparse_long_02_amd.workloads import Stack
     st = Stack(args.batch, args.ctx, dev, layout=args.layout)
     st.step()                       # eager warm-up: allocates workspaces before capture
     torch.cuda.synchronize()

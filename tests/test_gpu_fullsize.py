@@ -19,21 +19,17 @@ scores tie with the k-th within max(1e-6 relative, twice the kernel's measured s
 error on that query), at most one query in 64 (plus one) with a swap; quantised entries
 equal except for a few elements one rounding step apart."""
 import math
-import os
-import sys
 
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from compressed_sparse_long_02_amd import gen, ops
+from compressed_sparse_long_02_amd import gen, ops, workloads
 from tests import bruteforce as BF
 from tests.gpu_util import cap, check_topk, close_quantised, dev, host, max_abs, oracle_all_scores, score_error_bound
 
 pytestmark = pytest.mark.gpu
-
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _check_index(gi, gs, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None):
@@ -52,12 +48,11 @@ def _check_index(gi, gs, qi, qfmt, w, ki, kfmt, qpos, *, H_I, d_I, m, n_cap, k, 
 
 
 # ---------------------------------------------------------------------------
-# the 4-layer decode stack, exactly as the benchmark builds and launches it
+# the 4-layer decode stack, exactly as the benchmark builds and launches it (the package's
+# workloads, stepped through decode.py)
 # ---------------------------------------------------------------------------
 def _make_stack(layout):
-    sys.path.insert(0, ROOT)
-    import bench
-    st = bench.Stack(16, 1 << 20, torch.device("cuda:0"), layout=layout)
+    st = workloads.Stack(16, 1 << 20, torch.device("cuda:0"), layout=layout)
     st.step()
     torch.cuda.synchronize()
     return st
