@@ -647,22 +647,23 @@ __global__ void __launch_bounds__(MQ_NT, 2) k_attend_mq(AttendArgs a) {
 // lane by global_load_lds), so LDS carries 576 instead of 1024 bytes per row and
 // reader; MFMA operands are widened in registers (fp8 -> bf16, the hardware OCP
 // conversion, exact).
-//   The waves form two teams of four; team t takes the tiles u = t (mod 2), each over
-//   two steps, and the teams are one step apart, so on every SIMD one wave's softmax
-//   and conversions run beside the other wave's MFMAs; one barrier per step.
-//   Step u (scores): wave w of the team takes the 16 heads 16w .. 16w+15 over all dims:
-//   S^T = K.Q^T with 16x16x32 bf16 MFMA (A = K rows, B = Q, both from LDS), its own
-//   softmax, and the probabilities P^T (a bf16 hi + lo pair) to LDS.  The two 16-row
-//   MFMA blocks take rows 8(x/4) + x%4 (+4), so each lane's eight scores are rows
-//   8g .. 8g+7 of the tile: the k slots of its P^T fragment in the P.V product.
-//   Step u+1 (values): wave w takes a quarter of the head dims (D/4 from D*w/4) for all
-//   64 heads: O^T += V^T.P^T, one 8-bit LDS transpose read per 16 dims (two 16-bit
-//   ones for the RoPE dims), so every fp8 value of V is widened by one wave only.
+//   The waves form two teams of four; wave w of a team owns the 16 heads 16 (w%4) ..
+//   +15 across all dims (O^T, fp32, in registers) and computes its own scores and
+//   softmax, so no wave waits for another within a tile.  Team t takes the tiles
+//   u = t (mod 2), each over two steps: in step u the S^T = K.Q^T, the probabilities
+//   and the first blocks of O^T += V^T.P^T; in step u+1 the other blocks.  The teams
+//   are one step apart, so on every SIMD one wave's softmax and conversions run beside
+//   the other wave's MFMAs; one barrier per step.
+//   S^T: 16x16x32 bf16, A = K rows from LDS, B = Q from LDS.  The two 16-row MFMA blocks
+//   take rows 8(x/4) + x%4 (+4), so each lane's eight scores are rows 8g .. 8g+7 of the
+//   tile: exactly the k slots of its P^T operand in the 16x16x32 P.V, so P never leaves
+//   registers.  V^T: one 8-bit LDS transpose read per 16 dims (fp8), two 16-bit ones
+//   for the RoPE dims.
 // ---------------------------------------------------------------------------
 constexpr int F8_R = 64;           // RoPE dims this kernel takes (the pages' packed layout)
 constexpr int F8_T = 32;           // rows of a tile
 constexpr int F8_NST = 4;          // LDS stages: two tiles being computed, two in flight
-constexpr int F8_RCH = 4;          // tiles whose row pointers one resolve pass covers
+constexpr int F8_RCH = 8;          // tiles whose row pointers one resolve pass covers
 constexpr int F8_TNT = MQ_NT / 2;  // threads of a team
 
 // a stored row of 576 (d 512) or 320 (d 256) bytes, zero: the copy source of absent rows
@@ -691,14 +692,13 @@ struct F8Lds {
     static constexpr int QP = QSTR / 8;                      // 16-byte slots per Q row (two pads)
     static constexpr int QSEG = QP;                          // 1 KB copies of Q (64 rows x QP slots)
     static constexpr int NQ = (QSEG + MQ_NT / 64 - 1) / (MQ_NT / 64);   // Q copies per wave
-    static constexpr int NDW = D / 64;                       // 16-dim output blocks of a values wave
     static constexpr int TOTAL = QBYTES + F8_NST * STAGE;    // Q, stages (reused by the team merge)
-    static constexpr int MERGE = 4 * NDW * 4 * 64 * 16;      // team 1's O^T, then the softmax states
+    static constexpr int MERGE = 4 * (D / 16) * 64 * 16;     // team 1's O^T, then its softmax states
     static_assert(P % 2 == 1, "row stride must be an odd number of 16-byte slots");
-    static_assert(STAGE % 16 == 0 && NSEG >= 2, "stage layout");
-    static_assert(MERGE + 2 * 2 * 64 * 4 <= TOTAL, "merge space");
+    static_assert(NSEG >= 2, "stage layout");
+    static_assert(MERGE + 4 * 2 * 64 * 4 <= TOTAL, "merge space");
     static_assert(F8_RCH >= 3, "a chunk's table is rewritten only after its last tile is done");
-    static_assert(D % 128 == 0 && D / 4 >= F8_R, "S^T reads its 32-dim steps in groups; RoPE dims in wave 0");
+    static_assert(D % 128 == 0, "S^T reads its 32-dim steps in groups of four");
 };
 
 __device__ __forceinline__ int f8_row_off(int row, int rs) { return row * rs + 64 * (row >> 4); }
@@ -747,7 +747,8 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     using L = F8Lds<D>;
     constexpr int P = L::P, RS = L::RS, NI = L::NI, NST = F8_NST, RCH = F8_RCH, T = F8_T, R = F8_R;
     constexpr int QK = D / 32;                          // k-steps of S^T (32 dims)
-    constexpr int NDW = L::NDW;
+    constexpr int NDB = D / 16;                         // 16-dim output blocks
+    constexpr int NA = NDB / 16;                        // output blocks of a tile's first step
     constexpr int RK = R / 32, RV = R / 16;             // k-steps / output blocks over the RoPE dims
     constexpr int RB = L::RB;
     // s_waitcnt vmcnt(n), the other counters untouched (vmcnt in bits 3:0 and 15:14)
@@ -755,9 +756,9 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     constexpr int WAIT_NEXT = 0x0F70 | NI;              // the copies of the next step's tile have landed
     constexpr int WAIT_ALL = 0x0F70;
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::TOTAL];   // Q [head][dim] bf16, then stages
-    __shared__ __attribute__((aligned(16))) u32x4 p_s[2][4][2][64];  // P^T per team, head group, hi/lo, lane
     __shared__ const uint8_t* rowptr[2][RCH * T];                    // tile chunk c in table c & 1
     __shared__ uint32_t rowmask[2][RCH];
+    __shared__ int sidx[ATT_MAX_SIDX];
     const uint16_t* const q_s = (const uint16_t*)lds;
     uint8_t* const stages = lds + L::QBYTES;
 
@@ -768,7 +769,32 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     const int sp = (int)(lblk % gridDim.x), hb = (int)((lblk / gridDim.x) % gridDim.y);
     const int64_t bq = lblk / (gridDim.x * gridDim.y);
     const int b = (int)(bq / a.Tq);
-    const int wv_u = threadIdx.x >> 6;                  // wave
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
+    const int hg = wv & 3, team = wv >> 2, tt = tid & (F8_TNT - 1);
+    // Q of the block's 64 heads -> LDS by copies (slot k: piece k % QP of head k / QP; the
+    // pads and heads past H read the zero row; copies past the last segment repeat it);
+    // they complete with the first tile's rows
+    {
+        const int64_t q0 = (bq * a.H + (int64_t)hb * 64) * D * 2;
+#pragma unroll
+        for (int i = 0; i < L::NQ; ++i) {
+            int seg = wv + (MQ_NT / 64) * i;
+            seg = seg < L::QSEG ? seg : L::QSEG - 1;
+            const int kq = 64 * seg + lane;
+            const int hh = kq / L::QP, pc = kq - hh * L::QP;
+            const bool data = pc < D / 8 && hb * 64 + hh < a.H;
+            const uint8_t* src = data ? a.q + q0 + ((int64_t)hh * D + 8 * pc) * 2 : f8_zero_row;
+            copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(lds + 1024 * seg)));
+        }
+    }
+    // the split's slice of the index list (CSA), staged once: the row resolution then
+    // makes no global loads inside the tile loop (these loads complete after the Q
+    // copies, issued first, so the wait for them overlaps the Q latency)
+    if (a.idx) {
+        const int64_t vb = (int64_t)sp * a.rps;
+        const int64_t e_end = vb + a.rps < a.k ? vb + a.rps : (int64_t)a.k;
+        for (int64_t v = vb + tid; v < e_end; v += MQ_NT) sidx[v - vb] = a.idx[bq * a.k + v];
+    }
     const int64_t t = a.q_pos[bq];
     const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
     const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
@@ -779,331 +805,272 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     if (v_end > L_all) v_end = L_all;
     const int ntiles = v_end > v_begin ? (int)((v_end - v_begin + T - 1) / T) : 0;
 
-    // The split runs once, or twice when a logit outran the reference (below).  Every
-    // per-lane quantity is derived inside the pass from an opaque thread index, so that
-    // none of it is hoisted out of the pass and held across the tile loop in registers.
-    float m_seen = -INFINITY;                           // largest logit of the lane's rows (scores role)
-#pragma nounroll
+    // Row pointers and validity masks of the RCH tiles of chunk c -> table c & 1, one
+    // row per thread of the calling team; an absent row reads the zero row.
+    auto resolve_chunk = [&](int c) {
+        for (int rr = tt; rr < RCH * T; rr += F8_TNT) {
+            const uint8_t* p = nullptr;
+            {
+                const int64_t v = v_begin + (int64_t)(c * RCH) * T + rr;
+                if (v < v_end) {
+                    if (v < n_ent) {
+                        const int64_t s = a.idx ? (int64_t)sidx[v - v_begin] : v;
+                        if (s >= 0 && s < a.n_cap) p = att_entry_row(a, b, s, RB);
+                    } else {
+                        const int64_t pos = w0 + (v - n_ent);
+                        int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
+                        if (slot < 0) slot += a.kvw_rows;
+                        p = a.kvw + (int64_t)b * a.kvw_bstride + slot * RB;
+                    }
+                }
+                rowptr[c & 1][rr] = p ? p : f8_zero_row;
+            }
+            const uint64_t m = __ballot(p != nullptr);       // lanes 0..31: one tile, 32..63: the next
+            if ((rr & (T - 1)) == 0) rowmask[c & 1][rr / T] = (uint32_t)(m >> (lane & 32));
+        }
+    };
+    // Copy i of this wave for tile v -> stage v % NST: the 1 KB segment wv + 8 i (the
+    // last segment ends at the stage's end; copies past it repeat it); the lane's
+    // 16-byte slot k holds piece k % P of row k / P (rows 0..15), then four gap slots,
+    // then rows 16..31 the same way; pads, gaps and absent rows read the zero row.
+    // Every wave issues the same number of copies for every tile (the vmcnt waits count
+    // them), past the split's rows too.
+    auto issue_one = [&](int v, int i) {
+        const uint8_t* const* rp = rowptr[(v / RCH) & 1] + (v % RCH) * T;
+        uint8_t* st = stages + (v % NST) * L::STAGE;
+        const int seg = wv + (MQ_NT / 64) * i;
+        const int k0 = seg < L::NSEG - 1 ? 64 * seg : L::SLOTS - 64;
+        const int k = k0 + lane;
+        const int k2 = k < 16 * P ? k : k - 4;              // slot index with the gap removed
+        const int row = k2 / P, pc = k2 - row * P;
+        const bool data = (k < 16 * P || k >= 16 * P + 4) && pc < P - 1;
+        const uint8_t* src = data ? rp[row] + 16 * pc : f8_zero_row;
+        copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(st + 16 * k0)));
+    };
+    auto issue_copies = [&](int v) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) issue_one(v, i);
+    };
+
+    // Softmax with a fixed reference per head and team: m_ref = ATT_REF_LIFT above the
+    // largest logit (base 2) of the team's first tile that has a valid row; every
+    // probability is exp2(x - m_ref) and is never rescaled, so the O^T accumulators stay
+    // in place.  fp32 / bf16 hold x - m_ref <= ATT_HEADROOM with room to spare; if a
+    // later logit goes beyond, the block recomputes its split once with m_ref = the
+    // largest logit each wave saw.
+    v4f o[NDB];                                         // O^T: dims 16 db + 4g + i, heads 16 hg + col
+    float m_ref, l_lane, m_seen = -INFINITY;
+    const float sl2 = a.scale * CSL_LOG2E;
+    bool ovf = false;
+    u32x4 pb, pl;                                       // P^T of the wave's current tile, hi + lo
+
+    // per-lane LDS offsets within a stage
+    const int kofs0 = f8_row_off(8 * (col >> 2) + (col & 3), RS);       // S^T block 0: rows 8(x/4) + x%4
+    const int kofs1 = f8_row_off(8 * (col >> 2) + 4 + (col & 3), RS);   // block 1: the same + 4
+    const int v8ofs = f8_row_off(8 * g + (col >> 1), RS) + R + 8 * (col & 1);
+    const int v16ofs0 = f8_row_off(8 * g + (col >> 2), RS) + 8 * (col & 3);
+    const int v16ofs1 = f8_row_off(8 * g + 4 + (col >> 2), RS) + 8 * (col & 3);
+    const uint16_t* const qp = q_s + (16 * hg + col) * L::QSTR + 8 * g;
+
+    auto pv = [&](const uint8_t* st, int db) {
+        u32x4 va;
+        if (db < RV) {
+            const u32x2 t0 = lds_read_tr16((const uint16_t*)(st + v16ofs0 + 32 * db));
+            const u32x2 t1 = lds_read_tr16((const uint16_t*)(st + v16ofs1 + 32 * db));
+            va = u32x4{t0[0], t0[1], t1[0], t1[1]};
+        } else {
+            va = f8_widen(lds_read_tr8(st + v8ofs + 16 * db));   // fp8 dim d at byte R + d
+        }
+        o[db] = mfma_bf16(va, pb, o[db]);
+        o[db] = mfma_bf16(va, pl, o[db]);
+    };
+    // first step of tile u (stage u % NST): S^T, probabilities, output blocks 0..NA-1;
+    // the wave's copies of tile cv are spread over the work (a burst of copies from every
+    // wave at once stalls on the memory pipeline)
+    auto step_a = [&](int u, int cv) {
+        const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[(u / RCH) & 1][u % RCH]);   // block-uniform
+        const bool full = rmask == 0xffffffffu;         // wave-uniform
+        const uint8_t* st = stages + (u % NST) * L::STAGE;
+        v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        // groups of SG k-steps: every fragment of a group is read before the group's
+        // conversions and products, so the LDS latency is paid once per group
+        constexpr int SG = 4;
+#pragma unroll
+        for (int k0s = 0; k0s < QK; k0s += SG) {
+            if (k0s / SG < NI) issue_one(cv, k0s / SG);
+            u32x4 qf[SG], kb0[SG], kb1[SG];
+            u32x2 kr0[SG], kr1[SG];
+#pragma unroll
+            for (int j = 0; j < SG; ++j) {
+                const int ks = k0s + j;
+                qf[j] = *(const u32x4*)(qp + 32 * ks);
+                if (ks < RK) {                          // two 8-byte reads: the row stride suits b64
+                    const u32x2 x0 = *(const u32x2*)(st + kofs0 + 2 * (32 * ks + 8 * g));
+                    const u32x2 x1 = *(const u32x2*)(st + kofs0 + 2 * (32 * ks + 8 * g) + 8);
+                    const u32x2 y0 = *(const u32x2*)(st + kofs1 + 2 * (32 * ks + 8 * g));
+                    const u32x2 y1 = *(const u32x2*)(st + kofs1 + 2 * (32 * ks + 8 * g) + 8);
+                    kb0[j] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                    kb1[j] = u32x4{y0[0], y0[1], y1[0], y1[1]};
+                } else {                                // fp8 dim d at byte R + d
+                    kr0[j] = *(const u32x2*)(st + kofs0 + R + 32 * ks + 8 * g);
+                    kr1[j] = *(const u32x2*)(st + kofs1 + R + 32 * ks + 8 * g);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < SG; ++j) {
+                const int ks = k0s + j;
+                const u32x4 k0 = ks < RK ? kb0[j] : f8_widen(kr0[j]);
+                const u32x4 k1 = ks < RK ? kb1[j] : f8_widen(kr1[j]);
+                s0 = mfma_bf16(k0, qf[j], s0);
+                s1 = mfma_bf16(k1, qf[j], s1);
+            }
+        }
+#pragma unroll
+        for (int i = QK / SG; i < NI; ++i) issue_one(cv, i);
+        // ---- probabilities (lane: head col, rows 8g + j), as a bf16 pair hi + lo:
+        //      P = hi + lo to ~2^-17 relative, so P.V keeps fp32-level accuracy even
+        //      where V has large channels
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = s0[i] * sl2;
+            x[4 + i] = s1[i] * sl2;
+        }
+        if (!full) {
+            const uint32_t mine = rmask >> (8 * g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (!((mine >> j) & 1u)) x[j] = -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        m_seen = fmaxf(m_seen, mx);
+        if (__builtin_amdgcn_read_exec() & __ballot(m_ref == -INFINITY)) {   // no reference yet
+            const float tmax = cross4_max(mx);
+            if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + ATT_REF_LIFT;
+        }
+        ovf |= mx > m_ref + ATT_HEADROOM;
+        const float mr = m_ref == -INFINITY ? 0.f : m_ref;   // no reference: every x is -inf
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = __builtin_amdgcn_exp2f(x[j] - mr);        // 0 for invalid rows
+            ls += x[j];
+        }
+        l_lane += ls;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = x[2 * e], a1 = x[2 * e + 1];
+            const uint32_t h = pack_bf16x2(a0, a1);
+            pb[e] = h;
+            pl[e] = pack_bf16x2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
+        }
+#pragma unroll
+        for (int db = 0; db < NA; ++db) pv(st, db);
+    };
+    // second step of tile u: output blocks NA..NDB-1
+    auto step_b = [&](int u, int cv) {
+        const uint8_t* st = stages + (u % NST) * L::STAGE;
+        constexpr int GAP = (NDB - NA + NI - 1) / NI;   // output blocks between two copies
+#pragma unroll
+        for (int db = NA; db < NDB; ++db) {
+            if ((db - NA) % GAP == 0 && (db - NA) / GAP < NI) issue_one(cv, (db - NA) / GAP);
+            pv(st, db);
+        }
+    };
+
     for (int pass = 0; pass < 2; ++pass) {
-        const float m_init = cross4_max(m_seen);        // the reference of a second pass
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, wv = wv_u, g = lane >> 4, col = lane & 15;
-        const int w4 = wv & 3, team = wv >> 2, tt = tid & (F8_TNT - 1);
-
-        // Q of the block's 64 heads -> LDS by copies (slot k: piece k % QP of head k / QP; the
-        // pads and heads past H read the zero row; copies past the last segment repeat it);
-        // they complete with the first tile's rows
-        auto issue_q = [&]() {
-            const int64_t q0 = (bq * a.H + (int64_t)hb * 64) * D * 2;
 #pragma unroll
-            for (int i = 0; i < L::NQ; ++i) {
-                int seg = wv + (MQ_NT / 64) * i;
-                seg = seg < L::QSEG ? seg : L::QSEG - 1;
-                const int kq = 64 * seg + lane;
-                const int hh = kq / L::QP, pc = kq - hh * L::QP;
-                const bool data = pc < D / 8 && hb * 64 + hh < a.H;
-                const uint8_t* src = data ? a.q + q0 + ((int64_t)hh * D + 8 * pc) * 2 : f8_zero_row;
-                copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(lds + 1024 * seg)));
-            }
-        };
-        // Row pointers and validity masks of the RCH tiles of chunk c -> table c & 1, one
-        // row per thread of the calling team; an absent row reads the zero row.
-        auto resolve_chunk = [&](int c) {
-            for (int rr = tt; rr < RCH * T; rr += F8_TNT) {
-                const uint8_t* p = nullptr;
-                {
-                    const int64_t v = v_begin + (int64_t)(c * RCH) * T + rr;
-                    if (v < v_end) {
-                        if (v < n_ent) {
-                            const int64_t s = a.idx ? (int64_t)a.idx[bq * a.k + v] : v;
-                            if (s >= 0 && s < a.n_cap) p = att_entry_row(a, b, s, RB);
-                        } else {
-                            const int64_t pos = w0 + (v - n_ent);
-                            int64_t slot = (pos - a.kvw_pos0) % a.kvw_rows;
-                            if (slot < 0) slot += a.kvw_rows;
-                            p = a.kvw + (int64_t)b * a.kvw_bstride + slot * RB;
-                        }
-                    }
-                    rowptr[c & 1][rr] = p ? p : f8_zero_row;
-                }
-                const uint64_t m = __ballot(p != nullptr);       // lanes 0..31: one tile, 32..63: the next
-                if ((rr & (T - 1)) == 0) rowmask[c & 1][rr / T] = (uint32_t)(m >> (lane & 32));
-            }
-        };
-        // Copy i of this wave for tile v -> stage v % NST: the 1 KB segment wv + 8 i (the
-        // last segment ends at the stage's end; copies past it repeat it); the lane's
-        // 16-byte slot k holds piece k % P of row k / P (rows 0..15), then four gap slots,
-        // then rows 16..31 the same way; pads, gaps and absent rows read the zero row.
-        // Every wave issues the same number of copies for every tile (the vmcnt waits count
-        // them), past the split's rows too.
-        auto issue_one = [&](int v, int i) {
-            const uint8_t* const* rp = rowptr[(v / RCH) & 1] + (v % RCH) * T;
-            uint8_t* st = stages + (v % NST) * L::STAGE;
-            const int seg = wv + (MQ_NT / 64) * i;
-            const int k0 = seg < L::NSEG - 1 ? 64 * seg : L::SLOTS - 64;
-            // the lane's slot is recomputed at every copy (a few VALU): held across the tile
-            // loop for every copy, it would take registers the loop cannot spare
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int k = k0 + ln;
-            const int k2 = k < 16 * P ? k : k - 4;              // slot index with the gap removed
-            const int row = k2 / P, pc = k2 - row * P;
-            const bool data = (k < 16 * P || k >= 16 * P + 4) && pc < P - 1;
-            const uint8_t* src = data ? rp[row] + 16 * pc : f8_zero_row;
-            copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(st + 16 * k0)));
-        };
-        auto issue_copies = [&](int v) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) issue_one(v, i);
-        };
-
-        // Softmax with a fixed reference per head and team: m_ref = ATT_REF_LIFT above the
-        // largest logit (base 2) of the team's first tile that has a valid row; every
-        // probability is exp2(x - m_ref) and is never rescaled, so the O^T accumulators stay
-        // in place.  fp32 / bf16 hold x - m_ref <= ATT_HEADROOM with room to spare; if a
-        // later logit goes beyond, the block recomputes its split once with m_ref = the
-        // largest logit each wave saw.  (State of the heads 16 w4 + col, kept by the scores
-        // role.)
-        v4f o[NDW][4];                                      // O^T: dims 16 (NDW w4 + j) + 4g + i, heads 16 h + col
-        float m_ref, l_lane;
-        const float sl2 = a.scale * CSL_LOG2E;
-        bool ovf = false;
-
-        // per-lane LDS offsets within a stage
-        const int kofs0_l = f8_row_off(8 * (col >> 2) + (col & 3), RS);       // S^T block 0: rows 8(x/4) + x%4
-        const int kofs1_l = f8_row_off(8 * (col >> 2) + 4 + (col & 3), RS);   // block 1: the same + 4
-        const int v8ofs_l = f8_row_off(8 * g + (col >> 1), RS) + R + 8 * (col & 1);
-        const int v16ofs0_l = f8_row_off(8 * g + (col >> 2), RS) + 8 * (col & 3);
-        const int v16ofs1_l = f8_row_off(8 * g + 4 + (col >> 2), RS) + 8 * (col & 3);
-        const int qo_l = (16 * w4 + col) * L::QSTR + 8 * g;                  // Q fragment (bf16 index)
-
-        // scores of tile u (stage u % NST) for this wave's 16 heads -> P^T in LDS; the wave's
-        // copies of tile cv are spread over the work (a burst of copies from every wave at
-        // once stalls on the memory pipeline)
-        auto scores = [&](int u, int cv) {
-            const uint32_t rmask = __builtin_amdgcn_readfirstlane(rowmask[(u / RCH) & 1][u % RCH]);   // block-uniform
-            const bool full = rmask == 0xffffffffu;         // wave-uniform
-            const uint8_t* st = stages + (u % NST) * L::STAGE;
-            const int kofs0 = kofs0_l, kofs1 = kofs1_l;
-            const uint16_t* const qp = q_s + qo_l;
-            v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            // groups of SG k-steps: every fragment of a group is read before the group's
-            // conversions and products, so the LDS latency is paid once per group
-            constexpr int SG = 2;
-#pragma unroll
-            for (int k0s = 0; k0s < QK; k0s += SG) {
-                if (k0s / SG < NI) issue_one(cv, k0s / SG);
-                u32x4 qf[SG], kb0[SG], kb1[SG];
-                u32x2 kr0[SG], kr1[SG];
-#pragma unroll
-                for (int j = 0; j < SG; ++j) {
-                    const int ks = k0s + j;
-                    qf[j] = *(const u32x4*)(qp + 32 * ks);
-                    if (ks < RK) {                          // two 8-byte reads: the row stride suits b64
-                        const u32x2 x0 = *(const u32x2*)(st + kofs0 + 2 * (32 * ks + 8 * g));
-                        const u32x2 x1 = *(const u32x2*)(st + kofs0 + 2 * (32 * ks + 8 * g) + 8);
-                        const u32x2 y0 = *(const u32x2*)(st + kofs1 + 2 * (32 * ks + 8 * g));
-                        const u32x2 y1 = *(const u32x2*)(st + kofs1 + 2 * (32 * ks + 8 * g) + 8);
-                        kb0[j] = u32x4{x0[0], x0[1], x1[0], x1[1]};
-                        kb1[j] = u32x4{y0[0], y0[1], y1[0], y1[1]};
-                    } else {                                // fp8 dim d at byte R + d
-                        kr0[j] = *(const u32x2*)(st + kofs0 + R + 32 * ks + 8 * g);
-                        kr1[j] = *(const u32x2*)(st + kofs1 + R + 32 * ks + 8 * g);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < SG; ++j) {
-                    const int ks = k0s + j;
-                    const u32x4 k0 = ks < RK ? kb0[j] : f8_widen(kr0[j]);
-                    const u32x4 k1 = ks < RK ? kb1[j] : f8_widen(kr1[j]);
-                    s0 = mfma_bf16(k0, qf[j], s0);
-                    s1 = mfma_bf16(k1, qf[j], s1);
-                }
-                __builtin_amdgcn_sched_barrier(0);         // bounded read-ahead (registers)
-            }
-#pragma unroll
-            for (int i = QK / SG; i < NI; ++i) issue_one(cv, i);
-            // ---- probabilities (lane: head col, rows 8g + j), as a bf16 pair hi + lo:
-            //      P = hi + lo to ~2^-17 relative, so P.V keeps fp32-level accuracy even
-            //      where V has large channels
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = s0[i] * sl2;
-                x[4 + i] = s1[i] * sl2;
-            }
-            if (!full) {
-                const uint32_t mine = rmask >> (8 * g);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (!((mine >> j) & 1u)) x[j] = -INFINITY;
-            }
-            const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            m_seen = fmaxf(m_seen, mx);
-            if (__builtin_amdgcn_read_exec() & __ballot(m_ref == -INFINITY)) {   // no reference yet
-                const float tmax = cross4_max(mx);
-                if (m_ref == -INFINITY && tmax != -INFINITY) m_ref = tmax + ATT_REF_LIFT;
-            }
-            ovf |= mx > m_ref + ATT_HEADROOM;
-            const float mr = m_ref == -INFINITY ? 0.f : m_ref;   // no reference: every x is -inf
-            float ls = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                x[j] = __builtin_amdgcn_exp2f(x[j] - mr);        // 0 for invalid rows
-                ls += x[j];
-            }
-            l_lane += ls;
-            u32x4 pb, pl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a0 = x[2 * e], a1 = x[2 * e + 1];
-                const uint32_t h = pack_bf16x2(a0, a1);
-                pb[e] = h;
-                pl[e] = pack_bf16x2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
-            }
-            p_s[team][w4][0][lane] = pb;
-            p_s[team][w4][1][lane] = pl;
-        };
-        // values of tile u: O^T += V^T P^T over this wave's quarter of the dims, all 64 heads
-        auto values = [&](int u, int cv) {
-            const uint8_t* st = stages + (u % NST) * L::STAGE;
-            const int v8ofs = v8ofs_l, v16ofs0 = v16ofs0_l, v16ofs1 = v16ofs1_l;
-            u32x4 pb[4], pl[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                pb[h] = p_s[team][h][0][lane];
-                pl[h] = p_s[team][h][1][lane];
-            }
-            constexpr int GAP = (NDW + NI - 1) / NI;        // output blocks between two copies
-#pragma unroll
-            for (int j = 0; j < NDW; ++j) {
-                if (j % GAP == 0 && j / GAP < NI) issue_one(cv, j / GAP);
-                const int db = NDW * w4 + j;                // 16-dim block of the head dim
-                u32x4 va;
-                if (w4 == 0 && j < RV) {                    // RoPE dims (wave-uniform)
-                    const u32x2 t0 = lds_read_tr16((const uint16_t*)(st + v16ofs0 + 32 * db));
-                    const u32x2 t1 = lds_read_tr16((const uint16_t*)(st + v16ofs1 + 32 * db));
-                    va = u32x4{t0[0], t0[1], t1[0], t1[1]};
-                } else {
-                    va = f8_widen(lds_read_tr8(st + v8ofs + 16 * db));   // fp8 dim d at byte R + d
-                }
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    o[j][h] = mfma_bf16(va, pb[h], o[j][h]);
-                    o[j][h] = mfma_bf16(va, pl[h], o[j][h]);
-                }
-                // bounded read-ahead: O^T and P^T already hold 160 registers
-                if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
-#pragma unroll
-        for (int j = 0; j < NDW; ++j)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) o[j][h] = v4f{0.f, 0.f, 0.f, 0.f};
-        m_ref = pass == 0 ? -INFINITY : m_init;
+        for (int db = 0; db < NDB; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+        m_ref = pass == 0 ? -INFINITY : cross4_max(m_seen);
         l_lane = 0.f;
         ovf = false;
-        if (pass > 0) __syncthreads();                      // stages and tables of the first pass are free
-        // ---- prologue: Q (first pass), tiles 0 and 1 in flight; Q and tile 0 landed
-        if (pass == 0) issue_q();
+        pb = pl = u32x4{0, 0, 0, 0};
+        if (pass > 0) __syncthreads();                  // stages and tables of the first pass are free
+        // ---- prologue: tiles 0 and 1 in flight, Q (first pass) and tile 0 landed
+        lds_barrier();                                  // the index slice in LDS
         if (team == 0) resolve_chunk(0);
         lds_barrier();
         issue_copies(0);
         issue_copies(1);
-        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);              // this wave's copies of Q and tile 0
+        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);          // this wave's copies of Q and tile 0
         lds_barrier();
-        // ---- step u: team u&1 scores tile u, the other team takes the values of tile u-1;
-        //      tile u+2 goes into the stage tile u-2 freed
+        // ---- step u: team u&1 starts tile u, the other team finishes tile u-1; tile u+2
+        //      goes into the stage tile u-2 freed
         for (int u = 0; u <= ntiles; ++u) {
             if (team == (u & 1)) {
                 if (u < ntiles)
-                    scores(u, u + 2);
+                    step_a(u, u + 2);
                 else
                     issue_copies(u + 2);
             } else {
                 if (u > 0)
-                    values(u - 1, u + 2);
+                    step_b(u - 1, u + 2);
                 else
                     issue_copies(u + 2);
                 // the row table of the chunk whose first tile is copied two steps on
                 if ((u + 3) % RCH == 0) resolve_chunk((u + 3) / RCH);
             }
-            __builtin_amdgcn_s_waitcnt(WAIT_NEXT);          // this wave's copies of tile u+1
-            lds_barrier();                                  // tile u+1 and P^T visible, stage of tile u-1 free
+            __builtin_amdgcn_s_waitcnt(WAIT_NEXT);      // this wave's copies of tile u+1
+            lds_barrier();                              // tile u+1 visible, stage of tile u-1 free
         }
-        __builtin_amdgcn_s_waitcnt(WAIT_ALL);               // the copies past the split have landed
-        // the whole block redoes the split only if some wave overflowed; the merge below
-        // belongs to the pass that ends it, so no accumulator outlives a pass
-        if (__syncthreads_or(ovf ? 1 : 0) && pass == 0) continue;
+        __builtin_amdgcn_s_waitcnt(WAIT_ALL);           // the copies past the split have landed
+        // the whole block redoes the split only if some wave overflowed
+        if (!__syncthreads_or(ovf ? 1 : 0)) break;
+    }
 
-        // ---- merge the teams: every wave publishes the softmax state of its 16 heads; team 1
-        //      hands its O^T through LDS to the team-0 wave of the same dims, which
-        //      normalises and writes the output or the split's partial
-        v4f* mo = (v4f*)lds + w4 * NDW * 4 * 64;            // [w4][j][h][64]
-        float* sm = (float*)(lds + L::MERGE);               // [team][64]: reference
-        float* sl = sm + 2 * 64;                            // [team][64]: sum
-        {
-            const float lsum = cross4_sum(l_lane);
-            if (g == 0) {
-                sm[team * 64 + 16 * w4 + col] = m_ref;
-                sl[team * 64 + 16 * w4 + col] = lsum;
-            }
-        }
-        if (team == 1) {
+    // ---- merge the teams: team 1 hands (O^T, reference, sum) through LDS to the team-0
+    //      wave of the same heads, which normalises and writes the output or the split's
+    //      partial, one 16-dim block at a time
+    v4f* mo = (v4f*)lds + hg * NDB * 64;                // [hg][NDB][64]
+    float* mm = (float*)(lds + L::MERGE) + hg * 128;    // [hg][2][64]: reference, sum
+    if (team == 1) {
 #pragma unroll
-            for (int j = 0; j < NDW; ++j)
+        for (int db = 0; db < NDB; ++db) mo[db * 64 + lane] = o[db];
+        mm[lane] = m_ref;
+        mm[64 + lane] = l_lane;
+    }
+    __syncthreads();
+    if (team == 1) return;
+    const float mB = mm[lane], lB = mm[64 + lane];
+    const float M = fmaxf(m_ref, mB);
+    const float fA = m_ref == -INFINITY ? 0.f : exp2f(m_ref - M);
+    const float fB = mB == -INFINITY ? 0.f : exp2f(mB - M);
+    const float l_run = cross4_sum(l_lane * fA + lB * fB);
+    const int hh = 16 * hg + col;                       // head within the block
+    const int h = hb * 64 + hh;
+    float inv, lse;
+    if (a.nsplit == 1) {
+        att_finish(M, l_run, h < a.H ? a.sink : nullptr, h, inv, lse);
+    } else {                                        // a split's partial: no sink (the combine adds it)
+        inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        lse = l_run > 0.f ? (M + log2f(l_run)) * CSL_LN2 : -INFINITY;
+    }
+    const float cA = fA * inv, cB = fB * inv;
+    const int d0 = 4 * g;
+    float* of = nullptr;                                // fp32 destination (output or partial)
+    uint16_t* ob = nullptr;                             // bf16 output
+    if (a.nsplit > 1) {
+        const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
+        of = a.ws_o + prow * D + d0;
+        if (g == 0) a.ws_lse[prow] = lse;
+    } else if (h < a.H) {
+        if (a.out_fmt == F32)
+            of = (float*)a.out + (bq * a.H + h) * D + d0;
+        else
+            ob = (uint16_t*)a.out + (bq * a.H + h) * D + d0;
+        if (a.lse && g == 0) a.lse[bq * a.H + h] = lse;
+    }
+    if (!of && !ob) return;
 #pragma unroll
-                for (int h = 0; h < 4; ++h) mo[(j * 4 + h) * 64 + lane] = o[j][h];
-        }
-        __syncthreads();
-        if (team == 1) return;
-        const int d0 = 16 * NDW * w4 + 4 * g;               // first dim of the lane's block 0
+    for (int db = 0; db < NDB; ++db) {
+        const v4f oB = mo[db * 64 + lane];
+        float r[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int hh = 16 * h + col;                    // head within the block
-            const int hg = hb * 64 + hh;
-            const float mA = sm[hh], lA = sl[hh], mB = sm[64 + hh], lB = sl[64 + hh];
-            const float M = fmaxf(mA, mB);
-            const float fA = mA == -INFINITY ? 0.f : exp2f(mA - M);
-            const float fB = mB == -INFINITY ? 0.f : exp2f(mB - M);
-            const float l_run = lA * fA + lB * fB;
-            float inv, lse;
-            if (a.nsplit == 1) {
-                att_finish(M, l_run, hg < a.H ? a.sink : nullptr, hg, inv, lse);
-            } else {                                    // a split's partial: no sink (the combine adds it)
-                inv = l_run > 0.f ? 1.f / l_run : 0.f;
-                lse = l_run > 0.f ? (M + log2f(l_run)) * CSL_LN2 : -INFINITY;
-            }
-            const float cA = fA * inv, cB = fB * inv;
-            float* of = nullptr;                            // fp32 destination (output or partial)
-            uint16_t* ob = nullptr;                         // bf16 output
-            if (a.nsplit > 1) {
-                const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
-                of = a.ws_o + prow * D + d0;
-                if (w4 == 0 && g == 0) a.ws_lse[prow] = lse;
-            } else if (hg < a.H) {
-                if (a.out_fmt == F32)
-                    of = (float*)a.out + (bq * a.H + hg) * D + d0;
-                else
-                    ob = (uint16_t*)a.out + (bq * a.H + hg) * D + d0;
-                if (a.lse && w4 == 0 && g == 0) a.lse[bq * a.H + hg] = lse;
-            }
-            if (!of && !ob) continue;
-#pragma unroll
-            for (int j = 0; j < NDW; ++j) {
-                const v4f oB = mo[(j * 4 + h) * 64 + lane];
-                float r[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) r[i] = o[j][h][i] * cA + oB[i] * cB;
-                if (of)
-                    *(float4*)(of + 16 * j) = make_float4(r[0], r[1], r[2], r[3]);
-                else
-                    *(u32x2*)(ob + 16 * j) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-            }
-        }
-        return;
+        for (int i = 0; i < 4; ++i) r[i] = o[db][i] * cA + oB[i] * cB;
+        if (of)
+            *(float4*)(of + 16 * db) = make_float4(r[0], r[1], r[2], r[3]);
+        else
+            *(u32x2*)(ob + 16 * db) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
     }
 }
 
