@@ -142,7 +142,7 @@ def layer_cpu_baseline(ly, min_s=10.0):
     import oracle as O
     S = ly.sets[0]
     h = lambda x: x.detach().cpu().numpy()
-    a = {k: h(v) for k, v in S.items() if k not in ("out", "idx", "q")}
+    a = {k: h(v) for k, v in S.items() if torch.is_tensor(v) and k not in ("out", "idx", "q")}
     a["q"] = h(S["q"].view(torch.int16))
     qpos = np.full((ly.B, 1), ly.t, np.int32)
     i = (ly.t + 1) // ly.m - 1
