@@ -18,6 +18,12 @@
 // With few entries (decode: one per sequence) the channels are also split over
 // gridDim.z blocks of d / gridDim.z channels each, so that the launch still spans
 // a good part of the chip; each block recomputes the (cheap) window softmax.
+// Decode steps with one logit per token take a one-wave kernel instead
+// (k_compress_dec): the block returns at once when its token completes no entry;
+// otherwise every lane loads its share of the window's logits and the wave reduces
+// their maximum and sum with lane moves, each lane sums its rows with their final
+// weights, and the row groups are added with lane moves as well -- no LDS and no
+// barrier between the row loads and the store.
 #include <type_traits>
 
 #include "device.h"
@@ -326,6 +332,172 @@ __global__ void __launch_bounds__(256) k_compress_pair(CompressArgs a0, Compress
     else compress_body<BF16, OF1, true, 256>(a1, (int)blockIdx.z - gz0, gz1);
 }
 
+// ---- decode-time compression, one logit per token: one wave per block ----------------
+// Block (q, b, zi): the entry token q of sequence b completes, channels zi*dt .. +dt.
+// Every lane of the wave takes window slots l, l+64, .. for the softmax maximum and sum
+// (wave reductions, no LDS); lane (g, tr) then sums rows g, g+RG, .. of its 8 channels
+// with their final weights, and the RG row groups are added by lane moves.
+template <int OF>
+__device__ __forceinline__ void compress_dec_body(const CompressArgs& a, int zi, int gz) {
+    const int win = a.overlap ? 2 * a.m : a.m;
+    const int dt = a.d / gz;
+    const int TPR = dt / 8;                       // 4 .. 64, a power of two
+    const int RG = 64 / TPR;
+    const int lane = (int)threadIdx.x;
+    const int tr = lane & (TPR - 1), g = lane / TPR;
+    const int c0 = zi * dt + tr * 8;
+    const int b = blockIdx.y;
+    const int64_t q = blockIdx.x;
+    const int p = a.pos[(int64_t)b * a.n_e + q];
+    if (p < 0 || (p + 1) % a.m != 0) return;      // no entry completes (uniform)
+    const int64_t i = (p + 1) / a.m - 1;
+    const int64_t p0 = (i + 1) * a.m - win;
+    const int j0 = p0 < 0 ? (int)(-p0) : 0;
+    const uint8_t* xb = a.x + (int64_t)b * a.x_bstride;
+    const float* zb = (const float*)((const uint8_t*)a.z + (int64_t)b * a.z_bstride);
+    const int64_t xrb = 2 * (int64_t)a.d * a.x_roles;
+    const int role_off = a.x_roles == 2 ? a.d : 0;
+    // raw row of window slot j: a ring holds at least win rows, so one reduction of the
+    // window's first row suffices
+    int64_t rbase = p0 - a.x_pos0;
+    if (a.x_rows > 0) { rbase %= a.x_rows; if (rbase < 0) rbase += a.x_rows; }
+    auto xrow = [&](int j) {
+        const int64_t row = rbase + j;
+        return (a.x_rows > 0 && row >= a.x_rows) ? row - a.x_rows : row;
+    };
+    // the window's maximum logit and softmax sum, on every lane
+    float lgw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = lane + 64 * u;
+        lgw[u] = (j >= j0 && j < win) ? zb[xrow(j)] + a.bias[j] : -INFINITY;
+    }
+    float M = fmaxf(fmaxf(lgw[0], lgw[1]), fmaxf(lgw[2], lgw[3]));
+    M = cross4_max(row16_max(M));
+    float S = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S += lgw[u] == -INFINITY ? 0.f : expf(lgw[u] - M);
+    S = cross4_sum(row16_sum(S));
+    // this lane's rows, eight loads in flight at a time
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    const int jf = g + ((j0 - g + RG - 1) / RG) * RG * (j0 > g);
+    for (int jb = jf; jb < win; jb += 8 * RG) {
+        float xv[8][8], e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + u * RG;
+            const bool ok = j < win;
+            const int jc = ok ? j : jb;
+            const int64_t row = xrow(jc);
+            load8<BF16>(xb + row * xrb, c0 + (jc >= a.m ? role_off : 0), xv[u]);
+            e[u] = ok ? zb[row] + a.bias[jc] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = e[u] == -INFINITY ? 0.f : expf(e[u] - M);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, xv[u][c], acc[c]);
+        }
+    }
+    // add the row groups: rotations within 16-lane rows, then the row swaps
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float x = acc[c];
+        if (TPR <= 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+        if (TPR <= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+        if (TPR <= 16) {
+            const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+        }
+        if (TPR <= 32) {
+            const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+        }
+        acc[c] = x;
+    }
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = acc[c] / S;
+    bool writer = g == 0;
+    const int64_t orb = OF == BF16 ? 2 * (int64_t)a.d :
+                        (OF == KV_PACKED ? 2 * (int64_t)a.r + (a.d - a.r) : (int64_t)a.d / 2);
+    uint8_t* orow;
+    uint8_t* osc = nullptr;
+    if (!a.bt) {
+        writer = writer && i < a.n_cap;
+        orow = a.out + (int64_t)b * a.out_bstride + i * orb;
+        if (OF == MXFP4) osc = a.out_scales + (int64_t)b * a.sc_bstride + i * (a.d / 32);
+    } else {
+        const int64_t lb = i / a.epb;
+        const int32_t blk = lb < a.bt_stride ? a.bt[(int64_t)b * a.bt_stride + lb] : -1;
+        writer = writer && blk >= 0 && blk < a.n_blocks;
+        const int64_t off = i - lb * a.epb;
+        orow = a.out + (int64_t)blk * a.blk_bytes + off * orb;
+        if (OF == MXFP4) osc = a.out_scales + (int64_t)blk * a.sblk_bytes + off * (a.d / 32);
+    }
+    if (OF == BF16) {
+        if (writer) {
+            u32x4 o;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) o[k2] = f32_to_bf16_rne(v[2 * k2]) | (f32_to_bf16_rne(v[2 * k2 + 1]) << 16);
+            *(u32x4*)(orow + (int64_t)c0 * 2) = o;
+        }
+    } else if (OF == KV_PACKED) {
+        if (writer) {
+            if (c0 < a.r) {
+                u32x4 o;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2)
+                    o[k2] = f32_to_bf16_rne(v[2 * k2]) | (f32_to_bf16_rne(v[2 * k2 + 1]) << 16);
+                *(u32x4*)(orow + 2 * c0) = o;
+            } else {
+                u32x2 o;
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+                    o[k2] = f32_to_e4m3_rne_sat(v[4 * k2]) | (f32_to_e4m3_rne_sat(v[4 * k2 + 1]) << 8) |
+                            (f32_to_e4m3_rne_sat(v[4 * k2 + 2]) << 16) | (f32_to_e4m3_rne_sat(v[4 * k2 + 3]) << 24);
+                *(u32x2*)(orow + 2 * a.r + (c0 - a.r)) = o;
+            }
+        }
+    } else {  // MXFP4: lanes tr .. tr+3 (aligned) hold one 32-channel block
+        float am = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(v[c]));
+        am = fmaxf(am, shfl_xor(am, 1));
+        am = fmaxf(am, shfl_xor(am, 2));
+        const int ex = mx_block_exponent(am);
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w |= f32_to_e2m1_rne_sat(ldexpf(v[c], -ex)) << (4 * c);
+        if (writer) {
+            *(uint32_t*)(orow + c0 / 2) = w;
+            if ((c0 & 31) == 0) osc[c0 / 32] = (uint8_t)(ex + 127);
+        }
+    }
+}
+
+template <int OF>
+__global__ void __launch_bounds__(64) k_compress_dec(CompressArgs a) {
+    compress_dec_body<OF>(a, (int)blockIdx.z, (int)gridDim.z);
+}
+
+template <int OF0, int OF1>
+__global__ void __launch_bounds__(64) k_compress_dec_pair(CompressArgs a0, CompressArgs a1, int gz0, int gz1) {
+    if ((int)blockIdx.z < gz0) compress_dec_body<OF0>(a0, (int)blockIdx.z, gz0);
+    else compress_dec_body<OF1>(a1, (int)blockIdx.z - gz0, gz1);
+}
+
+// the decode kernel's shape: bf16 rows, one logit per token, a window of at most 256
+// slots, and a channel split into parts of 32 .. 512 channels
+static bool dec_shape(const CompressArgs& a, int gz) {
+    const int win = a.overlap ? 2 * a.m : a.m;
+    const int dt = a.d / gz;
+    return a.pos && a.x_fmt == BF16 && a.z_ch == 1 && win <= 256 && a.out_fmt != F32 && dt >= 32 && dt <= 512 &&
+           (dt & (dt - 1)) == 0;
+}
+
 // channel splits: halve the block's channels (keeping whole 32-channel groups)
 // while the launch has fewer than 256 entry blocks
 static int cmp_splits(const CompressArgs& a) {
@@ -348,6 +520,12 @@ static hipError_t launch_c3(const CompressArgs& a, hipStream_t s, int gz) {
 template <int XF, int OF>
 static hipError_t launch_c2(const CompressArgs& a, hipStream_t s) {
     const int gz = cmp_splits(a);
+    if constexpr (XF == BF16 && OF != F32) {
+        if (dec_shape(a, gz)) {
+            hipLaunchKernelGGL((k_compress_dec<OF>), dim3((unsigned)a.n_e, (unsigned)a.B, (unsigned)gz), dim3(64), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     return cmp_threads(a.d / gz, a.overlap ? 2 * a.m : a.m) == 1024 ? launch_c3<XF, OF, 1024>(a, s, gz)
                                                                     : launch_c3<XF, OF, 256>(a, s, gz);
 }
@@ -367,13 +545,23 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
     return a.x_fmt == F32 ? launch_c1<F32>(a, s) : launch_c1<BF16>(a, s);
 }
 
-// Both jobs in one launch when they take the fused kernel's shape (bf16 raw rows, one
-// logit per token, 256-thread blocks, a packed KV entry plus an MXFP4 or bf16 key);
-// otherwise one launch after the other.
+// Both jobs in one launch when they take a fused kernel's shape (bf16 raw rows, one
+// logit per token, a packed KV entry plus an MXFP4 or bf16 key): the one-wave decode
+// kernel, else the general one with 256-thread blocks; otherwise one launch after the
+// other.
 hipError_t launch_compress_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t s) {
     if (a0.B <= 0 || a0.n_e <= 0) return hipSuccess;
     const int gz0 = cmp_splits(a0), gz1 = cmp_splits(a1);
     const int w0 = a0.overlap ? 2 * a0.m : a0.m, w1 = a1.overlap ? 2 * a1.m : a1.m;
+    if (a0.B == a1.B && a0.n_e == a1.n_e && dec_shape(a0, gz0) && dec_shape(a1, gz1) && a0.out_fmt == KV_PACKED &&
+        (a1.out_fmt == MXFP4 || a1.out_fmt == BF16)) {
+        const dim3 grid((unsigned)a0.n_e, (unsigned)a0.B, (unsigned)(gz0 + gz1));
+        if (a1.out_fmt == MXFP4)
+            hipLaunchKernelGGL((k_compress_dec_pair<KV_PACKED, MXFP4>), grid, dim3(64), 0, s, a0, a1, gz0, gz1);
+        else
+            hipLaunchKernelGGL((k_compress_dec_pair<KV_PACKED, BF16>), grid, dim3(64), 0, s, a0, a1, gz0, gz1);
+        return hipGetLastError();
+    }
     const bool shape = a0.B == a1.B && a0.n_e == a1.n_e && a0.x_fmt == BF16 && a1.x_fmt == BF16 && a0.z_ch == 1 &&
                        a1.z_ch == 1 && cmp_threads(a0.d / gz0, w0) == 256 && cmp_threads(a1.d / gz1, w1) == 256 &&
                        a0.out_fmt == KV_PACKED && (a1.out_fmt == MXFP4 || a1.out_fmt == BF16);

@@ -39,6 +39,7 @@ CSA_CASES = [
     ("f32_cfg1", O.F32, 1, 64, 8, 128, 32, 512, 64, 128, 2048, "cfg1"),
     ("packed_many_q", O.KV_PACKED, 4, 200, 16, 256, 64, 400, 40, 8, 64, "ragged"),  # nsplit = 1 path
     ("packed_d64", O.KV_PACKED, 2, 3, 16, 64, 16, 700, 128, 32, 64, "ragged"),       # smallest head dim
+    ("packed_r32", O.KV_PACKED, 2, 2, 64, 512, 32, 3000, 512, 128, 300, "end"),     # RoPE width 32: other kernel
 ]
 
 
@@ -86,6 +87,7 @@ HCA_CASES = [
     ("bf16_d64", O.BF16, 2, 3, 16, 64, 0, 300, 4, 32, "ragged"),
     ("f32_d64", O.F32, 1, 4, 8, 64, 0, 150, 4, 16, "ragged"),
     ("packed_d256_h80", O.KV_PACKED, 2, 2, 80, 256, 64, 400, 16, 128, "end"),   # two head blocks, one partial
+    ("packed_r32", O.KV_PACKED, 2, 1, 64, 512, 32, 900, 128, 128, "end"),       # RoPE width 32: other kernel
 ]
 
 

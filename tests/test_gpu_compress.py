@@ -268,3 +268,48 @@ def test_compress_step_pair_equals_two_steps(gpu, roles, key_fmt, m0, paged, B, 
     assert (want[0] != before[0]).any() and (want[1] != before[1]).any()
     for w, g_ in zip(want, got):
         assert np.array_equal(w, g_)
+
+
+@pytest.mark.parametrize("x_fmt,z_ch,d,r,out_fmt", [(O.F32, 1, 128, 0, O.F32), (O.BF16, 256, 256, 0, O.F32),
+                                                    (O.BF16, 512, 512, 64, O.KV_PACKED), (O.BF16, 1, 96, 0, O.BF16),
+                                                    (O.BF16, 1, 512, 64, O.KV_PACKED)])
+def test_compress_step_general_and_wave_kernels(gpu, x_fmt, z_ch, d, r, out_fmt):
+    """Decode-time steps outside and inside the one-wave kernel's shape (fp32 rows or
+    outputs, per-channel logits, a channel part that is no power of two; and bf16 rows
+    with one logit per token) against the oracle's step: the first entry of a sequence
+    (half its window before position 0), later entries, tokens that complete none and a
+    negative position.  fp32 entries within fp32 rounding; quantised ones equal to the
+    oracle's except where its fp64 value sits on a rounding boundary."""
+    B, R, m = 3, 64, 4
+    pos = torch.tensor([[m - 1, m], [-1, 2 * m - 1], [29, 31]], dtype=torch.int32)
+    xr = gen.store(gen.normal((B, R, d), 930 + d), x_fmt)
+    zr = gen.random_logits((B, R, z_ch), 931)
+    bias = gen.random_logits((2 * m, z_ch), 932)
+    n_cap = 16
+    rb = O.row_bytes(out_fmt, d, r)
+    cache = torch.full((B, n_cap, rb), 0xA5, dtype=torch.uint8)
+    kw = dict(d=d, r=r, m=m, overlap=True)
+    out, _ = ops.kv_compress_step(dev(xr), x_fmt, dev(zr), dev(bias), dev(pos), out=dev(cache), out_fmt=out_fmt, **kw)
+    torch.cuda.synchronize()
+    got = host(out)
+    want, _, ent = O.kv_compress_step(host(xr), x_fmt, host(zr), host(bias), host(pos), out_fmt=out_fmt, **kw)
+    assert sorted(int(e) for e in ent.reshape(-1) if e >= 0) == [0, 1, 7]
+    touched = set()
+    for b in range(B):
+        for j in range(pos.shape[1]):
+            e = int(ent[b, j])
+            if e < 0:
+                continue
+            touched.add((b, e))
+            if out_fmt == O.F32:
+                g_ = got[b, e].view(np.float32).astype(np.float64)
+                w_ = want[b, j].astype(np.float64)
+                assert np.all(np.abs(g_ - w_) <= 2e-6 * (1.0 + np.abs(w_))), (b, e)
+            else:
+                dg = O.decode_rows(got[b, e][None], out_fmt, d, r, None)
+                dw = O.decode_rows(want[b, j][None], out_fmt, d, r, None)
+                assert np.mean(dg != dw) <= 2.0 / d, (b, e)
+    for b in range(B):
+        for e in range(n_cap):
+            if (b, e) not in touched:
+                assert np.all(got[b, e] == 0xA5), (b, e)
