@@ -99,24 +99,64 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
 // sign/exponent patterns that the top bits of real scores take.  A pass stops the
 // search early when the threshold bin holds exactly the remaining count.  Passes
 // run on registers: per pass, LDS atomics into one of two histograms (the other
-// is cleared meanwhile), then wave 0 alone locates the threshold digit -- two
-// barriers per pass.  The final compaction is one packed (greater, equal) scan.
+// is cleared meanwhile), then the block locates the threshold digit
+// (block_find_bin) -- three barriers per pass.  The final compaction is one packed
+// (greater, equal) scan.
 constexpr int TOPK_BINS = 2048;
-// Histograms are stored with 4 pad words after every 32 bins (bin b at b + 4*(b/32)),
-// so that lane L of the scanning wave, which reads bins 32L..32L+31 as 16-byte
-// vectors, starts at word 36L: 16 consecutive lanes then touch 16 different
-// 16-byte bank groups instead of the same two.
+// Histograms are stored with 4 pad words after every 32 bins (bin b at b + 4*(b/32)).
 constexpr int TOPK_HSZ = TOPK_BINS + TOPK_BINS / 8;
 __device__ __forceinline__ int hpad(uint32_t b) { return (int)(b + 4 * (b >> 5)); }
 constexpr int TOPK_BITS = 11;
 constexpr int TOPK_EMAX = 32;
 #define TOPK_SCRATCH(NT) (2 * TOPK_HSZ + 16 + 2 * ((NT) / 64) + 8)
 
+// The block locates, in a padded 2048-bin histogram, the bin b where the count of keys
+// in higher bins is < need <= that count + hist[b]: misc[0] = b, misc[1] = count
+// above, misc[2] = hist[b] (need >= 1 and <= the total).  Waves 0..3 (one per SIMD)
+// own 512 bins each, a lane 8 consecutive ones: two reads per lane, a wave scan, the
+// four wave totals through LDS (`wtot`, 16-byte aligned), then the lane whose bins
+// hold the crossing writes misc.  (Every wave of the block scanning its share made
+// the SIMDs issue the same fixed instructions four times over.)  Every thread calls
+// it; it contains one barrier, and the caller's next barrier publishes misc.
+__device__ __forceinline__ void block_find_bin(const uint32_t* hp, uint32_t need, uint32_t* misc, int* wtot) {
+    constexpr int BPL = 8;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const bool scan = wv < 4;
+    const int b0 = wv * 512 + lane * BPL;                // 8 consecutive bins in one 32-bin group
+    uint32_t h[BPL] = {};
+    int incl = 0, wt = 0;
+    if (scan) {
+        const u32x4 v0 = *(const u32x4*)(hp + hpad(b0));
+        const u32x4 v1 = *(const u32x4*)(hp + hpad(b0) + 4);
+        h[0] = v0[0]; h[1] = v0[1]; h[2] = v0[2]; h[3] = v0[3];
+        h[4] = v1[0]; h[5] = v1[1]; h[6] = v1[2]; h[7] = v1[3];
+        const uint32_t loc = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+        incl = wave_incl_scan((int)loc);
+        wt = __builtin_amdgcn_readlane(incl, 63);
+        if (lane == 0) wtot[wv] = wt;
+    }
+    lds_barrier();
+    if (scan) {
+        const u32x4 t4 = *(const u32x4*)wtot;
+        uint32_t c = (uint32_t)(wt - incl);              // keys in the bins of higher lanes of the wave
+#pragma unroll
+        for (int e = 1; e < 4; ++e) c += e > wv ? t4[e] : 0u;   // ... and of higher waves
+#pragma unroll
+        for (int e = BPL - 1; e >= 0; --e) {
+            const uint32_t cge = c + h[e];
+            if (cge >= need && c < need) { misc[0] = (uint32_t)(b0 + e); misc[1] = c; misc[2] = h[e]; }
+            c = cge;
+        }
+    }
+}
+
 // top_known >= 0: the caller guarantees every key < 2^(top_known + 1), and the
-// min / max phase is skipped.
+// min / max phase is skipped.  n_sat > 0: exactly n_sat keys equal sat_key, the
+// largest key, and n_sat < want -- they are taken without entering the histograms
+// (otherwise all of them would add into one bin, one LDS atomic after another).
 template <int NT, int EMAX, typename Emit>
 __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, int n, int want, uint32_t* sh,
-                                           Emit emit, int top_known = -1) {
+                                           Emit emit, int top_known = -1, uint32_t sat_key = 0u, int n_sat = 0) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int base = tid * E;
     uint32_t* hist0 = sh;
@@ -159,7 +199,8 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
             int top = 31 - __builtin_clz(lo ^ hi);   // highest differing bit
             uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
             uint32_t prefix = hi & pmask;
-            int w = want;
+            int w = want - n_sat;                    // taken from the keys below sat_key
+            const bool sat = n_sat > 0;
             bool exact = false;
             for (int pass = 0;; ++pass) {
                 uint32_t* hcur = (pass & 1) ? hist1 : hist0;
@@ -169,44 +210,12 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
                 const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
                 for (int x = 0; x < EMAX; ++x) {
-                    if (x < E && base + x < n && (kv[x] & pmask) == prefix) atomicAdd(&hcur[hpad((kv[x] >> shift) & dmask)], 1u);
+                    if (x < E && base + x < n && (kv[x] & pmask) == prefix && !(sat && kv[x] == sat_key))
+                        atomicAdd(&hcur[hpad((kv[x] >> shift) & dmask)], 1u);
                 }
                 for (int x = tid; x < TOPK_HSZ; x += NT) hnxt[x] = 0;
                 __syncthreads();
-                if (wv == 0) {
-                    // lane L owns bins [32L, 32L+32); counts of keys in bins above.
-                    // The bins are read twice (sum, then the walk) rather than held in
-                    // 32 registers next to the caller's keys.
-                    const u32x4* hp = (const u32x4*)(hcur + 36 * lane);
-                    uint32_t loc = 0;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const u32x4 v4 = hp[q];
-                        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
-                    }
-                    const int incl = wave_incl_scan((int)loc);
-                    const int tot = __shfl(incl, 63, 64);
-                    uint32_t c = (uint32_t)(tot - incl);   // keys in the bins of higher lanes
-                    // the lane's first bin, opaque to the compiler so that the 32 bin
-                    // numbers below are formed where used, not hoisted out of the pass loop
-                    int lb = 32 * lane;
-                    asm volatile("" : "+v"(lb));
-#pragma unroll
-                    for (int q = 7; q >= 0; --q) {
-                        const u32x4 v4 = hp[q];
-#pragma unroll
-                        for (int e = 3; e >= 0; --e) {
-                            const uint32_t hq = v4[e];
-                            const uint32_t cge = c + hq;
-                            if (cge >= (uint32_t)w && c < (uint32_t)w) {
-                                misc[0] = lb + 4 * q + e;
-                                misc[1] = c;
-                                misc[2] = hq;
-                            }
-                            c = cge;
-                        }
-                    }
-                }
+                block_find_bin(hcur, (uint32_t)w, misc, wsum);
                 __syncthreads();
                 const uint32_t dgt = misc[0];
                 w -= (int)misc[1];
@@ -253,36 +262,6 @@ __device__ __forceinline__ void block_topk(const uint32_t (&kv)[EMAX], int E, in
             }
         }
     }
-}
-
-// Wave 0 locates, in a padded 2048-bin histogram, the bin b where the count of keys in
-// higher bins is < need <= that count + hist[b]: misc[0] = b, misc[1] = count above,
-// misc[2] = hist[b].  Caller: wave 0 only, need >= 1 and <= total.
-__device__ __forceinline__ void find_bin(const uint32_t* hp, uint32_t need, uint32_t* misc) {
-    const int lane = threadIdx.x & 63;
-    const u32x4* h4 = (const u32x4*)(hp + 36 * lane);
-    uint32_t loc = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const u32x4 v4 = h4[q];
-        loc += (v4[0] + v4[1]) + (v4[2] + v4[3]);
-    }
-    const int incl = wave_incl_scan((int)loc);
-    const int tot = __shfl(incl, 63, 64);
-    uint32_t c = (uint32_t)(tot - incl);
-    int fb = -1;                                         // bin within the lane's 32 (a select, not 32 live constants)
-    uint32_t fa = 0, fc = 0;
-#pragma unroll
-    for (int q = 7; q >= 0; --q) {
-        const u32x4 v4 = h4[q];
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-            const uint32_t cge = c + v4[e];
-            if (cge >= need && c < need) { fb = 4 * q + e; fa = c; fc = v4[e]; }
-            c = cge;
-        }
-    }
-    if (fb >= 0) { misc[0] = 32 * lane + fb; misc[1] = fa; misc[2] = fc; }
 }
 
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t n_cap) {
@@ -383,7 +362,13 @@ template <int FMT, int DI, int HB, bool SPLIT>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
 k_idx_score(IndexArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-    const int sl = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    // the slices of one query run on one XCD (logical ids in XCD groups), the one its
+    // select block and its attention blocks also map to: their reads of the slices'
+    // candidate lists and of the selected indices then find them in that XCD's L2
+    const unsigned nblk = gridDim.x * gridDim.y * gridDim.z;
+    const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const unsigned lg = xcd_local_id(lin, nblk);
+    const int sl = (int)(lg % gridDim.x), j = (int)((lg / gridDim.x) % gridDim.y), b = (int)(lg / (gridDim.x * gridDim.y));
     const int64_t bq = (int64_t)b * a.Tq + j;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int E = a.S / IDX_NT;
@@ -484,8 +469,6 @@ k_idx_score(IndexArgs a) {
         // multiples of the channel interleave) and crowd the same HBM channels.  Block
         // i of nb therefore takes its groups in the rotated order starting at group
         // i*ngr/nb.
-        const unsigned nblk = gridDim.x * gridDim.y * gridDim.z;
-        const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
         const int rot = (int)(((uint64_t)lin * (uint64_t)ngr) / nblk);
         auto rotg = [&](int j) { return j + rot < ngr ? j + rot : j + rot - ngr; };
         KeyFrag<FMT, DI> fa[IDX_UNR], fb[IDX_UNR];
@@ -543,7 +526,7 @@ k_idx_score(IndexArgs a) {
         // of its nonzero bins from the top down to this one -- the counts at and above
         // the query's threshold bin are then exact.
         uint32_t* misc = hs + TOPK_HSZ + 16;
-        if (wv == 0) find_bin(hs, (uint32_t)(ns < a.k ? ns : a.k), misc);
+        block_find_bin(hs, (uint32_t)(ns < a.k ? ns : a.k), misc, (int*)(hs + TOPK_HSZ));
         constexpr int BPT = TOPK_BINS / IDX_NT;          // bins per thread: BPT*t .. BPT*t + BPT-1
         uint32_t keep[BPT];
 #pragma unroll
@@ -808,7 +791,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int64_t bq, int64
     for (int level = 0;; ++level) {
         uint32_t bin = b0.bin, above = b0.above, inbin = b0.inbin;
         if (level > 0 || !b0.have) {
-            if (wv == 0) find_bin(sh, (uint32_t)need, misc);
+            block_find_bin(sh, (uint32_t)need, misc, wsum);
             __syncthreads();
             bin = misc[0]; above = misc[1]; inbin = misc[2];
             __syncthreads();
@@ -1062,7 +1045,8 @@ constexpr int SEL_PF = 1024;                         // candidates a wave prefet
 __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     constexpr int NW = DSEL_NT / 64, WCAP = DSEL_CAP / NW, NR = SEL_PF / 64;
-    const int j = blockIdx.x, b = blockIdx.y;
+    const unsigned lg = xcd_local_id(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);   // XCD of the query's slices
+    const int j = (int)(lg % gridDim.x), b = (int)(lg / gridDim.x);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bq = (int64_t)b * a.Tq + j;
     const uint32_t* ckr = a.cand_key + bq * a.sstride;
@@ -1125,7 +1109,7 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
         }
     }
     __syncthreads();
-    if (wv == 0) find_bin(sh, (uint32_t)a.k, misc);
+    block_find_bin(sh, (uint32_t)a.k, misc, wsum);
     __syncthreads();
     const uint32_t bin = misc[0], above = misc[1], inbin = misc[2];
     const uint32_t lo = bin << (32 - TOPK_BITS);
@@ -1202,7 +1186,7 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
         block_topk<DSEL_NT>(kv2, E2, (int)nsurv, a.k, sh, [&](int pos, int i, uint32_t) {
             win[pos] = si[i];
             wkey[pos] = sk[i];
-        }, 32 - TOPK_BITS);
+        }, 32 - TOPK_BITS, span, (int)above);
         __syncthreads();
         for (int p = tid; p < a.k; p += DSEL_NT) {
             oi[p] = win[p];
