@@ -365,40 +365,54 @@ __device__ __forceinline__ void compress_dec_body(const CompressArgs& a, int zi,
         const int64_t row = rbase + j;
         return (a.x_rows > 0 && row >= a.x_rows) ? row - a.x_rows : row;
     };
-    // the window's maximum logit and softmax sum, on every lane
+    // the window's logits (slots l, l+64, ..), then this lane's first eight rows (all of its
+    // rows when win <= 8 RG) -- issued before the reductions need the logits, so that the
+    // logits and the rows are one memory round trip
+    // (every load from a clamped slot, and a slot outside the window masked by adding -inf
+    // rather than by a select: the compiler turns a select of a load into a branch around
+    // the load and waits for it inside the branch, one round trip after another)
     float lgw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int j = lane + 64 * u;
-        lgw[u] = (j >= j0 && j < win) ? zb[xrow(j)] + a.bias[j] : -INFINITY;
+        const int jc = j < j0 ? j0 : (j < win ? j : win - 1);
+        lgw[u] = (zb[xrow(jc)] + a.bias[jc]) + ((j >= j0 && j < win) ? 0.f : -INFINITY);
     }
-    float M = fmaxf(fmaxf(lgw[0], lgw[1]), fmaxf(lgw[2], lgw[3]));
-    M = cross4_max(row16_max(M));
-    float S = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) S += lgw[u] == -INFINITY ? 0.f : expf(lgw[u] - M);
-    S = cross4_sum(row16_sum(S));
-    // this lane's rows, eight loads in flight at a time
-    float acc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
     const int jf = g + ((j0 - g + RG - 1) / RG) * RG * (j0 > g);
-    for (int jb = jf; jb < win; jb += 8 * RG) {
-        float xv[8][8], e[8];
+    u32x4 xr[8];                                        // raw bf16 rows, widened at their FMAs
+    float e[8];
+    auto load_rows = [&](int jb) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = jb + u * RG;
             const bool ok = j < win;
             const int jc = ok ? j : jb;
             const int64_t row = xrow(jc);
-            load8<BF16>(xb + row * xrb, c0 + (jc >= a.m ? role_off : 0), xv[u]);
-            e[u] = ok ? zb[row] + a.bias[jc] : -INFINITY;
+            xr[u] = *(const u32x4*)(xb + row * xrb + 2 * (int64_t)(c0 + (jc >= a.m ? role_off : 0)));
+            e[u] = (zb[row] + a.bias[jc]) + (ok ? 0.f : -INFINITY);
         }
+    };
+    if (jf < win) load_rows(jf);
+    float M = fmaxf(fmaxf(lgw[0], lgw[1]), fmaxf(lgw[2], lgw[3]));
+    M = cross4_max(row16_max(M));
+    float S = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S += lgw[u] == -INFINITY ? 0.f : expf(lgw[u] - M);
+    S = cross4_sum(row16_sum(S));
+    // this lane's rows with their final weights, eight loads in flight at a time
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    for (int jb = jf; jb < win; jb += 8 * RG) {
+        if (jb > jf) load_rows(jb);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const float w = e[u] == -INFINITY ? 0.f : expf(e[u] - M);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, xv[u][c], acc[c]);
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(w, bf16_to_f32(xr[u][i] & 0xffffu), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(w, bf16_to_f32(xr[u][i] >> 16), acc[2 * i + 1]);
+            }
         }
     }
     // add the row groups: rotations within 16-lane rows, then the row swaps

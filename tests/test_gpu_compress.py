@@ -177,7 +177,8 @@ def test_compress_step_from_the_ring(gpu, roles, out_fmt, m, overlap, paged):
             assert np.array_equal(got[b, e], want[b, j]), (b, j, e)
             if out_fmt == O.MXFP4:
                 assert np.array_equal(got_sc[b, e], want_sc[b, j])
-            # byte-equal to kv_compress over the same ring rows, as a linear buffer
+            # byte-equal to kv_compress over the same ring rows, as a linear buffer (the
+            # general kernel: another summation order, the same bytes on these inputs)
             p_hi = int(pos[b, j])
             lin = np.stack([host(xr)[b, p % R] for p in range(p_hi - (2 * m if overlap else m) + 1, p_hi + 1)])
             zl = np.stack([host(zr)[b, p % R] for p in range(p_hi - (2 * m if overlap else m) + 1, p_hi + 1)])
