@@ -771,6 +771,9 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     const int b = (int)(bq / a.Tq);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, col = lane & 15;
     const int hg = wv & 3, team = wv >> 2, tt = tid & (F8_TNT - 1);
+    // the query's position: a scalar load, issued first, whose wait below does not wait
+    // for the LDS-DMA copies of Q
+    const int64_t t = ld_uniform<int32_t>(a.q_pos + bq);
     // Q of the block's 64 heads -> LDS by copies (slot k: piece k % QP of head k / QP; the
     // pads and heads past H read the zero row; copies past the last segment repeat it);
     // they complete with the first tile's rows
@@ -795,7 +798,6 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
         const int64_t e_end = vb + a.rps < a.k ? vb + a.rps : (int64_t)a.k;
         for (int64_t v = vb + tid; v < e_end; v += MQ_NT) sidx[v - vb] = a.idx[bq * a.k + v];
     }
-    const int64_t t = a.q_pos[bq];
     const int64_t n_ent = a.idx ? (int64_t)a.k : att_n_visible(t, a.m, a.n_cap);
     const int64_t n_win = (t >= 0 && a.W > 0) ? (t + 1 < a.W ? t + 1 : a.W) : 0;
     const int64_t w0 = t - n_win + 1;

@@ -163,6 +163,14 @@ __device__ __forceinline__ T ld_global(const void* p) {
     return *(const __attribute__((address_space(1))) T*)p;
 }
 
+// Load of a block-uniform value that no kernel of the launch writes, through the scalar
+// data cache (a scalar load, counted by lgkmcnt): waiting for it does not wait for the
+// vector-memory operations in flight, such as LDS-DMA copies the compiler cannot see.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const void* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // Reductions over each row of 16 lanes with DPP moves (VALU, no LDS round trip):
 // swap neighbours, swap pairs, mirror the halves of 8, mirror the halves of 16.
 // After each step the partners hold identical values, so every lane of the row ends
