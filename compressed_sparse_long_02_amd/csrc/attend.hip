@@ -23,7 +23,10 @@
 //  * fp32 rows (k_attend, 4 waves of 16 heads): 16x16x4 f32 MFMA, an online
 //    softmax with a lazy rescale, P staged through LDS.
 // Splits write (o, lse) partials that k_attend_combine merges in a fixed order
-// (deterministic, no atomics).
+// (deterministic, no atomics).  The split's o is normalised (a weighted mean of value
+// rows); the packed-row kernel stores it as fp16 scaled by ATT_PART_SCALE (half the
+// bytes written and read back; relative error 2^-12, four times below the bf16
+// output's rounding), the others as fp32.
 #include <type_traits>
 
 #include "device.h"
@@ -76,6 +79,9 @@ constexpr int ATT_MAX_SIDX = 1536;   // CSA split lengths are capped to this (ho
 constexpr float ATT_TAU = 8.0f;   // lazy rescale: keep the reference max until it trails by 2^8
 constexpr float ATT_HEADROOM = 64.0f;   // largest x - m_ref (base 2) accepted without a rescale
 constexpr float ATT_REF_LIFT = 32.0f;   // m_ref starts this far above the first tile's largest logit
+// fp16 split partials hold o * 2^-8: magnitudes up to 65504 * 2^8 stay finite, and below
+// 2^-6 (fp16 subnormals after the scale) the absolute error stays under 2^-17
+constexpr float ATT_PART_SCALE = 1.0f / 256.0f;
 
 // ---------------------------------------------------------------------------
 // fp32 rows (the fp32 parity configuration): 4 waves of 16 heads, 16x16x4 f32 MFMA, an
@@ -1049,11 +1055,12 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     }
     const float cA = fA * inv, cB = fB * inv;
     const int d0 = 4 * g;
-    float* of = nullptr;                                // fp32 destination (output or partial)
+    float* of = nullptr;                                // fp32 output
     uint16_t* ob = nullptr;                             // bf16 output
+    uint16_t* op = nullptr;                             // a split's partial: fp16, scaled by ATT_PART_SCALE
     if (a.nsplit > 1) {
         const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
-        of = a.ws_o + prow * D + d0;
+        op = (uint16_t*)a.ws_o + prow * D + d0;
         if (g == 0) a.ws_lse[prow] = lse;
     } else if (h < a.H) {
         if (a.out_fmt == F32)
@@ -1062,14 +1069,17 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
             ob = (uint16_t*)a.out + (bq * a.H + h) * D + d0;
         if (a.lse && g == 0) a.lse[bq * a.H + h] = lse;
     }
-    if (!of && !ob) return;
+    if (!of && !ob && !op) return;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         const v4f oB = mo[db * 64 + lane];
         float r[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] = o[db][i] * cA + oB[i] * cB;
-        if (of)
+        if (op)
+            *(u32x2*)(op + 16 * db) = u32x2{pack_f16x2(r[0] * ATT_PART_SCALE, r[1] * ATT_PART_SCALE),
+                                           pack_f16x2(r[2] * ATT_PART_SCALE, r[3] * ATT_PART_SCALE)};
+        else if (of)
             *(float4*)(of + 16 * db) = make_float4(r[0], r[1], r[2], r[3]);
         else
             *(u32x2*)(ob + 16 * db) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
@@ -1088,8 +1098,9 @@ constexpr int CMB_HEADS = 1;
 constexpr int CMB_UNR = 16;
 constexpr int CMB_NT = 128;
 
-template <int D>
+template <int D, bool PH>
 __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
+    using PT = std::conditional_t<PH, u32x2, float4>;  // four dims of a partial as stored
     extern __shared__ float wts[];   // [CMB_HEADS][nsplit] normalised weights, then lse
     // same XCD assignment of queries as the attention kernel (its partials are in that L2)
     const unsigned lblk = xcd_local_id(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
@@ -1108,17 +1119,18 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
     const int hw = h0 + (wv < CMB_HEADS ? wv : 0);
     const float l_first = (wv < CMB_HEADS && lane < ns) ? a.ws_lse[(base + lane) * 64 + hw] : -INFINITY;
     // ---- first loads: splits 0 .. CMB_UNR-1 of this thread's items (clamped: every load in bounds)
-    float4 v[ITEMS][CMB_UNR];
+    PT v[ITEMS][CMB_UNR];
+    const PT* const part = (const PT*)a.ws_o;           // [rows][D / 4]
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         int item = tid + it * CMB_NT;
         item = item < CMB_HEADS * C4 ? item : CMB_HEADS * C4 - 1;
         const int j = item / C4, c = (item - j * C4) * 4;
-        const float* src = a.ws_o + (base * 64 + h0 + j) * D + c;
+        const PT* src = part + ((base * 64 + h0 + j) * D + c) / 4;
 #pragma unroll
         for (int u = 0; u < CMB_UNR; ++u) {
             const int sc = u < ns ? u : ns - 1;
-            v[it][u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+            v[it][u] = src[(int64_t)sc * 64 * (D / 4)];
         }
     }
     if (wv < CMB_HEADS) {
@@ -1168,7 +1180,7 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
         const int j = ic / C4, c = (ic - j * C4) * 4;
         const int hh = h0 + j;
         const int h = hb * 64 + hh;
-        const float* src = a.ws_o + (base * 64 + hh) * D + c;
+        const PT* src = part + ((base * 64 + hh) * D + c) / 4;
         const float* wj = wts + j * ns;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s0 = 0; s0 < ns; s0 += CMB_UNR) {
@@ -1176,14 +1188,20 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
 #pragma unroll
                 for (int u = 0; u < CMB_UNR; ++u) {
                     const int sc = s0 + u < ns ? s0 + u : ns - 1;
-                    v[it][u] = *(const float4*)(src + (int64_t)sc * 64 * D);
+                    v[it][u] = src[(int64_t)sc * 64 * (D / 4)];
                 }
             }
 #pragma unroll
             for (int u = 0; u < CMB_UNR; ++u) {
-                const float w = s0 + u < ns ? wj[s0 + u] : 0.f;
-                acc.x = fmaf(w, v[it][u].x, acc.x); acc.y = fmaf(w, v[it][u].y, acc.y);
-                acc.z = fmaf(w, v[it][u].z, acc.z); acc.w = fmaf(w, v[it][u].w, acc.w);
+                float4 x;
+                if constexpr (PH) {
+                    x = make_float4(f16_lo(v[it][u][0]), f16_hi(v[it][u][0]), f16_lo(v[it][u][1]), f16_hi(v[it][u][1]));
+                } else {
+                    x = v[it][u];
+                }
+                const float w = s0 + u < ns ? wj[s0 + u] * (PH ? 1.f / ATT_PART_SCALE : 1.f) : 0.f;
+                acc.x = fmaf(w, x.x, acc.x); acc.y = fmaf(w, x.y, acc.y);
+                acc.z = fmaf(w, x.z, acc.z); acc.w = fmaf(w, x.w, acc.w);
             }
         }
         if (!valid || h >= a.H) continue;
@@ -1216,8 +1234,11 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + CMB_HEADS);
-    hipLaunchKernelGGL((k_attend_combine<D>), dim3((unsigned)(a.nhb * (64 / CMB_HEADS)), (unsigned)((int64_t)a.B * a.Tq)),
-                       dim3(CMB_NT), lds2, s, a);
+    const dim3 cgrid((unsigned)(a.nhb * (64 / CMB_HEADS)), (unsigned)((int64_t)a.B * a.Tq));
+    if (FMT == KV_PACKED && (D == 256 || D == 512) && a.r == F8_R)   // k_attend_f8: fp16 partials
+        hipLaunchKernelGGL((k_attend_combine<D, true>), cgrid, dim3(CMB_NT), lds2, s, a);
+    else
+        hipLaunchKernelGGL((k_attend_combine<D, false>), cgrid, dim3(CMB_NT), lds2, s, a);
     return hipGetLastError();
 }
 

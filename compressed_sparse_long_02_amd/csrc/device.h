@@ -81,6 +81,14 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
 
 // Two fp32 -> two bf16 in one dword (element 0 in the low half), round to nearest
 // even, by the gfx950 packed conversion.
+// Two fp32 values -> two fp16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
