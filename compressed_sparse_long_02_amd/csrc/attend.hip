@@ -24,9 +24,10 @@
 //    softmax with a lazy rescale, P staged through LDS.
 // Splits write (o, lse) partials that k_attend_combine merges in a fixed order
 // (deterministic, no atomics).  The split's o is normalised (a weighted mean of value
-// rows); the packed-row kernel stores it as fp16 scaled by ATT_PART_SCALE (half the
-// bytes written and read back; relative error 2^-12, four times below the bf16
-// output's rounding), the others as fp32.
+// rows); for a bf16 output the packed-row kernel stores it as fp16 scaled by
+// ATT_PART_SCALE (half the bytes written and read back; relative error 2^-12, eight
+// times below the bf16 output's own rounding); an fp32 output, and the other kernels,
+// keep fp32 partials.
 #include <type_traits>
 
 #include "device.h"
@@ -1055,12 +1056,15 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
     }
     const float cA = fA * inv, cB = fB * inv;
     const int d0 = 4 * g;
-    float* of = nullptr;                                // fp32 output
+    float* of = nullptr;                                // fp32 output or partial
     uint16_t* ob = nullptr;                             // bf16 output
-    uint16_t* op = nullptr;                             // a split's partial: fp16, scaled by ATT_PART_SCALE
-    if (a.nsplit > 1) {
+    uint16_t* op = nullptr;                             // a split's partial in fp16, scaled by ATT_PART_SCALE
+    if (a.nsplit > 1) {                                 // fp16 for a bf16 output, else fp32
         const int64_t prow = ((bq * a.nhb + hb) * a.nsplit + sp) * 64 + hh;
-        op = (uint16_t*)a.ws_o + prow * D + d0;
+        if (a.out_fmt == BF16)
+            op = (uint16_t*)a.ws_o + prow * D + d0;
+        else
+            of = a.ws_o + prow * D + d0;
         if (g == 0) a.ws_lse[prow] = lse;
     } else if (h < a.H) {
         if (a.out_fmt == F32)
@@ -1235,7 +1239,7 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
     if (e != hipSuccess || a.nsplit == 1) return e;
     const size_t lds2 = sizeof(float) * ((size_t)a.nsplit * CMB_HEADS + CMB_HEADS);
     const dim3 cgrid((unsigned)(a.nhb * (64 / CMB_HEADS)), (unsigned)((int64_t)a.B * a.Tq));
-    if (FMT == KV_PACKED && (D == 256 || D == 512) && a.r == F8_R)   // k_attend_f8: fp16 partials
+    if (FMT == KV_PACKED && (D == 256 || D == 512) && a.r == F8_R && a.out_fmt == BF16)   // k_attend_f8, fp16 partials
         hipLaunchKernelGGL((k_attend_combine<D, true>), cgrid, dim3(CMB_NT), lds2, s, a);
     else
         hipLaunchKernelGGL((k_attend_combine<D, false>), cgrid, dim3(CMB_NT), lds2, s, a);

@@ -152,7 +152,14 @@ def test_attend_bf16_output_and_determinism(gpu):
     b1, _ = ops.hca_attend(dev(q), dev(kvc), dev(kvw), dev(qpos), out_fmt=O.BF16, **kw)
     torch.cuda.synchronize()
     assert torch.equal(f1, f2) and torch.equal(l1, l2)
-    assert torch.equal(b1, f1.to(torch.bfloat16))
+    # bf16 output: the fp32 output rounded to bf16 (RNE: within 2^-8 of the value), except
+    # that its split partials are fp16 (within 2^-11 of the largest partial value of the
+    # row); where those move a value across a rounding boundary the two differ -- a
+    # fraction of the elements about the ratio of the two errors (measured: 8%)
+    bf, ff = b1.float(), f1
+    bound = 2.0 ** -8 * ff.abs() + 2.0 ** -10 * ff.abs().amax(dim=-1, keepdim=True)
+    assert bool(((bf - ff).abs() <= bound).all())
+    assert float((b1 != f1.to(torch.bfloat16)).float().mean()) < 0.2
 
 
 def test_logits_far_above_the_first_tile_are_recomputed(gpu):

@@ -138,9 +138,12 @@ def test_stack_attend(gpu, kind, layout, request):
     err = max_abs(h(go), oo)
     assert err <= 2e-2, "%s: max-abs %.3g" % (kind, err)
     assert max_abs(h(gl), ol) <= 2e-1
-    # the benchmark's own bf16 output agrees with the fp32 one up to bf16 rounding
+    # the benchmark's own bf16 output agrees with the fp32 one up to bf16 rounding (within
+    # 2^-8 of the value) and its fp16 split partials (within 2^-11 of the row's largest value)
     ob = host(L["out"][SAMPLE].float())
-    assert np.all(np.abs(ob - h(go)) <= 2.0 ** -8 * np.abs(h(go)) + 1e-6)
+    g32 = h(go)
+    bound = 2.0 ** -8 * np.abs(g32) + 2.0 ** -10 * np.abs(g32).max(axis=-1, keepdims=True) + 1e-6
+    assert np.all(np.abs(ob - g32) <= bound)
     print("stack %s (%s): max-abs %.3g" % (kind, layout, err))
 
 
