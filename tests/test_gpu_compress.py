@@ -314,3 +314,41 @@ def test_compress_step_general_and_wave_kernels(gpu, x_fmt, z_ch, d, r, out_fmt)
         for e in range(n_cap):
             if (b, e) not in touched:
                 assert np.all(got[b, e] == 0xA5), (b, e)
+
+
+@pytest.mark.parametrize("B,T,d,r,out_fmt", [(32, 2, 512, 64, O.KV_PACKED), (128, 2, 512, 64, O.KV_PACKED),
+                                             (96, 1, 128, 0, O.MXFP4), (40, 2, 256, 64, O.KV_PACKED),
+                                             (64, 2, 512, 64, O.KV_PACKED)])
+def test_compress_step_wide_batches(gpu, B, T, d, r, out_fmt):
+    """Decode steps over many sequences: fewer channel parts per launch, so the one-wave kernel
+    runs with 8, 16, 32 and 64 lanes per row (its other lane-move paths) -- against the oracle's
+    step, quantised entries equal except where the fp64 value sits on a rounding boundary."""
+    R, m = 32, 4
+    rng = np.random.default_rng(B * 7 + T)
+    base = rng.integers(0, 4000, size=B)
+    pos = torch.tensor(base[:, None] + np.arange(T)[None, :], dtype=torch.int32)
+    pos[0, 0] = m - 1                                     # a first entry (half its window before 0)
+    xr = gen.store(gen.normal((B, R, d), 950 + B), O.BF16)
+    zr = gen.random_logits((B, R, 1), 951)
+    bias = gen.random_logits((2 * m, 1), 952)
+    n_cap = 4096 // m + 1
+    rb = O.row_bytes(out_fmt, d, r)
+    cache = torch.full((B, n_cap, rb), 0xA5, dtype=torch.uint8)
+    scales = torch.full((B, n_cap, d // 32), 0xA5, dtype=torch.uint8) if out_fmt == O.MXFP4 else None
+    kw = dict(d=d, r=r, m=m, overlap=True)
+    out, sc = ops.kv_compress_step(dev(xr), O.BF16, dev(zr), dev(bias), dev(pos), out=dev(cache),
+                                   out_scales=dev(scales) if scales is not None else None, out_fmt=out_fmt, **kw)
+    torch.cuda.synchronize()
+    got, got_sc = host(out), (host(sc) if sc is not None else None)
+    want, want_sc, ent = O.kv_compress_step(host(xr), O.BF16, host(zr), host(bias), host(pos), out_fmt=out_fmt, **kw)
+    n = 0
+    for b in range(B):
+        for j in range(T):
+            e = int(ent[b, j])
+            if e < 0:
+                continue
+            n += 1
+            dg = O.decode_rows(got[b, e][None], out_fmt, d, r, None if got_sc is None else got_sc[b, e][None])
+            dw = O.decode_rows(want[b, j][None], out_fmt, d, r, None if want_sc is None else want_sc[b, j][None])
+            assert np.mean(dg != dw) <= 2.0 / d, (b, e)
+    assert n >= B // 8
