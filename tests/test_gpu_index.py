@@ -44,6 +44,9 @@ CASES = [
     ("fp4_multi", O.MXFP4, 2, 2, 64, 128, 20000, 4, 1024, "last"),
     ("fp4_short", O.MXFP4, 2, 3, 64, 128, 5000, 4, 1024, "ragged"),  # n(t) < k: padding
     ("f32_128", O.F32, 1, 5, 8, 128, 700, 1, 33, "ragged"),
+    # slices of 1024 keys and more, ragged positions
+    ("fp4_wide_slices_ragged", O.MXFP4, 2, 3, 64, 128, 40000, 4, 1024, "ragged"),
+    ("bf16_wide_slices_ragged", O.BF16, 1, 4, 16, 128, 60000, 4, 512, "ragged"),
 ]
 
 
@@ -75,7 +78,7 @@ def test_index_topk_parity(gpu, case):
     print("case %s: %s" % (case[0], st))
 
 
-@pytest.mark.parametrize("N,k", [(3000, 100), (30000, 1024)])
+@pytest.mark.parametrize("N,k", [(3000, 100), (30000, 1024), (200000, 1024)])
 def test_index_topk_ties_take_the_smallest_indices(gpu, N, k):
     # every key identical -> every score ties -> the first k indices win (the larger
     # case leaves more tied candidates than the split path's filter keeps in LDS, so
@@ -92,11 +95,12 @@ def test_index_topk_ties_take_the_smallest_indices(gpu, N, k):
     assert np.array_equal(host(gi)[0, 1], np.arange(k))
 
 
-def test_index_topk_clustered_scores_refine_the_threshold(gpu):
+@pytest.mark.parametrize("N", [40000, 200000])
+def test_index_topk_clustered_scores_refine_the_threshold(gpu, N):
     # keys = one shared key + 1% noise: nearly every score lands in the same top-11-bit
     # bin, more candidates than the split path's filter keeps in LDS, so the row select
-    # refines the threshold with the next digits
-    B, Tq, H_I, d_I, N, k = 1, 2, 16, 128, 40000, 1024
+    # refines the threshold with the next digits (N = 200000: slices of 2048 keys)
+    B, Tq, H_I, d_I, k = 1, 2, 16, 128, 1024
     base = gen.normal((1, 1, d_I), 21)
     keys = base.expand(B, N, d_I) + 0.01 * gen.normal((B, N, d_I), 22)
     q = gen.normal((B, Tq, H_I, d_I), 23)
@@ -161,6 +165,47 @@ def test_index_topk_is_deterministic(gpu):
     b = ops.index_topk(*args, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_index_topk_calls_in_a_row(gpu):
+    # Calls in a row on one workspace -- ragged positions, no visible entry at all, other
+    # positions, the first ones again -- each match the oracle (the repeat bit for bit):
+    # nothing a call leaves in the workspace changes the next one's result.
+    B, Tq, H_I, d_I, N, m, k = 2, 3, 64, 128, 50000, 4, 1024
+    qc, qs = gen.random_mxfp4(B * Tq * H_I, d_I, 51)
+    kc, ks = gen.random_mxfp4(B * N, d_I, 52)
+    qc, qs = qc.reshape(B, Tq, H_I, -1), qs.reshape(B, Tq, H_I, -1)
+    kc, ks = kc.reshape(B, N, -1), ks.reshape(B, N, -1)
+    w = gen.normal((B, Tq, H_I), 53, 1 / math.sqrt(H_I))
+    kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
+    oq = dict(qi_scales=host(qs), ki_scales=host(ks))
+    qd = BF.decode(host(qc), BF.MXFP4, d_I, scales=host(qs)).reshape(B, Tq, H_I, d_I)
+    kd = BF.decode(host(kc), BF.MXFP4, d_I, scales=host(ks)).reshape(B, N, d_I)
+    bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
+    rng = np.random.default_rng(54)
+    ragged = rng.integers(0, N * m + 40, size=(B, Tq)).astype(np.int32)
+    ragged[0, 1] = 3 * 16384 * m - 1                          # ends on a slice boundary of some plans
+    other = rng.integers(0, N * m, size=(B, Tq)).astype(np.int32)
+    empty = np.full((B, Tq), 1, np.int32)                     # t < m - 1: nothing visible
+    first = None
+    for n, p in enumerate([ragged, empty, other, ragged]):
+        qpos = torch.from_numpy(p)
+        gi, gs = ops.index_topk(dev(qc), dev(w), dev(kc), dev(qpos), fmt=O.MXFP4, k=k, qi_scales=dev(qs),
+                                ki_scales=dev(ks), **kw)
+        torch.cuda.synchronize()
+        gi_h, gs_h = host(gi), host(gs)
+        if n == 1:
+            assert np.all(gi_h == -1) and np.all(np.isneginf(gs_h))
+            continue
+        if n == 3:
+            assert np.array_equal(gi_h, first[0]) and np.array_equal(gs_h, first[1])
+            continue
+        oi, _ = O.index_topk(host(qc), O.MXFP4, host(w), host(kc), O.MXFP4, p, k=k, **kw, **oq)
+        allsc = oracle_all_scores(host(qc), O.MXFP4, host(w), host(kc), O.MXFP4, p, **kw, **oq)
+        st = check_topk(gi_h, gs_h, oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
+        print("call %d: %s" % (n, st))
+        if n == 0:
+            first = (gi_h, gs_h)
 
 
 DENSE_CASES = [
