@@ -406,7 +406,8 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
                       const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
                       const Paged* pg,
                       const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
-                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, bool use_scratch, void* stream) {
+                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, bool use_scratch, void* stream,
+                      const csl::CompressArgs* kvj = nullptr, const csl::CompressArgs* keyj = nullptr) {
     if (B < 0 || Tq < 0 || n_cap < 0) return fail(CSL_EINVAL, "%s: negative size", fn);
     if (B > 65535 || Tq > 65535) return fail(CSL_EUNSUPPORTED, "%s: B and Tq must be <= 65535", fn);
     if (m < 1) return fail(CSL_EINVAL, "%s: m must be >= 1", fn);
@@ -473,10 +474,53 @@ static int index_impl(const char* fn, const void* qi, int qi_fmt, const uint8_t*
         a.hist = (uint32_t*)((uint8_t*)ws + 4 * nr);
         a.seg_cnt = (int32_t*)(a.hist + q * nslices * csl::IDX_SLOT_W);
     }
-    return launched(csl::launch_index_topk(a, (hipStream_t)stream));
+    const hipStream_t s = (hipStream_t)stream;
+    if (kvj) {
+        // csa_index_step: the compression runs inside the scoring kernel when the key job
+        // writes exactly the keys this call reads and the shapes are the fused ones;
+        // otherwise the compression launch, then the index launch
+        const csl::CompressArgs& kj = *keyj;
+        const bool mx = ki_fmt == CSL_MXFP4;
+        const bool same_keys = kj.out == (const uint8_t*)ki && kj.out_fmt == ki_fmt && kj.d == d_I && kj.m == m &&
+            (mx ? kj.out_scales == ki_scales : true) &&
+            (pg ? (kj.bt == pg->bt && kj.bt_stride == pg->bt_stride && kj.epb == pg->epb &&
+                   kj.blk_bytes == pg->blk_bytes && kj.n_blocks == pg->n_blocks && (!mx || kj.sblk_bytes == pg->sblk_bytes))
+                : (!kj.bt && kj.out_bstride == ki_bstride && (!mx || kj.sc_bstride == ks_bstride)));
+        csl::IndexPre pre{*kvj, kj, 0, 0};
+        if (Tq == 1 && !dense && nslices > 1 && d_I == 128 && (mx || ki_fmt == CSL_BF16) && same_keys &&
+            csl::compress_pair_in_index(*kvj, kj, pre.gz_kv, pre.gz_key))
+            return launched(csl::launch_index_topk(a, s, &pre));
+        const hipError_t e = csl::launch_compress_pair(*kvj, kj, s);
+        if (e != hipSuccess) return launched(e);
+    }
+    return launched(csl::launch_index_topk(a, s));
 }
 
 extern "C" {
+
+int csa_index_step(const csl_compress_job* kv_job, const csl_compress_job* key_job,
+                   const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                   const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                   const int32_t* block_table, int64_t bt_stride, int entries_per_block, int64_t block_bytes,
+                   int64_t scale_block_bytes, int64_t n_blocks,
+                   const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa_index_step";
+    if (!kv_job || !key_job) return fail(CSL_EINVAL, "%s: null job", fn);
+    csl::CompressArgs a0, a1;
+    int rc = step_job(fn, *kv_job, q_pos, B, Tq, a0);
+    if (rc) return rc;
+    rc = step_job(fn, *key_job, q_pos, B, Tq, a1);
+    if (rc) return rc;
+    Paged pg;
+    if (block_table) {
+        pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+        pg.sblk_bytes = scale_block_bytes; pg.n_blocks = n_blocks;
+    }
+    return index_impl(fn, qi, qi_fmt, qi_scales, w, ki, ki_fmt, ki_scales, block_table ? 0 : ki_bstride,
+                      block_table ? 0 : ks_bstride, block_table ? &pg : nullptr, q_pos, B, Tq, H_I, d_I, m, n_cap, k,
+                      out_idx, out_score, ws, ws_bytes, false, stream, &a0, &a1);
+}
 
 int index_topk(const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
                const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,

@@ -30,6 +30,7 @@
 //  * Many queries (prefill): k_idx_dense_score scores 12 queries per block against
 //    LDS-staged key tiles with bf16 MFMA, writes every score key and a per-query
 //    histogram; k_idx_dense_select selects per query.
+#include "compress_dec.h"
 #include "device.h"
 #include "launch.h"
 
@@ -358,9 +359,19 @@ __host__ __device__ constexpr int64_t idx_row_bytes(int DI) {
 constexpr int SLOT_W = IDX_SLOT_W;
 constexpr int MAX_SLICES_PER_ROW = 1024;
 static_assert(SLOT_W >= TOPK_BINS + 1 && TOPK_BINS % IDX_NT == 0, "slice lists: whole bins per scoring thread");
-template <int FMT, int DI, int HB, bool SPLIT>
+//
+// PRE = true (several slices, one query per sequence): the kernel also runs the layer's
+// decode-time compression.  The indexer key of the entry the token completes is
+// compressed by waves 0 .. gz_key-1 of the block whose slice holds that entry, which
+// then join the scoring; that block takes the key's tile group last, and the wave that
+// loads it first waits (on an LDS count) until every key wave's stores are complete --
+// long since, unless the slice is short.  The KV entry's gz_kv channel parts are spread
+// one wave each over the blocks (from their last wave down), which also compress first
+// and then score (nothing in this kernel reads the KV entry).
+template <int FMT, int DI, int HB, bool SPLIT, bool PRE>
 __global__ void __launch_bounds__(IDX_NT) __attribute__((amdgpu_waves_per_eu(FMT == MXFP4 ? 4 : 2, 8)))
-k_idx_score(IndexArgs a) {
+k_idx_score(IndexArgs a, IndexPre pre) {
+    static_assert(!PRE || (SPLIT && FMT != F32), "compression runs on the several-slice path, MXFP4 or bf16 keys");
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     // the slices of one query run on one XCD (logical ids in XCD groups), the one its
     // select block and its attention blocks also map to: their reads of the slices'
@@ -383,11 +394,22 @@ k_idx_score(IndexArgs a) {
     const int64_t n = n_visible(t, a.m, a.n_cap);
     const int64_t s0 = (int64_t)sl * a.S;
     const int ns = (int)(n - s0 < 0 ? 0 : (n - s0 > a.S ? a.S : n - s0));
+    int64_t kv_job = -1;                                 // PRE: this wave's part of the KV entries
+    if constexpr (PRE) {
+        const int64_t jk = (int64_t)lg + (int64_t)nblk * (IDX_NT / 64 - 1 - wv);
+        kv_job = jk < (int64_t)a.B * pre.gz_kv ? jk : -1;
+    }
     if constexpr (SPLIT) {
-        if (ns <= 0) return;
+        if (ns <= 0) {
+            if constexpr (PRE) {
+                if (kv_job >= 0)
+                    compress_dec_body<KV_PACKED>(pre.kv, 0, (int)(kv_job / pre.gz_kv), (int)(kv_job % pre.gz_kv), pre.gz_kv);
+            }
+            return;
+        }
         for (int x = tid; x < TOPK_HSZ; x += IDX_NT) hs[x] = 0u;
     }
-    if (tid == 0) *ctr = 0u;
+    if (tid == 0) { ctr[0] = 0u; ctr[1] = 0u; }        // next tile group; PRE: key waves done
     // paged keys: the block ids of the slice's keys (a 16-key tile lies in one block)
     const int64_t blk0 = a.bt ? s0 / a.epb : 0;
     if (a.bt && ns > 0) {
@@ -397,7 +419,23 @@ k_idx_score(IndexArgs a) {
             ids[x] = (v >= 0 && v < a.n_blocks) ? v : -1;
         }
     }
+    // PRE: the entry e this token completes; the block compresses its key if e is visible
+    // and in this block's slice (its tile group: ge)
+    int ge = -1;
+    if constexpr (PRE) {
+        const int64_t e = (t + 1) / a.m - 1;
+        if (t >= 0 && (t + 1) % a.m == 0 && e < a.n_cap && e / a.S == sl) ge = (int)((e - s0) / (16 * IDX_UNR));
+    }
     __syncthreads();
+    if constexpr (PRE) {
+        if (ge >= 0 && wv < pre.gz_key) {
+            compress_dec_body<FMT>(pre.key, 0, b, wv, pre.gz_key);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the key's stores are complete ...
+            if (lane == 0) atomicAdd(&ctr[1], 1u);             // ... before this wave counts itself
+        }
+        if (kv_job >= 0)
+            compress_dec_body<KV_PACKED>(pre.kv, 0, (int)(kv_job / pre.gz_kv), (int)(kv_job % pre.gz_kv), pre.gz_kv);
+    }
 
     if (ns > 0) {
         // q fragments (A operand: rows = heads) and head weights, kept in registers
@@ -469,11 +507,18 @@ k_idx_score(IndexArgs a) {
         // multiples of the channel interleave) and crowd the same HBM channels.  Block
         // i of nb therefore takes its groups in the rotated order starting at group
         // i*ngr/nb.
-        const int rot = (int)(((uint64_t)lin * (uint64_t)ngr) / nblk);
+        // (PRE: the block that compressed the new key takes its group ge last)
+        const int rot = ge >= 0 ? (ge + 1 < ngr ? ge + 1 : 0) : (int)(((uint64_t)lin * (uint64_t)ngr) / nblk);
         auto rotg = [&](int j) { return j + rot < ngr ? j + rot : j + rot - ngr; };
         KeyFrag<FMT, DI> fa[IDX_UNR], fb[IDX_UNR];
         auto load_grp = [&](int j, KeyFrag<FMT, DI>(&f)[IDX_UNR]) {
             j = rotg(j < ngr ? j : ngr - 1);
+            if constexpr (PRE) {
+                if (j == ge)                             // the new key: wait for its writers
+                    while (__hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                           (uint32_t)pre.gz_key)
+                        __builtin_amdgcn_s_sleep(1);
+            }
 #pragma unroll
             for (int u = 0; u < IDX_UNR; ++u) load_tile(IDX_UNR * j + u, f[u]);
         };
@@ -1254,14 +1299,23 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
-template <int FMT, int DI, int HB, bool SPLIT>
-static void launch_score(const IndexArgs& a, hipStream_t s) {
+template <int FMT, int DI, int HB, bool SPLIT, bool PRE = false>
+static void launch_score(const IndexArgs& a, hipStream_t s, const IndexPre* pre = nullptr) {
     const int E = a.S / IDX_NT;
     const size_t nid = a.bt ? (size_t)a.S / 16 + 2 : 0;                                         // paged: block ids
     const size_t lds = SPLIT ? sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_HSZ + 32 + nid)   // keys, histogram, scan, misc, counter
                              : sizeof(uint32_t) * ((size_t)a.S + a.S / E + TOPK_SCRATCH(IDX_NT) + 4 + nid);   // keys, scratch, counter
     dim3 grid((unsigned)a.nslices, (unsigned)a.Tq, (unsigned)a.B);
-    hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT>), grid, dim3(IDX_NT), lds, s, a);
+    hipLaunchKernelGGL((k_idx_score<FMT, DI, HB, SPLIT, PRE>), grid, dim3(IDX_NT), lds, s, a, pre ? *pre : IndexPre{});
+}
+
+// several slices with the layer's compression (MXFP4 or bf16 d_I = 128 keys)
+template <int FMT>
+static void launch_score_pre(const IndexArgs& a, hipStream_t s, const IndexPre* pre) {
+    const int hb = (a.H_I + 15) / 16;
+    if (hb <= 1) launch_score<FMT, 128, 1, true, true>(a, s, pre);
+    else if (hb <= 4) launch_score<FMT, 128, 4, true, true>(a, s, pre);
+    else launch_score<FMT, 128, 8, true, true>(a, s, pre);
 }
 
 template <int FMT, int DI, bool SPLIT>
@@ -1308,8 +1362,17 @@ static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
     return hipSuccess;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s) {
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s, const IndexPre* pre) {
     if (a.B <= 0 || a.Tq <= 0) return hipSuccess;
+    if (pre) {
+        // the caller has checked: one query per sequence, several slices, d_I = 128,
+        // MXFP4 or bf16 keys written by the key job
+        if (a.ki_fmt == MXFP4) launch_score_pre<MXFP4>(a, s, pre);
+        else launch_score_pre<BF16>(a, s, pre);
+        hipLaunchKernelGGL(k_idx_split_select, dim3((unsigned)a.Tq, (unsigned)a.B), dim3(DSEL_NT),
+                           sel_lds() + sizeof(int) * MAX_SLICES_PER_ROW, s, a);
+        return hipGetLastError();
+    }
     if (a.dense) return launch_dense(a, s);
     if (a.nslices == 1) {
         launch_fmt<false>(a, s);

@@ -81,9 +81,17 @@ struct GprojArgs {
     uint8_t* out; int out_fmt;   // [M][G*R], F32 or BF16
 };
 
+// A CSA layer's decode-time compression jobs (its KV entry, its indexer key) run by the
+// indexer's scoring kernel before it scores (channel splits gz_kv, gz_key).
+struct IndexPre {
+    CompressArgs kv, key;
+    int gz_kv, gz_key;
+};
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t s);
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+bool compress_pair_in_index(const CompressArgs& kv, const CompressArgs& key, int& gz_kv, int& gz_key);
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s, const IndexPre* pre = nullptr);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_grouped_out_proj(const GprojArgs& a, hipStream_t s);
 

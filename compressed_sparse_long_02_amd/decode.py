@@ -93,9 +93,8 @@ def _pages(c, bt: Optional[BlockTable]):
 
 
 # ---- CSA ------------------------------------------------------------------------------
-def csa_compress(c: CsaCache, q_pos: torch.Tensor, bt: Optional[BlockTable] = None):
-    """Step 1: the KV entries and indexer keys the new tokens (positions q_pos int32 [B, T])
-    complete, pooled from the rings (window 2m, overlapping) into the cache."""
+def _csa_jobs(c: CsaCache, bt: Optional[BlockTable]):
+    """The compression jobs of a CSA layer: its KV entries and its indexer keys."""
     kv = dict(x_ring=c.kv_ring.raw, x_fmt=ops.BF16, z_ring=c.kv_ring.z, bias=c.kv_ring.bias, d=c.d, r=c.r, m=c.m,
               overlap=True, out_fmt=ops.KV_PACKED, x_roles=c.kv_ring.roles)
     key = dict(x_ring=c.key_ring.raw, x_fmt=ops.BF16, z_ring=c.key_ring.z, bias=c.key_ring.bias, d=c.d_I, m=c.m,
@@ -108,6 +107,13 @@ def csa_compress(c: CsaCache, q_pos: torch.Tensor, bt: Optional[BlockTable] = No
         kv.update(out=c.pool, pages=pg)
         key.update(out=c.pool[:, c.key_off:], pages=pg,
                    out_scales=c.pool[:, c.scale_off:] if c.key_fmt == ops.MXFP4 else None)
+    return kv, key
+
+
+def csa_compress(c: CsaCache, q_pos: torch.Tensor, bt: Optional[BlockTable] = None):
+    """Step 1: the KV entries and indexer keys the new tokens (positions q_pos int32 [B, T])
+    complete, pooled from the rings (window 2m, overlapping) into the cache."""
+    kv, key = _csa_jobs(c, bt)
     ops.kv_compress_step_pair(kv, key, q_pos)
 
 
@@ -121,6 +127,20 @@ def csa_select(c: CsaCache, q_pos, qi, w, *, H_I, k, qi_scales=None, out_idx=Non
         return ops.index_topk(qi, w, c.keys, q_pos, ki_scales=c.key_scales, **kw)
     return ops.index_topk(qi, w, c.pool[:, c.key_off:], q_pos, pages=_pages(c, bt),
                           ki_scales=c.pool[:, c.scale_off:] if c.key_fmt == ops.MXFP4 else None, **kw)
+
+
+def csa_compress_select(c: CsaCache, q_pos, qi, w, *, H_I, k, qi_scales=None, out_idx=None, with_scores=False,
+                        bt: Optional[BlockTable] = None):
+    """Steps 1 and 2 through one call (csa_index_step): the compression of the completed
+    entries, then the top-k; with one query per sequence the compression runs inside the
+    indexer's scoring kernel."""
+    kv, key = _csa_jobs(c, bt)
+    kw = dict(fmt=c.key_fmt, H_I=H_I, d_I=c.d_I, m=c.m, n_cap=c.n_cap, k=k, qi_scales=qi_scales, out_idx=out_idx,
+              with_scores=with_scores)
+    if bt is None:
+        return ops.csa_index_step(kv, key, qi, w, c.keys, q_pos, ki_scales=c.key_scales, **kw)
+    return ops.csa_index_step(kv, key, qi, w, c.pool[:, c.key_off:], q_pos, pages=_pages(c, bt),
+                              ki_scales=c.pool[:, c.scale_off:] if c.key_fmt == ops.MXFP4 else None, **kw)
 
 
 def csa_attend(c: CsaCache, q, idx, q_pos, *, H, W, scale, out=None, out_fmt=ops.BF16, with_lse=False, sink=None,
@@ -138,8 +158,7 @@ def csa_attend(c: CsaCache, q, idx, q_pos, *, H, W, scale, out=None, out_fmt=ops
 def csa_decode_step(c: CsaCache, q_pos, q, qi, w, *, H, H_I, k, W, scale, idx, out, qi_scales=None, sink=None,
                     bt: Optional[BlockTable] = None):
     """One CSA layer for the new tokens: compress, select, attend (out [B, T, H, d] bf16)."""
-    csa_compress(c, q_pos, bt)
-    csa_select(c, q_pos, qi, w, H_I=H_I, k=k, qi_scales=qi_scales, out_idx=idx, bt=bt)
+    csa_compress_select(c, q_pos, qi, w, H_I=H_I, k=k, qi_scales=qi_scales, out_idx=idx, bt=bt)
     csa_attend(c, q, idx, q_pos, H=H, W=W, scale=scale, out=out, sink=sink, bt=bt)
     return out
 

@@ -204,6 +204,43 @@ def index_topk(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, 
     return out_idx, out_score
 
 
+def csa_index_step(kv, key, qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None,
+                   out_idx=None, out_score=None, with_scores=True, pages=None):
+    """A CSA layer's compression (kv and key: dicts of kv_compress_step's keyword arguments
+    plus x_ring, x_fmt, z_ring and bias, as for kv_compress_step_pair) and its index_topk,
+    in that order, the compression inside the indexer's scoring kernel where the shapes
+    allow.  q_pos int32 [B, Tq] is also the jobs' token positions; the other arguments and
+    the results are index_topk's."""
+    _need_cuda(qi, w, ki, q_pos, qi_scales, ki_scales)
+    j0, j1 = _step_job(**kv), _step_job(**key)
+    B, Tq = q_pos.shape
+    _check_pos(q_pos, B)
+    if not qi.is_contiguous() or not w.is_contiguous() or w.dtype != torch.float32:
+        raise ValueError("qi and w must be contiguous (w float32)")
+    if pages is None:
+        _rows_ok(ki, row_bytes(fmt, d_I), "ki")
+    dev = q_pos.device
+    if out_idx is None:
+        out_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    if with_scores and out_score is None:
+        out_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    nb = int(_lib.lib().csl_index_topk_workspace(B, Tq, n_cap, k))
+    ws = workspace(nb, dev)
+    wsn = 0 if ws is None else ws.numel()
+    if pages is None:
+        bt, bts, epb, blk, sblk, nblk = None, 0, 0, 0, 0, 0
+        kbs, sbs = _bstride(ki), (_bstride(ki_scales) if ki_scales is not None else 0)
+    else:
+        bt, epb, blk, sblk, nblk = pages
+        _check_table(bt)
+        bts, kbs, sbs = bt.shape[1], 0, 0
+    rc = _lib.lib().csa_index_step(C.byref(j0), C.byref(j1), _ptr(qi), fmt, _ptr(qi_scales), _ptr(w), _ptr(ki), fmt,
+                                   _ptr(ki_scales), kbs, sbs, _ptr(bt), bts, epb, blk, sblk, nblk, _ptr(q_pos), B, Tq,
+                                   H_I, d_I, m, n_cap, k, _ptr(out_idx), _ptr(out_score), _ptr(ws), wsn, _stream())
+    check("csa_index_step", rc)
+    return out_idx, out_score
+
+
 def index_topk_noalloc(qi, w, ki, q_pos, *, fmt, H_I, d_I, m, n_cap, k, qi_scales=None, ki_scales=None,
                        out_idx, out_score=None):
     """index_topk through the entry point that allocates nothing: the caller passes the

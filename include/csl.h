@@ -206,6 +206,31 @@ int index_topk_paged(const void* qi, int qi_fmt, const uint8_t* qi_scales, const
                      int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_index_step -- a CSA layer's decode step up to the selection: the compression of
+ * the entries the new tokens complete ([X] section 2, CSA step 1: the KV entry and, by
+ * the indexer's own compressor, its key) followed by the lightning indexer's top-k over
+ * every complete key, the new one included ([X] section 2, CSA step 2).  The results
+ * are those of kv_compress_step_pair(kv_job, key_job, q_pos, B, Tq) followed by
+ * index_topk (block_table NULL: keys at ki + b*ki_bstride, scales at ki_scales +
+ * b*ks_bstride) or index_topk_paged (block_table given, with its geometry), on the same
+ * stream; every argument means what it means there, q_pos doubling as the jobs' token
+ * positions.  The key job should write the keys this call reads; the KV job's output
+ * must not overlap the keys or their scales.  With one query per sequence, entries
+ * spanning several scoring blocks, d_I = 128 MXFP4 or bf16 keys that the key job writes
+ * in place, and the one-wave compression shapes (bf16 rings, one logit per token), the
+ * compression runs inside the indexer's scoring kernel (one launch fewer); otherwise it
+ * is launched first.  Workspace: csl_index_topk_workspace(B, Tq, n_cap, k).  Both jobs
+ * and the index arguments are checked before anything is launched.
+ */
+int csa_index_step(const csl_compress_job* kv_job, const csl_compress_job* key_job,
+                   const void* qi, int qi_fmt, const uint8_t* qi_scales, const float* w,
+                   const void* ki, int ki_fmt, const uint8_t* ki_scales, int64_t ki_bstride, int64_t ks_bstride,
+                   const int32_t* block_table, int64_t bt_stride, int entries_per_block, int64_t block_bytes,
+                   int64_t scale_block_bytes, int64_t n_blocks,
+                   const int32_t* q_pos, int B, int Tq, int H_I, int d_I, int m, int64_t n_cap, int k,
+                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * index_topk_noalloc -- index_topk for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments and results as index_topk, without the workspace

@@ -202,3 +202,27 @@ def test_grouped_out_proj_rejects_bad_arguments_on_the_host():
     assert call(x=None) == _lib.CSL_EINVAL
     assert call(out_fmt=2) == _lib.CSL_EINVAL
     assert call(M=0) == _lib.CSL_OK
+
+
+def test_csa_index_step_checks_both_jobs_and_the_index_on_the_host():
+    L = _lib.lib()
+    job = dict(x_ring=16, x_fmt=1, x_roles=1, x_bstride=0, x_rows=16, z_ring=16, z_ch=1, z_bstride=0, bias=16, d=512,
+               r=64, m=4, overlap=1, out=16, out_fmt=2, out_scales=None, out_bstride=0, sc_bstride=0, n_cap=100,
+               block_table=None, bt_stride=0, entries_per_block=0, block_bytes=0, scale_block_bytes=0, n_blocks=0)
+    key = dict(job, d=128, r=0, out_fmt=3, out_scales=16)
+
+    def call(kv=job, ky=key, **over):
+        a = dict(qi=16, qi_fmt=3, qi_scales=16, w=16, ki=16, ki_fmt=3, ki_scales=16, ki_bstride=0, ks_bstride=0,
+                 block_table=None, bt_stride=0, entries_per_block=0, block_bytes=0, scale_block_bytes=0, n_blocks=0,
+                 q_pos=16, B=1, Tq=1, H_I=64, d_I=128, m=4, n_cap=100, k=64, out_idx=16, out_score=None, ws=None,
+                 ws_bytes=0, stream=None)
+        a.update(over)
+        j0 = _lib.CompressJob(**kv) if kv is not None else None
+        j1 = _lib.CompressJob(**ky) if ky is not None else None
+        return L.csa_index_step(C.byref(j0) if j0 else None, C.byref(j1) if j1 else None, *a.values())
+
+    assert call(kv=None) == _lib.CSL_EINVAL                          # a job is missing
+    assert call(kv=dict(job, x_rows=4)) == _lib.CSL_EINVAL           # the KV window is not in the ring
+    assert call(ky=dict(key, out_scales=None)) == _lib.CSL_EINVAL    # MXFP4 key without scales
+    assert call(k=0) == _lib.CSL_EUNSUPPORTED                        # the index arguments too
+    assert call(qi_fmt=1) == _lib.CSL_EUNSUPPORTED                   # qi and keys in different formats

@@ -25,6 +25,7 @@ import pytest
 import torch
 
 import oracle as O
+from compressed_sparse_long_02_amd import decode as D
 from compressed_sparse_long_02_amd import gen, ops, workloads
 from tests import bruteforce as BF
 from tests.gpu_util import cap, check_topk, close_quantised, dev, host, max_abs, oracle_all_scores, score_error_bound
@@ -99,6 +100,53 @@ def test_stack_compress_of_the_completed_entries(gpu, layout, request):
     ref, _ = O.kv_compress(h(hca["raw"]), O.BF16, h(hca["z"]), host(hca["bias"]), d=st.d, r=st.r, m=st.mh,
                            overlap=False, e_begin=ih, n_e=1, out_fmt=O.KV_PACKED, **ring)
     close_quantised(h(st.entries(hca)[:, ih:ih + 1]), ref, O.KV_PACKED, st.d, st.r, max_mismatch=len(SAMPLE))
+
+
+def _new_rows(st, c, i, zero=False):
+    """The packed KV entry, indexer key and key scales of entry i of every sequence, as
+    copies; zero=True clears them in the cache instead."""
+    kb, sb = c.d_I // 2, c.d_I // 32
+    if c.pool is None:
+        views = [c.entries[:, i], c.keys[:, i], c.key_scales[:, i]]
+        if zero:
+            for v in views:
+                v.zero_()
+            return None
+        return [v.clone() for v in views]
+    epb, erb = c.entries_per_block, st.rb
+    blk, off = st.bt[:, i // epb].long(), i % epb
+    spans = [(off * erb, (off + 1) * erb), (c.key_off + off * kb, c.key_off + (off + 1) * kb),
+             (c.scale_off + off * sb, c.scale_off + (off + 1) * sb)]
+    if zero:
+        for a, b in spans:
+            c.pool[blk, a:b] = 0
+        return None
+    return [c.pool[blk, a:b].clone() for a, b in spans]
+
+
+@pytest.mark.parametrize("layout", ["linear", "paged"])
+def test_stack_compress_inside_index_equals_separate_launches(gpu, layout, request):
+    """csa_index_step at the 1M stack shape (the compression inside the indexer's scoring
+    kernel) writes the same KV entry, indexer key and scales, and selects the same
+    entries with the same scores, as kv_compress_step_pair followed by index_topk: each
+    path runs on a cache whose new rows were cleared first."""
+    st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
+    L = st.layers[0]
+    c = L["dc"]
+    i = (st.t + 1) // st.m - 1
+    kw = dict(H_I=st.HI, k=st.k, qi_scales=L["qis"], with_scores=True, bt=st.btab)
+    _new_rows(st, c, i, zero=True)
+    D.csa_compress(c, st.q_pos, st.btab)
+    gi0, gs0 = D.csa_select(c, st.q_pos, L["qi"], L["w"], **kw)
+    rows0 = _new_rows(st, c, i)
+    _new_rows(st, c, i, zero=True)
+    gi1, gs1 = D.csa_compress_select(c, st.q_pos, L["qi"], L["w"], **kw)
+    rows1 = _new_rows(st, c, i)
+    torch.cuda.synchronize()
+    assert all(bool(torch.any(r != 0)) for r in rows0)
+    for a, b in zip(rows0, rows1):
+        assert torch.equal(a, b)
+    assert torch.equal(gi0, gi1) and torch.equal(gs0, gs1)
 
 
 @pytest.mark.parametrize("layout", ["linear", "paged"])

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle as O
+from compressed_sparse_long_02_amd import decode as D
 from compressed_sparse_long_02_amd import gen, ops
 from tests import bruteforce as BF
 from tests.gpu_util import cap, check_topk, dev, host, oracle_all_scores, score_error_bound
@@ -309,3 +310,69 @@ def test_index_topk_mxfp4_wide_block_scales(gpu):
     bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
     st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
     print("wide scales: %s" % st)
+
+
+@pytest.mark.parametrize("key_fmt", [O.MXFP4, O.BF16])
+def test_csa_index_step_compresses_before_it_scores(gpu, key_fmt):
+    # csa_index_step with one query per sequence and several slices per query compresses
+    # inside the indexer's scoring kernel: the block whose slice holds the new entry writes
+    # its key before any of its waves scores it.  With k >= n(t) every visible entry is
+    # selected, so the new key's score is in the output: a stale (cleared) key would score
+    # 0 there.  Positions: entries completing mid-cache, at the cache's last row, past
+    # n_cap (not stored, not visible) and a token completing nothing.
+    B, d, r, m, d_I, H_I, N, k, R = 4, 512, 64, 4, 128, 64, 1500, 2048, 16
+    t = np.array([4 * 1400 - 1, 4 * 1000 - 2, 4 * N - 1, 4 * N + 7], np.int32)
+    q_pos = dev(torch.from_numpy(t[:, None].copy()))
+    kv_ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d), 61))), dev(gen.random_logits((B, R, 1), 62)),
+                     dev(gen.random_logits((2 * m, 1), 63)))
+    key_ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d_I), 64, 1 / math.sqrt(d_I)))),
+                      dev(gen.random_logits((B, R, 1), 65)), dev(gen.random_logits((2 * m, 1), 66)))
+    rb = ops.row_bytes(O.KV_PACKED, d, r)
+    entries = dev(gen.store(gen.normal((B, N, d), 67), O.KV_PACKED, r))
+    if key_fmt == O.MXFP4:
+        kc, ks = gen.random_mxfp4(B * N, d_I, 68)
+        keys, kscales = dev(kc.reshape(B, N, -1)), dev(ks.reshape(B, N, -1))
+        qc, qs = gen.random_mxfp4(B * H_I, d_I, 69)
+        qi, qis = dev(qc.reshape(B, 1, H_I, -1)), dev(qs.reshape(B, 1, H_I, -1))
+    else:
+        keys, kscales = dev(gen.store(gen.normal((B, N, d_I), 68, 1 / math.sqrt(d_I)), O.BF16)), None
+        qi, qis = dev(gen.store(gen.normal((B, 1, H_I, d_I), 69, 1 / math.sqrt(d_I)), O.BF16)), None
+    w = dev(gen.normal((B, 1, H_I), 70, 1 / math.sqrt(H_I)))
+    c = D.CsaCache(d=d, r=r, m=m, d_I=d_I, key_fmt=key_fmt, n_cap=N, kv_ring=kv_ring, key_ring=key_ring,
+                   window=dev(torch.zeros((B, 128, rb), dtype=torch.uint8)), entries=entries, keys=keys,
+                   key_scales=kscales)
+    new = [(b, int(t[b] + 1) // m - 1) for b in range(B) if (t[b] + 1) % m == 0 and (t[b] + 1) // m - 1 < N]
+
+    def clear():
+        for b, i in new:
+            entries[b, i].zero_()
+            keys[b, i].zero_()
+            if kscales is not None:
+                kscales[b, i].zero_()
+
+    def snap():
+        return [x.clone() for x in (entries, keys) + ((kscales,) if kscales is not None else ())]
+
+    kw = dict(H_I=H_I, k=k, qi_scales=qis, with_scores=True)
+    clear()
+    D.csa_compress(c, q_pos)
+    gi0, gs0 = D.csa_select(c, q_pos, qi, w, **kw)
+    torch.cuda.synchronize()
+    s0 = snap()
+    clear()
+    gi1, gs1 = D.csa_compress_select(c, q_pos, qi, w, **kw)
+    torch.cuda.synchronize()
+    s1 = snap()
+    for a, b_ in zip(s0, s1):
+        assert torch.equal(a, b_)
+    assert torch.equal(gi0, gi1) and torch.equal(gs0, gs1)
+    gi_h, gs_h = host(gi1), host(gs1)
+    for b, i in new:
+        assert bool(torch.any(keys[b, i] != 0))
+        n = i + 1
+        assert np.array_equal(gi_h[b, 0, :n], np.arange(n)) and np.all(gi_h[b, 0, n:] == -1)
+        # the new key's score from the oracle on the stored bytes
+        oq = dict(qi_scales=host(qis[b:b + 1]), ki_scales=host(kscales[b:b + 1])) if qis is not None else {}
+        allsc = oracle_all_scores(host(qi[b:b + 1]), key_fmt, host(w[b:b + 1]), host(keys[b:b + 1]), key_fmt,
+                                  t[b:b + 1, None], H_I=H_I, d_I=d_I, m=m, n_cap=N, **oq)
+        assert abs(gs_h[b, 0, i] - allsc[0, 0, i]) <= 1e-3 * max(1.0, abs(allsc[0, 0, i])), (b, i)
