@@ -54,11 +54,12 @@ INDEX_SOURCES = ["compressed_sparse_long_02_amd/csrc/index_topk.hip", "compresse
                  "compressed_sparse_long_02_amd/csrc/launch.h"]
 
 
-def recorded_traffic(B, ctx):
+def recorded_traffic(B, ctx, layout):
     """HBM bytes per index_topk launch from the committed FETCH_SIZE / WRITE_SIZE summary, when that
-    summary was taken on this workload and the kernel sources are unchanged since; else None."""
+    summary was taken on this workload (linear caches) and the kernel sources are unchanged since;
+    else None."""
     import hashlib
-    if B != 16 or ctx != 1 << 20 or not os.path.exists(COUNTERS):
+    if B != 16 or ctx != 1 << 20 or layout != "linear" or not os.path.exists(COUNTERS):
         return None
     fields = {}
     for line in open(COUNTERS):
@@ -387,7 +388,7 @@ def main():
     ach = ib / (t_idx * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": "index_topk (MXFP4 scores + top-1024 of 262,144 per sequence)",
             "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.batch, args.ctx), "bytes_per_launch": ib, "ms_per_launch": round(t_idx, 4)}
+            "traffic": recorded_traffic(args.batch, args.ctx, args.layout), "bytes_per_launch": ib, "ms_per_launch": round(t_idx, 4)}
     # the indexer's contraction as MFMA work: 2 * H_I * d_I flops per (query, entry), on the
     # scaled FP4 MFMA (dense fp4 peak 10.1 PFLOP/s)
     idx_tf = 2.0 * st.HI * st.dI * st.N * st.B / (t_idx * 1e-3) / 1e12
