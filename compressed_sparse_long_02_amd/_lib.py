@@ -16,7 +16,7 @@ CSL_OK, CSL_EINVAL, CSL_EUNSUPPORTED, CSL_EWORKSPACE, CSL_ELAUNCH, CSL_EDEVICE =
 
 # every symbol include/csl.h declares
 EXPORTS = ["csl_row_bytes", "kv_compress", "kv_compress_step", "kv_compress_step_pair", "index_topk", "index_topk_paged",
-           "csa_index_step",
+           "csa_index_step", "hca_attend_step",
            "csl_index_topk_workspace", "index_topk_noalloc", "csl_noalloc_scratch_bytes", "csa_attend", "hca_attend",
            "csa_attend_paged", "hca_attend_paged", "csl_attend_workspace", "grouped_out_proj", "csl_status_string",
            "csl_last_error", "csl_version"]
@@ -89,6 +89,10 @@ def lib() -> C.CDLL:
     L.hca_attend_paged.restype = i32
     L.hca_attend_paged.argtypes = [vp, i32, vp, i32, vp, i64, i32, i64, i64, i64, i32, vp, i64, i64, i64, vp,
                                    vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, sz, vp]
+    L.hca_attend_step.restype = i32
+    L.hca_attend_step.argtypes = [C.POINTER(CompressJob), vp, i32, vp, i32, i64, vp, i64, i32, i64, i64, i64, i32,
+                                  vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, sz,
+                                  vp]
     L.csl_attend_workspace.restype = sz
     L.csl_attend_workspace.argtypes = [i32, i32, i32, i32, i64]
     L.grouped_out_proj.restype = i32

@@ -566,7 +566,8 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
                        const Paged* pg, int64_t n_cap, const int32_t* idx, int k, int m, const void* kv_w,
                        int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
                        const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale, void* out,
-                       int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+                       int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream,
+                       const csl::CompressArgs* kvj = nullptr) {
     int rc = validate_attend(fn, q, q_fmt, kv_c, kv_fmt, pg ? 0 : kvc_bstride, n_cap, kv_w, kvw_bstride, kvw_rows,
                              q_pos, W, B, Tq, H, d, r, out, out_fmt);
     if (rc) return rc;
@@ -597,7 +598,23 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
         a.ws_o = (float*)ws;
         a.ws_lse = (float*)((uint8_t*)ws + ((rows * d * 4 + 255) & ~(size_t)255));
     }
-    return launched(csl::launch_attend(a, (hipStream_t)stream));
+    const hipStream_t s = (hipStream_t)stream;
+    if (kvj) {
+        // hca_attend_step: the compression runs inside the attention kernel when the job
+        // writes exactly the entries this call reads and the shapes are the fused ones;
+        // otherwise the compression launch, then the attention
+        const csl::CompressArgs& j = *kvj;
+        const bool same = j.out == (const uint8_t*)kv_c && j.out_fmt == kv_fmt && j.d == d && j.r == r && j.m == m &&
+            (pg ? (j.bt == pg->bt && j.bt_stride == pg->bt_stride && j.epb == pg->epb && j.blk_bytes == pg->blk_bytes &&
+                   j.n_blocks == pg->n_blocks)
+                : (!j.bt && j.out_bstride == kvc_bstride));
+        csl::AttendPre pre{j, 0};
+        if (same && csl::attend_takes_pre(a) && csl::compress_in_attend(j, pre.gz))
+            return launched(csl::launch_attend(a, s, &pre));
+        const hipError_t e = csl::launch_compress(j, s);
+        if (e != hipSuccess) return launched(e);
+    }
+    return launched(csl::launch_attend(a, s));
 }
 
 static int csa_check(const char* fn, const int32_t* idx, int k, int B, int Tq) {
@@ -642,6 +659,28 @@ int csa_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, 
     return attend_impl("csa_attend_paged", q, q_fmt, kv_pool, kv_fmt, 0, &pg, n_cap, idx, k, 1, kv_w, kvw_bstride,
                        kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out, out_fmt, out_lse, ws, ws_bytes,
                        stream);
+}
+
+int hca_attend_step(const csl_compress_job* kv_job, const void* q, int q_fmt, const void* kv_c, int kv_fmt,
+                    int64_t kvc_bstride, const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                    int64_t block_bytes, int64_t n_blocks, int64_t n_cap, int m,
+                    const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
+                    const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                    void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "hca_attend_step";
+    if (!kv_job) return fail(CSL_EINVAL, "%s: null job", fn);
+    if (m < 1) return fail(CSL_EINVAL, "%s: m must be >= 1", fn);
+    csl::CompressArgs a0;
+    int rc = step_job(fn, *kv_job, q_pos, B, Tq, a0);
+    if (rc) return rc;
+    Paged pg;
+    if (block_table) {
+        pg.bt = block_table; pg.bt_stride = bt_stride; pg.epb = entries_per_block; pg.blk_bytes = block_bytes;
+        pg.n_blocks = n_blocks;
+    }
+    return attend_impl(fn, q, q_fmt, kv_c, kv_fmt, block_table ? 0 : kvc_bstride, block_table ? &pg : nullptr, n_cap,
+                       nullptr, 0, m, kv_w, kvw_bstride, kvw_pos0, kvw_rows, sink, q_pos, W, B, Tq, H, d, r, scale, out,
+                       out_fmt, out_lse, ws, ws_bytes, stream, &a0);
 }
 
 int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, const int32_t* block_table,

@@ -30,6 +30,7 @@
 // keep fp32 partials.
 #include <type_traits>
 
+#include "compress_dec.h"
 #include "device.h"
 #include "launch.h"
 
@@ -749,8 +750,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D>
-__global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
+// PRE = true (one query per sequence): the split whose rows hold the entry the token
+// completes first compresses that entry into the cache (every wave a channel part of the
+// one-wave compression, its stores complete before the block's first barrier), so the
+// copies of its tiles read the new row.  The compression's loads and stores all complete
+// before the kernel issues its first tile copy, so they take no place in the kernel's
+// counts of copies in flight.
+template <int D, bool PRE>
+__global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a, AttendPre pre) {
     using L = F8Lds<D>;
     constexpr int P = L::P, RS = L::RS, NI = L::NI, NST = F8_NST, RCH = F8_RCH, T = F8_T, R = F8_R;
     constexpr int QK = D / 32;                          // k-steps of S^T (32 dims)
@@ -987,6 +994,15 @@ __global__ void __launch_bounds__(MQ_NT) k_attend_f8(AttendArgs a) {
         }
     };
 
+    if constexpr (PRE) {
+        // the entry e this token completes is row e of the list when it is visible
+        const int64_t e = (t + 1) / a.m - 1;
+        if (t >= 0 && (t + 1) % a.m == 0 && e < a.n_cap && hb == 0 && e / a.rps == sp) {
+            for (int z = wv; z < pre.gz; z += MQ_NT / 64) compress_dec_body<KV_PACKED>(pre.kv, 0, b, z, pre.gz);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    }
+
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1222,14 +1238,16 @@ __global__ void __launch_bounds__(CMB_NT) k_attend_combine(AttendArgs a) {
 }
 
 template <int D, int FMT>
-static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
+static hipError_t launch_att2(const AttendArgs& a, hipStream_t s, const AttendPre* pre) {
     dim3 grid((unsigned)a.nsplit, (unsigned)a.nhb, (unsigned)((int64_t)a.B * a.Tq));
     if (a.idx && a.rps > ATT_MAX_SIDX) return hipErrorInvalidValue;
     if constexpr (FMT == F32) {
         hipLaunchKernelGGL((k_attend<D>), grid, dim3(ATT_NT), 0, s, a);
     } else if constexpr (FMT == KV_PACKED && (D == 256 || D == 512)) {
-        if (a.r == F8_R)
-            hipLaunchKernelGGL((k_attend_f8<D>), grid, dim3(MQ_NT), 0, s, a);
+        if (a.r == F8_R && pre)
+            hipLaunchKernelGGL((k_attend_f8<D, true>), grid, dim3(MQ_NT), 0, s, a, *pre);
+        else if (a.r == F8_R)
+            hipLaunchKernelGGL((k_attend_f8<D, false>), grid, dim3(MQ_NT), 0, s, a, AttendPre{});
         else
             hipLaunchKernelGGL((k_attend_mq<D, FMT>), grid, dim3(MQ_NT), 0, s, a);
     } else {
@@ -1247,21 +1265,28 @@ static hipError_t launch_att2(const AttendArgs& a, hipStream_t s) {
 }
 
 template <int D>
-static hipError_t launch_att1(const AttendArgs& a, hipStream_t s) {
+static hipError_t launch_att1(const AttendArgs& a, hipStream_t s, const AttendPre* pre) {
     switch (a.kv_fmt) {
-    case F32: return launch_att2<D, F32>(a, s);
-    case BF16: return launch_att2<D, BF16>(a, s);
-    default: return launch_att2<D, KV_PACKED>(a, s);
+    case F32: return launch_att2<D, F32>(a, s, nullptr);
+    case BF16: return launch_att2<D, BF16>(a, s, nullptr);
+    default: return launch_att2<D, KV_PACKED>(a, s, pre);
     }
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+// the calls whose kernel can compress the layer's new entry first: packed rows with the
+// bf16 RoPE part the packed-row kernel takes, one query per sequence
+bool attend_takes_pre(const AttendArgs& a) {
+    return a.kv_fmt == KV_PACKED && (a.d == 256 || a.d == 512) && a.r == F8_R && a.Tq == 1;
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s, const AttendPre* pre) {
     if (a.B <= 0 || a.Tq <= 0) return hipSuccess;
+    if (pre && !attend_takes_pre(a)) return hipErrorInvalidValue;
     switch (a.d) {
-    case 64: return launch_att1<64>(a, s);
-    case 128: return launch_att1<128>(a, s);
-    case 256: return launch_att1<256>(a, s);
-    default: return launch_att1<512>(a, s);
+    case 64: return launch_att1<64>(a, s, nullptr);
+    case 128: return launch_att1<128>(a, s, nullptr);
+    case 256: return launch_att1<256>(a, s, pre);
+    default: return launch_att1<512>(a, s, pre);
     }
 }
 

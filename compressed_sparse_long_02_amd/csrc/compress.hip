@@ -411,6 +411,13 @@ bool compress_pair_in_index(const CompressArgs& kv, const CompressArgs& key, int
            kv.out_fmt == KV_PACKED && (key.out_fmt == MXFP4 || key.out_fmt == BF16);
 }
 
+// The decode job the packed-row attention kernel can compress before it attends: the
+// one-wave shape, a packed KV entry.  Sets the channel split.
+bool compress_in_attend(const CompressArgs& kv, int& gz) {
+    gz = cmp_splits(kv);
+    return dec_shape(kv, gz) && kv.out_fmt == KV_PACKED;
+}
+
 // Both jobs in one launch when they take a fused kernel's shape (bf16 raw rows, one
 // logit per token, a packed KV entry plus an MXFP4 or bf16 key): the one-wave decode
 // kernel, else the general one with 256-thread blocks; otherwise one launch after the

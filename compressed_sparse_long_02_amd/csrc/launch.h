@@ -92,7 +92,14 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 hipError_t launch_compress_pair(const CompressArgs& a0, const CompressArgs& a1, hipStream_t s);
 bool compress_pair_in_index(const CompressArgs& kv, const CompressArgs& key, int& gz_kv, int& gz_key);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s, const IndexPre* pre = nullptr);
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// An HCA layer's decode-time compression job run by the attention kernel (channel split gz).
+struct AttendPre {
+    CompressArgs kv;
+    int gz;
+};
+bool compress_in_attend(const CompressArgs& kv, int& gz);
+bool attend_takes_pre(const AttendArgs& a);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s, const AttendPre* pre = nullptr);
 hipError_t launch_grouped_out_proj(const GprojArgs& a, hipStream_t s);
 
 }  // namespace csl

@@ -185,8 +185,23 @@ def hca_attend(c: HcaCache, q, q_pos, *, H, W, scale, out=None, out_fmt=ops.BF16
                                 block_bytes=c.block_bytes, n_blocks=bt.n_blocks, **kw)
 
 
+def hca_compress_attend(c: HcaCache, q, q_pos, *, H, W, scale, out=None, out_fmt=ops.BF16, with_lse=False,
+                        sink=None, bt: Optional[BlockTable] = None):
+    """Step 1 and the attention through one call (hca_attend_step); with one query per
+    sequence the compression runs inside the attention kernel."""
+    job = dict(x_ring=c.kv_ring.raw, x_fmt=ops.BF16, z_ring=c.kv_ring.z, bias=c.kv_ring.bias, d=c.d, r=c.r, m=c.m,
+               overlap=False, out_fmt=ops.KV_PACKED, x_roles=c.kv_ring.roles)
+    kw = dict(kv_fmt=ops.KV_PACKED, n_cap=c.n_cap, m=c.m, kvw_pos0=0, kvw_rows=c.window.shape[1], W=W, H=H, d=c.d,
+              r=c.r, scale=scale, out_fmt=out_fmt, out=out, with_lse=with_lse, sink=sink)
+    if bt is None:
+        job.update(out=c.entries)
+        return ops.hca_attend_step(job, q, c.entries, c.window, q_pos, **kw)
+    job.update(out=c.pool, pages=_pages(c, bt))
+    return ops.hca_attend_step(job, q, c.pool, c.window, q_pos,
+                               pages=(bt.table, c.entries_per_block, c.block_bytes, bt.n_blocks), **kw)
+
+
 def hca_decode_step(c: HcaCache, q_pos, q, *, H, W, scale, out, sink=None, bt: Optional[BlockTable] = None):
     """One HCA layer for the new tokens: compress, attend (out [B, T, H, d] bf16)."""
-    hca_compress(c, q_pos, bt)
-    hca_attend(c, q, q_pos, H=H, W=W, scale=scale, out=out, sink=sink, bt=bt)
+    hca_compress_attend(c, q, q_pos, H=H, W=W, scale=scale, out=out, sink=sink, bt=bt)
     return out

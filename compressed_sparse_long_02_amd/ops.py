@@ -270,7 +270,7 @@ def _q_fmt(q):
 
 
 def _attend(name, q, kv_c, kv_w, q_pos, idx, *, kv_fmt, n_cap, m, kvw_pos0, kvw_rows, W, H, d, r, scale, out_fmt,
-            out, lse, with_lse, sink=None, pages=None):
+            out, lse, with_lse, sink=None, pages=None, job=None):
     _need_cuda(q, kv_c, kv_w, q_pos, idx, out, lse, sink)
     B, Tq = q_pos.shape
     if q_pos.dtype != torch.int32 or not q_pos.is_contiguous() or not q.is_contiguous():
@@ -294,7 +294,15 @@ def _attend(name, q, kv_c, kv_w, q_pos, idx, *, kv_fmt, n_cap, m, kvw_pos0, kvw_
             _ptr(out), out_fmt, _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous()):
         raise ValueError("idx must be contiguous int32 [B, Tq, k]")
-    if pages is None:
+    if job is not None:
+        if pages is None:
+            geo = (_bstride(kv_c), None, 0, 0, 0, 0)
+        else:
+            bt, epb, blk_bytes, n_blocks = pages
+            _check_table(bt)
+            geo = (0, _ptr(bt), bt.shape[1], epb, blk_bytes, n_blocks)
+        rc = L.hca_attend_step(C.byref(job), _ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, *geo, n_cap, m, *tail)
+    elif pages is None:
         if name == "csa_attend":
             rc = L.csa_attend(_ptr(q), _q_fmt(q), _ptr(kv_c), kv_fmt, _bstride(kv_c), n_cap, _ptr(idx),
                               idx.shape[-1], *tail)
@@ -311,6 +319,21 @@ def _attend(name, q, kv_c, kv_w, q_pos, idx, *, kv_fmt, n_cap, m, kvw_pos0, kvw_
         name += "_paged"
     check(name, rc)
     return out, lse
+
+
+def hca_attend_step(job, q, kv_c, kv_w, q_pos, *, kv_fmt, n_cap, m, kvw_pos0, kvw_rows, W, H, d, r=0, scale,
+                    out_fmt=F32, out=None, lse=None, with_lse=True, sink=None, pages=None):
+    """An HCA layer's compression (job: a dict of kv_compress_step's keyword arguments plus
+    x_ring, x_fmt, z_ring and bias, q_pos doubling as the token positions) and its
+    attention, in that order, the compression inside the attention kernel where the shapes
+    allow.  kv_c: the dense entries [B, N, row], or with pages = (block_table, entries per
+    block, block bytes, n_blocks) the pool.  The other arguments and the results are
+    hca_attend's."""
+    j = _step_job(**job)
+    _check_pos(q_pos, q_pos.shape[0])
+    return _attend("hca_attend_step", q, kv_c, kv_w, q_pos, None, kv_fmt=kv_fmt, n_cap=n_cap, m=m,
+                   kvw_pos0=kvw_pos0, kvw_rows=kvw_rows, W=W, H=H, d=d, r=r, scale=scale, out_fmt=out_fmt, out=out,
+                   lse=lse, with_lse=with_lse, sink=sink, pages=pages, job=j)
 
 
 def csa_attend(q, kv_c, idx, kv_w, q_pos, *, kv_fmt, n_cap, kvw_pos0, kvw_rows, W, H, d, r=0, scale,

@@ -324,6 +324,29 @@ int hca_attend_paged(const void* q, int q_fmt, const void* kv_pool, int kv_fmt, 
                      const float* sink, const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
                      void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * hca_attend_step -- an HCA layer's decode step: the compression of the entries the new
+ * tokens complete ([X] section 2, HCA subsection: the CSA compression at m' = 128, no
+ * overlap) followed by the dense attention over every complete entry plus the window.
+ * The results are those of kv_compress_step(kv_job's arguments, pos = q_pos, T = Tq)
+ * followed by hca_attend (block_table NULL: entries at kv_c + b*kvc_bstride) or
+ * hca_attend_paged (block_table given, kv_c the pool), on the same stream; every argument
+ * means what it means there.  The job should write the entries this call reads.  With
+ * one query per sequence, packed rows of the RoPE width 64 and d 256 or 512, a job that
+ * writes those entries in place (same buffer and strides, or the same block table) and
+ * the one-wave compression shape (bf16 ring, one logit per token), the compression runs
+ * inside the attention kernel, by the split that attends the new entry (one launch
+ * fewer); otherwise it is launched first.  Workspace: csl_attend_workspace(B, Tq, H, d,
+ * n_cap + W).  The job and the attention arguments are checked before anything is
+ * launched.
+ */
+int hca_attend_step(const csl_compress_job* kv_job, const void* q, int q_fmt, const void* kv_c, int kv_fmt,
+                    int64_t kvc_bstride, const int32_t* block_table, int64_t bt_stride, int entries_per_block,
+                    int64_t block_bytes, int64_t n_blocks, int64_t n_cap, int m,
+                    const void* kv_w, int64_t kvw_bstride, int64_t kvw_pos0, int64_t kvw_rows, const float* sink,
+                    const int32_t* q_pos, int W, int B, int Tq, int H, int d, int r, float scale,
+                    void* out, int out_fmt, float* out_lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for csa_attend[_paged] (rows_max = k + W) or hca_attend[_paged]
  * (rows_max = n_cap + W) with these sizes; 0 when no split partials are needed. */
 size_t csl_attend_workspace(int B, int Tq, int H, int d, int64_t rows_max);

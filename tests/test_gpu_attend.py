@@ -244,3 +244,44 @@ def test_attention_sink_with_nothing_attended(gpu):
     torch.cuda.synchronize()
     assert torch.all(o == 0)
     assert torch.allclose(l.detach().cpu(), sink.expand(B, 2, H), rtol=1e-6, atol=1e-6)
+
+
+def test_hca_attend_step_compresses_before_it_attends(gpu):
+    # hca_attend_step with one query per sequence compresses inside the attention kernel,
+    # by the split whose rows hold the new entry, before that split copies any tile.  HCA
+    # attends every complete entry, so a stale (cleared) new row would change the output.
+    # Positions: entries completing at the cache's last row and mid-cache, a token that
+    # completes nothing, and one whose entry lies past n_cap (not stored, not attended).
+    from compressed_sparse_long_02_amd import decode as D
+    B, d, r, H, m, N, W, R = 4, 512, 64, 64, 128, 40, 128, 256
+    t = np.array([N * m - 1, 20 * m - 1, 30 * m + 5, 50 * m - 1], np.int32)
+    q_pos = dev(torch.from_numpy(t[:, None].copy()))
+    rb = ops.row_bytes(O.KV_PACKED, d, r)
+    ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d), 81))), dev(gen.random_logits((B, R, 1), 82)),
+                  dev(gen.random_logits((m, 1), 83)))
+    window = dev(gen.store(gen.normal((B, W, d), 84), O.KV_PACKED, r))
+    entries = dev(gen.store(gen.normal((B, N, d), 85), O.KV_PACKED, r))
+    q = dev(gen.normal((B, 1, H, d), 86).to(torch.bfloat16))
+    c = D.HcaCache(d=d, r=r, m=m, n_cap=N, kv_ring=ring, window=window, entries=entries)
+    new = [(b, int(t[b] + 1) // m - 1) for b in range(B) if (t[b] + 1) % m == 0 and (t[b] + 1) // m - 1 < N]
+    scale = 1 / math.sqrt(d)
+    kw = dict(H=H, W=W, scale=scale, out_fmt=O.F32, with_lse=True)
+
+    def clear():
+        for b, i in new:
+            entries[b, i].zero_()
+
+    clear()
+    D.hca_compress(c, q_pos)
+    o0, l0 = D.hca_attend(c, q, q_pos, **kw)
+    torch.cuda.synchronize()
+    e0 = entries.clone()
+    clear()
+    o1, l1 = D.hca_compress_attend(c, q, q_pos, **kw)
+    torch.cuda.synchronize()
+    assert all(bool(torch.any(entries[b, i] != 0)) for b, i in new)
+    assert torch.equal(e0, entries)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    oo, ol = O.hca_attend(_oracle_q(q), O.BF16, host(entries), O.KV_PACKED, N, m, host(window), 0, W, t[:, None],
+                          W=W, H=H, d=d, r=r, scale=scale)
+    assert max_abs(host(o1), oo) <= TOL[O.KV_PACKED]

@@ -149,6 +149,45 @@ def test_stack_compress_inside_index_equals_separate_launches(gpu, layout, reque
     assert torch.equal(gi0, gi1) and torch.equal(gs0, gs1)
 
 
+def _hca_row(st, c, i, zero=False):
+    """The packed HCA entry i of every sequence (a copy); zero=True clears it instead."""
+    if c.pool is None:
+        if zero:
+            c.entries[:, i].zero_()
+            return None
+        return c.entries[:, i].clone()
+    epb, erb = c.entries_per_block, st.rb
+    blk, off = st.bt[:, i // epb].long(), i % epb
+    if zero:
+        c.pool[blk, off * erb:(off + 1) * erb] = 0
+        return None
+    return c.pool[blk, off * erb:(off + 1) * erb].clone()
+
+
+@pytest.mark.parametrize("layout", ["linear", "paged"])
+def test_stack_hca_compress_inside_attend_equals_separate_launches(gpu, layout, request):
+    """hca_attend_step at the 1M stack shape (the compression inside the attention kernel,
+    by the split that attends the new entry) writes the same entry and the same output
+    and lse as kv_compress_step followed by hca_attend, each path run on a cache whose new
+    row was cleared first (a stale row would change every sequence's output)."""
+    st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
+    L = st.layers[1]
+    c = L["dc"]
+    i = (st.t + 1) // st.mh - 1
+    kw = dict(H=st.H, W=st.W, scale=st.scale, with_lse=True, bt=st.btab)
+    _hca_row(st, c, i, zero=True)
+    D.hca_compress(c, st.q_pos, st.btab)
+    o0, l0 = D.hca_attend(c, L["q"], st.q_pos, **kw)
+    r0 = _hca_row(st, c, i)
+    _hca_row(st, c, i, zero=True)
+    o1, l1 = D.hca_compress_attend(c, L["q"], st.q_pos, **kw)
+    r1 = _hca_row(st, c, i)
+    torch.cuda.synchronize()
+    assert bool(torch.any(r0 != 0))
+    assert torch.equal(r0, r1)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 @pytest.mark.parametrize("layout", ["linear", "paged"])
 def test_stack_index_topk_1M_mxfp4(gpu, layout, request):
     st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
