@@ -369,7 +369,8 @@ constexpr int DENSE_MIN_TQ = 64;
 constexpr size_t DENSE_WS_MAX = (size_t)2 << 30;
 
 bool dense_path(int fmt, int d_I, int H_I, int Tq) {
-    return fmt == CSL_BF16 && d_I == 128 && (H_I == 16 || H_I == 32 || H_I == 64 || H_I == 128) && Tq >= DENSE_MIN_TQ;
+    return (fmt == CSL_BF16 || fmt == CSL_MXFP4) && d_I == 128 && (H_I == 16 || H_I == 32 || H_I == 64 || H_I == 128) &&
+           Tq >= DENSE_MIN_TQ;
 }
 int dense_tc(int B, int Tq, int64_t n_cap) {
     // queries per pass: a multiple of 12 (the score kernel's query group), the passes

@@ -656,9 +656,23 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
-template <int HB>
+// MXFP4 keys (d_I = 128): a key is 64 bytes of codes (LDS rows of 80 bytes, an odd
+// number of 16-byte slots) and four e8m0 scales; one scaled FP4 MFMA 16x16x128 per 16
+// heads and 16 keys takes the whole key, its scale operands the blocks' exponents.
+template <int FMT>
+struct DenseKeys {
+    static constexpr int RB = FMT == MXFP4 ? 64 : 256;           // bytes of a key row
+    static constexpr int STR = FMT == MXFP4 ? 80 : DNS_KSTR;     // bytes per key row in LDS
+    static constexpr int CPK = RB / 16;                          // 16-byte chunks per key
+    static constexpr int KS = FMT == MXFP4 ? 1 : 4;              // MFMAs per 16 keys and 16 heads
+};
+
+template <int FMT, int HB>
 __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t kt[2][DNS_KT * DNS_KSTR];
+    using DK = DenseKeys<FMT>;
+    static_assert(FMT == BF16 || FMT == MXFP4, "bf16 or MXFP4 keys");
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][DNS_KT * DK::STR];
+    __shared__ uint32_t ksc[2][FMT == MXFP4 ? DNS_KT : 1];        // MXFP4: a key's four scales
     // per-query histograms, two 16-bit counts per word (a block sees at most 4096 keys)
     __shared__ uint32_t hist[DNS_QB * TOPK_BINS / 2];
     __shared__ int64_t nq[DNS_QB];
@@ -684,47 +698,75 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
     const int64_t bq = (int64_t)b * a.Tq + jq_c;
 
     // query fragments (A operand, rows = heads) and head weights of this wave's query
-    u32x4 qa[HB][4];
+    u32x4 qa[HB][DK::KS];
+    int qsc[HB];                                         // MXFP4: the e8m0 scale of lane group g's block
     float wh[HB][4];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int h = hb * 16 + col;
-        const uint8_t* qrow = a.qi + (bq * a.H_I + (h < a.H_I ? h : 0)) * 256;
+        const int64_t qr = bq * a.H_I + (h < a.H_I ? h : 0);
+        const uint8_t* qrow = a.qi + qr * DK::RB;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 v = *(const u32x4*)(qrow + 64 * ks + 16 * g);
+        for (int ks = 0; ks < DK::KS; ++ks) {
+            const u32x4 v = *(const u32x4*)(qrow + (FMT == MXFP4 ? 16 * g : 64 * ks + 16 * g));
             qa[hb][ks] = (h < a.H_I && n > 0) ? v : u32x4{0, 0, 0, 0};
         }
+        qsc[hb] = FMT == MXFP4 ? (int)a.qi_scales[qr * 4 + g] : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = hb * 16 + 4 * g + i;
             wh[hb][i] = hh < a.H_I ? a.w[bq * a.H_I + hh] : 0.f;
         }
     }
-    // key tiles: thread tid moves chunks c = tid + 512 j (key c / 16, 16-byte piece c % 16);
-    // keys past the range re-read the range's last key (scored, then ignored)
+    // key tiles: thread tid moves chunks c = tid + DNS_NT j (key c / CPK, 16-byte piece
+    // c % CPK); MXFP4: the threads after the code chunks move one key's four scales each.
+    // Keys past the range re-read the range's last key (scored, then ignored).
     const uint8_t* kbase = a.ki + (int64_t)b * a.ki_bstride;
-    constexpr int NR = (DNS_KT * 16 + DNS_NT - 1) / DNS_NT;   // 16-byte chunks per thread and tile
+    const uint8_t* sbase = FMT == MXFP4 ? a.ki_scales + (int64_t)b * a.ks_bstride : nullptr;
+    constexpr int NCH = DNS_KT * DK::CPK;                   // code chunks per tile
+    constexpr int NR = (NCH + DNS_NT - 1) / DNS_NT;         // 16-byte chunks per thread and tile
+    static_assert(FMT != MXFP4 || NCH + DNS_KT <= DNS_NT, "MXFP4: one chunk or one scale word per thread");
     u32x4 R[NR];
+    uint32_t RS = 0u;
+    auto key_at = [&](int t, int kk) {
+        const int64_t key = k0 + (int64_t)t * DNS_KT + kk;
+        return key < k1 ? key : k1 - 1;
+    };
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const int c = tid + DNS_NT * j < DNS_KT * 16 ? tid + DNS_NT * j : DNS_KT * 16 - 1;
-            int64_t key = k0 + (int64_t)t * DNS_KT + (c >> 4);
-            key = key < k1 ? key : k1 - 1;
-            const uint8_t* kp = kbase + key * 256;
-            if (a.bt) {                                  // paged keys (an absent block reads key 0 of the query)
+            const int c = tid + DNS_NT * j < NCH ? tid + DNS_NT * j : NCH - 1;
+            const int64_t key = key_at(t, c / DK::CPK);
+            const uint8_t* kp = kbase + key * DK::RB;
+            if (a.bt) {                                  // paged keys (an absent block reads the query's row)
                 const int32_t blk = a.bt[(int64_t)b * a.bt_stride + key / a.epb];
-                kp = (blk >= 0 && blk < a.n_blocks) ? a.ki + (int64_t)blk * a.blk_bytes + (key % a.epb) * 256 : a.qi;
+                kp = (blk >= 0 && blk < a.n_blocks) ? a.ki + (int64_t)blk * a.blk_bytes + (key % a.epb) * DK::RB : a.qi;
             }
-            R[j] = ld_global<u32x4>(kp + 16 * (c & 15));
+            R[j] = ld_global<u32x4>(kp + 16 * (c % DK::CPK));
+        }
+        if constexpr (FMT == MXFP4) {
+            const int kk = tid - NCH;                    // this thread's key for the scales
+            if (kk >= 0 && kk < DNS_KT) {
+                const int64_t key = key_at(t, kk);
+                const uint8_t* sp = sbase + key * 4;
+                if (a.bt) {
+                    const int32_t blk = a.bt[(int64_t)b * a.bt_stride + key / a.epb];
+                    sp = (blk >= 0 && blk < a.n_blocks) ? a.ki_scales + (int64_t)blk * a.sblk_bytes + (key % a.epb) * 4
+                                                        : a.qi_scales;
+                }
+                RS = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8) | ((uint32_t)sp[2] << 16) | ((uint32_t)sp[3] << 24);
+            }
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             const int c = tid + DNS_NT * j;
-            if (c < DNS_KT * 16) *(u32x4*)(&kt[buf][(c >> 4) * DNS_KSTR + 16 * (c & 15)]) = R[j];
+            if (c < NCH) *(u32x4*)(&kt[buf][(c / DK::CPK) * DK::STR + 16 * (c % DK::CPK)]) = R[j];
+        }
+        if constexpr (FMT == MXFP4) {
+            const int kk = tid - NCH;
+            if (kk >= 0 && kk < DNS_KT) ksc[buf][kk] = RS;
         }
     };
     uint32_t* srow = a.scores + ((int64_t)b * a.Tc + jl) * a.sstride;
@@ -739,7 +781,7 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
         // 16-lane swap leave block u's totals in lane row 0, 2, 1, 3), so every lane then
         // stores one key and counts it
         if (n > 0) {
-            const uint8_t* tb = &kt[t & 1][col * DNS_KSTR + 16 * g];
+            const uint8_t* tb = &kt[t & 1][col * DK::STR + 16 * g];
 #pragma unroll
             for (int k4 = 0; k4 < DNS_KT / 64; ++k4) {
                 float p[4];
@@ -749,11 +791,18 @@ __global__ void __launch_bounds__(DNS_NT, 3) k_idx_dense_score(IndexArgs a) {
                     v4f acc[HB];
 #pragma unroll
                     for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (FMT == MXFP4) {
+                        const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DK::STR);
+                        const int bs = (int)((ksc[t & 1][16 * kb + col] >> (8 * g)) & 0xffu);
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DNS_KSTR + 64 * ks);
+                        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_fp4(qa[hb][0], bf, qsc[hb], bs, acc[hb]);
+                    } else {
 #pragma unroll
-                        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16(qa[hb][ks], bf, acc[hb]);
+                        for (int ks = 0; ks < 4; ++ks) {
+                            const u32x4 bf = *(const u32x4*)(tb + 16 * kb * DK::STR + 64 * ks);
+#pragma unroll
+                            for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16(qa[hb][ks], bf, acc[hb]);
+                        }
                     }
                     float part = 0.f;
 #pragma unroll
@@ -1351,10 +1400,17 @@ static hipError_t launch_dense(IndexArgs a, hipStream_t s) {
         dim3 grid((unsigned)((a.n_cap + DNS_KT * DNS_TPB - 1) / (DNS_KT * DNS_TPB)), (unsigned)((tc + DNS_QB - 1) / DNS_QB),
                   (unsigned)a.B);
         if (grid.x == 0) grid.x = 1;
-        if (hb <= 1) hipLaunchKernelGGL(k_idx_dense_score<1>, grid, dim3(DNS_NT), 0, s, a);
-        else if (hb <= 2) hipLaunchKernelGGL(k_idx_dense_score<2>, grid, dim3(DNS_NT), 0, s, a);
-        else if (hb <= 4) hipLaunchKernelGGL(k_idx_dense_score<4>, grid, dim3(DNS_NT), 0, s, a);
-        else hipLaunchKernelGGL(k_idx_dense_score<8>, grid, dim3(DNS_NT), 0, s, a);
+        if (a.ki_fmt == MXFP4) {
+            if (hb <= 1) hipLaunchKernelGGL((k_idx_dense_score<MXFP4, 1>), grid, dim3(DNS_NT), 0, s, a);
+            else if (hb <= 2) hipLaunchKernelGGL((k_idx_dense_score<MXFP4, 2>), grid, dim3(DNS_NT), 0, s, a);
+            else if (hb <= 4) hipLaunchKernelGGL((k_idx_dense_score<MXFP4, 4>), grid, dim3(DNS_NT), 0, s, a);
+            else hipLaunchKernelGGL((k_idx_dense_score<MXFP4, 8>), grid, dim3(DNS_NT), 0, s, a);
+        } else {
+            if (hb <= 1) hipLaunchKernelGGL((k_idx_dense_score<BF16, 1>), grid, dim3(DNS_NT), 0, s, a);
+            else if (hb <= 2) hipLaunchKernelGGL((k_idx_dense_score<BF16, 2>), grid, dim3(DNS_NT), 0, s, a);
+            else if (hb <= 4) hipLaunchKernelGGL((k_idx_dense_score<BF16, 4>), grid, dim3(DNS_NT), 0, s, a);
+            else hipLaunchKernelGGL((k_idx_dense_score<BF16, 8>), grid, dim3(DNS_NT), 0, s, a);
+        }
         hipLaunchKernelGGL(k_idx_dense_select, dim3((unsigned)tc, (unsigned)a.B), dim3(DSEL_NT), sel_lds(), s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

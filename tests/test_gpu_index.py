@@ -210,26 +210,32 @@ def test_index_topk_calls_in_a_row(gpu):
 
 
 DENSE_CASES = [
-    # (name, B, Tq, H_I, N, m, k, positions): Tq >= 64 with a bf16 d_I = 128 indexer takes the
-    # many-query path (every score to HBM, then one select per query)
-    ("dense_h64", 1, 96, 64, 20000, 4, 512, "ragged"),
-    ("dense_h16_b2", 2, 64, 16, 9000, 4, 256, "ragged"),
-    ("dense_h32_small_n", 1, 70, 32, 700, 1, 1024, "ragged"),     # many queries with n(t) < k
+    # (name, fmt, B, Tq, H_I, N, m, k, positions): Tq >= 64 with a bf16 or MXFP4 d_I = 128
+    # indexer takes the many-query path (every score to HBM, then one select per query)
+    ("dense_h64", O.BF16, 1, 96, 64, 20000, 4, 512, "ragged"),
+    ("dense_h16_b2", O.BF16, 2, 64, 16, 9000, 4, 256, "ragged"),
+    ("dense_h32_small_n", O.BF16, 1, 70, 32, 700, 1, 1024, "ragged"),     # many queries with n(t) < k
+    ("dense_fp4_h64", O.MXFP4, 1, 96, 64, 20000, 4, 1024, "ragged"),
+    ("dense_fp4_h16_b2", O.MXFP4, 2, 64, 16, 9000, 4, 256, "ragged"),
+    ("dense_fp4_h128_tail", O.MXFP4, 1, 75, 128, 5003, 4, 512, "last"),   # a partial last query group and key tile
 ]
 
 
 @pytest.mark.parametrize("case", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
 def test_index_topk_many_queries(gpu, case):
-    _, B, Tq, H_I, N, m, k, pk = case
-    d_I, fmt = 128, O.BF16
-    qi, _, ki, _, qd, kd = _inputs(fmt, B, Tq, H_I, d_I, N, 900 + N)
+    _, fmt, B, Tq, H_I, N, m, k, pk = case
+    d_I = 128
+    qi, qs, ki, ks, qd, kd = _inputs(fmt, B, Tq, H_I, d_I, N, 900 + N)
     w = gen.normal((B, Tq, H_I), 901 + N, 1 / math.sqrt(H_I))
     qpos = _positions(pk, B, Tq, N, m).to(torch.int32)
     kw = dict(H_I=H_I, d_I=d_I, m=m, n_cap=N)
-    gi, gs = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=fmt, k=k, **kw)
+    gi, gs = ops.index_topk(dev(qi), dev(w), dev(ki), dev(qpos), fmt=fmt, k=k,
+                            qi_scales=dev(qs) if qs is not None else None,
+                            ki_scales=dev(ks) if ks is not None else None, **kw)
     torch.cuda.synchronize()
-    oi, _ = O.index_topk(host(qi), fmt, host(w), host(ki), fmt, host(qpos), k=k, **kw)
-    allsc = oracle_all_scores(host(qi), fmt, host(w), host(ki), fmt, host(qpos), **kw)
+    oq = dict(qi_scales=None if qs is None else host(qs), ki_scales=None if ks is None else host(ks))
+    oi, _ = O.index_topk(host(qi), fmt, host(w), host(ki), fmt, host(qpos), k=k, **kw, **oq)
+    allsc = oracle_all_scores(host(qi), fmt, host(w), host(ki), fmt, host(qpos), **kw, **oq)
     bound = np.stack([score_error_bound(qd[b], host(w)[b].astype(np.float64), kd[b]) for b in range(B)])
     st = check_topk(host(gi), host(gs), oi, allsc, k, bound=bound, max_swapped=cap(B * Tq))
     print("case %s: %s" % (case[0], st))

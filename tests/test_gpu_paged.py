@@ -94,7 +94,7 @@ def test_paged_attention_skips_missing_blocks(gpu):
     assert max_abs(host(o), oo) <= 2e-2 and max_abs(host(l), ol) <= 2e-1
 
 
-@pytest.mark.parametrize("fmt,N,Tq", [(O.MXFP4, 40000, 1), (O.BF16, 20000, 2), (O.BF16, 6000, 64)])
+@pytest.mark.parametrize("fmt,N,Tq", [(O.MXFP4, 40000, 1), (O.BF16, 20000, 2), (O.BF16, 6000, 64), (O.MXFP4, 6000, 64)])
 def test_paged_index_equals_linear_and_oracle(gpu, fmt, N, Tq):
     """index_topk_paged over keys that share their blocks with other data (as in a CSA
     block of 32 entries + 32 keys + scales): identical to index_topk on the linear keys,
