@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--workload", choices=["stack", "prefill", "csa_decode", "hca_decode"], default="stack",
                    help="stack: the 4-layer decode stack (default); prefill: one CSA prefill chunk; csa_decode: one "
                         "CSA layer, batch 8 at 128K; hca_decode: one HCA layer, batch 4 at 1M")
+    p.add_argument("--indexer", choices=["bf16", "mxfp4"], default="bf16",
+                   help="prefill workload: the indexer's queries and keys in bf16 (default) or MXFP4")
     p.add_argument("--layout", choices=["linear", "paged"], default="linear",
                    help="compressed cache of the stack: dense per sequence, or 128-token blocks behind a block table")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -84,8 +86,10 @@ def prefill_cpu_baseline(pf, nq):
     h = lambda x: x.detach().cpu().numpy()
     qi, w, qpos = h(pf.qi[:, sel]), h(pf.w[:, sel]), h(pf.q_pos[:, sel])
     keys, cache, kvw, q = h(pf.keys), h(pf.cache), h(pf.kvw), h(pf.q[:, sel].view(torch.int16))
+    sc = {} if pf.qis is None else dict(qi_scales=h(pf.qis[:, sel]), ki_scales=h(pf.kscales))
     t0 = time.perf_counter()
-    idx, _ = O.index_topk(qi, O.BF16, w, keys, O.BF16, qpos, H_I=pf.HI, d_I=pf.dI, m=pf.m, n_cap=pf.N, k=pf.k)
+    idx, _ = O.index_topk(qi, pf.key_fmt, w, keys, pf.key_fmt, qpos, H_I=pf.HI, d_I=pf.dI, m=pf.m, n_cap=pf.N,
+                          k=pf.k, **sc)
     O.csa_attend(q, O.BF16, cache, O.KV_PACKED, pf.N, idx, kvw, pf.T0 - pf.W, pf.W + pf.C, qpos, W=pf.W, H=pf.H,
                  d=pf.d, r=pf.r, scale=1 / math.sqrt(pf.d))
     dt = time.perf_counter() - t0
@@ -98,8 +102,10 @@ def main_prefill(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("[bench] building the prefill-chunk inputs", file=sys.stderr, flush=True)
+    from compressed_sparse_long_02_amd import ops
     from compressed_sparse_long_02_amd.workloads import Prefill
-    pf = Prefill(dev)
+    fp4 = args.indexer == "mxfp4"
+    pf = Prefill(dev, key_fmt=ops.MXFP4 if fp4 else ops.BF16)
     pf.step()
     torch.cuda.synchronize()
     steps, warm = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
@@ -116,8 +122,10 @@ def main_prefill(args):
     t_cmp = time_calls(pf.compress, 3)
     fi = pf.index_flops()
     ach = fi / (t_idx * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": "index_topk (bf16 64x128 indexer, 8192 queries x 264,192 entries, top-1024)",
-            "achieved": round(ach, 1), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4),
+    peak = 10100.0 if fp4 else 2500.0                  # dense FP4 / bf16 MFMA peaks of the part
+    roof = {"bound": "mfma", "kernel": "index_topk (%s 64x128 indexer, 8192 queries x 264,192 entries, top-1024)"
+                                       % args.indexer,
+            "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
             "traffic": None, "flops_per_launch": fi, "ms_per_launch": round(t_idx, 3)}
     kernels = {"index_topk": {"ms": round(t_idx, 3), "TFLOP/s": round(ach, 1)},
                "csa_attend": {"ms": round(t_att, 3), "TFLOP/s": round(pf.attend_flops() / (t_att * 1e-3) / 1e12, 1)},
@@ -126,10 +134,11 @@ def main_prefill(args):
     line = {
         "metric": "CSA prefill-chunk tokens/sec at 1M ctx; indexer MFMA %", "value": round(pf.C / (ms * 1e-3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(ms, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4+bf16" if fp4 else "bf16",
+        "data": "synthetic",
         "config": {"workload": "CSA prefill chunk: 8192 tokens on 1,048,576 cached (compress + index + attend)",
                    "global_batch": 1, "seq_len": pf.T0 + pf.C, "heads": pf.H, "head_dim": pf.d,
-                   "indexer": "bf16 64x128, top-k 1024", "parallelism": "single GPU"},
+                   "indexer": "%s 64x128, top-k 1024" % args.indexer, "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)

@@ -249,22 +249,31 @@ class Stack:
 
 class Prefill:
     """One CSA layer appending a chunk of 8,192 tokens to 1,048,576 cached ones: compress the
-    chunk's 2,048 entries (KV and bf16 indexer keys, with the 4 look-back rows), index the
-    8,192 queries against the 264,192 entries (64 heads x 128, bf16, top-1024, causal) and
-    attend with 128 heads of 512 over the selected entries plus a 128-token window."""
+    chunk's 2,048 entries (KV and indexer keys, with the 4 look-back rows), index the 8,192
+    queries against the 264,192 entries (64 heads x 128, top-1024, causal) and attend with 128
+    heads of 512 over the selected entries plus a 128-token window.  The indexer's queries and
+    keys are bf16, or MXFP4 (key_fmt=ops.MXFP4: cached keys drawn as random codes and block
+    scales, the chunk's keys compressed to MXFP4, the queries quantised to MXFP4)."""
 
-    def __init__(self, device):
+    def __init__(self, device, key_fmt=ops.BF16):
+        self.key_fmt = key_fmt
         self.H, self.d, self.r, self.m, self.HI, self.dI, self.k, self.W, self.C = 128, 512, 64, 4, 64, 128, 1024, 128, 8192
         self.T0 = 1 << 20
         self.N0 = self.T0 // self.m
         self.N = (self.T0 + self.C) // self.m
         d, r, dI, m, C, W = self.d, self.r, self.dI, self.m, self.C, self.W
         self.cache = torch.empty((1, self.N, d + r), dtype=torch.uint8, device=device)
-        self.keys = torch.empty((1, self.N, dI * 2), dtype=torch.uint8, device=device)
+        fp4 = key_fmt == ops.MXFP4
+        self.keys = torch.empty((1, self.N, dI // 2 if fp4 else dI * 2), dtype=torch.uint8, device=device)
+        self.kscales = torch.empty((1, self.N, dI // 32), dtype=torch.uint8, device=device) if fp4 else None
         for s0 in range(0, self.N0, 32768):
             c = min(32768, self.N0 - s0)
             self.cache[:, s0:s0 + c] = gen.pack_kv(gen.normal((1, c, d), 5000 + s0, device=device), r)
-            self.keys[:, s0:s0 + c] = gen.bf16_bytes(gen.normal((1, c, dI), 6000 + s0, device=device))
+            if fp4:
+                kc, ks = gen.random_mxfp4(c, dI, 6000 + s0, device=device)
+                self.keys[0, s0:s0 + c], self.kscales[0, s0:s0 + c] = kc, ks
+            else:
+                self.keys[:, s0:s0 + c] = gen.bf16_bytes(gen.normal((1, c, dI), 6000 + s0, device=device))
         self.x = gen.bf16_bytes(gen.normal((1, C + m, d), 7001, device=device))
         self.xi = gen.bf16_bytes(gen.normal((1, C + m, dI), 7002, device=device))
         self.z = gen.random_logits((1, C + m, 1), 7003, device=device)
@@ -273,7 +282,11 @@ class Prefill:
         self.bias_i = gen.random_logits((2 * m, 1), 7006, device=device)
         self.kvw = gen.pack_kv(gen.normal((1, W + C, d), 7007, device=device), r)
         self.q_pos = torch.arange(self.T0, self.T0 + C, dtype=torch.int32, device=device).view(1, C)
-        self.qi = gen.bf16_bytes(gen.normal((1, C, self.HI, dI), 7008, device=device))
+        if fp4:
+            qc, qs = gen.random_mxfp4(C * self.HI, dI, 7008, device=device)
+            self.qi, self.qis = qc.reshape(1, C, self.HI, -1), qs.reshape(1, C, self.HI, -1)
+        else:
+            self.qi, self.qis = gen.bf16_bytes(gen.normal((1, C, self.HI, dI), 7008, device=device)), None
         self.w = gen.normal((1, C, self.HI), 7009, 1 / math.sqrt(self.HI), device=device)
         self.q = gen.normal((1, C, self.H, d), 7010, device=device).to(torch.bfloat16)
         self.idx = torch.empty((1, C, self.k), dtype=torch.int32, device=device)
@@ -286,13 +299,15 @@ class Prefill:
         kw = dict(m=self.m, overlap=True, e_begin=self.N0, n_e=ne, x_pos0=self.T0 - self.m)
         F.kv_compress(self.x, F.BF16, self.z, self.bias, d=self.d, r=self.r, out_fmt=F.KV_PACKED,
                       out=self.cache[:, self.N0:self.N], **kw)
-        F.kv_compress(self.xi, F.BF16, self.zi, self.bias_i, d=self.dI, out_fmt=F.BF16,
-                      out=self.keys[:, self.N0:self.N], **kw)
+        F.kv_compress(self.xi, F.BF16, self.zi, self.bias_i, d=self.dI, out_fmt=self.key_fmt,
+                      out=self.keys[:, self.N0:self.N],
+                      out_scales=None if self.kscales is None else self.kscales[:, self.N0:self.N], **kw)
 
     def index(self):
         F = ops
-        F.index_topk(self.qi, self.w, self.keys, self.q_pos, fmt=F.BF16, H_I=self.HI, d_I=self.dI, m=self.m,
-                     n_cap=self.N, k=self.k, out_idx=self.idx, with_scores=False)
+        F.index_topk(self.qi, self.w, self.keys, self.q_pos, fmt=self.key_fmt, H_I=self.HI, d_I=self.dI, m=self.m,
+                     n_cap=self.N, k=self.k, out_idx=self.idx, with_scores=False, qi_scales=self.qis,
+                     ki_scales=self.kscales)
 
     def attend(self):
         F = ops

@@ -363,6 +363,27 @@ def test_csa_prefill_chunk_8192_on_1m(gpu):
           % (len(sq), edges, nbad, nbadk, stats, err))
 
 
+def test_mxfp4_prefill_index_8192_on_1m(gpu):
+    """The prefill chunk's indexer with MXFP4 queries and keys (the pages' FP4 indexer QK):
+    8,192 queries against 264,192 entries through the many-query path with the scaled FP4
+    MFMA; 64 evenly spaced queries plus the first and last of every pass checked against
+    the oracle."""
+    pf = workloads.Prefill(torch.device("cuda:0"), key_fmt=O.MXFP4)
+    pf.compress()
+    gi, gs = ops.index_topk(pf.qi, pf.w, pf.keys, pf.q_pos, fmt=O.MXFP4, H_I=pf.HI, d_I=pf.dI, m=pf.m,
+                            n_cap=pf.N, k=pf.k, qi_scales=pf.qis, ki_scales=pf.kscales)
+    torch.cuda.synchronize()
+    C = pf.C
+    tc = dense_pass_rows(1, C, pf.N)
+    edges = {q for p0 in range(0, C, tc) for q in (p0, min(p0 + tc, C) - 1)}
+    sq = sorted(edges | set(np.linspace(0, C - 1, 64).astype(int).tolist()))
+    hq = lambda x: host(x[:, sq])
+    stats = _check_index(hq(gi), hq(gs), hq(pf.qi), O.MXFP4, hq(pf.w), host(pf.keys), O.MXFP4, hq(pf.q_pos),
+                         H_I=pf.HI, d_I=pf.dI, m=pf.m, n_cap=pf.N, k=pf.k, qi_scales=hq(pf.qis),
+                         ki_scales=host(pf.kscales))
+    print("mxfp4 prefill index: %d queries checked; %s" % (len(sq), stats))
+
+
 def dense_pass_rows(B, Tq, n_cap):
     """Queries per pass of the many-query indexer, as the library plans them: passes of a
     multiple of 12 queries, as even as possible, each with at most 2 GiB of score rows
