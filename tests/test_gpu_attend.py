@@ -285,3 +285,33 @@ def test_hca_attend_step_compresses_before_it_attends(gpu):
     oo, ol = O.hca_attend(_oracle_q(q), O.BF16, host(entries), O.KV_PACKED, N, m, host(window), 0, W, t[:, None],
                           W=W, H=H, d=d, r=r, scale=scale)
     assert max_abs(host(o1), oo) <= TOL[O.KV_PACKED]
+
+
+@pytest.mark.parametrize("Tq,d", [(2, 512), (1, 128)])
+def test_hca_attend_step_unfused_shapes_equal_separate_calls(gpu, Tq, d):
+    # Shapes the attention kernel does not compress for -- two query tokens per sequence, or
+    # a head dim the packed-row kernel does not take -- run the compression launch, then
+    # hca_attend: the same bytes as the two separate calls.
+    from compressed_sparse_long_02_amd import decode as D
+    B, r, H, m, N, W, R = 3, 64 if d == 512 else 32, 64, 128, 30, 128, 256
+    last = np.array([N * m - 1, 20 * m - 1, 25 * m + 7], np.int32)
+    t = np.stack([last - (Tq - 1 - j) for j in range(Tq)], axis=1).astype(np.int32)
+    q_pos = dev(torch.from_numpy(t.copy()))
+    ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d), 181))), dev(gen.random_logits((B, R, 1), 182)),
+                  dev(gen.random_logits((m, 1), 183)))
+    window = dev(gen.store(gen.normal((B, W, d), 184), O.KV_PACKED, r))
+    q = dev(gen.normal((B, Tq, H, d), 186).to(torch.bfloat16))
+    outs = []
+    for fused in (False, True):
+        entries = dev(gen.store(gen.normal((B, N, d), 185), O.KV_PACKED, r))
+        c = D.HcaCache(d=d, r=r, m=m, n_cap=N, kv_ring=ring, window=window, entries=entries)
+        kw = dict(H=H, W=W, scale=1 / math.sqrt(d), out_fmt=O.F32, with_lse=True)
+        if fused:
+            o, l = D.hca_compress_attend(c, q, q_pos, **kw)
+        else:
+            D.hca_compress(c, q_pos)
+            o, l = D.hca_attend(c, q, q_pos, **kw)
+        torch.cuda.synchronize()
+        outs.append((entries, o, l))
+    for a, b_ in zip(*outs):
+        assert torch.equal(a, b_)

@@ -382,3 +382,40 @@ def test_csa_index_step_compresses_before_it_scores(gpu, key_fmt):
         allsc = oracle_all_scores(host(qi[b:b + 1]), key_fmt, host(w[b:b + 1]), host(keys[b:b + 1]), key_fmt,
                                   t[b:b + 1, None], H_I=H_I, d_I=d_I, m=m, n_cap=N, **oq)
         assert abs(gs_h[b, 0, i] - allsc[0, 0, i]) <= 1e-3 * max(1.0, abs(allsc[0, 0, i])), (b, i)
+
+
+@pytest.mark.parametrize("Tq,N", [(2, 1500), (1, 400)])
+def test_csa_index_step_unfused_shapes_equal_separate_calls(gpu, Tq, N):
+    # Shapes the scoring kernel does not compress for -- two query tokens per sequence, or
+    # a single scoring slice per query -- run the compression launch, then index_topk:
+    # the same bytes as the two separate calls.
+    B, d, r, m, d_I, H_I, k, R = 3, 512, 64, 4, 128, 64, 256, 16
+    last = np.array([4 * (N - 10) - 1, 4 * (N // 2) - 2, 4 * N - 1], np.int32)
+    t = np.stack([last - (Tq - 1 - j) for j in range(Tq)], axis=1).astype(np.int32)
+    q_pos = dev(torch.from_numpy(t.copy()))
+    kv_ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d), 91))), dev(gen.random_logits((B, R, 1), 92)),
+                     dev(gen.random_logits((2 * m, 1), 93)))
+    key_ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d_I), 94, 1 / math.sqrt(d_I)))),
+                      dev(gen.random_logits((B, R, 1), 95)), dev(gen.random_logits((2 * m, 1), 96)))
+    rb = ops.row_bytes(O.KV_PACKED, d, r)
+    kc, ks = gen.random_mxfp4(B * N, d_I, 97)
+    qc, qs = gen.random_mxfp4(B * Tq * H_I, d_I, 98)
+    qi, qis = dev(qc.reshape(B, Tq, H_I, -1)), dev(qs.reshape(B, Tq, H_I, -1))
+    w = dev(gen.normal((B, Tq, H_I), 99, 1 / math.sqrt(H_I)))
+    outs = []
+    for fused in (False, True):
+        entries = dev(gen.store(gen.normal((B, N, d), 90), O.KV_PACKED, r))
+        keys, kscales = dev(kc.reshape(B, N, -1)), dev(ks.reshape(B, N, -1))
+        c = D.CsaCache(d=d, r=r, m=m, d_I=d_I, key_fmt=O.MXFP4, n_cap=N, kv_ring=kv_ring, key_ring=key_ring,
+                       window=dev(torch.zeros((B, 128, rb), dtype=torch.uint8)), entries=entries, keys=keys,
+                       key_scales=kscales)
+        kw = dict(H_I=H_I, k=k, qi_scales=qis, with_scores=True)
+        if fused:
+            gi, gs = D.csa_compress_select(c, q_pos, qi, w, **kw)
+        else:
+            D.csa_compress(c, q_pos)
+            gi, gs = D.csa_select(c, q_pos, qi, w, **kw)
+        torch.cuda.synchronize()
+        outs.append((entries, keys, kscales, gi, gs))
+    for a, b_ in zip(*outs):
+        assert torch.equal(a, b_)
