@@ -188,6 +188,49 @@ def test_stack_hca_compress_inside_attend_equals_separate_launches(gpu, layout, 
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
 
 
+def test_stack_step_graph_replays_equal_the_eager_step(gpu, stack):
+    """The decode step as bench.py times it: captured once in a HIP graph and replayed three
+    times, with eager work between the replays (the outputs and the new cache rows cleared);
+    every replay writes the eager step's indices, outputs and cache rows, byte for byte."""
+    st = stack
+    csa, hca = st.layers[0], st.layers[1]
+    i, ih = (st.t + 1) // st.m - 1, (st.t + 1) // st.mh - 1
+
+    def clear():
+        for L in st.layers:
+            L["out"].zero_()
+            if L["kind"] == "csa":
+                L["idx"].fill_(-7)
+        _new_rows(st, csa["dc"], i, zero=True)
+        _hca_row(st, hca["dc"], ih, zero=True)
+
+    def snap():
+        return ([L["out"].clone() for L in st.layers] + [L["idx"].clone() for L in st.layers if L["kind"] == "csa"]
+                + _new_rows(st, csa["dc"], i) + [_hca_row(st, hca["dc"], ih)])
+
+    clear()
+    st.step()
+    torch.cuda.synchronize()
+    ref = snap()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            st.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snap()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), "replay %d differs" % rep
+    del g
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("layout", ["linear", "paged"])
 def test_stack_index_topk_1M_mxfp4(gpu, layout, request):
     st = request.getfixturevalue("stack" if layout == "linear" else "paged_stack")
