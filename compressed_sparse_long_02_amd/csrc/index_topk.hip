@@ -1127,7 +1127,9 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_dense_select(IndexArgs a) {
 // count of keys in it and above.  Every such key is in some slice's candidate segment (a
 // slice kept all keys at or above its own threshold bin, which is at most the query's).
 // Usual case: wave w compacts the keys at or above the bin of its contiguous run of
-// slices (the prefetched part, then the rest) into its own LDS region, the regions are
+// slices (the prefetched part, then the rest, eight rounds of loads at a time, their
+// addresses clamped into the segment so that all eight are in flight together) into its
+// own LDS region, the regions are
 // joined in wave order (= entry order), and a radix select over their offsets from the
 // bin's lower edge, the keys above the bin clamped to its upper edge (22 bits, two
 // passes, no min / max phase), gives the exact top k.  Otherwise (a region overflows:
@@ -1222,21 +1224,22 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
             }
             got += __builtin_popcountll(m);
         };
-        // segment entries [e_from, c) of slice sl, four rounds of 64 at a time
+        // segment entries [e_from, c) of slice sl, eight rounds of 64 at a time (clamped into [0, c), so all are in flight together)
         auto stream = [&](int sl, int e_from, int c) {
             const uint32_t* kk = ckr + (int64_t)sl * a.S;
             const int32_t* ii = cir + (int64_t)sl * a.S;
-            for (int e0 = e_from; e0 < c; e0 += 256) {
-                uint32_t kr[4];
-                int32_t ir[4];
+            for (int e0 = e_from; e0 < c; e0 += 512) {
+                uint32_t kr[8];
+                int32_t ir[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const int e = e0 + 64 * u + lane;
-                    kr[u] = e < c ? kk[e] : 0u;
-                    ir[u] = e < c ? ii[e] : 0;
+                    const int ec = e < c ? e : c - 1;
+                    kr[u] = kk[ec];
+                    ir[u] = ii[ec];
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) put(e0 + 64 * u + lane < c && kr[u] >= lo, kr[u], ir[u]);
+                for (int u = 0; u < 8; ++u) put(e0 + 64 * u + lane < c && kr[u] >= lo, kr[u], ir[u]);
             }
         };
 #pragma unroll
