@@ -1148,37 +1148,46 @@ __global__ void __launch_bounds__(DSEL_NT) k_idx_split_select(IndexArgs a) {
     const uint32_t* ckr = a.cand_key + bq * a.sstride;
     const int32_t* cir = a.cand_idx + bq * a.sstride;
     const uint32_t* slots = a.hist + bq * (int64_t)a.nslices * SLOT_W;
-    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
-    const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
-    // Wave w compacts the contiguous slices [w q, w q + q) (q = ceil(nseg / 16)), so that
-    // its region, and the regions joined in wave order, keep entry order.
-    const int q = (nseg + NW - 1) / NW;
-    const int s_lo = wv * q, s_hi = s_lo + q < nseg ? s_lo + q : nseg;
+    // Wave w compacts the contiguous slices [w q, w q + q) (q = ceil(nseg / 16), nseg the
+    // slices with keys), so that its region, and the regions joined in wave order, keep
+    // entry order.
     // ---- prefetch: slice wv's list head and first 64 list entries (for the histogram),
-    // and the count and first SEL_PF candidates of slice s_lo (indices only where a key is
-    // present)
-    const bool lmine = wv < nseg && n > a.k;
-    const bool mine = s_lo < nseg && n > a.k;
+    // and the count and first SEL_PF candidates of slice s_lo.  Issued before the query's
+    // position arrives, for q as if every slice held keys (addresses clamped into the
+    // workspace rows; the values are masked by the counts later); issued again for the
+    // query's own q when that differs.
+    const int nsl = a.nslices;
     uint32_t lc = 0, le = 0, pk[NR];
     int32_t pi[NR];
     int cnt = 0;
-    if (lmine) {
-        const uint32_t* li = slots + (int64_t)wv * SLOT_W;
+    auto prefetch = [&](int q_) {
+        const int wl = wv < nsl ? wv : nsl - 1;
+        const uint32_t* li = slots + (int64_t)wl * SLOT_W;
         lc = li[0];
         le = li[1 + lane];                               // read within the slot (lists hold <= 2048 entries)
-    }
-    if (mine) cnt = a.seg_cnt[bq * a.nslices + s_lo];
-    {
-        const uint32_t* kk = ckr + (int64_t)s_lo * a.S;
-        const int32_t* ii = cir + (int64_t)s_lo * a.S;
-        const int64_t nsw = mine ? (n - (int64_t)s_lo * a.S < a.S ? n - (int64_t)s_lo * a.S : a.S) : 0;   // the slice's keys
+        const int sc = wv * q_ < nsl ? wv * q_ : nsl - 1;
+        cnt = a.seg_cnt[bq * nsl + sc];
+        const uint32_t* kk = ckr + (int64_t)sc * a.S;
+        const int32_t* ii = cir + (int64_t)sc * a.S;
+        const int64_t room = a.sstride - (int64_t)sc * a.S;   // the segment's entries inside the row
+        const int cap = (int)(room < a.S ? room : a.S);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int e = 64 * r + lane;
-            pk[r] = e < nsw ? kk[e] : 0u;                // within the slice's segment (entries < n)
-            pi[r] = e < nsw ? ii[e] : 0;
+            const int ec = e < cap ? e : cap - 1;
+            pk[r] = kk[ec];
+            pi[r] = ii[ec];
         }
-    }
+    };
+    const int q_all = (nsl + NW - 1) / NW;
+    prefetch(q_all);
+    const int64_t n = n_visible(a.q_pos[bq], a.m, a.n_cap);
+    const int nseg = (int)((n + a.S - 1) / a.S);         // slices with keys
+    const int q = (nseg + NW - 1) / NW;
+    const int s_lo = wv * q, s_hi = s_lo + q < nseg ? s_lo + q : nseg;
+    const bool lmine = wv < nseg && n > a.k;
+    const bool mine = s_lo < nseg && n > a.k;
+    if (q != q_all && n > a.k) prefetch(q);              // block-uniform
     if (n <= a.k) {
         take_all(a, bq, n, ckr, tid, DSEL_NT);
         return;
