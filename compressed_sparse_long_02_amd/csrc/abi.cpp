@@ -609,8 +609,15 @@ static int attend_impl(const char* fn, const void* q, int q_fmt, const void* kv_
             (pg ? (j.bt == pg->bt && j.bt_stride == pg->bt_stride && j.epb == pg->epb && j.blk_bytes == pg->blk_bytes &&
                    j.n_blocks == pg->n_blocks)
                 : (!j.bt && j.out_bstride == kvc_bstride));
+        // The split that attends the newest entry compresses it before its tiles; that pays
+        // only when the split has rows to spare: at a full context (the newest entry is row
+        // n_cap - 1) its split must hold at most half the rows of the others.
+        const int64_t se = n_cap > 0 ? (n_cap - 1) / rps : 0;
+        const int64_t l_all = n_cap + W;
+        const int64_t rows_e = (l_all < (se + 1) * rps ? l_all : (se + 1) * rps) - se * rps;
+        const bool slack = nsplit > 1 && 2 * rows_e <= rps;
         csl::AttendPre pre{j, 0};
-        if (same && csl::attend_takes_pre(a) && csl::compress_in_attend(j, pre.gz))
+        if (same && slack && csl::attend_takes_pre(a) && csl::compress_in_attend(j, pre.gz))
             return launched(csl::launch_attend(a, s, &pre));
         const hipError_t e = csl::launch_compress(j, s);
         if (e != hipSuccess) return launched(e);

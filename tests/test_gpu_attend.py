@@ -250,11 +250,13 @@ def test_hca_attend_step_compresses_before_it_attends(gpu):
     # hca_attend_step with one query per sequence compresses inside the attention kernel,
     # by the split whose rows hold the new entry, before that split copies any tile.  HCA
     # attends every complete entry, so a stale (cleared) new row would change the output.
+    # The kernel compresses only where the split holding the cache's last entry has rows to
+    # spare: N = 17000 plans 60 splits of 288 rows, the last one 136 (8 entries, the window).
     # Positions: entries completing at the cache's last row and mid-cache, a token that
     # completes nothing, and one whose entry lies past n_cap (not stored, not attended).
     from compressed_sparse_long_02_amd import decode as D
-    B, d, r, H, m, N, W, R = 4, 512, 64, 64, 128, 40, 128, 256
-    t = np.array([N * m - 1, 20 * m - 1, 30 * m + 5, 50 * m - 1], np.int32)
+    B, d, r, H, m, N, W, R = 4, 512, 64, 64, 128, 17000, 128, 256
+    t = np.array([N * m - 1, 20 * m - 1, 30 * m + 5, (N + 10) * m - 1], np.int32)
     q_pos = dev(torch.from_numpy(t[:, None].copy()))
     rb = ops.row_bytes(O.KV_PACKED, d, r)
     ring = D.Ring(dev(gen.bf16_bytes(gen.normal((B, R, d), 81))), dev(gen.random_logits((B, R, 1), 82)),
